@@ -1,0 +1,12 @@
+"""CPU fp64 oracle for causal scaled-dot-product attention.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py, never by the library.  See attention.py.
+"""
+from .attention import (  # noqa: F401
+    attention_backward,
+    attention_forward,
+    attention_head,
+    head_backward,
+    head_forward,
+)

@@ -1,0 +1,133 @@
+"""Plain fp64 CPU oracle for scaled-dot-product attention, forward and backward.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  The library
+never routes through it, and it shares no code with the GPU path.
+
+What it computes is the plain definition, written out with the full score matrix
+materialised per (batch, head).  The fused GPU method reaches the same result up
+to rounding order (the flash formulation is exact, see "Cooperative tensors,
+reductions, and building a fused attention kernel", §1 "Why cooperative tensors
+exist"), so the oracle is the definition, not the tiled algorithm:
+
+* scores, softmax and output: S = scale * Q K^T, P = softmax over each row of S,
+  O = P V  (same guide, §1; Forge RESEARCH.md §6 "Fused attention design",
+  where the scale multiplies Q K^T before the softmax);
+* causal mask: for query row i, key column j takes part only when j <= i, with
+  row and column in global coordinates (same guide, §5.3 causal-mask snippet and
+  §9 "the assembled kernel");
+* log-sum-exp: one value per query row, L_i = m_i + ln(l_i) with m_i the row
+  maximum and l_i the sum of exp(s_ij - m_i), natural log, in the scaled score
+  domain (Forge RESEARCH.md §6, the quantity the forward saves for backward);
+* backward: with upstream gradient dO, dV = P^T dO, dP = dO V^T,
+  delta_i = sum_j P_ij dP_ij, dS = P o (dP - delta), dQ = scale * dS K,
+  dK = scale * dS^T Q  (Forge RESEARCH.md §6, the dQ / dK-dV pass description
+  with P recomputed from L, and the "D term" paragraph; the chain rule through
+  softmax).
+
+All arithmetic is float64.  Inputs are widened exactly from the float32 values
+the GPU consumes (bf16 inputs are bf16-exact float32 values).  Masked entries are
+excluded exactly: they contribute 0 to every sum, which is what a finite mask
+value on the GPU reaches whenever a row has at least one visible key (always
+true for causal self-attention: key i is visible to query i).
+
+Parity status: pinned.  Each function here is checked in tests/test_oracle_pins.py
+against closed forms, invariants, central finite differences, torch's float64
+scaled_dot_product_attention on tiny shapes, and the one numeric cell the pages
+print (Rigel §6, the 455.9375 accumulator probe).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "head_forward",
+    "head_backward",
+    "attention_forward",
+    "attention_backward",
+    "attention_head",
+]
+
+
+def _visible(S: int, causal: bool) -> np.ndarray:
+    """Boolean [S, S] matrix: True where query i may attend key j (j <= i if causal)."""
+    if not causal:
+        return np.ones((S, S), dtype=bool)
+    i = np.arange(S)[:, None]
+    j = np.arange(S)[None, :]
+    return j <= i
+
+
+def _probabilities(q, k, scale, causal):
+    """Scores, visibility, row max, row LSE and P for one head (all float64)."""
+    S = q.shape[0]
+    s = scale * (q @ k.T)
+    vis = _visible(S, causal)
+    s_vis = np.where(vis, s, -np.inf)
+    m = s_vis.max(axis=1)  # finite: every row has >= 1 visible key
+    e = np.where(vis, np.exp(s - m[:, None]), 0.0)
+    l = e.sum(axis=1)
+    lse = m + np.log(l)
+    p = np.where(vis, np.exp(s - lse[:, None]), 0.0)
+    return s, vis, lse, p
+
+
+def head_forward(q, k, v, scale: float, causal: bool = True):
+    """One head: q [S, D], k [S, D], v [S, Dv] -> (o [S, Dv], lse [S]), float64."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    _, _, lse, p = _probabilities(q, k, scale, causal)
+    o = p @ v
+    return o, lse
+
+
+def head_backward(q, k, v, do, scale: float, causal: bool = True):
+    """One head: gradients of sum(dO * O) -> (dq, dk, dv), plus (o, lse), float64."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    _, _, lse, p = _probabilities(q, k, scale, causal)
+    o = p @ v
+    dv = p.T @ do
+    dp = do @ v.T
+    delta = (p * dp).sum(axis=1)
+    ds = p * (dp - delta[:, None])
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv, o, lse
+
+
+def attention_head(q, k, v, do, scale: float, causal: bool = True) -> dict:
+    """All five outputs of one head as a dict (o, lse, dq, dk, dv)."""
+    dq, dk, dv, o, lse = head_backward(q, k, v, do, scale, causal)
+    return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+
+
+def _heads(x):
+    B, H = x.shape[:2]
+    for b in range(B):
+        for h in range(H):
+            yield b, h
+
+
+def attention_forward(q, k, v, scale: float, causal: bool = True):
+    """[B, H, S, D] inputs -> (o [B, H, S, D], lse [B, H, S]), float64, head by head."""
+    B, H, S, _ = q.shape
+    o = np.empty(v.shape, dtype=np.float64)
+    lse = np.empty((B, H, S), dtype=np.float64)
+    for b, h in _heads(q):
+        o[b, h], lse[b, h] = head_forward(q[b, h], k[b, h], v[b, h], scale, causal)
+    return o, lse
+
+
+def attention_backward(q, k, v, do, scale: float, causal: bool = True):
+    """[B, H, S, D] inputs -> (dq, dk, dv), float64, head by head."""
+    dq = np.empty(q.shape, dtype=np.float64)
+    dk = np.empty(k.shape, dtype=np.float64)
+    dv = np.empty(v.shape, dtype=np.float64)
+    for b, h in _heads(q):
+        dq[b, h], dk[b, h], dv[b, h], _, _ = head_backward(
+            q[b, h], k[b, h], v[b, h], do[b, h], scale, causal)
+    return dq, dk, dv

@@ -1,0 +1,130 @@
+"""Seeded synthetic inputs for causal attention: Q, K, V and the upstream gradient dO.
+
+This module is shared by the oracle side and the GPU side of every test and of the
+bench.  It holds no attention arithmetic, only random draws and the float32 ->
+bfloat16 rounding that turns a draw into a bf16 tensor.
+
+Draw recipe (one recipe for every workload):
+
+* one numpy ``PCG64(seed)`` generator per call;
+* float32 standard normals drawn in the order Q, K, V, dO, each of shape [B, H, S, D];
+* each draw multiplied by its standard deviation in float32;
+* for bf16 workloads, every value rounded to the nearest bfloat16, ties to even.
+
+The returned arrays are float32 holding exactly the values the GPU consumes, so
+the oracle and the GPU path read identical numbers.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+__all__ = [
+    "Workload",
+    "WORKLOADS",
+    "make_inputs",
+    "f32_to_bf16_bits",
+    "bf16_bits_to_f32",
+    "round_to_bf16",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One attention workload: shape, input dtype and the draw scales."""
+
+    name: str
+    B: int
+    H: int
+    S: int
+    D: int
+    dtype: str  # "f32" or "bf16"
+    sigma_qk: float = 1.0
+    sigma_v: float = 1.0
+    sigma_do: float = 1.0
+    causal: bool = True
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def flops(self) -> float:
+        """Algorithmic fwd+bwd FLOPs, 7*B*H*S^2*D for causal (half of dense)."""
+        dense = 14.0 * self.B * self.H * self.S * self.S * self.D
+        return dense / 2.0 if self.causal else dense
+
+    @property
+    def fwd_flops(self) -> float:
+        dense = 4.0 * self.B * self.H * self.S * self.S * self.D
+        return dense / 2.0 if self.causal else dense
+
+    @property
+    def bwd_flops(self) -> float:
+        return self.flops - self.fwd_flops
+
+    def with_shape(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads the library is measured and checked on.
+WORKLOADS = {
+    "tiny_f32": Workload("tiny_f32", 1, 4, 128, 64, "f32", 1.0, 1.0, 1.0),
+    "gpt12m_bf16": Workload("gpt12m_bf16", 8, 6, 256, 64, "bf16", 1.0, 1.0, 0.1),
+    "gpt125m_bf16": Workload("gpt125m_bf16", 8, 12, 1024, 64, "bf16", 1.0, 1.0, 0.1),
+    "gpt205m_bf16": Workload("gpt205m_bf16", 4, 16, 2048, 64, "bf16", 1.0, 1.0, 0.1),
+    "long8191_bf16": Workload("long8191_bf16", 1, 16, 8191, 128, "bf16", 4.0, 1.0, 0.1),
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return the uint16 bit patterns.
+
+    NaN stays NaN (quiet); infinities stay infinite; values beyond the bf16 range
+    round to infinity as IEEE rounding prescribes.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    rounded = (u + 0x7FFF + lsb) >> 16
+    nan = np.isnan(x)
+    out = rounded.astype(np.uint16)
+    if nan.any():
+        out = np.where(nan, ((u >> 16) | 0x40).astype(np.uint16), out)
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns to float32 (exact)."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """float32 -> nearest bfloat16 value, returned as float32."""
+    return bf16_bits_to_f32(f32_to_bf16_bits(x))
+
+
+def make_inputs(w: Workload, seed: int = 0) -> dict:
+    """Draw Q, K, V, dO for workload ``w`` from ``PCG64(seed)``.
+
+    Returns a dict with float32 arrays ``q, k, v, do`` of shape [B, H, S, D]
+    (bf16-exact for bf16 workloads) and, for bf16 workloads, their uint16 bit
+    patterns under ``q_bits, k_bits, v_bits, do_bits``.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shape = (w.B, w.H, w.S, w.D)
+    out = {}
+    for name, sigma in (("q", w.sigma_qk), ("k", w.sigma_qk), ("v", w.sigma_v), ("do", w.sigma_do)):
+        x = rng.standard_normal(size=shape, dtype=np.float32)
+        x *= np.float32(sigma)
+        if w.dtype == "bf16":
+            bits = f32_to_bf16_bits(x)
+            out[name + "_bits"] = bits
+            x = bf16_bits_to_f32(bits)
+        elif w.dtype != "f32":
+            raise ValueError(f"unknown dtype {w.dtype!r}")
+        out[name] = x
+    return out

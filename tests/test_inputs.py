@@ -1,0 +1,70 @@
+"""Seeded generator: determinism, bf16 rounding, draw scales."""
+import numpy as np
+import pytest
+
+import seeded_inputs as si
+
+
+def test_same_seed_same_bytes():
+    w = si.WORKLOADS["gpt12m_bf16"].with_shape(B=1, H=2, S=64)
+    a = si.make_inputs(w, seed=0)
+    b = si.make_inputs(w, seed=0)
+    c = si.make_inputs(w, seed=1)
+    for n in ("q", "k", "v", "do"):
+        assert a[n].tobytes() == b[n].tobytes()
+        assert a[n + "_bits"].tobytes() == b[n + "_bits"].tobytes()
+        assert a[n].tobytes() != c[n].tobytes()
+
+
+def test_bf16_round_to_nearest_even_ties():
+    # 1 + 2^-8 lies exactly halfway between bf16 neighbours 1 and 1 + 2^-7:
+    # the tie goes to the even mantissa (1.0).
+    x = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8),
+                  1.0 + 2.0 ** -8 + 2.0 ** -20, 65504.0, 0.0, -0.0], dtype=np.float32)
+    r = si.round_to_bf16(x)
+    assert r[0] == 1.0
+    assert r[1] == 1.0 + 2.0 ** -6  # tie between 1+2^-7 (odd) and 1+2^-6 (even)
+    assert r[2] == -1.0
+    assert r[3] == 1.0 + 2.0 ** -7  # above the tie rounds up
+    assert r[4] == 65536.0
+    assert r[5] == 0.0 and not np.signbit(r[5])
+    assert r[6] == 0.0 and np.signbit(r[6])
+
+
+def test_bf16_special_values():
+    x = np.array([np.inf, -np.inf, np.nan, 3.4e38], dtype=np.float32)
+    r = si.round_to_bf16(x)
+    assert r[0] == np.inf and r[1] == -np.inf and np.isnan(r[2])
+    assert r[3] == np.inf  # beyond the largest finite bf16
+
+
+def test_bf16_matches_torch_conversion():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(100000) * np.exp(rng.uniform(-20, 20, 100000))).astype(np.float32)
+    ours = si.f32_to_bf16_bits(x)
+    theirs = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, theirs)
+
+
+def test_values_are_bf16_exact_and_scaled():
+    w = si.WORKLOADS["long8191_bf16"].with_shape(S=512)
+    x = si.make_inputs(w, seed=0)
+    for n, sigma in (("q", 4.0), ("k", 4.0), ("v", 1.0), ("do", 0.1)):
+        np.testing.assert_array_equal(si.round_to_bf16(x[n]), x[n])
+        assert abs(x[n].std() / sigma - 1.0) < 0.01
+        assert abs(x[n].mean()) < 0.01 * sigma
+
+
+def test_f32_workload_untouched():
+    w = si.WORKLOADS["tiny_f32"]
+    x = si.make_inputs(w, seed=0)
+    assert "q_bits" not in x
+    rng = np.random.Generator(np.random.PCG64(0))
+    np.testing.assert_array_equal(x["q"], rng.standard_normal((1, 4, 128, 64), dtype=np.float32))
+
+
+def test_flop_convention():
+    w = si.WORKLOADS["gpt205m_bf16"]
+    assert w.flops == pytest.approx(120.26e9, rel=1e-3)
+    assert w.fwd_flops == pytest.approx(34.36e9, rel=1e-3)

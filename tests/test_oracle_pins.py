@@ -1,0 +1,301 @@
+"""Pins for the fp64 oracle: checks against things other than the oracle itself.
+
+Each test is chosen so that a plausible slip in the oracle (a dropped scale, a
+mask off by one, a transposed operand, a wrong sign in the softmax backward, a
+log2-vs-ln LSE, a missing delta term) fails at least one of them:
+
+* closed forms: one token; identical keys (uniform attention -> running mean of
+  V, LSE = scale*q.k + ln(count)); constant V; zero upstream gradient;
+* invariants: P rows sum to 1 and vanish above the diagonal (read out through
+  V = identity); O_0 = V_0 and dQ_0 = 0; causality; sum_j dK_j = 0;
+  sum_j dV_j = sum_i dO_i; dV of the last key; shift invariance of the keys;
+  head permutation;
+* central finite differences of L = sum(dO * O) in float64;
+* torch's float64 scaled_dot_product_attention with autograd (a library
+  routine the attention guide's Core AI section uses as the definition) on
+  tiny shapes;
+* the one numeric cell the pages print: Rigel §6's accumulator-width probe,
+  448 + 127 * 0.0625 = 455.9375 (tests/golden/accumulator_width.json).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import attention_backward, attention_forward, attention_head, head_backward, head_forward
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(rng, *shape, sigma=1.0):
+    return rng.standard_normal(shape) * sigma
+
+
+# ---------------------------------------------------------------- closed forms
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_single_token(causal):
+    rng = np.random.default_rng(1)
+    q, k, v, do = (_rand(rng, 1, 7) for _ in range(4))
+    scale = 0.37
+    r = attention_head(q, k, v, do, scale, causal)
+    np.testing.assert_array_equal(r["o"], v)
+    assert r["lse"][0] == pytest.approx(scale * float(q[0] @ k[0]), abs=1e-14)
+    np.testing.assert_allclose(r["dq"], 0.0, atol=1e-15)
+    np.testing.assert_allclose(r["dk"], 0.0, atol=1e-15)
+    np.testing.assert_allclose(r["dv"], do, atol=1e-15)
+
+
+def test_identical_keys_causal_is_running_mean():
+    rng = np.random.default_rng(2)
+    S, D = 11, 5
+    q = _rand(rng, S, D)
+    krow = _rand(rng, D)
+    k = np.tile(krow, (S, 1))
+    v = _rand(rng, S, 3)
+    scale = 0.8
+    o, lse = head_forward(q, k, v, scale, causal=True)
+    counts = np.arange(1, S + 1)
+    running_mean = np.cumsum(v, axis=0) / counts[:, None]
+    np.testing.assert_allclose(o, running_mean, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(lse, scale * (q @ krow) + np.log(counts), rtol=1e-13, atol=1e-13)
+
+
+def test_identical_keys_dense_is_mean():
+    rng = np.random.default_rng(3)
+    S, D = 9, 4
+    q = _rand(rng, S, D)
+    krow = _rand(rng, D)
+    k = np.tile(krow, (S, 1))
+    v = _rand(rng, S, D)
+    o, lse = head_forward(q, k, v, 1.3, causal=False)
+    np.testing.assert_allclose(o, np.tile(v.mean(axis=0), (S, 1)), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(lse, 1.3 * (q @ krow) + np.log(S), rtol=1e-13, atol=1e-13)
+
+
+def test_zero_queries_uniform_attention():
+    rng = np.random.default_rng(4)
+    S, D = 8, 6
+    q = np.zeros((S, D))
+    k, v = _rand(rng, S, D), _rand(rng, S, D)
+    o, lse = head_forward(q, k, v, 0.5, causal=True)
+    counts = np.arange(1, S + 1)
+    np.testing.assert_allclose(o, np.cumsum(v, axis=0) / counts[:, None], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse, np.log(counts), rtol=1e-14, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_constant_values_give_zero_qk_gradients(causal):
+    rng = np.random.default_rng(5)
+    S, D = 10, 6
+    q, k, do = _rand(rng, S, D), _rand(rng, S, D), _rand(rng, S, D)
+    c = _rand(rng, D)
+    v = np.tile(c, (S, 1))
+    r = attention_head(q, k, v, do, 0.4, causal)
+    np.testing.assert_allclose(r["o"], v, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(r["dq"], 0.0, atol=1e-13)
+    np.testing.assert_allclose(r["dk"], 0.0, atol=1e-13)
+
+
+def test_zero_upstream_gradient():
+    rng = np.random.default_rng(6)
+    q, k, v = (_rand(rng, 7, 4) for _ in range(3))
+    r = attention_head(q, k, v, np.zeros((7, 4)), 0.5, True)
+    for name in ("dq", "dk", "dv"):
+        np.testing.assert_array_equal(r[name], 0.0)
+
+
+# ----------------------------------------------------------------- invariants
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_probabilities_via_identity_values(causal):
+    """With V = I the output is P itself: rows sum to 1, zero above the diagonal."""
+    rng = np.random.default_rng(7)
+    S, D = 13, 5
+    q, k = _rand(rng, S, D, sigma=2.0), _rand(rng, S, D, sigma=2.0)
+    p, lse = head_forward(q, k, np.eye(S), 0.6, causal)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-12)
+    assert (p >= 0).all()
+    if causal:
+        assert (p[np.triu_indices(S, 1)] == 0.0).all()
+        assert (np.diag(p) > 0).all()
+    # softmax definition, entry by entry, against the returned LSE
+    s = 0.6 * q @ k.T
+    for i in range(S):
+        for j in range(S):
+            if causal and j > i:
+                continue
+            assert p[i, j] == pytest.approx(np.exp(s[i, j] - lse[i]), rel=1e-12)
+
+
+def test_first_row_and_first_query_gradient():
+    rng = np.random.default_rng(8)
+    S, D = 12, 8
+    q, k, v, do = (_rand(rng, S, D) for _ in range(4))
+    r = attention_head(q, k, v, do, 0.35, True)
+    np.testing.assert_array_equal(r["o"][0], v[0])
+    np.testing.assert_allclose(r["dq"][0], 0.0, atol=1e-15)
+
+
+def test_causality_future_keys_do_not_leak():
+    rng = np.random.default_rng(9)
+    S, D, cut = 16, 8, 6
+    q, k, v, do = (_rand(rng, S, D) for _ in range(4))
+    o1, lse1 = head_forward(q, k, v, 0.3, True)
+    k2, v2 = k.copy(), v.copy()
+    k2[cut + 1:] = _rand(rng, S - cut - 1, D, sigma=5.0)
+    v2[cut + 1:] = _rand(rng, S - cut - 1, D, sigma=5.0)
+    o2, lse2 = head_forward(q, k2, v2, 0.3, True)
+    np.testing.assert_array_equal(o1[: cut + 1], o2[: cut + 1])
+    np.testing.assert_array_equal(lse1[: cut + 1], lse2[: cut + 1])
+    assert not np.allclose(o1[cut + 1:], o2[cut + 1:])
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_gradient_sums(causal):
+    rng = np.random.default_rng(10)
+    S, D = 17, 6
+    q, k, v, do = (_rand(rng, S, D) for _ in range(4))
+    r = attention_head(q, k, v, do, 0.45, causal)
+    # each row of dS sums to zero, so the key gradients sum to zero
+    np.testing.assert_allclose(r["dk"].sum(axis=0), 0.0, atol=1e-12)
+    # each row of P sums to one, so the value gradients sum to the upstream sum
+    np.testing.assert_allclose(r["dv"].sum(axis=0), do.sum(axis=0), atol=1e-12)
+    # delta_i = dO_i . O_i equals sum_j P_ij dP_ij (P read out via V = I)
+    p, _ = head_forward(q, k, np.eye(S), 0.45, causal)
+    dp = do @ v.T
+    np.testing.assert_allclose((p * dp).sum(axis=1), (do * r["o"]).sum(axis=1), rtol=1e-12, atol=1e-12)
+
+
+def test_last_key_gradient():
+    rng = np.random.default_rng(11)
+    S, D = 9, 5
+    q, k, v, do = (_rand(rng, S, D) for _ in range(4))
+    r = attention_head(q, k, v, do, 0.5, True)
+    p, _ = head_forward(q, k, np.eye(S), 0.5, True)
+    np.testing.assert_allclose(r["dv"][S - 1], p[S - 1, S - 1] * do[S - 1], rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_key_shift_invariance(causal):
+    rng = np.random.default_rng(12)
+    S, D, scale = 14, 7, 0.42
+    q, k, v, do = (_rand(rng, S, D) for _ in range(4))
+    u = _rand(rng, D)
+    a = attention_head(q, k, v, do, scale, causal)
+    b = attention_head(q, k + u, v, do, scale, causal)
+    for name in ("o", "dq", "dk", "dv"):
+        np.testing.assert_allclose(b[name], a[name], rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(b["lse"], a["lse"] + scale * (q @ u), rtol=1e-12, atol=1e-12)
+
+
+def test_batched_matches_per_head_and_heads_permute():
+    rng = np.random.default_rng(13)
+    B, H, S, D = 2, 3, 10, 4
+    q, k, v, do = (_rand(rng, B, H, S, D) for _ in range(4))
+    o, lse = attention_forward(q, k, v, 0.5, True)
+    dq, dk, dv = attention_backward(q, k, v, do, 0.5, True)
+    for b in range(B):
+        for h in range(H):
+            r = attention_head(q[b, h], k[b, h], v[b, h], do[b, h], 0.5, True)
+            np.testing.assert_array_equal(o[b, h], r["o"])
+            np.testing.assert_array_equal(lse[b, h], r["lse"])
+            np.testing.assert_array_equal(dq[b, h], r["dq"])
+            np.testing.assert_array_equal(dk[b, h], r["dk"])
+            np.testing.assert_array_equal(dv[b, h], r["dv"])
+    perm = [2, 0, 1]
+    o2, lse2 = attention_forward(q[:, perm], k[:, perm], v[:, perm], 0.5, True)
+    np.testing.assert_array_equal(o2, o[:, perm])
+    np.testing.assert_array_equal(lse2, lse[:, perm])
+
+
+# ------------------------------------------------------- finite differences
+
+
+def _loss(q, k, v, do, scale, causal):
+    o, _ = head_forward(q, k, v, scale, causal)
+    return float((do * o).sum())
+
+
+@pytest.mark.parametrize("S,D", [(5, 3), (9, 8)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_central_finite_differences(S, D, causal):
+    rng = np.random.default_rng(100 + S + D)
+    scale = 1.0 / np.sqrt(D)
+    q, k, v, do = (_rand(rng, S, D) for _ in range(4))
+    dq, dk, dv, _, _ = head_backward(q, k, v, do, scale, causal)
+    h = 1e-5
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + h
+            lp = _loss(q, k, v, do, scale, causal)
+            x[idx] = old - h
+            lm = _loss(q, k, v, do, scale, causal)
+            x[idx] = old
+            fd[idx] = (lp - lm) / (2 * h)
+        err = np.abs(fd - g).max() / max(np.abs(g).max(), 1e-300)
+        assert err <= 1e-6, (name, err)
+
+
+def test_lse_gradient_finite_difference():
+    """d LSE_i / d q_i = scale * sum_j P_ij k_j: pins LSE as a natural-log log-sum-exp."""
+    rng = np.random.default_rng(14)
+    S, D, scale = 6, 4, 0.7
+    q, k = _rand(rng, S, D), _rand(rng, S, D)
+    p, lse = head_forward(q, k, np.eye(S), scale, True)
+    i, h = 4, 1e-6
+    for d in range(D):
+        qp, qm = q.copy(), q.copy()
+        qp[i, d] += h
+        qm[i, d] -= h
+        _, lp = head_forward(qp, k, np.eye(S), scale, True)
+        _, lm = head_forward(qm, k, np.eye(S), scale, True)
+        fd = (lp[i] - lm[i]) / (2 * h)
+        assert fd == pytest.approx(scale * float(p[i] @ k[:, d]), rel=1e-7, abs=1e-9)
+
+
+# ---------------------------------------------------------- library routine
+
+
+@pytest.mark.parametrize("S,D", [(1, 8), (7, 4), (33, 16)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_against_torch_sdpa_float64(S, D, causal):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(200 + S)
+    B, H = 2, 3
+    scale = 1.0 / np.sqrt(D)
+    q, k, v, do = (_rand(rng, B, H, S, D) for _ in range(4))
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+    to.backward(torch.tensor(do, dtype=torch.float64))
+    o, lse = attention_forward(q, k, v, scale, causal)
+    dq, dk, dv = attention_backward(q, k, v, do, scale, causal)
+    np.testing.assert_allclose(o, to.detach().numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-10, atol=1e-12)
+    scores = scale * torch.tensor(q) @ torch.tensor(k).transpose(-1, -2)
+    if causal:
+        scores = scores.masked_fill(torch.ones(S, S, dtype=torch.bool).triu(1), float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(scores, dim=-1).numpy(), rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------- printed numeric cell
+
+
+def test_accumulator_width_cell():
+    with open(os.path.join(GOLDEN, "accumulator_width.json")) as f:
+        g = json.load(f)
+    D = g["D"]
+    q = np.full((1, D), g["q"]["rest"])
+    q[0, 0] = g["q"]["first"]
+    k = np.full((1, D), g["k"]["rest"])
+    k[0, 0] = g["k"]["first"]
+    o, lse = head_forward(q, k, np.ones((1, 2)), g["scale"], True)
+    assert lse[0] == g["lse"]  # exact: every term and partial sum is a dyadic rational
+    assert g["lse_with_narrow_accumulator"] != g["lse"]
