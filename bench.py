@@ -1,0 +1,263 @@
+"""Forward + backward causal attention throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step = attn_fwd + attn_bwd (delta preprocess, dK/dV pass, dQ pass) over one
+batch of synthetic inputs already resident in HBM.  Prints ONE JSON line:
+forward+backward TFLOP/s under the 7*B*H*S^2*D causal convention, the roofline
+of the dominant kernel (algorithmic FLOPs / its average HIP-event duration over a
+timed pass), and the fp64 CPU oracle timed on a bounded sample of the same
+workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import seeded_inputs as si  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
+PEAK_F32_TFLOPS = 157.3    # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gpt205m_bf16", choices=sorted(si.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="only run this many fwd+bwd steps and exit (for rocprofv3), no JSON")
+    return ap.parse_args()
+
+
+def kernel_units(w):
+    """Algorithmic work per launch of each kernel.
+
+    One 'GEMM unit' is one S x S x D contraction over the visible (causal) half:
+    B*H*S^2*D FLOPs (2 FLOPs per multiply-add, halved by causality).  The
+    forward does 2 units (QK^T, PV); the backward's 5 units are S, dP, dV, dK in
+    the dK/dV pass and dQ in the dQ pass (the dQ pass's recomputed S and dP are
+    not algorithmic work).
+    """
+    unit = w.B * w.H * w.S * w.S * w.D * (1.0 if w.causal else 2.0)
+    elem = 2 if w.dtype == "bf16" else 4
+    tensor = w.B * w.H * w.S * w.D * elem
+    rows = w.B * w.H * w.S * 4
+    return {
+        "fwd": {"flops": 2 * unit, "bytes": 3 * tensor + tensor + rows},
+        "bwd_preprocess": {"flops": 0.0, "bytes": 2 * tensor + rows},
+        "bwd_dkdv": {"flops": 4 * unit, "bytes": 4 * tensor + 2 * rows + 2 * tensor},
+        "bwd_dq": {"flops": 1 * unit, "bytes": 4 * tensor + 2 * rows + tensor},
+    }
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it still matches the kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    import hashlib
+    text = open(TRAFFIC_FILE).read()
+    m = re.search(rf"^{re.escape(kernel)}\s+{re.escape(workload)}\s+(\S+)\s+(\S+)\s+(\S+)\s*$", text, flags=re.M)
+    if not m:
+        return None
+    src_hash, fetch_b, write_b = m.group(1), float(m.group(2)), float(m.group(3))
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "causal_attention_flash_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    if h.hexdigest()[:16] != src_hash:
+        return None
+    return fetch_b + write_b
+
+
+def cpu_baseline(w, x, target_s: float):
+    """Time the fp64 oracle (fwd + bwd, head by head) on a bounded sample of the workload."""
+    from oracle import attention_head
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        cores = os.cpu_count() or 1
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    per_head = w.flops / len(heads)
+    done = 0
+    t0 = time.perf_counter()
+    for b, h in heads:
+        attention_head(x["q"][b, h], x["k"][b, h], x["v"][b, h], x["do"][b, h], w.scale, w.causal)
+        done += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(done * per_head / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{done} of {len(heads)} heads (S={w.S}, D={w.D}), fwd+bwd in fp64, {dt:.1f} s",
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(every (batch, head) is independent; see the sharding note in the design). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import causal_attention_flash_amd as caf
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    caf.load_library()
+    dev = torch.device("cuda:0")
+    w = si.WORKLOADS[args.workload]
+    x = si.make_inputs(w, seed=0)
+
+    def dev_t(name):
+        if w.dtype == "bf16":
+            return torch.from_numpy(x[name + "_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x[name]).to(dev)
+
+    q, k, v, do = (dev_t(n) for n in ("q", "k", "v", "do"))
+    B, H, S, D = q.shape
+    dt = caf.ATTN_BF16 if w.dtype == "bf16" else caf.ATTN_F32
+    causal = int(w.causal)
+    scale = w.scale
+    bd = caf._binding
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    nws = bd.c_attn_bwd_workspace_bytes(B, H, S, D, dt)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    P = {n: t.data_ptr() for n, t in dict(q=q, k=k, v=v, o=o, lse=lse, do=do, dq=dq, dk=dk, dv=dv, ws=ws).items()}
+
+    def chk(st, where):
+        if st != 0:
+            raise caf.AttnError(st, where)
+
+    def fwd():
+        chk(bd.c_attn_fwd(P["q"], P["k"], P["v"], P["o"], P["lse"], B, H, S, D, scale, causal, dt, stream), "fwd")
+
+    def bwd():
+        chk(bd.c_attn_bwd(P["q"], P["k"], P["v"], P["o"], P["do"], P["lse"], P["dq"], P["dk"], P["dv"], P["ws"],
+                          nws, B, H, S, D, scale, causal, dt, stream), "bwd")
+
+    def pre():
+        chk(bd.c_attn_bwd_preprocess(P["o"], P["do"], P["ws"], B, H, S, D, dt, stream), "pre")
+
+    def dkdv():
+        chk(bd.c_attn_bwd_dkdv(P["q"], P["k"], P["v"], P["do"], P["lse"], P["ws"], P["dk"], P["dv"], B, H, S, D,
+                               scale, causal, dt, stream), "dkdv")
+
+    def dqk():
+        chk(bd.c_attn_bwd_dq(P["q"], P["k"], P["v"], P["do"], P["lse"], P["ws"], P["dq"], B, H, S, D, scale,
+                             causal, dt, stream), "dq")
+
+    if args.profile_steps:
+        for i in range(args.profile_steps):
+            fwd()
+            bwd()
+        torch.cuda.synchronize()
+        print(f"profile run: {args.profile_steps} steps of {w.name} done", flush=True)
+        return
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps of fwd + bwd
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        fwd()
+        bwd()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = gpu_ms / args.steps
+
+    # ---- per-kernel durations: the same K steps, each kernel bracketed by events
+    names = ("fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq")
+    calls = (fwd, pre, dkdv, dqk)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        evs[i][0].record()
+        for j, fn in enumerate(calls):
+            fn()
+            evs[i][j + 1].record()
+    torch.cuda.synchronize()
+    durations = {n: [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]
+                 for j, n in enumerate(names)}
+    per_kernel = {n: statistics.median(d) for n, d in durations.items()}
+    per_kernel_mean = {n: sum(d) / len(d) for n, d in durations.items()}
+
+    units = kernel_units(w)
+    dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: per_kernel_mean[n])
+    dom_ms = per_kernel_mean[dom]
+    mfma_peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    achieved = units[dom]["flops"] / (dom_ms * 1e-3) / 1e12
+    traffic = read_traffic(dom, w.name)
+
+    value = w.flops * args.steps / (gpu_ms * 1e-3) / 1e12
+    result = {
+        "metric": "causal attention fwd+bwd TFLOP/s (bf16) on 1 GPU; % of MFMA peak",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "D": w.D, "causal": bool(w.causal),
+                   "global_batch": w.B, "seq_len": w.S, "parallelism": "none (1 GPU)"},
+        "pct_of_mfma_peak": round(100.0 * value / mfma_peak, 3),
+        "wall_s_timed": round(wall, 4),
+        "kernel_ms": {n: round(per_kernel_mean[n], 5) for n in names},
+        "kernel_ms_median": {n: round(per_kernel[n], 5) for n in names},
+        "roofline": {
+            "kernel": dom,
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": mfma_peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / mfma_peak, 5),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

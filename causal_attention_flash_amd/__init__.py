@@ -1,0 +1,24 @@
+"""Fused causal scaled-dot-product attention for AMD Instinct MI355X (gfx950).
+
+Python binding of the C ABI in include/attn.h (libcausal_attn.so, hand-written
+HIP kernels).  The binding marshals torch tensors to pointers and the current
+stream; all computation runs in the library's kernels.
+
+    o, lse = attn_fwd(q, k, v, scale=None, causal=True)
+    dq, dk, dv = attn_bwd(q, k, v, o, do, lse, scale=None, causal=True)
+"""
+from ._binding import (  # noqa: F401
+    ATTN_BF16,
+    ATTN_F32,
+    LIB_PATH,
+    SIGNATURES,
+    STATUS_NAMES,
+    AttnError,
+    attn_bwd,
+    attn_bwd_dkdv,
+    attn_bwd_dq,
+    attn_bwd_preprocess,
+    attn_fwd,
+    load_library,
+    status_string,
+)

@@ -1,0 +1,258 @@
+// C ABI of libcausal_attn.so: argument validation, then kernel launches on the
+// caller's stream.  The declarations and the contract are in include/attn.h.
+//
+// Validation happens before anything is enqueued: unsupported combinations are
+// rejected loudly rather than run wrong (Iron "Kernel Engineering Guide", §2.5
+// on selectors), and argument kinds and counts are checked up front, before any
+// work (the TorchMetalKernel checks in "Cooperative tensors, reductions, and
+// building a fused attention kernel", §12).
+// Any combination outside the supported set returns a status; there is no
+// fallback path.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/attn.h"
+#include "attn_launch.h"
+
+namespace {
+
+using attn::LaunchArgs;
+
+struct Span {
+    const void* p;
+    size_t bytes;
+};
+
+bool overlaps(const Span& a, const Span& b) {
+    if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_bytes(attn_dtype dt) { return dt == ATTN_BF16 ? 2 : 4; }
+
+// Sizes, D, dtype.  Sets *empty when there is nothing to compute.
+attn_status check_shape(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, bool* empty) {
+    if (B < 0 || H < 0 || S < 0 || D < 0) return ATTN_ERR_SHAPE;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    *empty = (B == 0 || H == 0 || S == 0);
+    if (*empty) return ATTN_OK;
+    // B*H*S < 2^31 and S*D < 2^31, checked without overflow.
+    const int64_t lim = (int64_t)INT32_MAX;
+    if (B > lim || H > lim || S > lim) return ATTN_ERR_SHAPE;
+    if (B * H > lim || B * H * S > lim) return ATTN_ERR_SHAPE;
+    if (S * D > lim) return ATTN_ERR_SHAPE;
+    return ATTN_OK;
+}
+
+attn_status check_scale_causal(float scale, int causal) {
+    if (causal != 0 && causal != 1) return ATTN_ERR_UNSUPPORTED;
+    if (!(scale > 0.f) || !isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
+    return ATTN_OK;
+}
+
+attn_status check_ptrs(std::initializer_list<const void*> ps) {
+    for (const void* p : ps)
+        if (!p) return ATTN_ERR_NULL;
+    for (const void* p : ps)
+        if (!aligned16(p)) return ATTN_ERR_ALIGNMENT;
+    return ATTN_OK;
+}
+
+attn_status check_alias(std::initializer_list<Span> outs, std::initializer_list<Span> ins) {
+    for (auto o = outs.begin(); o != outs.end(); ++o) {
+        for (const Span& i : ins)
+            if (overlaps(*o, i)) return ATTN_ERR_ALIAS;
+        for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+            if (overlaps(*o, *o2)) return ATTN_ERR_ALIAS;
+    }
+    return ATTN_OK;
+}
+
+attn_status from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+struct Sizes {
+    size_t tensor;  // bytes of one [B,H,S,D] tensor
+    size_t rows;    // bytes of one [B,H,S] fp32 vector
+};
+
+Sizes sizes(int64_t B, int64_t H, int64_t S, int64_t D, attn_dtype dt) {
+    const size_t n = (size_t)B * (size_t)H * (size_t)S;
+    return {n * (size_t)D * (size_t)elem_bytes(dt), n * sizeof(float)};
+}
+
+LaunchArgs base_args(int64_t B, int64_t H, int64_t S, int64_t D, float scale, int causal, void* stream) {
+    LaunchArgs a;
+    a.BH = B * H;
+    a.S = S;
+    a.D = D;
+    a.scale = scale;
+    a.causal = causal;
+    a.stream = (hipStream_t)stream;
+    return a;
+}
+
+attn_status run_preprocess(LaunchArgs a, attn_dtype dt) {
+    return from_hip(attn::launch_bwd_preprocess(a, elem_bytes(dt)));
+}
+attn_status run_dkdv(const LaunchArgs& a, attn_dtype dt) {
+    return from_hip(dt == ATTN_BF16 ? attn::launch_bwd_dkdv_bf16(a) : attn::launch_bwd_dkdv_f32(a));
+}
+attn_status run_dq(const LaunchArgs& a, attn_dtype dt) {
+    return from_hip(dt == ATTN_BF16 ? attn::launch_bwd_dq_bf16(a) : attn::launch_bwd_dq_f32(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(attn_status s) {
+    switch (s) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_NULL: return "a required pointer is NULL";
+        case ATTN_ERR_SHAPE: return "negative size, or sizes beyond B*H*S < 2^31 and S*D < 2^31";
+        case ATTN_ERR_UNSUPPORTED:
+            return "unsupported: D must be 64 or 128, dtype ATTN_F32 or ATTN_BF16, causal 0 or 1, scale finite and > 0";
+        case ATTN_ERR_ALIGNMENT: return "a device pointer is not 16-byte aligned";
+        case ATTN_ERR_WORKSPACE: return "workspace is NULL or smaller than attn_bwd_workspace_bytes()";
+        case ATTN_ERR_HIP: return "the HIP runtime reported an error at launch";
+        case ATTN_ERR_ALIAS: return "an output buffer overlaps an input or another output";
+    }
+    return "unknown attn_status";
+}
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                     int64_t S, int64_t D, float scale, int causal, attn_dtype dtype, void* stream) {
+    bool empty = false;
+    attn_status st = check_shape(B, H, S, D, dtype, &empty);
+    if (st == ATTN_OK) st = check_scale_causal(scale, causal);
+    if (st != ATTN_OK || empty) return st;
+    if ((st = check_ptrs({q, k, v, o, lse})) != ATTN_OK) return st;
+    const Sizes z = sizes(B, H, S, D, dtype);
+    if ((st = check_alias({{o, z.tensor}, {lse, z.rows}}, {{q, z.tensor}, {k, z.tensor}, {v, z.tensor}})) != ATTN_OK)
+        return st;
+    LaunchArgs a = base_args(B, H, S, D, scale, causal, stream);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    return from_hip(dtype == ATTN_BF16 ? attn::launch_fwd_bf16(a) : attn::launch_fwd_f32(a));
+}
+
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D, attn_dtype dtype) {
+    bool empty = false;
+    if (check_shape(B, H, S, D, dtype, &empty) != ATTN_OK || empty) return 0;
+    return sizes(B, H, S, D, dtype).rows;
+}
+
+attn_status attn_bwd_preprocess(const void* o, const void* dout, float* delta, int64_t B, int64_t H, int64_t S,
+                                int64_t D, attn_dtype dtype, void* stream) {
+    bool empty = false;
+    attn_status st = check_shape(B, H, S, D, dtype, &empty);
+    if (st != ATTN_OK || empty) return st;
+    if ((st = check_ptrs({o, dout, delta})) != ATTN_OK) return st;
+    const Sizes z = sizes(B, H, S, D, dtype);
+    if ((st = check_alias({{delta, z.rows}}, {{o, z.tensor}, {dout, z.tensor}})) != ATTN_OK) return st;
+    LaunchArgs a = base_args(B, H, S, D, 1.f, 1, stream);
+    a.o_in = o;
+    a.dout = dout;
+    a.delta = delta;
+    return run_preprocess(a, dtype);
+}
+
+attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                          const float* delta, void* dk, void* dv, int64_t B, int64_t H, int64_t S, int64_t D,
+                          float scale, int causal, attn_dtype dtype, void* stream) {
+    bool empty = false;
+    attn_status st = check_shape(B, H, S, D, dtype, &empty);
+    if (st == ATTN_OK) st = check_scale_causal(scale, causal);
+    if (st != ATTN_OK || empty) return st;
+    if ((st = check_ptrs({q, k, v, dout, lse, delta, dk, dv})) != ATTN_OK) return st;
+    const Sizes z = sizes(B, H, S, D, dtype);
+    if ((st = check_alias({{dk, z.tensor}, {dv, z.tensor}}, {{q, z.tensor},
+                                                              {k, z.tensor},
+                                                              {v, z.tensor},
+                                                              {dout, z.tensor},
+                                                              {lse, z.rows},
+                                                              {delta, z.rows}})) != ATTN_OK)
+        return st;
+    LaunchArgs a = base_args(B, H, S, D, scale, causal, stream);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.dout = dout;
+    a.lse_in = lse;
+    a.delta_in = delta;
+    a.dk = dk;
+    a.dv = dv;
+    return run_dkdv(a, dtype);
+}
+
+attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                        const float* delta, void* dq, int64_t B, int64_t H, int64_t S, int64_t D, float scale,
+                        int causal, attn_dtype dtype, void* stream) {
+    bool empty = false;
+    attn_status st = check_shape(B, H, S, D, dtype, &empty);
+    if (st == ATTN_OK) st = check_scale_causal(scale, causal);
+    if (st != ATTN_OK || empty) return st;
+    if ((st = check_ptrs({q, k, v, dout, lse, delta, dq})) != ATTN_OK) return st;
+    const Sizes z = sizes(B, H, S, D, dtype);
+    if ((st = check_alias({{dq, z.tensor}}, {{q, z.tensor},
+                                              {k, z.tensor},
+                                              {v, z.tensor},
+                                              {dout, z.tensor},
+                                              {lse, z.rows},
+                                              {delta, z.rows}})) != ATTN_OK)
+        return st;
+    LaunchArgs a = base_args(B, H, S, D, scale, causal, stream);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.dout = dout;
+    a.lse_in = lse;
+    a.delta_in = delta;
+    a.dq = dq;
+    return run_dq(a, dtype);
+}
+
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                     void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                     int64_t S, int64_t D, float scale, int causal, attn_dtype dtype, void* stream) {
+    bool empty = false;
+    attn_status st = check_shape(B, H, S, D, dtype, &empty);
+    if (st == ATTN_OK) st = check_scale_causal(scale, causal);
+    if (st != ATTN_OK || empty) return st;
+    if ((st = check_ptrs({q, k, v, o, dout, lse, dq, dk, dv})) != ATTN_OK) return st;
+    const Sizes z = sizes(B, H, S, D, dtype);
+    if (!workspace || workspace_bytes < z.rows) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ATTN_ERR_ALIGNMENT;
+    if ((st = check_alias({{dq, z.tensor}, {dk, z.tensor}, {dv, z.tensor}, {workspace, z.rows}},
+                          {{q, z.tensor},
+                           {k, z.tensor},
+                           {v, z.tensor},
+                           {o, z.tensor},
+                           {dout, z.tensor},
+                           {lse, z.rows}})) != ATTN_OK)
+        return st;
+    LaunchArgs a = base_args(B, H, S, D, scale, causal, stream);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o_in = o;
+    a.dout = dout;
+    a.lse_in = lse;
+    a.delta = (float*)workspace;
+    a.delta_in = (const float*)workspace;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    if ((st = run_preprocess(a, dtype)) != ATTN_OK) return st;
+    if ((st = run_dkdv(a, dtype)) != ATTN_OK) return st;
+    return run_dq(a, dtype);
+}
+
+}  // extern "C"

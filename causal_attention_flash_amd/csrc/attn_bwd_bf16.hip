@@ -1,0 +1,384 @@
+// Backward pass, bf16 inputs, fp32 accumulation (gfx950, v_mfma_f32_32x32x16_bf16).
+//
+// Structure: the atomic-free three-stage backward of Forge RESEARCH.md §6 and the
+// Forge paper ("Ecosystem survey"): a preprocess computes delta = rowsum(dO o O)
+// once per query row (attn_preprocess.hip); a dK/dV pass runs parallel over key
+// tiles and loops over query tiles; a dQ pass runs parallel over query tiles and
+// loops over key tiles.  Both recompute P = exp(S - L) from the saved
+// log-sum-exp, so no rescaling is needed (Forge "Attention kernel design": "the
+// backward pass needs none of this").  Transposed products are obtained by
+// swapping operand roles rather than moving data (same section): the dK/dV pass
+// forms S = Q K^T and dP = dO V^T with keys on the lanes, and the dQ pass forms
+// S^T = K Q^T and dP^T = V dO^T with queries on the lanes.
+//
+// Per-element work on a score tile, with L2 = LSE*log2(e):
+//   P  = exp2(s*scale*log2(e) - L2)           (0 where masked)
+//   dS = P o (dP - delta)
+// dV += P^T dO, dK += scale * dS^T Q           (dK/dV pass)
+// dQ += scale * dS K                           (dQ pass)
+//
+// Register and LDS budget (the pages' central finding is that this backward is
+// bound by register pressure): each wave keeps its own K and V (dK/dV pass) or
+// Q and dO (dQ pass) as MFMA operands in registers, plus two fp32 accumulators
+// of 32 rows x D; the streamed operand tiles are double-buffered in LDS.
+#include "attn_launch.h"
+#include "attn_tiles.h"
+
+namespace attn {
+
+// ============================================================== dK / dV pass
+
+template <int D, int BMQ>
+struct DkdvCfg {
+    static constexpr int NW = 4;
+    static constexpr int NT = NW * 64;
+    static constexpr int BNK = NW * 32;  // keys per workgroup (32 per wave)
+    using QT = PairTile<BMQ, D, NT>;     // Q and dO tiles, row-major and transposed
+    static constexpr int QROW = QT::ROW_ELEMS;
+    static constexpr int QTR = QT::TRANS_ELEMS;
+    static constexpr int BUF_ELEMS = 2 * (QROW + QTR);  // Q, Q^T, dO, dO^T
+    static constexpr int BUF_STATS = 2 * BMQ;           // lse2, delta (fp32)
+};
+
+template <int D, int BMQ>
+__global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int S, int nblk, int total, float c, float scale,
+    int causal) {
+    using Cfg = DkdvCfg<D, BMQ>;
+    constexpr int NT = Cfg::NT, BNK = Cfg::BNK;
+    constexpr int RSTR = Cfg::QT::RSTR, TSTR = Cfg::QT::TSTR;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Cfg::BUF_ELEMS];
+    __shared__ __attribute__((aligned(16))) float sstat[2 * Cfg::BUF_STATS];
+
+    const int w = xcd_work_index(blockIdx.x, total);
+    const int head = w / nblk;
+    const int kblk = w % nblk;  // low key blocks see the most queries: first
+    const int n0 = kblk * BNK;
+    const size_t base = (size_t)head * S * D;
+    const uint16_t* Qh = Q + base;
+    const uint16_t* dOh = dO + base;
+    const float* Lh = LSE + (size_t)head * S;
+    const float* Dh = Delta + (size_t)head * S;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, n = lane & 31;
+    const int kw0 = n0 + wave * 32;
+    const int key = kw0 + n;  // the key this lane's C columns belong to
+
+    // K and V as B operands (keys on the lanes), d = 16ks+8h..+7.
+    bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+        if (key < S) {
+            a = ldg16(K + base + (size_t)key * D + ks * 16 + 8 * h);
+            b = ldg16(V + base + (size_t)key * D + ks * 16 + 8 * h);
+        }
+        kf[ks] = as_bf16x8(a);
+        vf[ks] = as_bf16x8(b);
+    }
+
+    f32x16 dkacc[D / 32], dvacc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            dkacc[db][r] = 0.f;
+            dvacc[db][r] = 0.f;
+        }
+
+    const int t0 = causal ? n0 / BMQ : 0;
+    const int ntiles = (S + BMQ - 1) / BMQ;
+
+    typename Cfg::QT qt, ot;
+    RowStats<BMQ, NT> st;
+    auto bufp = [&](int b) { return smem + b * Cfg::BUF_ELEMS; };
+    auto stat = [&](int b) { return sstat + b * Cfg::BUF_STATS; };
+    auto stage = [&](int b) {
+        uint16_t* s = bufp(b);
+        qt.store_rows(s, tid);
+        qt.store_trans(s + Cfg::QROW, tid);
+        ot.store_rows(s + Cfg::QROW + Cfg::QTR, tid);
+        ot.store_trans(s + 2 * Cfg::QROW + Cfg::QTR, tid);
+        st.store(stat(b), stat(b) + BMQ, tid);
+    };
+    auto fetch = [&](int t) {
+        qt.load(Qh, t * BMQ, S, tid);
+        ot.load(dOh, t * BMQ, S, tid);
+        st.load(Lh, Dh, t * BMQ, S, tid);
+    };
+
+    if (t0 < ntiles) {
+        fetch(t0);
+        stage(0);
+        if (t0 + 1 < ntiles) fetch(t0 + 1);
+    }
+    __syncthreads();
+
+    for (int t = t0; t < ntiles; ++t) {
+        const int b = (t - t0) & 1;
+        const uint16_t* Qs = bufp(b);
+        const uint16_t* Qt = Qs + Cfg::QROW;
+        const uint16_t* dOs = Qt + Cfg::QTR;
+        const uint16_t* dOt = dOs + Cfg::QROW;
+        const float* L2s = stat(b);
+        const float* DLs = L2s + BMQ;
+        const int qt0 = t * BMQ;
+        const bool active = !causal || qt0 + BMQ - 1 >= kw0;
+        if (active) {
+            const bool need_mask = (causal && qt0 < kw0 + 31) || (qt0 + BMQ > S);
+#pragma unroll
+            for (int qb = 0; qb < BMQ / 32; ++qb) {
+                // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
+                f32x16 sacc, pacc;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    sacc[r] = 0.f;
+                    pacc[r] = 0.f;
+                }
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    const int off = (qb * 32 + n) * RSTR + ks * 16 + 8 * h;
+                    sacc = mfma32(as_bf16x8(lds16(Qs + off)), kf[ks], sacc);
+                    pacc = mfma32(as_bf16x8(lds16(dOs + off)), vf[ks], pacc);
+                }
+                // P and dS; query rows of register r are qb*32 + crow(r, h)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int rl = qb * 32 + 8 * g + 4 * h;
+                    const f32x4 l2 = *reinterpret_cast<const f32x4*>(L2s + rl);
+                    const f32x4 dl = *reinterpret_cast<const f32x4*>(DLs + rl);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = 4 * g + i;
+                        float p = fast_exp2(fmaf(sacc[r], c, -l2[i]));
+                        if (need_mask && causal && key > qt0 + rl + i) p = 0.f;
+                        sacc[r] = p;
+                        pacc[r] = p * (pacc[r] - dl[i]);
+                    }
+                }
+                // dV^T += dO^T P ; dK^T += Q^T dS  (contraction over these 32 queries)
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    const bf16x8 pb = pack_operand(sacc, c2);
+                    const bf16x8 sb = pack_operand(pacc, c2);
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db) {
+                        const int off = (db * 32 + n) * TSTR + (qb * 2 + c2) * 16 + 8 * h;
+                        dvacc[db] = mfma32(as_bf16x8(lds16(dOt + off)), pb, dvacc[db]);
+                        dkacc[db] = mfma32(as_bf16x8(lds16(Qt + off)), sb, dkacc[db]);
+                    }
+                }
+            }
+        }
+        if (t + 1 < ntiles) {
+            stage(b ^ 1);
+            if (t + 2 < ntiles) fetch(t + 2);
+        }
+        __syncthreads();
+    }
+
+    if (key < S) {
+        uint16_t* dKr = dK + base + (size_t)key * D;
+        uint16_t* dVr = dV + base + (size_t)key * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = db * 32 + 8 * g + 4 * h;
+                u32x2 uk, uv;
+                uk[0] = pack_bf16x2(dkacc[db][4 * g + 0] * scale, dkacc[db][4 * g + 1] * scale);
+                uk[1] = pack_bf16x2(dkacc[db][4 * g + 2] * scale, dkacc[db][4 * g + 3] * scale);
+                uv[0] = pack_bf16x2(dvacc[db][4 * g + 0], dvacc[db][4 * g + 1]);
+                uv[1] = pack_bf16x2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]);
+                *reinterpret_cast<u32x2*>(dKr + d) = uk;
+                *reinterpret_cast<u32x2*>(dVr + d) = uv;
+            }
+    }
+}
+
+template <int D, int BMQ>
+static hipError_t launch_dkdv(const LaunchArgs& a) {
+    using Cfg = DkdvCfg<D, BMQ>;
+    const int nblk = (int)((a.S + Cfg::BNK - 1) / Cfg::BNK);
+    const int64_t total = (int64_t)nblk * a.BH;
+    if (total > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, BMQ>), dim3((unsigned)total), dim3(Cfg::NT), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, a.lse_in, a.delta_in, (uint16_t*)a.dk, (uint16_t*)a.dv,
+                       (int)a.S, nblk, (int)total, a.scale * kLog2e, a.scale, a.causal);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv_bf16(const LaunchArgs& a) {
+    if (a.D == 64) return launch_dkdv<64, 64>(a);
+    if (a.D == 128) return launch_dkdv<128, 32>(a);
+    return hipErrorInvalidValue;
+}
+
+// ================================================================== dQ pass
+
+template <int D, int BNK>
+struct DqCfg {
+    static constexpr int NW = 4;
+    static constexpr int NT = NW * 64;
+    static constexpr int BMQ = NW * 32;  // queries per workgroup (32 per wave)
+    using KT = PairTile<BNK, D, NT>;     // K (row-major + transposed) and V (row-major)
+    static constexpr int KROW = KT::ROW_ELEMS;
+    static constexpr int KTR = KT::TRANS_ELEMS;
+    static constexpr int BUF_ELEMS = 2 * KROW + KTR;
+};
+
+template <int D, int BNK>
+__global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
+    uint16_t* __restrict__ dQ, int S, int nblk, int total, float c, float scale, int causal) {
+    using Cfg = DqCfg<D, BNK>;
+    constexpr int BMQ = Cfg::BMQ;
+    constexpr int RSTR = Cfg::KT::RSTR, TSTR = Cfg::KT::TSTR;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Cfg::BUF_ELEMS];
+
+    const int w = xcd_work_index(blockIdx.x, total);
+    const int head = w / nblk;
+    const int qblk = nblk - 1 - (w % nblk);  // high query blocks see the most keys: first
+    const int q0 = qblk * BMQ;
+    const size_t base = (size_t)head * S * D;
+    const uint16_t* Kh = K + base;
+    const uint16_t* Vh = V + base;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, n = lane & 31;
+    const int qw0 = q0 + wave * 32;
+    const int q = qw0 + n;  // the query this lane's C columns belong to
+
+    bf16x8 qf[D / 16], of[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+        if (q < S) {
+            a = ldg16(Q + base + (size_t)q * D + ks * 16 + 8 * h);
+            b = ldg16(dO + base + (size_t)q * D + ks * 16 + 8 * h);
+        }
+        qf[ks] = as_bf16x8(a);
+        of[ks] = as_bf16x8(b);
+    }
+    const float l2 = q < S ? LSE[(size_t)head * S + q] * kLog2e : INFINITY;
+    const float dl = q < S ? Delta[(size_t)head * S + q] : 0.f;
+
+    f32x16 dqacc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
+
+    const int kend = causal ? min(S, q0 + BMQ) : S;
+    const int ntiles = (kend + BNK - 1) / BNK;
+
+    typename Cfg::KT kt, vt;
+    auto bufp = [&](int b) { return smem + b * Cfg::BUF_ELEMS; };
+    auto stage = [&](int b) {
+        uint16_t* s = bufp(b);
+        kt.store_rows(s, tid);
+        kt.store_trans(s + Cfg::KROW, tid);
+        vt.store_rows(s + Cfg::KROW + Cfg::KTR, tid);
+    };
+    auto fetch = [&](int t) {
+        kt.load(Kh, t * BNK, S, tid);
+        vt.load(Vh, t * BNK, S, tid);
+    };
+
+    fetch(0);
+    stage(0);
+    if (ntiles > 1) fetch(1);
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        const uint16_t* Ks = bufp(t & 1);
+        const uint16_t* Kt = Ks + Cfg::KROW;
+        const uint16_t* Vs = Kt + Cfg::KTR;
+        const int k0 = t * BNK;
+        const bool active = !causal || k0 <= qw0 + 31;
+        if (active) {
+            const bool need_mask = (causal && k0 + BNK - 1 > qw0) || (k0 + BNK > S);
+#pragma unroll
+            for (int kb = 0; kb < BNK / 32; ++kb) {
+                // S^T = K Q^T and dP^T = V dO^T: 32 keys x this wave's 32 queries
+                f32x16 sacc, pacc;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    sacc[r] = 0.f;
+                    pacc[r] = 0.f;
+                }
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    const int off = (kb * 32 + n) * RSTR + ks * 16 + 8 * h;
+                    sacc = mfma32(as_bf16x8(lds16(Ks + off)), qf[ks], sacc);
+                    pacc = mfma32(as_bf16x8(lds16(Vs + off)), of[ks], pacc);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float p = fast_exp2(fmaf(sacc[r], c, -l2));
+                    if (need_mask) {
+                        const int kk = k0 + kb * 32 + crow(r, h);
+                        if ((causal && kk > q) || kk >= S) p = 0.f;
+                    }
+                    pacc[r] = p * (pacc[r] - dl);
+                }
+                // dQ^T += K^T dS^T (contraction over these 32 keys)
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    const bf16x8 sb = pack_operand(pacc, c2);
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db) {
+                        const int off = (db * 32 + n) * TSTR + (kb * 2 + c2) * 16 + 8 * h;
+                        dqacc[db] = mfma32(as_bf16x8(lds16(Kt + off)), sb, dqacc[db]);
+                    }
+                }
+            }
+        }
+        if (t + 1 < ntiles) {
+            stage((t + 1) & 1);
+            if (t + 2 < ntiles) fetch(t + 2);
+        }
+        __syncthreads();
+    }
+
+    if (q < S) {
+        uint16_t* dQr = dQ + base + (size_t)q * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x2 u;
+                u[0] = pack_bf16x2(dqacc[db][4 * g + 0] * scale, dqacc[db][4 * g + 1] * scale);
+                u[1] = pack_bf16x2(dqacc[db][4 * g + 2] * scale, dqacc[db][4 * g + 3] * scale);
+                *reinterpret_cast<u32x2*>(dQr + db * 32 + 8 * g + 4 * h) = u;
+            }
+    }
+}
+
+template <int D, int BNK>
+static hipError_t launch_dq(const LaunchArgs& a) {
+    using Cfg = DqCfg<D, BNK>;
+    const int nblk = (int)((a.S + Cfg::BMQ - 1) / Cfg::BMQ);
+    const int64_t total = (int64_t)nblk * a.BH;
+    if (total > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, BNK>), dim3((unsigned)total), dim3(Cfg::NT), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, a.lse_in, a.delta_in, (uint16_t*)a.dq, (int)a.S, nblk,
+                       (int)total, a.scale * kLog2e, a.scale, a.causal);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_bf16(const LaunchArgs& a) {
+    if (a.D == 64) return launch_dq<64, 64>(a);
+    if (a.D == 128) return launch_dq<128, 32>(a);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace attn

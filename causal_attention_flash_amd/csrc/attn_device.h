@@ -1,0 +1,134 @@
+// Device-side building blocks shared by the gfx950 attention kernels.
+//
+// MFMA used: v_mfma_f32_32x32x16_bf16 (one wave computes a 32x32 fp32 tile from
+// a 32x16 and a 16x32 bf16 operand).  Register layouts, per lane l of the 64-lane
+// wave, with h = l / 32 (the lane half) and n = l % 32:
+//
+//   A operand (32 x 16, row i, contraction index k): lane l holds row i = n and
+//     eight consecutive k slots 8h .. 8h+7 (one bf16x8 register quad).
+//   B operand (16 x 32, contraction index k, column j): lane l holds column j = n
+//     and the same eight k slots 8h .. 8h+7.
+//   C/D (32 x 32 fp32): lane l holds column j = n; register r in [0, 16) holds
+//     row 8*(r/4) + 4*h + (r%4).
+//
+// Only the pairing of A's and B's k slots matters to a contraction, so any
+// consistent relabelling of the contraction index is free.  The kernels use that
+// to feed a C tile straight back as an operand: C registers 8c .. 8c+7 of a lane
+// hold rows 16c + 8*(v/4) + 4h + (v%4), v = 0..7, so they form the k slots of
+// one 16-deep contraction step whose k order is "rows 16c + {0..3, 8..11}" for
+// h = 0 and "rows 16c + {4..7, 12..15}" for h = 1.  The operand on the other
+// side is read from LDS in exactly that order (kperm16 below stores it that way,
+// so one 16-byte LDS read fetches the eight values).
+//
+// This is the AMD counterpart of the problem the pages spend a section on
+// (pairing softmax row statistics with accumulator lanes when the lane map is
+// hidden; "Cooperative tensors ..." §8.5 and Forge "Attention kernel design").
+// Here the lane map is fixed by the instruction, so the row statistics live in
+// the lane that owns the row and the rescale is a per-lane multiply.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <float.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row of the 32x32 C tile held by register r of a lane in half h.
+__device__ __forceinline__ int crow(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// Position, inside a 16-wide group, at which index t (0..15) is stored so that
+// lane half h finds contraction slots v = 0..7 at positions 8h + v.  The map
+// swaps the middle two groups of four: {0..3, 4..7, 8..11, 12..15} ->
+// {0..3, 8..11, 4..7, 12..15}.
+__device__ __forceinline__ int kperm16(int t) {
+    const int g = t >> 2;
+    const int pg = (g == 1) ? 2 : (g == 2) ? 1 : g;
+    return (pg << 2) | (t & 3);
+}
+__device__ __forceinline__ int kperm(int t) { return (t & ~15) | kperm16(t & 15); }
+
+// Two fp32 -> packed bf16 (round to nearest even), a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    bf16x2 r = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Eight consecutive C registers (8c .. 8c+7) -> one bf16x8 operand quad.
+__device__ __forceinline__ bf16x8 pack_operand(const f32x16& acc, int c) {
+    u32x4 u;
+    u[0] = pack_bf16x2(acc[8 * c + 0], acc[8 * c + 1]);
+    u[1] = pack_bf16x2(acc[8 * c + 2], acc[8 * c + 3]);
+    u[2] = pack_bf16x2(acc[8 * c + 4], acc[8 * c + 5]);
+    u[3] = pack_bf16x2(acc[8 * c + 6], acc[8 * c + 7]);
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+// Reductions over the lane pair (l, l ^ 32).  v_permlane32_swap exchanges the
+// upper half of its first register with the lower half of its second; given x in
+// both, every lane ends up holding x[l % 32] in one result and x[l % 32 + 32] in
+// the other, so a symmetric reduction of the two results is the pair reduction
+// whichever result is which.
+__device__ __forceinline__ float half_max(float x) {
+    const uint32_t u = __float_as_uint(x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+    const uint32_t u = __float_as_uint(x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ u32x4 lds16(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Low halves of two words -> one word (a's low half in the low half).
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+// High halves of two words -> one word (a's high half in the low half).
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// Work-item order for a 1-D grid of `total` blocks dispatched round-robin over
+// the 8 XCDs: consecutive work items land on the same XCD, so the blocks that
+// share a head's K/V (or Q/dO) also share that XCD's L2.
+__device__ __forceinline__ int xcd_work_index(int bid, int total) {
+    constexpr int kXcd = 8;
+    const int per = total / kXcd;
+    const int rem = total % kXcd;
+    const int xcd = bid % kXcd;
+    const int slot = bid / kXcd;
+    // XCDs with index < rem receive one extra block.
+    const int base = xcd * per + (xcd < rem ? xcd : rem);
+    return base + slot;
+}
+
+}  // namespace attn

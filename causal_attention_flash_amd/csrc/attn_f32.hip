@@ -1,0 +1,291 @@
+// fp32 inputs: forward, dK/dV and dQ on the vector ALUs, fp32 throughout.
+//
+// Same method as the bf16 MFMA path (Forge RESEARCH.md §6: online softmax with a
+// saved LSE; atomic-free backward recomputing P from the LSE; delta from the
+// preprocess), laid out for exact fp32 products instead of matrix cores: G = D/32
+// lanes share one row (a query, or a key for the dK/dV pass), each lane holding 32
+// consecutive columns, and dot products are finished with cross-lane xors inside
+// the G-lane group.  The streamed rows are staged in LDS, where all groups read
+// the same row (a broadcast).  This path serves fp32 callers and small problems;
+// the bf16 kernels carry the throughput.
+#include "attn_launch.h"
+#include "attn_device.h"
+
+namespace attn {
+
+constexpr int kF32Tile = 32;  // streamed rows per LDS tile
+
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int s = 1; s < G; s <<= 1) x += __shfl_xor(x, s);
+    return x;
+}
+
+// Cooperative load of `rows` rows of D floats starting at row0 into LDS
+// (zero beyond S).
+template <int D>
+__device__ __forceinline__ void stage_rows_f32(float* dst, const float* __restrict__ src, int row0, int S, int tid) {
+    constexpr int CH = kF32Tile * D / 4;  // 16-byte chunks
+#pragma unroll
+    for (int c = tid; c < CH; c += 256) {
+        const int row = c / (D / 4);
+        const int col = (c % (D / 4)) * 4;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (row0 + row < S) v = *reinterpret_cast<const f32x4*>(src + (size_t)(row0 + row) * D + col);
+        *reinterpret_cast<f32x4*>(dst + row * D + col) = v;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                                      const float* __restrict__ V, float* __restrict__ O,
+                                                      float* __restrict__ LSE, int S, int nblk, int total, float c,
+                                                      int causal) {
+    constexpr int G = D / 32, R = 256 / G;
+    __shared__ __attribute__((aligned(16))) float Ks[kF32Tile * D];
+    __shared__ __attribute__((aligned(16))) float Vs[kF32Tile * D];
+    const int w = xcd_work_index(blockIdx.x, total);
+    const int head = w / nblk;
+    const int blk = nblk - 1 - (w % nblk);
+    const int q0 = blk * R;
+    const size_t base = (size_t)head * S * D;
+    const int tid = threadIdx.x;
+    const int part = tid % G;
+    const int q = q0 + tid / G;
+
+    float qv[32], ov[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+        qv[e] = q < S ? Q[base + (size_t)q * D + part * 32 + e] : 0.f;
+        ov[e] = 0.f;
+    }
+    float m = -FLT_MAX, l = 0.f;
+    const int kend = causal ? min(S, q0 + R) : S;
+    for (int k0 = 0; k0 < kend; k0 += kF32Tile) {
+        __syncthreads();
+        stage_rows_f32<D>(Ks, K + base, k0, S, tid);
+        stage_rows_f32<D>(Vs, V + base, k0, S, tid);
+        __syncthreads();
+        float sv[kF32Tile];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kF32Tile; ++j) {
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < 32; ++e) d = fmaf(qv[e], Ks[j * D + part * 32 + e], d);
+            d = group_sum<G>(d);
+            const int key = k0 + j;
+            const bool vis = key < S && (!causal || key <= q);
+            sv[j] = vis ? d : -INFINITY;
+            mx = fmaxf(mx, sv[j]);
+        }
+        const float mn = fmaxf(m, mx * c);
+        const float f = exp2f(m - mn);
+        m = mn;
+        l *= f;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) ov[e] *= f;
+#pragma unroll
+        for (int j = 0; j < kF32Tile; ++j) {
+            const float p = exp2f(fmaf(sv[j], c, -m));
+            l += p;
+#pragma unroll
+            for (int e = 0; e < 32; ++e) ov[e] = fmaf(p, Vs[j * D + part * 32 + e], ov[e]);
+        }
+    }
+    if (q < S) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) O[base + (size_t)q * D + part * 32 + e] = ov[e] * inv;
+        if (part == 0) LSE[(size_t)head * S + q] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                                     const float* __restrict__ V, const float* __restrict__ dO,
+                                                     const float* __restrict__ LSE, const float* __restrict__ Delta,
+                                                     float* __restrict__ dQ, int S, int nblk, int total, float c,
+                                                     float scale, int causal) {
+    constexpr int G = D / 32, R = 256 / G;
+    __shared__ __attribute__((aligned(16))) float Ks[kF32Tile * D];
+    __shared__ __attribute__((aligned(16))) float Vs[kF32Tile * D];
+    const int w = xcd_work_index(blockIdx.x, total);
+    const int head = w / nblk;
+    const int blk = nblk - 1 - (w % nblk);
+    const int q0 = blk * R;
+    const size_t base = (size_t)head * S * D;
+    const int tid = threadIdx.x;
+    const int part = tid % G;
+    const int q = q0 + tid / G;
+
+    float qv[32], dov[32], acc[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+        const size_t off = base + (size_t)q * D + part * 32 + e;
+        qv[e] = q < S ? Q[off] : 0.f;
+        dov[e] = q < S ? dO[off] : 0.f;
+        acc[e] = 0.f;
+    }
+    const float l2 = q < S ? LSE[(size_t)head * S + q] * kLog2e : INFINITY;
+    const float dl = q < S ? Delta[(size_t)head * S + q] : 0.f;
+    const int kend = causal ? min(S, q0 + R) : S;
+    for (int k0 = 0; k0 < kend; k0 += kF32Tile) {
+        __syncthreads();
+        stage_rows_f32<D>(Ks, K + base, k0, S, tid);
+        stage_rows_f32<D>(Vs, V + base, k0, S, tid);
+        __syncthreads();
+#pragma unroll 4
+        for (int j = 0; j < kF32Tile; ++j) {
+            float s = 0.f, dp = 0.f;
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+                s = fmaf(qv[e], Ks[j * D + part * 32 + e], s);
+                dp = fmaf(dov[e], Vs[j * D + part * 32 + e], dp);
+            }
+            s = group_sum<G>(s);
+            dp = group_sum<G>(dp);
+            const int key = k0 + j;
+            const bool vis = key < S && (!causal || key <= q);
+            const float p = vis ? exp2f(fmaf(s, c, -l2)) : 0.f;
+            const float ds = p * (dp - dl);
+#pragma unroll
+            for (int e = 0; e < 32; ++e) acc[e] = fmaf(ds, Ks[j * D + part * 32 + e], acc[e]);
+        }
+    }
+    if (q < S) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) dQ[base + (size_t)q * D + part * 32 + e] = acc[e] * scale;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                                       const float* __restrict__ V, const float* __restrict__ dO,
+                                                       const float* __restrict__ LSE,
+                                                       const float* __restrict__ Delta, float* __restrict__ dK,
+                                                       float* __restrict__ dV, int S, int nblk, int total, float c,
+                                                       float scale, int causal) {
+    constexpr int G = D / 32, R = 256 / G;
+    __shared__ __attribute__((aligned(16))) float Qs[kF32Tile * D];
+    __shared__ __attribute__((aligned(16))) float Os[kF32Tile * D];
+    __shared__ float L2s[kF32Tile], DLs[kF32Tile];
+    const int w = xcd_work_index(blockIdx.x, total);
+    const int head = w / nblk;
+    const int blk = w % nblk;
+    const int n0 = blk * R;
+    const size_t base = (size_t)head * S * D;
+    const int tid = threadIdx.x;
+    const int part = tid % G;
+    const int key = n0 + tid / G;
+
+    float kv[32], vv[32], dk[32], dv[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+        const size_t off = base + (size_t)key * D + part * 32 + e;
+        kv[e] = key < S ? K[off] : 0.f;
+        vv[e] = key < S ? V[off] : 0.f;
+        dk[e] = 0.f;
+        dv[e] = 0.f;
+    }
+    const int qstart = causal ? n0 : 0;
+    for (int qt0 = qstart; qt0 < S; qt0 += kF32Tile) {
+        __syncthreads();
+        stage_rows_f32<D>(Qs, Q + base, qt0, S, tid);
+        stage_rows_f32<D>(Os, dO + base, qt0, S, tid);
+        if (tid < kF32Tile) {
+            const int qq = qt0 + tid;
+            L2s[tid] = qq < S ? LSE[(size_t)head * S + qq] * kLog2e : INFINITY;
+            DLs[tid] = qq < S ? Delta[(size_t)head * S + qq] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int j = 0; j < kF32Tile; ++j) {
+            float s = 0.f, dp = 0.f;
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+                s = fmaf(kv[e], Qs[j * D + part * 32 + e], s);
+                dp = fmaf(vv[e], Os[j * D + part * 32 + e], dp);
+            }
+            s = group_sum<G>(s);
+            dp = group_sum<G>(dp);
+            const int qq = qt0 + j;
+            const bool vis = qq < S && (!causal || key <= qq);
+            const float p = vis ? exp2f(fmaf(s, c, -L2s[j])) : 0.f;
+            const float ds = p * (dp - DLs[j]);
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+                dv[e] = fmaf(p, Os[j * D + part * 32 + e], dv[e]);
+                dk[e] = fmaf(ds, Qs[j * D + part * 32 + e], dk[e]);
+            }
+        }
+    }
+    if (key < S) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+            const size_t off = base + (size_t)key * D + part * 32 + e;
+            dK[off] = dk[e] * scale;
+            dV[off] = dv[e];
+        }
+    }
+}
+
+template <int D>
+static int f32_blocks(const LaunchArgs& a, int* nblk) {
+    constexpr int R = 256 / (D / 32);
+    *nblk = (int)((a.S + R - 1) / R);
+    const int64_t total = (int64_t)(*nblk) * a.BH;
+    return total > INT32_MAX ? -1 : (int)total;
+}
+
+template <int D>
+static hipError_t fwd_f32(const LaunchArgs& a) {
+    int nblk;
+    const int total = f32_blocks<D>(a, &nblk);
+    if (total < 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3(total), dim3(256), 0, a.stream, (const float*)a.q,
+                       (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, (int)a.S, nblk, total,
+                       a.scale * kLog2e, a.causal);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t dq_f32(const LaunchArgs& a) {
+    int nblk;
+    const int total = f32_blocks<D>(a, &nblk);
+    if (total < 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((dq_f32_kernel<D>), dim3(total), dim3(256), 0, a.stream, (const float*)a.q,
+                       (const float*)a.k, (const float*)a.v, (const float*)a.dout, a.lse_in, a.delta_in,
+                       (float*)a.dq, (int)a.S, nblk, total, a.scale * kLog2e, a.scale, a.causal);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t dkdv_f32(const LaunchArgs& a) {
+    int nblk;
+    const int total = f32_blocks<D>(a, &nblk);
+    if (total < 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((dkdv_f32_kernel<D>), dim3(total), dim3(256), 0, a.stream, (const float*)a.q,
+                       (const float*)a.k, (const float*)a.v, (const float*)a.dout, a.lse_in, a.delta_in,
+                       (float*)a.dk, (float*)a.dv, (int)a.S, nblk, total, a.scale * kLog2e, a.scale, a.causal);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_f32(const LaunchArgs& a) {
+    if (a.D == 64) return fwd_f32<64>(a);
+    if (a.D == 128) return fwd_f32<128>(a);
+    return hipErrorInvalidValue;
+}
+hipError_t launch_bwd_dq_f32(const LaunchArgs& a) {
+    if (a.D == 64) return dq_f32<64>(a);
+    if (a.D == 128) return dq_f32<128>(a);
+    return hipErrorInvalidValue;
+}
+hipError_t launch_bwd_dkdv_f32(const LaunchArgs& a) {
+    if (a.D == 64) return dkdv_f32<64>(a);
+    if (a.D == 128) return dkdv_f32<128>(a);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace attn

@@ -1,0 +1,253 @@
+// Forward pass, bf16 inputs, fp32 accumulation: O and LSE for one tile of queries
+// per workgroup (gfx950, v_mfma_f32_32x32x16_bf16).
+//
+// Method: the FlashAttention-2 online softmax of Forge RESEARCH.md §6 ("Fused
+// attention design"): per key tile, m_new = max(m, rowmax S), P = exp2(S - m_new)
+// with scale*log2(e) folded into the exponent, l = l*factor + rowsum P,
+// O = O*factor + P V, divide by l once after the loop, save L = m + log l.
+// Causal tiles entirely above the diagonal are skipped and only tiles that cross
+// the diagonal (or the sequence end) pay per-element masking (same section,
+// "Causal masking"); masked scores are excluded with a mask that can never make
+// exp produce NaN (the -inf - -inf hazard named there and in §6.3 of
+// "Cooperative tensors, reductions, and building a fused attention kernel").
+//
+// gfx950 mapping:
+// * 4 waves per workgroup, split-Q: each wave owns QB blocks of 32 query rows
+//   and never shares row statistics with another wave.
+// * The score tile is computed transposed, S^T = K Q^T, so each lane owns one
+//   query (C column) and the row max / row sum are in-lane reductions plus one
+//   exchange between the two lane halves (v_permlane32_swap).
+// * P^T, packed to bf16 straight from the C registers, is the B operand of
+//   O^T += V^T P^T; V^T is staged in LDS in the matching key order, so the
+//   rescale O *= factor is a per-lane multiply (no diag-matrix product).
+// * The O rescale is skipped unless some row max in the wave grew by more than
+//   kRescaleSlack (log2 units): P values are then bounded by 2^kRescaleSlack,
+//   which fp32 accumulation and bf16 P absorb; the result is the same function,
+//   only the reference point of the exponent differs.
+// * Q stays in registers for the whole key loop; K (row-major) and V^T tiles of
+//   64 keys are double-buffered in LDS, the next tile's global loads in flight
+//   while the current one is multiplied.
+#include "attn_launch.h"
+#include "attn_tiles.h"
+
+namespace attn {
+
+constexpr float kRescaleSlack = 8.0f;
+
+template <int D, int QB>
+struct FwdCfg {
+    static constexpr int NW = 4;
+    static constexpr int NT = NW * 64;
+    static constexpr int BM = NW * 32 * QB;  // queries per workgroup
+    static constexpr int BN = 64;            // keys per tile
+    using KT = PairTile<BN, D, NT>;
+    static constexpr int KELEMS = KT::ROW_ELEMS;
+    static constexpr int VELEMS = KT::TRANS_ELEMS;
+    static constexpr int BUF = KELEMS + VELEMS;
+    static constexpr int LDS_BYTES = 2 * BUF * 2;
+};
+
+template <int D, int QB>
+__global__ __launch_bounds__(256) void fwd_bf16_kernel(const uint16_t* __restrict__ Q,
+                                                       const uint16_t* __restrict__ K,
+                                                       const uint16_t* __restrict__ V,
+                                                       uint16_t* __restrict__ O, float* __restrict__ LSE,
+                                                       int S, int nblk, int total, float c, int causal) {
+    using Cfg = FwdCfg<D, QB>;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN;
+    constexpr int KSTR = Cfg::KT::RSTR, VSTR = Cfg::KT::TSTR;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Cfg::BUF];
+
+    const int w = xcd_work_index(blockIdx.x, total);
+    const int head = w / nblk;
+    const int qblk = nblk - 1 - (w % nblk);  // most work first
+    const int q0 = qblk * BM;
+    const size_t base = (size_t)head * S * D;
+    const uint16_t* Qh = Q + base;
+    const uint16_t* Kh = K + base;
+    const uint16_t* Vh = V + base;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, n = lane & 31;
+    const int qw0 = q0 + wave * 32 * QB;
+
+    const int kend = causal ? min(S, q0 + BM) : S;
+    const int ntiles = (kend + BN - 1) / BN;
+
+    // Q as the B operand of S^T = K Q^T: lane holds query qw0+32qb+n, d = 16ks+8h..+7.
+    bf16x8 qf[QB][D / 16];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int q = qw0 + qb * 32 + n;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            u32x4 u = {0u, 0u, 0u, 0u};
+            if (q < S) u = ldg16(Qh + (size_t)q * D + ks * 16 + 8 * h);
+            qf[qb][ks] = as_bf16x8(u);
+        }
+    }
+
+    f32x16 oacc[QB][D / 32];
+    float m[QB], l[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        m[qb] = -FLT_MAX;
+        l[qb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
+    }
+
+    typename Cfg::KT kt, vt;
+    kt.load(Kh, 0, S, tid);
+    vt.load(Vh, 0, S, tid);
+    kt.store_rows(smem, tid);
+    vt.store_trans(smem + Cfg::KELEMS, tid);
+    if (ntiles > 1) {
+        kt.load(Kh, BN, S, tid);
+        vt.load(Vh, BN, S, tid);
+    }
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        const uint16_t* Ks = smem + (t & 1) * Cfg::BUF;
+        const uint16_t* Vt = Ks + Cfg::KELEMS;
+        const int k0 = t * BN;
+        const bool active = !causal || k0 <= qw0 + 32 * QB - 1;
+        if (active) {
+            // ---- S^T = K Q^T for BN keys x 32*QB queries
+            f32x16 sacc[QB][BN / 32];
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    const bf16x8 kf = as_bf16x8(lds16(Ks + (kb * 32 + n) * KSTR + ks * 16 + 8 * h));
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = mfma32(kf, qf[qb][ks], sacc[qb][kb]);
+                }
+            }
+            // ---- mask, row max (raw scores; c > 0 so max commutes with scaling)
+            const bool need_mask = (causal && k0 + BN - 1 > qw0) || (k0 + BN > S);
+            float mx[QB];
+            bool grow = false;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const int q = qw0 + qb * 32 + n;
+                float v = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        if (need_mask) {
+                            const int key = k0 + kb * 32 + crow(r, h);
+                            if ((causal && key > q) || key >= S) sacc[qb][kb][r] = -INFINITY;
+                        }
+                        v = fmaxf(v, sacc[qb][kb][r]);
+                    }
+                v = half_max(v) * c;
+                mx[qb] = v;
+                grow |= v > m[qb] + kRescaleSlack;
+            }
+            // ---- rescale only when some row max in the wave grew past the slack
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    const float mn = fmaxf(m[qb], mx[qb]);
+                    const float f = fast_exp2(m[qb] - mn);
+                    m[qb] = mn;
+                    l[qb] *= f;
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= f;
+                }
+            }
+            // ---- P = exp2(s*c - m), row sums, bf16 operands
+            bf16x8 pf[QB][BN / 16];
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                float ls = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float p = fast_exp2(fmaf(sacc[qb][kb][r], c, -m[qb]));
+                        sacc[qb][kb][r] = p;
+                        ls += p;
+                    }
+                    pf[qb][2 * kb] = pack_operand(sacc[qb][kb], 0);
+                    pf[qb][2 * kb + 1] = pack_operand(sacc[qb][kb], 1);
+                }
+                l[qb] += ls;
+            }
+            // ---- O^T += V^T P^T
+#pragma unroll
+            for (int ks = 0; ks < BN / 16; ++ks) {
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const bf16x8 vf = as_bf16x8(lds16(Vt + (db * 32 + n) * VSTR + ks * 16 + 8 * h));
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32(vf, pf[qb][ks], oacc[qb][db]);
+                }
+            }
+        }
+        if (t + 1 < ntiles) {
+            uint16_t* nxt = smem + ((t + 1) & 1) * Cfg::BUF;
+            kt.store_rows(nxt, tid);
+            vt.store_trans(nxt + Cfg::KELEMS, tid);
+            if (t + 2 < ntiles) {
+                kt.load(Kh, (t + 2) * BN, S, tid);
+                vt.load(Vh, (t + 2) * BN, S, tid);
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- epilogue: O = O / l (l == 0 -> 0), LSE = (m + log2 l) * ln 2
+    uint16_t* Oh = O + base;
+    float* Lh = LSE + (size_t)head * S;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int q = qw0 + qb * 32 + n;
+        const float lt = half_sum(l[qb]);
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        if (q < S) {
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    u32x2 u;
+                    u[0] = pack_bf16x2(oacc[qb][db][4 * g + 0] * inv, oacc[qb][db][4 * g + 1] * inv);
+                    u[1] = pack_bf16x2(oacc[qb][db][4 * g + 2] * inv, oacc[qb][db][4 * g + 3] * inv);
+                    *reinterpret_cast<u32x2*>(Oh + (size_t)q * D + db * 32 + 8 * g + 4 * h) = u;
+                }
+            if (h == 0) Lh[q] = lt > 0.f ? (m[qb] + __log2f(lt)) * kLn2 : -INFINITY;
+        }
+    }
+}
+
+template <int D, int QB>
+static hipError_t launch_fwd(const LaunchArgs& a) {
+    using Cfg = FwdCfg<D, QB>;
+    const int nblk = (int)((a.S + Cfg::BM - 1) / Cfg::BM);
+    const int64_t total = (int64_t)nblk * a.BH;
+    if (total > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, QB>), dim3((unsigned)total), dim3(Cfg::NT), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
+                       (int)a.S, nblk, (int)total, a.scale * kLog2e, a.causal);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16(const LaunchArgs& a) {
+    if (a.D == 64) return launch_fwd<64, 1>(a);
+    if (a.D == 128) return launch_fwd<128, 1>(a);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace attn

@@ -1,0 +1,44 @@
+// Internal launch interface between the C ABI (attn_api.hip) and the kernel
+// files.  Arguments arrive here already validated: D in {64, 128}, S >= 1,
+// B*H >= 1, pointers non-null, aligned and non-overlapping, scale > 0 finite.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct LaunchArgs {
+    const void* q = nullptr;
+    const void* k = nullptr;
+    const void* v = nullptr;
+    const void* o_in = nullptr;  // forward output read by the backward preprocess
+    const void* dout = nullptr;
+    const float* lse_in = nullptr;
+    const float* delta_in = nullptr;
+    void* o = nullptr;
+    float* lse = nullptr;
+    float* delta = nullptr;
+    void* dq = nullptr;
+    void* dk = nullptr;
+    void* dv = nullptr;
+    int64_t BH = 0;  // batch * heads
+    int64_t S = 0;
+    int64_t D = 0;
+    float scale = 0.f;
+    int causal = 1;
+    hipStream_t stream = nullptr;
+};
+
+hipError_t launch_fwd_bf16(const LaunchArgs& a);
+hipError_t launch_bwd_dkdv_bf16(const LaunchArgs& a);
+hipError_t launch_bwd_dq_bf16(const LaunchArgs& a);
+
+hipError_t launch_fwd_f32(const LaunchArgs& a);
+hipError_t launch_bwd_dkdv_f32(const LaunchArgs& a);
+hipError_t launch_bwd_dq_f32(const LaunchArgs& a);
+
+// delta = rowsum(dO o O) for either element type (elem_bytes 2 = bf16, 4 = f32).
+hipError_t launch_bwd_preprocess(const LaunchArgs& a, int elem_bytes);
+
+}  // namespace attn

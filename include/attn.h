@@ -1,0 +1,143 @@
+/*
+ * attn.h - fused causal scaled-dot-product attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libcausal_attn.so.  Plain pointers and sizes only; every pointer named
+ * "device" is HIP device memory, every size is an element count unless it says
+ * bytes.  The caller owns every buffer and the stream; the library never
+ * allocates, frees, synchronises or keeps a pointer past the call.  Work is
+ * enqueued asynchronously on `stream` (a hipStream_t; NULL = the default stream),
+ * so buffers must stay alive until the stream has passed that point.
+ *
+ * What is computed (per batch b and head h, all indices in [0, S)):
+ *
+ *   s_ij  = scale * sum_d q_id k_jd
+ *   query i sees key j iff (!causal || j <= i)            (top-left aligned mask)
+ *   LSE_i = ln sum_{j visible} exp(s_ij)                  (natural log, fp32)
+ *   P_ij  = exp(s_ij - LSE_i) for visible j, else 0
+ *   O_i   = sum_j P_ij v_j
+ *   dV_j  = sum_i P_ij dO_i
+ *   dP_ij = dO_i . v_j,   delta_i = dO_i . O_i,   dS_ij = P_ij (dP_ij - delta_i)
+ *   dQ_i  = scale * sum_j dS_ij k_j,   dK_j = scale * sum_i dS_ij q_i
+ *
+ * Sources: attention as S = QK^T, row softmax, O = PV and the causal mask
+ * "column > row is masked" follow "Cooperative tensors, reductions, and building
+ * a fused attention kernel" (§1, §5.3, §8.7).  The online-softmax forward that
+ * saves one log-sum-exp per row, the three-stage atomic-free backward
+ * (delta = rowsum(dO o O) preprocess, a dQ pass parallel over queries, a dK/dV
+ * pass parallel over keys, both recomputing P from the saved LSE) follow Forge
+ * RESEARCH.md §6 "Fused attention design (flash-style)" and the Forge paper,
+ * sections "Ecosystem survey" and "Attention kernel design".
+ *
+ * Layout: Q, K, V, O, dO, dQ, dK, dV are contiguous [B, H, S, D] (D innermost);
+ * LSE and delta are contiguous [B, H, S] fp32.  Tensor element type is `dtype`
+ * (ATTN_F32: float, ATTN_BF16: bfloat16 bit patterns); accumulation and all
+ * softmax statistics are fp32 whatever the input type.  Outputs are written in
+ * the input type, rounded to nearest even.
+ *
+ * Supported set: D in {64, 128}; dtype in {ATTN_F32, ATTN_BF16}; causal in {0, 1};
+ * finite scale; any S >= 1 (no tile-multiple requirement); B*H*S*D < 2^62 and
+ * S*D < 2^31.  B, H or S equal to 0 is an empty problem: ATTN_OK, nothing
+ * enqueued, pointers not read.
+ *
+ * Errors: every argument is validated before anything is enqueued.  On any
+ * error status nothing is launched and no output is touched.  ATTN_ERR_HIP
+ * reports a launch failure read back with hipGetLastError (the stream may then
+ * hold part of the work).  Outputs must not overlap inputs or each other
+ * (ATTN_ERR_ALIAS).  All device pointers must be 16-byte aligned.
+ *
+ * Determinism: no atomics; results are bitwise identical run to run for the
+ * same inputs, sizes and library build.
+ */
+#ifndef CAUSAL_ATTN_H
+#define CAUSAL_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_dtype {
+    ATTN_F32 = 0,  /* float32 tensors */
+    ATTN_BF16 = 1  /* bfloat16 tensors (uint16 bit patterns) */
+} attn_dtype;
+
+typedef enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+    ATTN_ERR_SHAPE = 2,       /* a negative size, or sizes whose products overflow the limits */
+    ATTN_ERR_UNSUPPORTED = 3, /* D, dtype, causal flag or scale outside the supported set */
+    ATTN_ERR_ALIGNMENT = 4,   /* a device pointer not aligned to 16 bytes */
+    ATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than attn_bwd_workspace_bytes() */
+    ATTN_ERR_HIP = 6,         /* the HIP runtime reported an error when launching */
+    ATTN_ERR_ALIAS = 7        /* an output overlaps an input or another output */
+} attn_status;
+
+/*
+ * Forward pass: O and LSE from Q, K, V.
+ *   q, k, v : device, [B,H,S,D] of dtype, read only.
+ *   o       : device, [B,H,S,D] of dtype, fully overwritten.
+ *   lse     : device, [B,H,S] fp32, fully overwritten (natural-log log-sum-exp of
+ *             the scaled, masked scores; the backward pass takes it back).
+ *   scale   : multiplies QK^T before the softmax (typically 1/sqrt(D)).
+ *   causal  : 1 = query i sees keys j <= i; 0 = every key.
+ * Source: Forge RESEARCH.md §6 (online-softmax recurrence, divide by the row sum
+ * once after the loop, L = m + log l saved per row).
+ */
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int64_t B, int64_t H, int64_t S, int64_t D,
+                     float scale, int causal, attn_dtype dtype, void* stream);
+
+/*
+ * Bytes of device workspace attn_bwd needs: the fp32 delta vector, B*H*S*4 bytes.
+ * Returns 0 for an empty or invalid problem.
+ */
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D, attn_dtype dtype);
+
+/*
+ * Backward pass: dQ, dK, dV from Q, K, V, the forward's O and LSE, and dO.
+ *   q, k, v, o, dout : device, [B,H,S,D] of dtype, read only (o = the forward output).
+ *   lse              : device, [B,H,S] fp32, read only (the forward's LSE).
+ *   dq, dk, dv       : device, [B,H,S,D] of dtype, fully overwritten.
+ *   workspace        : device, at least attn_bwd_workspace_bytes() bytes, owned by the
+ *                      caller; clobbered; must not overlap any other argument.
+ * Enqueues, in order: delta = rowsum(dO o O) (fp32), the dK/dV pass, the dQ pass.
+ * Source: Forge RESEARCH.md §6 (the "D term" paragraph and the two-kernel,
+ * atomic-free backward that recomputes P = exp(S - L) per tile).
+ */
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse,
+                     void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes,
+                     int64_t B, int64_t H, int64_t S, int64_t D,
+                     float scale, int causal, attn_dtype dtype, void* stream);
+
+/*
+ * The three stages attn_bwd enqueues, exposed one by one (same argument rules).
+ * attn_bwd is exactly attn_bwd_preprocess + attn_bwd_dkdv + attn_bwd_dq on one
+ * stream.
+ *   delta : device, [B,H,S] fp32; written by the preprocess, read by the others.
+ */
+attn_status attn_bwd_preprocess(const void* o, const void* dout, float* delta,
+                                int64_t B, int64_t H, int64_t S, int64_t D,
+                                attn_dtype dtype, void* stream);
+
+attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                          const float* lse, const float* delta, void* dk, void* dv,
+                          int64_t B, int64_t H, int64_t S, int64_t D,
+                          float scale, int causal, attn_dtype dtype, void* stream);
+
+attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                        const float* lse, const float* delta, void* dq,
+                        int64_t B, int64_t H, int64_t S, int64_t D,
+                        float scale, int causal, attn_dtype dtype, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* attn_status_string(attn_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CAUSAL_ATTN_H */

@@ -1,0 +1,165 @@
+"""C ABI: the library loads, exports every declared symbol, and validates arguments.
+
+These run on the CPU: every call here fails validation (or is an empty problem),
+and the library returns before it touches the HIP runtime, so no GPU is needed.
+Fake device pointers are plain aligned integers that are never dereferenced.
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+import causal_attention_flash_amd as caf
+from causal_attention_flash_amd import _binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, HIP, ALIAS = range(8)
+BF16, F32 = bd.ATTN_BF16, bd.ATTN_F32
+
+# distinct, 16-byte aligned, far apart fake device addresses
+P = [0x10_0000_0000 * (i + 1) for i in range(12)]
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    decls = {}
+    for m in re.finditer(r"^(?:const\s+)?[\w\s\*]+?\b(attn_\w+)\s*\(([^;]*?)\)\s*;", text, flags=re.M | re.S):
+        name, args = m.group(1), m.group(2).strip()
+        decls[name] = 0 if args in ("", "void") else args.count(",") + 1
+    return decls
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.LIB_PATH):
+        pytest.fail(f"{bd.LIB_PATH} not built: run `python -m causal_attention_flash_amd.build`")
+    return bd.load_library()
+
+
+def test_header_declares_the_boundary():
+    decls = _declared_functions()
+    assert set(decls) == {"attn_fwd", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_preprocess",
+                          "attn_bwd_dkdv", "attn_bwd_dq", "attn_status_string"}
+    for name, nargs in decls.items():
+        assert len(bd.SIGNATURES[name][1]) == nargs, name
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", bd.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = {line.split()[-1] for line in out.stdout.splitlines() if line.strip()}
+    for name in _declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        s = bd.status_string(code)
+        assert isinstance(s, str) and s
+    assert bd.status_string(99) == "unknown attn_status"
+    assert bd.status_string(OK) == "ok"
+
+
+def fwd(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=2, H=3, S=100, D=64, scale=0.125, causal=1, dtype=BF16)
+    a.update(kw)
+    return bd.c_attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["S"], a["D"], a["scale"],
+                         a["causal"], a["dtype"], 0)
+
+
+def bwd(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], do=P[4], lse=P[5], dq=P[6], dk=P[7], dv=P[8], ws=P[9],
+             ws_bytes=2 * 3 * 100 * 4, B=2, H=3, S=100, D=64, scale=0.125, causal=1, dtype=BF16)
+    a.update(kw)
+    return bd.c_attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["ws"],
+                         a["ws_bytes"], a["B"], a["H"], a["S"], a["D"], a["scale"], a["causal"], a["dtype"], 0)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=0), NULL), (dict(k=0), NULL), (dict(v=0), NULL), (dict(o=0), NULL), (dict(lse=0), NULL),
+    (dict(S=-1), SHAPE), (dict(B=-2), SHAPE), (dict(H=-1), SHAPE),
+    (dict(B=1 << 20, H=1 << 11, S=1), SHAPE),          # B*H*S = 2^31
+    (dict(B=1, H=1, S=1 << 25, D=64), SHAPE),           # S*D = 2^31
+    (dict(D=96), UNSUP), (dict(D=32), UNSUP), (dict(D=256), UNSUP),
+    (dict(dtype=2), UNSUP), (dict(dtype=-1), UNSUP),
+    (dict(causal=2), UNSUP), (dict(causal=-1), UNSUP),
+    (dict(scale=0.0), UNSUP), (dict(scale=-0.5), UNSUP), (dict(scale=float("nan")), UNSUP),
+    (dict(scale=float("inf")), UNSUP),
+    (dict(q=P[0] + 8), ALIGN), (dict(lse=P[4] + 4), ALIGN), (dict(o=P[3] + 2), ALIGN),
+    (dict(o=P[0]), ALIAS), (dict(lse=P[1] + 64), ALIAS), (dict(lse=P[3] + 16), ALIAS),
+])
+def test_fwd_validation(lib, kw, expect):
+    assert fwd(**kw) == expect
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(S=0), dict(B=0, q=0, k=0, v=0, o=0, lse=0)])
+def test_fwd_empty_problem_is_ok_without_pointers(lib, kw):
+    assert fwd(**kw) == OK
+
+
+def test_fwd_empty_still_checks_the_supported_set(lib):
+    assert fwd(B=0, D=96) == UNSUP
+    assert fwd(B=0, dtype=7) == UNSUP
+    assert fwd(B=0, S=-1) == SHAPE
+
+
+def test_fwd_adjacent_buffers_do_not_alias(lib):
+    # o placed exactly after q (B*H*S*D*2 bytes): touching, not overlapping.  Then the
+    # call passes validation and would launch, so instead shrink lse onto q's tail.
+    n = 2 * 3 * 100 * 64 * 2
+    assert fwd(lse=P[0] + n - 16) == ALIAS
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(ws=0), WS), (dict(ws_bytes=2 * 3 * 100 * 4 - 1), WS), (dict(ws_bytes=0), WS),
+    (dict(ws=P[9] + 4), ALIGN),
+    (dict(ws=P[0]), ALIAS), (dict(dq=P[1]), ALIAS), (dict(dk=P[6]), ALIAS), (dict(dv=P[5]), ALIAS),
+    (dict(o=0), NULL), (dict(do=0), NULL), (dict(dq=0), NULL),
+    (dict(D=80), UNSUP), (dict(S=-3), SHAPE), (dict(scale=-1.0), UNSUP),
+])
+def test_bwd_validation(lib, kw, expect):
+    assert bwd(**kw) == expect
+
+
+def test_bwd_empty_is_ok(lib):
+    assert bwd(S=0, ws=0, ws_bytes=0, q=0) == OK
+
+
+def test_workspace_bytes(lib):
+    assert bd.c_attn_bwd_workspace_bytes(2, 3, 100, 64, BF16) == 2 * 3 * 100 * 4
+    assert bd.c_attn_bwd_workspace_bytes(1, 16, 8191, 128, BF16) == 16 * 8191 * 4
+    assert bd.c_attn_bwd_workspace_bytes(1, 4, 128, 64, F32) == 4 * 128 * 4
+    assert bd.c_attn_bwd_workspace_bytes(0, 3, 100, 64, BF16) == 0
+    assert bd.c_attn_bwd_workspace_bytes(2, 3, 100, 96, BF16) == 0
+    assert bd.c_attn_bwd_workspace_bytes(2, 3, -1, 64, BF16) == 0
+
+
+def test_stage_entry_points_validate(lib):
+    assert bd.c_attn_bwd_preprocess(P[0], P[1], 0, 2, 3, 100, 64, BF16) == NULL
+    assert bd.c_attn_bwd_preprocess(P[0], P[1], P[0], 2, 3, 100, 64, BF16) == ALIAS
+    assert bd.c_attn_bwd_preprocess(P[0], P[1], P[2], 2, 3, 100, 48, BF16) == UNSUP
+    assert bd.c_attn_bwd_dkdv(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[6], 2, 3, 100, 64, 0.1, 1, BF16) == ALIAS
+    assert bd.c_attn_bwd_dkdv(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], 2, 3, 100, 64, 0.1, 3, BF16) == UNSUP
+    assert bd.c_attn_bwd_dq(P[0], P[1], P[2], P[3], P[4], 0, P[6], 2, 3, 100, 64, 0.1, 1, BF16) == NULL
+    assert bd.c_attn_bwd_dq(P[0], P[1], P[2], P[3], P[4], P[5], P[4] + 32, 2, 3, 100, 64, 0.1, 1, BF16) == ALIAS
+
+
+def test_torch_wrapper_rejects_cpu_tensors(lib):
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        caf.attn_fwd(q, q, q)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    saved = bd._lib
+    bd._lib = None
+    try:
+        with pytest.raises(ImportError, match="no fallback"):
+            bd.load_library(str(tmp_path / "nope.so"))
+    finally:
+        bd._lib = saved

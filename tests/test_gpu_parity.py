@@ -1,0 +1,191 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Inputs come from seeded_inputs (same bytes on both sides).  Small workloads are
+compared on every element; the two large ones (B=4 H=16 S=2048 D=64 and
+B=1 H=16 S=8191 D=128) run on the GPU at full size, in the launch configuration
+bench.py times, and are compared on sampled heads that the oracle computes in
+full.  Tolerances: tests/gpu_util.py.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import seeded_inputs as si
+from oracle import attention_head
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def oracle_heads(x, w, heads, causal=True, scale=None):
+    """Oracle outputs for the listed (b, h) heads, stacked in that order."""
+    scale = w.scale if scale is None else scale
+    res = {n: [] for n in gu.OUTPUTS}
+    for b, h in heads:
+        r = attention_head(x["q"][b, h], x["k"][b, h], x["v"][b, h], x["do"][b, h], scale, causal)
+        for n in gu.OUTPUTS:
+            res[n].append(r[n])
+    return {n: np.stack(v) for n, v in res.items()}
+
+
+def all_heads(w):
+    return [(b, h) for b in range(w.B) for h in range(w.H)]
+
+
+# sampled heads for the full-size workloads: first, last and a spread between
+SAMPLES = {
+    "gpt205m_bf16": [(0, 0), (0, 7), (1, 3), (2, 12), (3, 15)],
+    "long8191_bf16": [(0, 0), (0, 15)],
+}
+
+
+@pytest.fixture(scope="module")
+def device():
+    return gu.require_gpu()
+
+
+@pytest.mark.parametrize("name", list(si.WORKLOADS))
+def test_workload_parity(device, name):
+    w = si.WORKLOADS[name]
+    print(f"\n[parity] {name}: B={w.B} H={w.H} S={w.S} D={w.D} {w.dtype}", flush=True)
+    x = si.make_inputs(w, seed=0)
+    gpu = gu.run_gpu(x, w, device)
+    heads = SAMPLES.get(name, all_heads(w))
+    ref = oracle_heads(x, w, heads)
+    gu.check(gu.errors(gpu, ref, heads), w.dtype, f"{name} heads={len(heads)}")
+    # O_0 = V_0 exactly for causal attention (one visible key, weight exactly 1)
+    for b, h in heads:
+        np.testing.assert_array_equal(gpu["o"][b, h, 0], x["v"][b, h, 0])
+    # bf16 output rounding alone would exceed the tolerance at |x| >= 8
+    if w.dtype == "bf16":
+        for n in ("o", "dq", "dk", "dv"):
+            assert np.abs(ref[n]).max() < 8.0, f"{n}: reference magnitude too large for an absolute bf16 bound"
+
+
+EDGE_S = [1, 2, 31, 33, 63, 64, 65, 127, 129, 255, 257]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("S", EDGE_S)
+def test_edge_shapes(device, S, D, dtype, causal):
+    w = si.Workload("edge", 2, 3, S, D, dtype, 1.0, 1.0, 0.1 if dtype == "bf16" else 1.0, causal)
+    print(f"\n[edge] S={S} D={D} {dtype} causal={causal}", flush=True)
+    x = si.make_inputs(w, seed=S * 7 + D)
+    gpu = gu.run_gpu(x, w, device, causal=causal)
+    ref = oracle_heads(x, w, all_heads(w), causal=causal)
+    gu.check(gu.errors(gpu, ref, all_heads(w)), dtype, f"S={S} D={D} {dtype} causal={causal}")
+
+
+@pytest.mark.parametrize("S", [300, 1000])
+def test_ragged_tails_long_d128_large_logits(device, S):
+    """Tails that are not a tile multiple with the sigma=4 query/key draw of the long workload."""
+    w = si.WORKLOADS["long8191_bf16"].with_shape(B=1, H=2, S=S)
+    x = si.make_inputs(w, seed=S)
+    gpu = gu.run_gpu(x, w, device)
+    ref = oracle_heads(x, w, all_heads(w))
+    gu.check(gu.errors(gpu, ref, all_heads(w)), "bf16", f"long draw S={S}")
+
+
+def test_accumulator_width_cell(device):
+    """Rigel §6: 448 + 127 * 0.0625 = 455.9375 needs a wide (fp32) accumulator for QK^T."""
+    import causal_attention_flash_amd as caf
+    torch = gu.torch_mod()
+    with open(os.path.join(GOLDEN, "accumulator_width.json")) as f:
+        g = json.load(f)
+    D = g["D"]
+    for dt in (torch.bfloat16, torch.float32):
+        q = torch.full((1, 1, 1, D), g["q"]["rest"], dtype=dt, device=device)
+        k = torch.full((1, 1, 1, D), g["k"]["rest"], dtype=dt, device=device)
+        q[0, 0, 0, 0] = g["q"]["first"]
+        k[0, 0, 0, 0] = g["k"]["first"]
+        v = torch.randn(1, 1, 1, D, device=device).to(dt)
+        o, lse = caf.attn_fwd(q, k, v, scale=g["scale"], causal=True)
+        torch.cuda.synchronize()
+        assert abs(lse.item() - g["lse"]) <= 1e-3, (dt, lse.item())
+        assert torch.equal(o, v)
+
+
+def test_all_negative_logits(device):
+    """Every score negative: a zero-initialised running max would corrupt P and LSE."""
+    w = si.Workload("neg", 2, 2, 200, 64, "bf16", 1.0, 1.0, 0.1)
+    x = si.make_inputs(w, seed=5)
+    x["q"] = si.round_to_bf16(np.abs(x["q"]) + 0.5)
+    x["k"] = si.round_to_bf16(-np.abs(x["k"]) - 0.5)
+    for n in ("q", "k"):
+        x[n + "_bits"] = si.f32_to_bf16_bits(x[n])
+    gpu = gu.run_gpu(x, w, device)
+    ref = oracle_heads(x, w, all_heads(w))
+    assert ref["lse"].max() < 0
+    gu.check(gu.errors(gpu, ref, all_heads(w)), "bf16", "all-negative logits")
+
+
+def test_backward_fed_with_oracle_forward(device):
+    """Isolate the backward: feed it the oracle's O (rounded to bf16) and LSE."""
+    import causal_attention_flash_amd as caf
+    torch = gu.torch_mod()
+    w = si.WORKLOADS["gpt125m_bf16"].with_shape(B=2, H=3)
+    x = si.make_inputs(w, seed=3)
+    ref = oracle_heads(x, w, all_heads(w))
+    q, k, v, do = (gu.to_device(x, n, "bf16", device) for n in ("q", "k", "v", "do"))
+    o = torch.from_numpy(si.f32_to_bf16_bits(ref["o"].astype(np.float32)).view(np.int16)).to(device)
+    o = o.view(torch.bfloat16).reshape(q.shape)
+    lse = torch.from_numpy(ref["lse"].astype(np.float32)).to(device).reshape(w.B, w.H, w.S)
+    dq, dk, dv = caf.attn_bwd(q, k, v, o, do, lse, scale=w.scale)
+    torch.cuda.synchronize()
+    gpu = {"o": ref["o"].reshape(w.B, w.H, w.S, w.D), "lse": ref["lse"].reshape(w.B, w.H, w.S),
+           "dq": gu.to_host64(dq), "dk": gu.to_host64(dk), "dv": gu.to_host64(dv)}
+    gu.check(gu.errors(gpu, ref, all_heads(w)), "bf16", "backward from oracle O/LSE")
+
+
+def test_stages_equal_attn_bwd_and_deterministic(device):
+    import causal_attention_flash_amd as caf
+    torch = gu.torch_mod()
+    w = si.WORKLOADS["gpt125m_bf16"].with_shape(B=2, H=4)
+    x = si.make_inputs(w, seed=11)
+    q, k, v, do = (gu.to_device(x, n, "bf16", device) for n in ("q", "k", "v", "do"))
+    o, lse = caf.attn_fwd(q, k, v)
+    o2, lse2 = caf.attn_fwd(q, k, v)
+    dq, dk, dv = caf.attn_bwd(q, k, v, o, do, lse)
+    delta = caf.attn_bwd_preprocess(o, do)
+    dk2, dv2 = caf.attn_bwd_dkdv(q, k, v, do, lse, delta)
+    dq2 = caf.attn_bwd_dq(q, k, v, do, lse, delta)
+    dq3, dk3, dv3 = caf.attn_bwd(q, k, v, o, do, lse)
+    torch.cuda.synchronize()
+    for a, b in ((o, o2), (lse, lse2), (dq, dq2), (dk, dk2), (dv, dv2), (dq, dq3), (dk, dk3), (dv, dv3)):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+    # delta is dO . O per row (fp32 accumulation of bf16 products)
+    ref_delta = (do.float() * o.float()).sum(-1)
+    assert torch.allclose(delta, ref_delta, rtol=1e-5, atol=1e-5)
+
+
+def test_empty_problem(device):
+    import causal_attention_flash_amd as caf
+    torch = gu.torch_mod()
+    q = torch.empty(0, 2, 16, 64, dtype=torch.bfloat16, device=device)
+    o, lse = caf.attn_fwd(q, q, q)
+    dq, dk, dv = caf.attn_bwd(q, q, q, o, q, lse)
+    torch.cuda.synchronize()
+    assert o.shape == q.shape and lse.shape == (0, 2, 16) and dq.shape == q.shape
+
+
+def test_full_size_invariants(device):
+    """Headline workload at full size: properties that hold for every head."""
+    w = si.WORKLOADS["gpt205m_bf16"]
+    x = si.make_inputs(w, seed=0)
+    gpu = gu.run_gpu(x, w, device)
+    # O_0 = V_0 exactly, dQ_0 = 0 exactly, for all 64 heads
+    np.testing.assert_array_equal(gpu["o"][:, :, 0], x["v"][:, :, 0])
+    np.testing.assert_array_equal(gpu["dq"][:, :, 0], 0.0)
+    # sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i per head (up to bf16 rounding of the outputs)
+    np.testing.assert_allclose(gpu["dk"].sum(axis=2), 0.0, atol=0.05)
+    np.testing.assert_allclose(gpu["dv"].sum(axis=2), x["do"].astype(np.float64).sum(axis=2), atol=0.05)
+    # LSE_0 = scale * q_0 . k_0 (one visible key)
+    lse0 = w.scale * np.einsum("bhd,bhd->bh", x["q"][:, :, 0].astype(np.float64), x["k"][:, :, 0])
+    np.testing.assert_allclose(gpu["lse"][:, :, 0], lse0, atol=1e-4)
