@@ -180,9 +180,11 @@ def test_full_size_invariants(device):
     w = si.WORKLOADS["gpt205m_bf16"]
     x = si.make_inputs(w, seed=0)
     gpu = gu.run_gpu(x, w, device)
-    # O_0 = V_0 exactly, dQ_0 = 0 exactly, for all 64 heads
+    # O_0 = V_0 exactly for all 64 heads.  dQ_0 is zero in exact arithmetic
+    # (dS_00 = P_00 (dP_00 - delta_0) with dP_00 = delta_0); on the GPU dP_00 comes
+    # from the MFMA and delta_0 from the preprocess, summed in different orders.
     np.testing.assert_array_equal(gpu["o"][:, :, 0], x["v"][:, :, 0])
-    np.testing.assert_array_equal(gpu["dq"][:, :, 0], 0.0)
+    np.testing.assert_allclose(gpu["dq"][:, :, 0], 0.0, atol=1e-6)
     # sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i per head (up to bf16 rounding of the outputs)
     np.testing.assert_allclose(gpu["dk"].sum(axis=2), 0.0, atol=0.05)
     np.testing.assert_allclose(gpu["dv"].sum(axis=2), x["do"].astype(np.float64).sum(axis=2), atol=0.05)
