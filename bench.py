@@ -175,11 +175,19 @@ def main():
                              causal, dt, stream), "dq")
 
     if args.profile_steps:
+        # A plain copy of known size first: the counters' reading for it calibrates
+        # FETCH_SIZE / WRITE_SIZE to bytes (copy_bytes read, copy_bytes written).
+        copy_bytes = 1 << 29
+        src = torch.ones(copy_bytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
         for i in range(args.profile_steps):
             fwd()
             bwd()
         torch.cuda.synchronize()
-        print(f"profile run: {args.profile_steps} steps of {w.name} done", flush=True)
+        print(f"profile run: copy of {copy_bytes} bytes, then {args.profile_steps} steps of {w.name}", flush=True)
         return
 
     for _ in range(args.warmup):

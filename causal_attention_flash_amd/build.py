@@ -28,6 +28,9 @@ CFLAGS = [
     f"--offload-arch={ARCH}",
     # no packed fp32 arithmetic (v_pk_*_f32) in generated device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the softmax reads every score, so AGPR-resident
+    # accumulators would cost a v_accvgpr_read per element and per iteration
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"),

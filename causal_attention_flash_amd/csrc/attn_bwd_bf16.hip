@@ -21,6 +21,8 @@
 // bound by register pressure): each wave keeps its own K and V (dK/dV pass) or
 // Q and dO (dQ pass) as MFMA operands in registers, plus two fp32 accumulators
 // of 32 rows x D; the streamed operand tiles are double-buffered in LDS.
+#include <type_traits>
+
 #include "attn_launch.h"
 #include "attn_tiles.h"
 
@@ -118,61 +120,71 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(
     }
     __syncthreads();
 
-    for (int t = t0; t < ntiles; ++t) {
-        const int b = (t - t0) & 1;
+    // One query tile against this wave's 32 keys; MASK instantiates the causal
+    // mask for tiles that cross the diagonal (query rows past S need no mask:
+    // their lse2 is +inf, so P is exactly 0 there).
+    auto tile = [&](auto mask_tag, int b, int qt0) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         const uint16_t* Qs = bufp(b);
         const uint16_t* Qt = Qs + Cfg::QROW;
         const uint16_t* dOs = Qt + Cfg::QTR;
         const uint16_t* dOt = dOs + Cfg::QROW;
         const float* L2s = stat(b);
         const float* DLs = L2s + BMQ;
-        const int qt0 = t * BMQ;
-        const bool active = !causal || qt0 + BMQ - 1 >= kw0;
-        if (active) {
-            const bool need_mask = (causal && qt0 < kw0 + 31) || (qt0 + BMQ > S);
 #pragma unroll
-            for (int qb = 0; qb < BMQ / 32; ++qb) {
-                // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
-                f32x16 sacc, pacc;
+        for (int qb = 0; qb < BMQ / 32; ++qb) {
+            // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
+            f32x16 sacc, pacc;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    sacc[r] = 0.f;
-                    pacc[r] = 0.f;
-                }
+            for (int r = 0; r < 16; ++r) {
+                sacc[r] = 0.f;
+                pacc[r] = 0.f;
+            }
 #pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks) {
-                    const int off = (qb * 32 + n) * RSTR + ks * 16 + 8 * h;
-                    sacc = mfma32(as_bf16x8(lds16(Qs + off)), kf[ks], sacc);
-                    pacc = mfma32(as_bf16x8(lds16(dOs + off)), vf[ks], pacc);
-                }
-                // P and dS; query rows of register r are qb*32 + crow(r, h)
+            for (int ks = 0; ks < D / 16; ++ks) {
+                const int off = (qb * 32 + n) * RSTR + ks * 16 + 8 * h;
+                sacc = mfma32(as_bf16x8(lds16(Qs + off)), kf[ks], sacc);
+                pacc = mfma32(as_bf16x8(lds16(dOs + off)), vf[ks], pacc);
+            }
+            // P and dS; query rows of register r are qb*32 + crow(r, h)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int rl = qb * 32 + 8 * g + 4 * h;
-                    const f32x4 l2 = *reinterpret_cast<const f32x4*>(L2s + rl);
-                    const f32x4 dl = *reinterpret_cast<const f32x4*>(DLs + rl);
+            for (int g = 0; g < 4; ++g) {
+                const int rl = qb * 32 + 8 * g + 4 * h;
+                const f32x4 l2 = *reinterpret_cast<const f32x4*>(L2s + rl);
+                const f32x4 dl = *reinterpret_cast<const f32x4*>(DLs + rl);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = 4 * g + i;
-                        float p = fast_exp2(fmaf(sacc[r], c, -l2[i]));
-                        if (need_mask && causal && key > qt0 + rl + i) p = 0.f;
-                        sacc[r] = p;
-                        pacc[r] = p * (pacc[r] - dl[i]);
-                    }
-                }
-                // dV^T += dO^T P ; dK^T += Q^T dS  (contraction over these 32 queries)
-#pragma unroll
-                for (int c2 = 0; c2 < 2; ++c2) {
-                    const bf16x8 pb = pack_operand(sacc, c2);
-                    const bf16x8 sb = pack_operand(pacc, c2);
-#pragma unroll
-                    for (int db = 0; db < D / 32; ++db) {
-                        const int off = (db * 32 + n) * TSTR + (qb * 2 + c2) * 16 + 8 * h;
-                        dvacc[db] = mfma32(as_bf16x8(lds16(dOt + off)), pb, dvacc[db]);
-                        dkacc[db] = mfma32(as_bf16x8(lds16(Qt + off)), sb, dkacc[db]);
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * g + i;
+                    float p = fast_exp2(fmaf(sacc[r], c, -l2[i]));
+                    if constexpr (MASK) p = key > qt0 + rl + i ? 0.f : p;
+                    sacc[r] = p;
+                    pacc[r] = p * (pacc[r] - dl[i]);
                 }
             }
+            // dV^T += dO^T P ; dK^T += Q^T dS  (contraction over these 32 queries)
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                const bf16x8 pb = pack_operand(sacc, c2);
+                const bf16x8 sb = pack_operand(pacc, c2);
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const int off = (db * 32 + n) * TSTR + (qb * 2 + c2) * 16 + 8 * h;
+                    dvacc[db] = mfma32(as_bf16x8(lds16(dOt + off)), pb, dvacc[db]);
+                    dkacc[db] = mfma32(as_bf16x8(lds16(Qt + off)), sb, dkacc[db]);
+                }
+            }
+        }
+    };
+
+    for (int t = t0; t < ntiles; ++t) {
+        const int b = (t - t0) & 1;
+        const int qt0 = t * BMQ;
+        // wave-uniform: skip query tiles entirely before this wave's first key
+        if (!causal || qt0 + BMQ - 1 >= kw0) {
+            if (causal && qt0 < kw0 + 31)
+                tile(std::true_type{}, b, qt0);
+            else
+                tile(std::false_type{}, b, qt0);
         }
         if (t + 1 < ntiles) {
             stage(b ^ 1);
@@ -297,49 +309,58 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(
     if (ntiles > 1) fetch(1);
     __syncthreads();
 
-    for (int t = 0; t < ntiles; ++t) {
-        const uint16_t* Ks = bufp(t & 1);
+    // One key tile against this wave's 32 queries; MASK instantiates the causal
+    // and sequence-end mask for tiles that cross the diagonal or the end.
+    auto tile = [&](auto mask_tag, int b, int k0) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const uint16_t* Ks = bufp(b);
         const uint16_t* Kt = Ks + Cfg::KROW;
         const uint16_t* Vs = Kt + Cfg::KTR;
-        const int k0 = t * BNK;
-        const bool active = !causal || k0 <= qw0 + 31;
-        if (active) {
-            const bool need_mask = (causal && k0 + BNK - 1 > qw0) || (k0 + BNK > S);
 #pragma unroll
-            for (int kb = 0; kb < BNK / 32; ++kb) {
-                // S^T = K Q^T and dP^T = V dO^T: 32 keys x this wave's 32 queries
-                f32x16 sacc, pacc;
+        for (int kb = 0; kb < BNK / 32; ++kb) {
+            // S^T = K Q^T and dP^T = V dO^T: 32 keys x this wave's 32 queries
+            f32x16 sacc, pacc;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    sacc[r] = 0.f;
-                    pacc[r] = 0.f;
+            for (int r = 0; r < 16; ++r) {
+                sacc[r] = 0.f;
+                pacc[r] = 0.f;
+            }
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) {
+                const int off = (kb * 32 + n) * RSTR + ks * 16 + 8 * h;
+                sacc = mfma32(as_bf16x8(lds16(Ks + off)), qf[ks], sacc);
+                pacc = mfma32(as_bf16x8(lds16(Vs + off)), of[ks], pacc);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float p = fast_exp2(fmaf(sacc[r], c, -l2));
+                if constexpr (MASK) {
+                    const int kk = k0 + kb * 32 + crow(r, h);
+                    p = ((causal && kk > q) || kk >= S) ? 0.f : p;
                 }
+                pacc[r] = p * (pacc[r] - dl);
+            }
+            // dQ^T += K^T dS^T (contraction over these 32 keys)
 #pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks) {
-                    const int off = (kb * 32 + n) * RSTR + ks * 16 + 8 * h;
-                    sacc = mfma32(as_bf16x8(lds16(Ks + off)), qf[ks], sacc);
-                    pacc = mfma32(as_bf16x8(lds16(Vs + off)), of[ks], pacc);
-                }
+            for (int c2 = 0; c2 < 2; ++c2) {
+                const bf16x8 sb = pack_operand(pacc, c2);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float p = fast_exp2(fmaf(sacc[r], c, -l2));
-                    if (need_mask) {
-                        const int kk = k0 + kb * 32 + crow(r, h);
-                        if ((causal && kk > q) || kk >= S) p = 0.f;
-                    }
-                    pacc[r] = p * (pacc[r] - dl);
-                }
-                // dQ^T += K^T dS^T (contraction over these 32 keys)
-#pragma unroll
-                for (int c2 = 0; c2 < 2; ++c2) {
-                    const bf16x8 sb = pack_operand(pacc, c2);
-#pragma unroll
-                    for (int db = 0; db < D / 32; ++db) {
-                        const int off = (db * 32 + n) * TSTR + (kb * 2 + c2) * 16 + 8 * h;
-                        dqacc[db] = mfma32(as_bf16x8(lds16(Kt + off)), sb, dqacc[db]);
-                    }
+                for (int db = 0; db < D / 32; ++db) {
+                    const int off = (db * 32 + n) * TSTR + (kb * 2 + c2) * 16 + 8 * h;
+                    dqacc[db] = mfma32(as_bf16x8(lds16(Kt + off)), sb, dqacc[db]);
                 }
             }
+        }
+    };
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int k0 = t * BNK;
+        // wave-uniform: skip key tiles entirely after this wave's last query
+        if (!causal || k0 <= qw0 + 31) {
+            if ((causal && k0 + BNK - 1 > qw0) || k0 + BNK > S)
+                tile(std::true_type{}, t & 1, k0);
+            else
+                tile(std::false_type{}, t & 1, k0);
         }
         if (t + 1 < ntiles) {
             stage((t + 1) & 1);

@@ -77,6 +77,18 @@ __device__ __forceinline__ bf16x8 pack_operand(const f32x16& acc, int c) {
     return __builtin_bit_cast(bf16x8, u);
 }
 
+// acc + the sum of eight bf16 values, two per v_dot2_f32_bf16 (fp32 accumulate).
+// The pairs are built element by element: a __builtin_bit_cast applied to one
+// element of a vector register was seen to read element 0 for every index.
+__device__ __forceinline__ float sum_bf16x8(const bf16x8& x, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{x[0], x[1]}, one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{x[2], x[3]}, one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{x[4], x[5]}, one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{x[6], x[7]}, one, acc, false);
+    return acc;
+}
+
 // Reductions over the lane pair (l, l ^ 32).  v_permlane32_swap exchanges the
 // upper half of its first register with the lower half of its second; given x in
 // both, every lane ends up holding x[l % 32] in one result and x[l % 32 + 32] in

@@ -27,6 +27,8 @@
 // * Q stays in registers for the whole key loop; K (row-major) and V^T tiles of
 //   64 keys are double-buffered in LDS, the next tile's global loads in flight
 //   while the current one is multiplied.
+#include <type_traits>
+
 #include "attn_launch.h"
 #include "attn_tiles.h"
 
@@ -111,91 +113,102 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const uint16_t* __restric
     }
     __syncthreads();
 
+    // One key tile of the online softmax; MASK instantiates the per-element
+    // causal / sequence-end mask (only tiles crossing the diagonal or the end).
+    auto tile = [&](auto mask_tag, const uint16_t* Ks, const uint16_t* Vt, int k0) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        // ---- S^T = K Q^T for BN keys x 32*QB queries
+        f32x16 sacc[QB][BN / 32];
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) {
+                const bf16x8 kf = as_bf16x8(lds16(Ks + (kb * 32 + n) * KSTR + ks * 16 + 8 * h));
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = mfma32(kf, qf[qb][ks], sacc[qb][kb]);
+            }
+        }
+        // ---- mask, row max (raw scores; c > 0 so max commutes with scaling)
+        float mx[QB];
+        bool grow = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int q = qw0 + qb * 32 + n;
+            float v = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    if constexpr (MASK) {
+                        const int key = k0 + kb * 32 + crow(r, h);
+                        const bool kill = (causal && key > q) || key >= S;
+                        sacc[qb][kb][r] = kill ? -INFINITY : sacc[qb][kb][r];
+                    }
+                    v = fmaxf(v, sacc[qb][kb][r]);
+                }
+            v = half_max(v) * c;
+            mx[qb] = v;
+            grow |= v > m[qb] + kRescaleSlack;
+        }
+        // ---- rescale only when some row max in the wave grew past the slack
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const float mn = fmaxf(m[qb], mx[qb]);
+                const float f = fast_exp2(m[qb] - mn);
+                m[qb] = mn;
+                l[qb] *= f;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= f;
+            }
+        }
+        // ---- P = exp2(s*c - m) rounded to bf16; the row sum adds the same
+        // rounded values the PV product multiplies, so numerator and
+        // denominator of O = (P V) / l carry the same rounding (a row whose
+        // weight sits on one key reproduces that key's V row).
+        bf16x8 pf[QB][BN / 16];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            float ls = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = fast_exp2(fmaf(sacc[qb][kb][r], c, -m[qb]));
+                pf[qb][2 * kb] = pack_operand(sacc[qb][kb], 0);
+                pf[qb][2 * kb + 1] = pack_operand(sacc[qb][kb], 1);
+                ls = sum_bf16x8(pf[qb][2 * kb], ls);
+                ls = sum_bf16x8(pf[qb][2 * kb + 1], ls);
+            }
+            l[qb] += ls;
+        }
+        // ---- O^T += V^T P^T
+#pragma unroll
+        for (int ks = 0; ks < BN / 16; ++ks) {
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const bf16x8 vf = as_bf16x8(lds16(Vt + (db * 32 + n) * VSTR + ks * 16 + 8 * h));
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32(vf, pf[qb][ks], oacc[qb][db]);
+            }
+        }
+    };
+
     for (int t = 0; t < ntiles; ++t) {
         const uint16_t* Ks = smem + (t & 1) * Cfg::BUF;
         const uint16_t* Vt = Ks + Cfg::KELEMS;
         const int k0 = t * BN;
-        const bool active = !causal || k0 <= qw0 + 32 * QB - 1;
-        if (active) {
-            // ---- S^T = K Q^T for BN keys x 32*QB queries
-            f32x16 sacc[QB][BN / 32];
-#pragma unroll
-            for (int kb = 0; kb < BN / 32; ++kb) {
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = 0.f;
-#pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks) {
-                    const bf16x8 kf = as_bf16x8(lds16(Ks + (kb * 32 + n) * KSTR + ks * 16 + 8 * h));
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = mfma32(kf, qf[qb][ks], sacc[qb][kb]);
-                }
-            }
-            // ---- mask, row max (raw scores; c > 0 so max commutes with scaling)
-            const bool need_mask = (causal && k0 + BN - 1 > qw0) || (k0 + BN > S);
-            float mx[QB];
-            bool grow = false;
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const int q = qw0 + qb * 32 + n;
-                float v = -INFINITY;
-#pragma unroll
-                for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        if (need_mask) {
-                            const int key = k0 + kb * 32 + crow(r, h);
-                            if ((causal && key > q) || key >= S) sacc[qb][kb][r] = -INFINITY;
-                        }
-                        v = fmaxf(v, sacc[qb][kb][r]);
-                    }
-                v = half_max(v) * c;
-                mx[qb] = v;
-                grow |= v > m[qb] + kRescaleSlack;
-            }
-            // ---- rescale only when some row max in the wave grew past the slack
-            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    const float mn = fmaxf(m[qb], mx[qb]);
-                    const float f = fast_exp2(m[qb] - mn);
-                    m[qb] = mn;
-                    l[qb] *= f;
-#pragma unroll
-                    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= f;
-                }
-            }
-            // ---- P = exp2(s*c - m), row sums, bf16 operands
-            bf16x8 pf[QB][BN / 16];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                float ls = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < BN / 32; ++kb) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float p = fast_exp2(fmaf(sacc[qb][kb][r], c, -m[qb]));
-                        sacc[qb][kb][r] = p;
-                        ls += p;
-                    }
-                    pf[qb][2 * kb] = pack_operand(sacc[qb][kb], 0);
-                    pf[qb][2 * kb + 1] = pack_operand(sacc[qb][kb], 1);
-                }
-                l[qb] += ls;
-            }
-            // ---- O^T += V^T P^T
-#pragma unroll
-            for (int ks = 0; ks < BN / 16; ++ks) {
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const bf16x8 vf = as_bf16x8(lds16(Vt + (db * 32 + n) * VSTR + ks * 16 + 8 * h));
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32(vf, pf[qb][ks], oacc[qb][db]);
-                }
-            }
+        // wave-uniform: skip tiles entirely above this wave's diagonal
+        if (!causal || k0 <= qw0 + 32 * QB - 1) {
+            if ((causal && k0 + BN - 1 > qw0) || k0 + BN > S)
+                tile(std::true_type{}, Ks, Vt, k0);
+            else
+                tile(std::false_type{}, Ks, Vt, k0);
         }
         if (t + 1 < ntiles) {
             uint16_t* nxt = smem + ((t + 1) & 1) * Cfg::BUF;
