@@ -20,7 +20,9 @@
 // Register and LDS budget (the pages' central finding is that this backward is
 // bound by register pressure): each wave keeps its own K and V (dK/dV pass) or
 // Q and dO (dQ pass) as MFMA operands in registers, plus two fp32 accumulators
-// of 32 rows x D; the streamed operand tiles are double-buffered in LDS.
+// of 32 rows x D; the streamed operand tiles are double-buffered in LDS,
+// row-major only: the contractions over their rows read them through the
+// transposing LDS read (lds_tr_operand).
 #include <type_traits>
 
 #include "attn_launch.h"
@@ -35,11 +37,11 @@ struct DkdvCfg {
     static constexpr int NW = 4;
     static constexpr int NT = NW * 64;
     static constexpr int BNK = NW * 32;  // keys per workgroup (32 per wave)
-    using QT = PairTile<BMQ, D, NT>;     // Q and dO tiles, row-major and transposed
-    static constexpr int QROW = QT::ROW_ELEMS;
-    static constexpr int QTR = QT::TRANS_ELEMS;
-    static constexpr int BUF_ELEMS = 2 * (QROW + QTR);  // Q, Q^T, dO, dO^T
-    static constexpr int BUF_STATS = 2 * BMQ;           // lse2, delta (fp32)
+    using QT = RowTile<BMQ, D, NT>;      // Q and dO tiles, row-major
+    static constexpr int STR = QT::STR;
+    static constexpr int QE = QT::ELEMS;
+    static constexpr int BUF_ELEMS = 2 * QE;   // Q, dO
+    static constexpr int BUF_STATS = 2 * BMQ;  // lse2, delta (fp32)
 };
 
 template <int D, int BMQ>
@@ -50,7 +52,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(
     int causal) {
     using Cfg = DkdvCfg<D, BMQ>;
     constexpr int NT = Cfg::NT, BNK = Cfg::BNK;
-    constexpr int RSTR = Cfg::QT::RSTR, TSTR = Cfg::QT::TSTR;
+    constexpr int STR = Cfg::STR;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Cfg::BUF_ELEMS];
     __shared__ __attribute__((aligned(16))) float sstat[2 * Cfg::BUF_STATS];
 
@@ -101,10 +103,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(
     auto stat = [&](int b) { return sstat + b * Cfg::BUF_STATS; };
     auto stage = [&](int b) {
         uint16_t* s = bufp(b);
-        qt.store_rows(s, tid);
-        qt.store_trans(s + Cfg::QROW, tid);
-        ot.store_rows(s + Cfg::QROW + Cfg::QTR, tid);
-        ot.store_trans(s + 2 * Cfg::QROW + Cfg::QTR, tid);
+        qt.store(s, tid);
+        ot.store(s + Cfg::QE, tid);
         st.store(stat(b), stat(b) + BMQ, tid);
     };
     auto fetch = [&](int t) {
@@ -126,9 +126,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(
     auto tile = [&](auto mask_tag, int b, int qt0) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const uint16_t* Qs = bufp(b);
-        const uint16_t* Qt = Qs + Cfg::QROW;
-        const uint16_t* dOs = Qt + Cfg::QTR;
-        const uint16_t* dOt = dOs + Cfg::QROW;
+        const uint16_t* dOs = Qs + Cfg::QE;
         const float* L2s = stat(b);
         const float* DLs = L2s + BMQ;
 #pragma unroll
@@ -142,7 +140,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(
             }
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks) {
-                const int off = (qb * 32 + n) * RSTR + ks * 16 + 8 * h;
+                const int off = (qb * 32 + n) * STR + ks * 16 + 8 * h;
                 sacc = mfma32(as_bf16x8(lds16(Qs + off)), kf[ks], sacc);
                 pacc = mfma32(as_bf16x8(lds16(dOs + off)), vf[ks], pacc);
             }
@@ -161,16 +159,17 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(
                     pacc[r] = p * (pacc[r] - dl[i]);
                 }
             }
-            // dV^T += dO^T P ; dK^T += Q^T dS  (contraction over these 32 queries)
+            // dV^T += dO^T P ; dK^T += Q^T dS  (contraction over these 32 queries;
+            // dO^T and Q^T read transposed from the row-major tiles)
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
                 const bf16x8 pb = pack_operand(sacc, c2);
                 const bf16x8 sb = pack_operand(pacc, c2);
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const int off = (db * 32 + n) * TSTR + (qb * 2 + c2) * 16 + 8 * h;
-                    dvacc[db] = mfma32(as_bf16x8(lds16(dOt + off)), pb, dvacc[db]);
-                    dkacc[db] = mfma32(as_bf16x8(lds16(Qt + off)), sb, dkacc[db]);
+                    const int r0 = (qb * 2 + c2) * 16;
+                    dvacc[db] = mfma32(lds_tr_operand<STR>(dOs, r0, db * 32, lane), pb, dvacc[db]);
+                    dkacc[db] = mfma32(lds_tr_operand<STR>(Qs, r0, db * 32, lane), sb, dkacc[db]);
                 }
             }
         }
@@ -238,10 +237,10 @@ struct DqCfg {
     static constexpr int NW = 4;
     static constexpr int NT = NW * 64;
     static constexpr int BMQ = NW * 32;  // queries per workgroup (32 per wave)
-    using KT = PairTile<BNK, D, NT>;     // K (row-major + transposed) and V (row-major)
-    static constexpr int KROW = KT::ROW_ELEMS;
-    static constexpr int KTR = KT::TRANS_ELEMS;
-    static constexpr int BUF_ELEMS = 2 * KROW + KTR;
+    using KT = RowTile<BNK, D, NT>;      // K and V tiles, row-major
+    static constexpr int STR = KT::STR;
+    static constexpr int KE = KT::ELEMS;
+    static constexpr int BUF_ELEMS = 2 * KE;  // K, V
 };
 
 template <int D, int BNK>
@@ -251,7 +250,7 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(
     uint16_t* __restrict__ dQ, int S, int nblk, int total, float c, float scale, int causal) {
     using Cfg = DqCfg<D, BNK>;
     constexpr int BMQ = Cfg::BMQ;
-    constexpr int RSTR = Cfg::KT::RSTR, TSTR = Cfg::KT::TSTR;
+    constexpr int STR = Cfg::STR;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Cfg::BUF_ELEMS];
 
     const int w = xcd_work_index(blockIdx.x, total);
@@ -295,9 +294,8 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(
     auto bufp = [&](int b) { return smem + b * Cfg::BUF_ELEMS; };
     auto stage = [&](int b) {
         uint16_t* s = bufp(b);
-        kt.store_rows(s, tid);
-        kt.store_trans(s + Cfg::KROW, tid);
-        vt.store_rows(s + Cfg::KROW + Cfg::KTR, tid);
+        kt.store(s, tid);
+        vt.store(s + Cfg::KE, tid);
     };
     auto fetch = [&](int t) {
         kt.load(Kh, t * BNK, S, tid);
@@ -314,8 +312,7 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(
     auto tile = [&](auto mask_tag, int b, int k0) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const uint16_t* Ks = bufp(b);
-        const uint16_t* Kt = Ks + Cfg::KROW;
-        const uint16_t* Vs = Kt + Cfg::KTR;
+        const uint16_t* Vs = Ks + Cfg::KE;
 #pragma unroll
         for (int kb = 0; kb < BNK / 32; ++kb) {
             // S^T = K Q^T and dP^T = V dO^T: 32 keys x this wave's 32 queries
@@ -327,7 +324,7 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(
             }
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks) {
-                const int off = (kb * 32 + n) * RSTR + ks * 16 + 8 * h;
+                const int off = (kb * 32 + n) * STR + ks * 16 + 8 * h;
                 sacc = mfma32(as_bf16x8(lds16(Ks + off)), qf[ks], sacc);
                 pacc = mfma32(as_bf16x8(lds16(Vs + off)), of[ks], pacc);
             }
@@ -340,15 +337,14 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(
                 }
                 pacc[r] = p * (pacc[r] - dl);
             }
-            // dQ^T += K^T dS^T (contraction over these 32 keys)
+            // dQ^T += K^T dS^T (contraction over these 32 keys; K^T read
+            // transposed from the row-major K tile)
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
                 const bf16x8 sb = pack_operand(pacc, c2);
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const int off = (db * 32 + n) * TSTR + (kb * 2 + c2) * 16 + 8 * h;
-                    dqacc[db] = mfma32(as_bf16x8(lds16(Kt + off)), sb, dqacc[db]);
-                }
+                for (int db = 0; db < D / 32; ++db)
+                    dqacc[db] = mfma32(lds_tr_operand<STR>(Ks, (kb * 2 + c2) * 16, db * 32, lane), sb, dqacc[db]);
             }
         }
     };

@@ -17,8 +17,8 @@
 // hold rows 16c + 8*(v/4) + 4h + (v%4), v = 0..7, so they form the k slots of
 // one 16-deep contraction step whose k order is "rows 16c + {0..3, 8..11}" for
 // h = 0 and "rows 16c + {4..7, 12..15}" for h = 1.  The operand on the other
-// side is read from LDS in exactly that order (kperm16 below stores it that way,
-// so one 16-byte LDS read fetches the eight values).
+// side is read from a row-major LDS tile in exactly that order by the gfx950
+// transposing LDS read (lds_tr_operand below).
 //
 // This is the AMD counterpart of the problem the pages spend a section on
 // (pairing softmax row statistics with accumulator lanes when the lane map is
@@ -50,16 +50,31 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 // Row of the 32x32 C tile held by register r of a lane in half h.
 __device__ __forceinline__ int crow(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-// Position, inside a 16-wide group, at which index t (0..15) is stored so that
-// lane half h finds contraction slots v = 0..7 at positions 8h + v.  The map
-// swaps the middle two groups of four: {0..3, 4..7, 8..11, 12..15} ->
-// {0..3, 8..11, 4..7, 12..15}.
-__device__ __forceinline__ int kperm16(int t) {
-    const int g = t >> 2;
-    const int pg = (g == 1) ? 2 : (g == 2) ? 1 : g;
-    return (pg << 2) | (t & 3);
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Operand for a contraction over the ROWS of a row-major bf16 LDS tile T (row
+// stride STR elements): lane (n, h) receives T[r0 + kslot(v)][c0 + n] for
+// v = 0..7, with kslot(v) = 8*(v/4) + 4*h + (v%4) -- the row order of C
+// registers 8c .. 8c+7, so the result pairs with pack_operand() of a C tile.
+//
+// Built from two ds_read_b64_tr_b16.  That instruction works on groups of 16
+// lanes: lane i of a group receives, as element k, element (i % 4) of the
+// 4-element chunk addressed by lane 4k + i/4 of the same group.  Lane j of group
+// g therefore addresses row r0 + 4*(g/2) + j/4 (plus 8 for the second read) at
+// column c0 + 16*(g%2) + 4*(j%4).  c0 and STR must keep those 8-byte aligned.
+template <int STR>
+__device__ __forceinline__ bf16x8 lds_tr_operand(const uint16_t* T, int r0, int c0, int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    const int row = r0 + 4 * (g >> 1) + (j >> 2);
+    const int col = c0 + 16 * (g & 1) + 4 * (j & 3);
+    const uint16_t* p = T + row * STR + col;
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * STR));
+    const i16x8 r = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, r);
 }
-__device__ __forceinline__ int kperm(int t) { return (t & ~15) | kperm16(t & 15); }
 
 // Two fp32 -> packed bf16 (round to nearest even), a in the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {

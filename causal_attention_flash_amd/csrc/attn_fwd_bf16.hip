@@ -18,15 +18,18 @@
 //   query (C column) and the row max / row sum are in-lane reductions plus one
 //   exchange between the two lane halves (v_permlane32_swap).
 // * P^T, packed to bf16 straight from the C registers, is the B operand of
-//   O^T += V^T P^T; V^T is staged in LDS in the matching key order, so the
-//   rescale O *= factor is a per-lane multiply (no diag-matrix product).
+//   O^T += V^T P^T; V stays row-major in LDS and its transposed operand comes
+//   from ds_read_b64_tr_b16, in the key order of the C registers.  The rescale
+//   O *= factor is a per-lane multiply (no diag-matrix product).
 // * The O rescale is skipped unless some row max in the wave grew by more than
 //   kRescaleSlack (log2 units): P values are then bounded by 2^kRescaleSlack,
 //   which fp32 accumulation and bf16 P absorb; the result is the same function,
 //   only the reference point of the exponent differs.
-// * Q stays in registers for the whole key loop; K (row-major) and V^T tiles of
-//   64 keys are double-buffered in LDS, the next tile's global loads in flight
-//   while the current one is multiplied.
+// * Software pipeline: K runs one tile ahead of V in LDS, so iteration t issues
+//   the MFMAs of S^T for tile t+1 next to the exp/max/sum VALU work of tile t
+//   (the MFMA unit works asynchronously from the VALU), then O += V_t P_t.
+//   Q stays in registers for the whole loop; the next tiles' global loads are in
+//   flight while the current one is multiplied; one barrier per tile.
 #include <type_traits>
 
 #include "attn_launch.h"
@@ -42,11 +45,9 @@ struct FwdCfg {
     static constexpr int NT = NW * 64;
     static constexpr int BM = NW * 32 * QB;  // queries per workgroup
     static constexpr int BN = 64;            // keys per tile
-    using KT = PairTile<BN, D, NT>;
-    static constexpr int KELEMS = KT::ROW_ELEMS;
-    static constexpr int VELEMS = KT::TRANS_ELEMS;
-    static constexpr int BUF = KELEMS + VELEMS;
-    static constexpr int LDS_BYTES = 2 * BUF * 2;
+    using Tile = RowTile<BN, D, NT>;
+    static constexpr int STR = Tile::STR;
+    static constexpr int TE = Tile::ELEMS;   // one K or V tile in LDS (elements)
 };
 
 template <int D, int QB>
@@ -56,9 +57,9 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const uint16_t* __restric
                                                        uint16_t* __restrict__ O, float* __restrict__ LSE,
                                                        int S, int nblk, int total, float c, int causal) {
     using Cfg = FwdCfg<D, QB>;
-    constexpr int BM = Cfg::BM, BN = Cfg::BN;
-    constexpr int KSTR = Cfg::KT::RSTR, VSTR = Cfg::KT::TSTR;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Cfg::BUF];
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, STR = Cfg::STR, TE = Cfg::TE;
+    constexpr int KB = BN / 32;  // 32-key blocks per tile
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TE];  // K[2], V[2]
 
     const int w = xcd_work_index(blockIdx.x, total);
     const int head = w / nblk;
@@ -75,7 +76,12 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const uint16_t* __restric
     const int qw0 = q0 + wave * 32 * QB;
 
     const int kend = causal ? min(S, q0 + BM) : S;
-    const int ntiles = (kend + BN - 1) / BN;
+    const int ntiles = (kend + BN - 1) / BN;  // tiles the workgroup stages
+    // tiles this wave multiplies: the causal ones up to its last query
+    const int nw = causal ? min(ntiles, (qw0 + 32 * QB - 1) / BN + 1) : ntiles;
+
+    auto kbuf = [&](int t) { return smem + (t & 1) * TE; };
+    auto vbuf = [&](int t) { return smem + (2 + (t & 1)) * TE; };
 
     // Q as the B operand of S^T = K Q^T: lane holds query qw0+32qb+n, d = 16ks+8h..+7.
     bf16x8 qf[QB][D / 16];
@@ -102,36 +108,29 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const uint16_t* __restric
             for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
     }
 
-    typename Cfg::KT kt, vt;
-    kt.load(Kh, 0, S, tid);
-    vt.load(Vh, 0, S, tid);
-    kt.store_rows(smem, tid);
-    vt.store_trans(smem + Cfg::KELEMS, tid);
-    if (ntiles > 1) {
-        kt.load(Kh, BN, S, tid);
-        vt.load(Vh, BN, S, tid);
-    }
-    __syncthreads();
-
-    // One key tile of the online softmax; MASK instantiates the per-element
-    // causal / sequence-end mask (only tiles crossing the diagonal or the end).
-    auto tile = [&](auto mask_tag, const uint16_t* Ks, const uint16_t* Vt, int k0) {
-        constexpr bool MASK = decltype(mask_tag)::value;
-        // ---- S^T = K Q^T for BN keys x 32*QB queries
-        f32x16 sacc[QB][BN / 32];
+    // S^T tile for the keys of tile t: sacc[qb][kb] (zeroed, then accumulated)
+    auto scores = [&](f32x16 (&sacc)[QB][KB], int t) {
+        const uint16_t* Ks = kbuf(t);
 #pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks) {
-                const bf16x8 kf = as_bf16x8(lds16(Ks + (kb * 32 + n) * KSTR + ks * 16 + 8 * h));
+                const bf16x8 kf = as_bf16x8(lds16(Ks + (kb * 32 + n) * STR + ks * 16 + 8 * h));
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = mfma32(kf, qf[qb][ks], sacc[qb][kb]);
             }
         }
+    };
+
+    // Softmax of tile t's scores and O += V_t P_t.  MASK instantiates the
+    // per-element causal / sequence-end mask (tiles crossing the diagonal or S).
+    auto softmax_pv = [&](auto mask_tag, f32x16 (&sacc)[QB][KB], int t) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const int k0 = t * BN;
         // ---- mask, row max (raw scores; c > 0 so max commutes with scaling)
         float mx[QB];
         bool grow = false;
@@ -140,7 +139,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const uint16_t* __restric
             const int q = qw0 + qb * 32 + n;
             float v = -INFINITY;
 #pragma unroll
-            for (int kb = 0; kb < BN / 32; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     if constexpr (MASK) {
@@ -177,7 +176,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const uint16_t* __restric
         for (int qb = 0; qb < QB; ++qb) {
             float ls = 0.f;
 #pragma unroll
-            for (int kb = 0; kb < BN / 32; ++kb) {
+            for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = fast_exp2(fmaf(sacc[qb][kb][r], c, -m[qb]));
                 pf[qb][2 * kb] = pack_operand(sacc[qb][kb], 0);
@@ -187,39 +186,60 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const uint16_t* __restric
             }
             l[qb] += ls;
         }
-        // ---- O^T += V^T P^T
+        // ---- O^T += V^T P^T, V^T read transposed from the row-major V tile
+        const uint16_t* Vs = vbuf(t);
 #pragma unroll
         for (int ks = 0; ks < BN / 16; ++ks) {
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-                const bf16x8 vf = as_bf16x8(lds16(Vt + (db * 32 + n) * VSTR + ks * 16 + 8 * h));
+                const bf16x8 vf = lds_tr_operand<STR>(Vs, ks * 16, db * 32, lane);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32(vf, pf[qb][ks], oacc[qb][db]);
             }
         }
     };
 
-    for (int t = 0; t < ntiles; ++t) {
-        const uint16_t* Ks = smem + (t & 1) * Cfg::BUF;
-        const uint16_t* Vt = Ks + Cfg::KELEMS;
+    // One pipelined step: the next tile's scores, then this tile's softmax and PV.
+    auto step = [&](int t, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB]) {
+        if (t + 1 < nw) scores(nxt, t + 1);
         const int k0 = t * BN;
-        // wave-uniform: skip tiles entirely above this wave's diagonal
-        if (!causal || k0 <= qw0 + 32 * QB - 1) {
-            if ((causal && k0 + BN - 1 > qw0) || k0 + BN > S)
-                tile(std::true_type{}, Ks, Vt, k0);
-            else
-                tile(std::false_type{}, Ks, Vt, k0);
-        }
-        if (t + 1 < ntiles) {
-            uint16_t* nxt = smem + ((t + 1) & 1) * Cfg::BUF;
-            kt.store_rows(nxt, tid);
-            vt.store_trans(nxt + Cfg::KELEMS, tid);
-            if (t + 2 < ntiles) {
-                kt.load(Kh, (t + 2) * BN, S, tid);
-                vt.load(Vh, (t + 2) * BN, S, tid);
-            }
-        }
+        if ((causal && k0 + BN - 1 > qw0) || k0 + BN > S)
+            softmax_pv(std::true_type{}, cur, t);
+        else
+            softmax_pv(std::false_type{}, cur, t);
+    };
+
+    // ---- prologue: K_0, V_0, K_1 in LDS; V_1 and K_2 in flight in registers
+    typename Cfg::Tile kt, vt;
+    kt.load(Kh, 0, S, tid);
+    vt.load(Vh, 0, S, tid);
+    kt.store(kbuf(0), tid);
+    vt.store(vbuf(0), tid);
+    if (ntiles > 1) {
+        kt.load(Kh, BN, S, tid);
+        vt.load(Vh, BN, S, tid);
+        kt.store(kbuf(1), tid);
+        if (ntiles > 2) kt.load(Kh, 2 * BN, S, tid);
+    }
+    __syncthreads();
+
+    f32x16 sa[QB][KB], sb[QB][KB];
+    if (nw > 0) scores(sa, 0);
+
+    // Iteration t: stage K_{t+2} (into K_t's buffer, consumed last iteration) and
+    // V_{t+1} (into V_{t-1}'s buffer), start the loads of K_{t+3} and V_{t+2},
+    // compute, then one barrier.
+    auto iteration = [&](int t, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB]) {
+        if (t + 2 < ntiles) kt.store(kbuf(t), tid);
+        if (t + 1 < ntiles) vt.store(vbuf(t + 1), tid);
+        if (t + 3 < ntiles) kt.load(Kh, (t + 3) * BN, S, tid);
+        if (t + 2 < ntiles) vt.load(Vh, (t + 2) * BN, S, tid);
+        if (t < nw) step(t, cur, nxt);
         __syncthreads();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        iteration(t, sa, sb);
+        if (t + 1 < ntiles) iteration(t + 1, sb, sa);
     }
 
     // ---- epilogue: O = O / l (l == 0 -> 0), LSE = (m + log2 l) * ln 2

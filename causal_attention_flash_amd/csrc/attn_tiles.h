@@ -1,16 +1,13 @@
 // Global -> LDS staging of bf16 row tiles ([rows][D], D contiguous) for the
 // gfx950 attention kernels.  A tile is fetched with 16-byte loads into
-// registers first (issued one iteration ahead, so the loads overlap the MFMA
-// work on the previous tile), then written to LDS in one or both of two forms:
+// registers first (issued an iteration ahead, so the loads overlap the MFMA work
+// on earlier tiles), then written to LDS row-major as [ROWS][D + 8].
 //
-//   row-major   [ROWS][D + 8]   operand reads of 8 consecutive d (16 bytes);
-//   transposed  [D][ROWS + 8]   operand reads of 8 rows at one d, stored in the
-//                               kperm order of attn_device.h so that one
-//                               16-byte read returns a lane's 8 k slots.
-//
-// The +8 element pad per LDS row staggers consecutive rows across banks for the
-// 16-byte operand reads.  Rows at or beyond S are zero-filled, so tail tiles
-// need no special path in the loads.
+// Operand reads of 8 consecutive columns use 16-byte ds_read_b128; operand reads
+// that contract over the rows use the transposing read (lds_tr_operand), so no
+// tile is ever stored transposed.  The 8-element pad per row staggers
+// consecutive rows across LDS banks for both kinds of read.  Rows at or beyond S
+// are zero-filled, so tail tiles need no special path downstream of the load.
 #pragma once
 
 #include "attn_device.h"
@@ -18,62 +15,35 @@
 namespace attn {
 
 template <int ROWS, int D, int NT = 256>
-struct PairTile {
-    static constexpr int RSTR = D + 8;      // row-major LDS stride (elements)
-    static constexpr int TSTR = ROWS + 8;   // transposed LDS stride (elements)
-    static constexpr int CPR = D / 8;       // 16-byte chunks per row
-    static constexpr int UNITS = (ROWS / 2) * CPR;  // units of 2 rows x 8 columns
-    static constexpr int PT = (UNITS + NT - 1) / NT;
+struct RowTile {
+    static constexpr int STR = D + 8;          // LDS row stride (elements)
+    static constexpr int ELEMS = ROWS * STR;   // LDS footprint (elements)
+    static constexpr int CPR = D / 8;          // 16-byte chunks per row
+    static constexpr int CHUNKS = ROWS * CPR;
+    static constexpr int PT = (CHUNKS + NT - 1) / NT;
     static_assert(ROWS % 32 == 0 && D % 32 == 0, "tile shape");
-    static constexpr int ROW_ELEMS = ROWS * RSTR;
-    static constexpr int TRANS_ELEMS = D * TSTR;
 
-    u32x4 r0[PT], r1[PT];
+    u32x4 r[PT];
 
     __device__ __forceinline__ void load(const uint16_t* __restrict__ g, int row0, int S, int tid) {
 #pragma unroll
         for (int i = 0; i < PT; ++i) {
-            const int u = tid + i * NT;
-            u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-            if (UNITS % NT == 0 || u < UNITS) {
-                const int p = u / CPR;
-                const int col = (u % CPR) * 8;
-                const int row = row0 + 2 * p;
-                if (row < S) a = ldg16(g + (size_t)row * D + col);
-                if (row + 1 < S) b = ldg16(g + (size_t)(row + 1) * D + col);
+            const int c = tid + i * NT;
+            u32x4 a = {0u, 0u, 0u, 0u};
+            if (CHUNKS % NT == 0 || c < CHUNKS) {
+                const int row = row0 + c / CPR;
+                if (row < S) a = ldg16(g + (size_t)row * D + (c % CPR) * 8);
             }
-            r0[i] = a;
-            r1[i] = b;
+            r[i] = a;
         }
     }
 
-    __device__ __forceinline__ void store_rows(uint16_t* s, int tid) const {
+    __device__ __forceinline__ void store(uint16_t* s, int tid) const {
 #pragma unroll
         for (int i = 0; i < PT; ++i) {
-            const int u = tid + i * NT;
-            if (UNITS % NT == 0 || u < UNITS) {
-                const int p = u / CPR;
-                const int col = (u % CPR) * 8;
-                *reinterpret_cast<u32x4*>(s + (2 * p) * RSTR + col) = r0[i];
-                *reinterpret_cast<u32x4*>(s + (2 * p + 1) * RSTR + col) = r1[i];
-            }
-        }
-    }
-
-    __device__ __forceinline__ void store_trans(uint16_t* s, int tid) const {
-#pragma unroll
-        for (int i = 0; i < PT; ++i) {
-            const int u = tid + i * NT;
-            if (UNITS % NT == 0 || u < UNITS) {
-                const int p = u / CPR;
-                const int col = (u % CPR) * 8;
-                const int pos = kperm(2 * p);  // even; row 2p+1 lands at pos+1
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    *reinterpret_cast<uint32_t*>(s + (col + 2 * e) * TSTR + pos) = pack_lo(r0[i][e], r1[i][e]);
-                    *reinterpret_cast<uint32_t*>(s + (col + 2 * e + 1) * TSTR + pos) = pack_hi(r0[i][e], r1[i][e]);
-                }
-            }
+            const int c = tid + i * NT;
+            if (CHUNKS % NT == 0 || c < CHUNKS)
+                *reinterpret_cast<u32x4*>(s + (c / CPR) * STR + (c % CPR) * 8) = r[i];
         }
     }
 };
