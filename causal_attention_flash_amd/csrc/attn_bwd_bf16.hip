@@ -30,11 +30,18 @@
 
 namespace attn {
 
+#ifndef DKDV_NW
+#define DKDV_NW 4
+#endif
+#ifndef DQ_NW
+#define DQ_NW 4
+#endif
+
 // ============================================================== dK / dV pass
 
-template <int D, int BMQ>
+template <int D, int BMQ, int NW_>
 struct DkdvCfg {
-    static constexpr int NW = 4;
+    static constexpr int NW = NW_;
     static constexpr int NT = NW * 64;
     static constexpr int BNK = NW * 32;  // keys per workgroup (32 per wave)
     using QT = RowTile<BMQ, D, NT>;      // Q and dO tiles, row-major
@@ -44,21 +51,21 @@ struct DkdvCfg {
     static constexpr int BUF_STATS = 2 * BMQ;  // lse2, delta (fp32)
 };
 
-template <int D, int BMQ>
-__global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(
+template <int D, int BMQ, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int S, int nblk, int total, float c, float scale,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int S, int nblk, int BH, float c, float scale,
     int causal) {
-    using Cfg = DkdvCfg<D, BMQ>;
+    using Cfg = DkdvCfg<D, BMQ, NW>;
     constexpr int NT = Cfg::NT, BNK = Cfg::BNK;
     constexpr int STR = Cfg::STR;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Cfg::BUF_ELEMS];
     __shared__ __attribute__((aligned(16))) float sstat[2 * Cfg::BUF_STATS];
 
-    const int w = xcd_work_index(blockIdx.x, total);
-    const int head = w / nblk;
-    const int kblk = w % nblk;  // low key blocks see the most queries: first
+    const WorkItem wi = heavy_first(blockIdx.x, BH);
+    const int head = wi.head;
+    const int kblk = wi.rank;  // low key blocks see the most queries: first
     const int n0 = kblk * BNK;
     const size_t base = (size_t)head * S * D;
     const uint16_t* Qh = Q + base;
@@ -211,30 +218,30 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(
     }
 }
 
-template <int D, int BMQ>
+template <int D, int BMQ, int NW>
 static hipError_t launch_dkdv(const LaunchArgs& a) {
-    using Cfg = DkdvCfg<D, BMQ>;
+    using Cfg = DkdvCfg<D, BMQ, NW>;
     const int nblk = (int)((a.S + Cfg::BNK - 1) / Cfg::BNK);
     const int64_t total = (int64_t)nblk * a.BH;
     if (total > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, BMQ>), dim3((unsigned)total), dim3(Cfg::NT), 0, a.stream,
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, BMQ, NW>), dim3((unsigned)total), dim3(Cfg::NT), 0, a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse_in, a.delta_in, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                       (int)a.S, nblk, (int)total, a.scale * kLog2e, a.scale, a.causal);
+                       (int)a.S, nblk, (int)a.BH, a.scale * kLog2e, a.scale, a.causal);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_dkdv_bf16(const LaunchArgs& a) {
-    if (a.D == 64) return launch_dkdv<64, 64>(a);
-    if (a.D == 128) return launch_dkdv<128, 32>(a);
+    if (a.D == 64) return launch_dkdv<64, 64, DKDV_NW>(a);
+    if (a.D == 128) return launch_dkdv<128, 32, DKDV_NW>(a);
     return hipErrorInvalidValue;
 }
 
 // ================================================================== dQ pass
 
-template <int D, int BNK>
+template <int D, int BNK, int NW_>
 struct DqCfg {
-    static constexpr int NW = 4;
+    static constexpr int NW = NW_;
     static constexpr int NT = NW * 64;
     static constexpr int BMQ = NW * 32;  // queries per workgroup (32 per wave)
     using KT = RowTile<BNK, D, NT>;      // K and V tiles, row-major
@@ -243,19 +250,19 @@ struct DqCfg {
     static constexpr int BUF_ELEMS = 2 * KE;  // K, V
 };
 
-template <int D, int BNK>
-__global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(
+template <int D, int BNK, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
-    uint16_t* __restrict__ dQ, int S, int nblk, int total, float c, float scale, int causal) {
-    using Cfg = DqCfg<D, BNK>;
+    uint16_t* __restrict__ dQ, int S, int nblk, int BH, float c, float scale, int causal) {
+    using Cfg = DqCfg<D, BNK, NW>;
     constexpr int BMQ = Cfg::BMQ;
     constexpr int STR = Cfg::STR;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Cfg::BUF_ELEMS];
 
-    const int w = xcd_work_index(blockIdx.x, total);
-    const int head = w / nblk;
-    const int qblk = nblk - 1 - (w % nblk);  // high query blocks see the most keys: first
+    const WorkItem wi = heavy_first(blockIdx.x, BH);
+    const int head = wi.head;
+    const int qblk = nblk - 1 - wi.rank;  // high query blocks see the most keys: first
     const int q0 = qblk * BMQ;
     const size_t base = (size_t)head * S * D;
     const uint16_t* Kh = K + base;
@@ -379,22 +386,22 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(
     }
 }
 
-template <int D, int BNK>
+template <int D, int BNK, int NW>
 static hipError_t launch_dq(const LaunchArgs& a) {
-    using Cfg = DqCfg<D, BNK>;
+    using Cfg = DqCfg<D, BNK, NW>;
     const int nblk = (int)((a.S + Cfg::BMQ - 1) / Cfg::BMQ);
     const int64_t total = (int64_t)nblk * a.BH;
     if (total > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, BNK>), dim3((unsigned)total), dim3(Cfg::NT), 0, a.stream,
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, BNK, NW>), dim3((unsigned)total), dim3(Cfg::NT), 0, a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse_in, a.delta_in, (uint16_t*)a.dq, (int)a.S, nblk,
-                       (int)total, a.scale * kLog2e, a.scale, a.causal);
+                       (int)a.BH, a.scale * kLog2e, a.scale, a.causal);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq_bf16(const LaunchArgs& a) {
-    if (a.D == 64) return launch_dq<64, 64>(a);
-    if (a.D == 128) return launch_dq<128, 32>(a);
+    if (a.D == 64) return launch_dq<64, 64, DQ_NW>(a);
+    if (a.D == 128) return launch_dq<128, 32, DQ_NW>(a);
     return hipErrorInvalidValue;
 }
 

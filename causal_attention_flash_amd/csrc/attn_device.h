@@ -144,18 +144,16 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
     return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
-// Work-item order for a 1-D grid of `total` blocks dispatched round-robin over
-// the 8 XCDs: consecutive work items land on the same XCD, so the blocks that
-// share a head's K/V (or Q/dO) also share that XCD's L2.
-__device__ __forceinline__ int xcd_work_index(int bid, int total) {
-    constexpr int kXcd = 8;
-    const int per = total / kXcd;
-    const int rem = total % kXcd;
-    const int xcd = bid % kXcd;
-    const int slot = bid / kXcd;
-    // XCDs with index < rem receive one extra block.
-    const int base = xcd * per + (xcd < rem ? xcd : rem);
-    return base + slot;
-}
+// Block order for a 1-D grid of nblk * BH blocks (BH = batch x heads): block b
+// works on head b % BH at position rank = b / BH in its head's order of causal
+// work, heaviest first.  Blocks are dispatched in index order as slots free up,
+// so every head's heaviest blocks start first and the light ones pack in behind
+// them (greedy list scheduling in decreasing order), which keeps the tail of the
+// grid short.  The dispatcher assigns block b to XCD b % 8, so whenever BH is a
+// multiple of 8 all blocks of one head run on one XCD and share its L2.
+struct WorkItem {
+    int head, rank;
+};
+__device__ __forceinline__ WorkItem heavy_first(int bid, int BH) { return {bid % BH, bid / BH}; }
 
 }  // namespace attn

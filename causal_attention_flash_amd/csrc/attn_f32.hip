@@ -40,14 +40,14 @@ __device__ __forceinline__ void stage_rows_f32(float* dst, const float* __restri
 template <int D>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                       const float* __restrict__ V, float* __restrict__ O,
-                                                      float* __restrict__ LSE, int S, int nblk, int total, float c,
+                                                      float* __restrict__ LSE, int S, int nblk, int BH, float c,
                                                       int causal) {
     constexpr int G = D / 32, R = 256 / G;
     __shared__ __attribute__((aligned(16))) float Ks[kF32Tile * D];
     __shared__ __attribute__((aligned(16))) float Vs[kF32Tile * D];
-    const int w = xcd_work_index(blockIdx.x, total);
-    const int head = w / nblk;
-    const int blk = nblk - 1 - (w % nblk);
+    const WorkItem wi = heavy_first(blockIdx.x, BH);
+    const int head = wi.head;
+    const int blk = nblk - 1 - wi.rank;
     const int q0 = blk * R;
     const size_t base = (size_t)head * S * D;
     const int tid = threadIdx.x;
@@ -106,14 +106,14 @@ template <int D>
 __global__ __launch_bounds__(256) void dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                      const float* __restrict__ V, const float* __restrict__ dO,
                                                      const float* __restrict__ LSE, const float* __restrict__ Delta,
-                                                     float* __restrict__ dQ, int S, int nblk, int total, float c,
+                                                     float* __restrict__ dQ, int S, int nblk, int BH, float c,
                                                      float scale, int causal) {
     constexpr int G = D / 32, R = 256 / G;
     __shared__ __attribute__((aligned(16))) float Ks[kF32Tile * D];
     __shared__ __attribute__((aligned(16))) float Vs[kF32Tile * D];
-    const int w = xcd_work_index(blockIdx.x, total);
-    const int head = w / nblk;
-    const int blk = nblk - 1 - (w % nblk);
+    const WorkItem wi = heavy_first(blockIdx.x, BH);
+    const int head = wi.head;
+    const int blk = nblk - 1 - wi.rank;
     const int q0 = blk * R;
     const size_t base = (size_t)head * S * D;
     const int tid = threadIdx.x;
@@ -165,15 +165,15 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(const float* __restrict__
                                                        const float* __restrict__ V, const float* __restrict__ dO,
                                                        const float* __restrict__ LSE,
                                                        const float* __restrict__ Delta, float* __restrict__ dK,
-                                                       float* __restrict__ dV, int S, int nblk, int total, float c,
+                                                       float* __restrict__ dV, int S, int nblk, int BH, float c,
                                                        float scale, int causal) {
     constexpr int G = D / 32, R = 256 / G;
     __shared__ __attribute__((aligned(16))) float Qs[kF32Tile * D];
     __shared__ __attribute__((aligned(16))) float Os[kF32Tile * D];
     __shared__ float L2s[kF32Tile], DLs[kF32Tile];
-    const int w = xcd_work_index(blockIdx.x, total);
-    const int head = w / nblk;
-    const int blk = w % nblk;
+    const WorkItem wi = heavy_first(blockIdx.x, BH);
+    const int head = wi.head;
+    const int blk = wi.rank;
     const int n0 = blk * R;
     const size_t base = (size_t)head * S * D;
     const int tid = threadIdx.x;
@@ -245,7 +245,7 @@ static hipError_t fwd_f32(const LaunchArgs& a) {
     const int total = f32_blocks<D>(a, &nblk);
     if (total < 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3(total), dim3(256), 0, a.stream, (const float*)a.q,
-                       (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, (int)a.S, nblk, total,
+                       (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, (int)a.S, nblk, (int)a.BH,
                        a.scale * kLog2e, a.causal);
     return hipGetLastError();
 }
@@ -257,7 +257,7 @@ static hipError_t dq_f32(const LaunchArgs& a) {
     if (total < 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL((dq_f32_kernel<D>), dim3(total), dim3(256), 0, a.stream, (const float*)a.q,
                        (const float*)a.k, (const float*)a.v, (const float*)a.dout, a.lse_in, a.delta_in,
-                       (float*)a.dq, (int)a.S, nblk, total, a.scale * kLog2e, a.scale, a.causal);
+                       (float*)a.dq, (int)a.S, nblk, (int)a.BH, a.scale * kLog2e, a.scale, a.causal);
     return hipGetLastError();
 }
 
@@ -268,7 +268,7 @@ static hipError_t dkdv_f32(const LaunchArgs& a) {
     if (total < 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL((dkdv_f32_kernel<D>), dim3(total), dim3(256), 0, a.stream, (const float*)a.q,
                        (const float*)a.k, (const float*)a.v, (const float*)a.dout, a.lse_in, a.delta_in,
-                       (float*)a.dk, (float*)a.dv, (int)a.S, nblk, total, a.scale * kLog2e, a.scale, a.causal);
+                       (float*)a.dk, (float*)a.dv, (int)a.S, nblk, (int)a.BH, a.scale * kLog2e, a.scale, a.causal);
     return hipGetLastError();
 }
 

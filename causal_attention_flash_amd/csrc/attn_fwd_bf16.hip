@@ -12,7 +12,7 @@
 // "Cooperative tensors, reductions, and building a fused attention kernel").
 //
 // gfx950 mapping:
-// * 4 waves per workgroup, split-Q: each wave owns QB blocks of 32 query rows
+// * NW waves per workgroup, split-Q: each wave owns QB blocks of 32 query rows
 //   and never shares row statistics with another wave.
 // * The score tile is computed transposed, S^T = K Q^T, so each lane owns one
 //   query (C column) and the row max / row sum are in-lane reductions plus one
@@ -37,11 +37,15 @@
 
 namespace attn {
 
+#ifndef FWD_NW
+#define FWD_NW 4
+#endif
+
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D, int QB>
+template <int D, int QB, int NW_>
 struct FwdCfg {
-    static constexpr int NW = 4;
+    static constexpr int NW = NW_;
     static constexpr int NT = NW * 64;
     static constexpr int BM = NW * 32 * QB;  // queries per workgroup
     static constexpr int BN = 64;            // keys per tile
@@ -50,20 +54,20 @@ struct FwdCfg {
     static constexpr int TE = Tile::ELEMS;   // one K or V tile in LDS (elements)
 };
 
-template <int D, int QB>
-__global__ __launch_bounds__(256) void fwd_bf16_kernel(const uint16_t* __restrict__ Q,
+template <int D, int QB, int NW>
+__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __restrict__ Q,
                                                        const uint16_t* __restrict__ K,
                                                        const uint16_t* __restrict__ V,
                                                        uint16_t* __restrict__ O, float* __restrict__ LSE,
-                                                       int S, int nblk, int total, float c, int causal) {
-    using Cfg = FwdCfg<D, QB>;
+                                                       int S, int nblk, int BH, float c, int causal) {
+    using Cfg = FwdCfg<D, QB, NW>;
     constexpr int BM = Cfg::BM, BN = Cfg::BN, STR = Cfg::STR, TE = Cfg::TE;
     constexpr int KB = BN / 32;  // 32-key blocks per tile
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TE];  // K[2], V[2]
 
-    const int w = xcd_work_index(blockIdx.x, total);
-    const int head = w / nblk;
-    const int qblk = nblk - 1 - (w % nblk);  // most work first
+    const WorkItem wi = heavy_first(blockIdx.x, BH);
+    const int head = wi.head;
+    const int qblk = nblk - 1 - wi.rank;  // most work first
     const int q0 = qblk * BM;
     const size_t base = (size_t)head * S * D;
     const uint16_t* Qh = Q + base;
@@ -108,30 +112,42 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const uint16_t* __restric
             for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
     }
 
-    // S^T tile for the keys of tile t: sacc[qb][kb] (zeroed, then accumulated)
-    auto scores = [&](f32x16 (&sacc)[QB][KB], int t) {
+    // K rows of tile t as A operands of S^T = K Q^T:
+    // kf[kb][ks] = K[t*BN + 32kb + n][16ks + 8h .. +7].
+    auto load_k = [&](bf16x8 (&kf)[KB][D / 16], int t) {
         const uint16_t* Ks = kbuf(t);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
+            for (int ks = 0; ks < D / 16; ++ks)
+                kf[kb][ks] = as_bf16x8(lds16(Ks + (kb * 32 + n) * STR + ks * 16 + 8 * h));
+    };
+    // S^T tile from K operands already in registers; the first contraction step
+    // starts from a zero accumulator.
+    auto mma_scores = [&](f32x16 (&sacc)[QB][KB], const bf16x8 (&kf)[KB][D / 16]) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = 0.f;
+        for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                const bf16x8 kf = as_bf16x8(lds16(Ks + (kb * 32 + n) * STR + ks * 16 + 8 * h));
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = mfma32(kf, qf[qb][ks], sacc[qb][kb]);
-            }
-        }
+                for (int qb = 0; qb < QB; ++qb)
+                    sacc[qb][kb] = mfma32(kf[kb][ks], qf[qb][ks], ks == 0 ? f32x16{} : sacc[qb][kb]);
     };
 
-    // Softmax of tile t's scores and O += V_t P_t.  MASK instantiates the
-    // per-element causal / sequence-end mask (tiles crossing the diagonal or S).
-    auto softmax_pv = [&](auto mask_tag, f32x16 (&sacc)[QB][KB], int t) {
+    // One key tile t: softmax of its scores `cur` and O += V_t P_t.  With NEXT,
+    // the scores of tile t+1 are computed into `nxt` in the same straight-line
+    // block as this tile's exp work, so the MFMAs run under the VALU work.
+    // MASK instantiates the per-element causal / sequence-end mask; only a
+    // wave's last tile can need it (its earlier tiles lie entirely below the
+    // diagonal and before S), and the last tile has no successor.
+    auto step = [&](auto mask_tag, auto next_tag, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB], int t) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        const int k0 = t * BN;
+        constexpr bool NEXT = decltype(next_tag)::value;
+        bf16x8 kf[KB][D / 16];
+        if constexpr (NEXT) load_k(kf, t + 1);
+
         // ---- mask, row max (raw scores; c > 0 so max commutes with scaling)
+        const int k0 = t * BN;
         float mx[QB];
         bool grow = false;
 #pragma unroll
@@ -145,21 +161,56 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const uint16_t* __restric
                     if constexpr (MASK) {
                         const int key = k0 + kb * 32 + crow(r, h);
                         const bool kill = (causal && key > q) || key >= S;
-                        sacc[qb][kb][r] = kill ? -INFINITY : sacc[qb][kb][r];
+                        cur[qb][kb][r] = kill ? -INFINITY : cur[qb][kb][r];
                     }
-                    v = fmaxf(v, sacc[qb][kb][r]);
+                    v = fmaxf(v, cur[qb][kb][r]);
                 }
             v = half_max(v) * c;
             mx[qb] = v;
             grow |= v > m[qb] + kRescaleSlack;
         }
-        // ---- rescale only when some row max in the wave grew past the slack
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        // The reference point of the exponent moves only when some row max in
+        // the wave grew past the slack (wave-uniform decision); P values are
+        // otherwise bounded by 2^kRescaleSlack, which fp32 accumulation and
+        // bf16 P absorb.
+        const bool resc = __builtin_amdgcn_ballot_w64(grow) != 0;
+        float mn[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) mn[qb] = resc ? fmaxf(m[qb], mx[qb]) : m[qb];
+
+        if constexpr (NEXT) mma_scores(nxt, kf);
+
+        // ---- P = exp2(s*c - m) rounded to bf16; the row sum adds the same
+        // rounded values the PV product multiplies, so numerator and
+        // denominator of O = (P V) / l carry the same rounding (a row whose
+        // weight sits on one key reproduces that key's V row).
+        bf16x8 pf[QB][BN / 16];
+        float ls[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            ls[qb] = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) cur[qb][kb][r] = fast_exp2(fmaf(cur[qb][kb][r], c, -mn[qb]));
+                pf[qb][2 * kb] = pack_operand(cur[qb][kb], 0);
+                pf[qb][2 * kb + 1] = pack_operand(cur[qb][kb], 1);
+                ls[qb] = sum_bf16x8(pf[qb][2 * kb], ls[qb]);
+                ls[qb] = sum_bf16x8(pf[qb][2 * kb + 1], ls[qb]);
+            }
+        }
+        // V^T operands, read transposed from the row-major V tile
+        const uint16_t* Vs = vbuf(t);
+        bf16x8 vf[BN / 16][D / 32];
+#pragma unroll
+        for (int ks = 0; ks < BN / 16; ++ks)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) vf[ks][db] = lds_tr_operand<STR>(Vs, ks * 16, db * 32, lane);
+
+        if (resc) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                const float mn = fmaxf(m[qb], mx[qb]);
-                const float f = fast_exp2(m[qb] - mn);
-                m[qb] = mn;
+                const float f = fast_exp2(m[qb] - mn[qb]);
                 l[qb] *= f;
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db)
@@ -167,46 +218,18 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const uint16_t* __restric
                     for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= f;
             }
         }
-        // ---- P = exp2(s*c - m) rounded to bf16; the row sum adds the same
-        // rounded values the PV product multiplies, so numerator and
-        // denominator of O = (P V) / l carry the same rounding (a row whose
-        // weight sits on one key reproduces that key's V row).
-        bf16x8 pf[QB][BN / 16];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            float ls = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = fast_exp2(fmaf(sacc[qb][kb][r], c, -m[qb]));
-                pf[qb][2 * kb] = pack_operand(sacc[qb][kb], 0);
-                pf[qb][2 * kb + 1] = pack_operand(sacc[qb][kb], 1);
-                ls = sum_bf16x8(pf[qb][2 * kb], ls);
-                ls = sum_bf16x8(pf[qb][2 * kb + 1], ls);
-            }
-            l[qb] += ls;
+            m[qb] = mn[qb];
+            l[qb] += ls[qb];
         }
-        // ---- O^T += V^T P^T, V^T read transposed from the row-major V tile
-        const uint16_t* Vs = vbuf(t);
+        // ---- O^T += V^T P^T
 #pragma unroll
-        for (int ks = 0; ks < BN / 16; ++ks) {
+        for (int ks = 0; ks < BN / 16; ++ks)
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const bf16x8 vf = lds_tr_operand<STR>(Vs, ks * 16, db * 32, lane);
+            for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32(vf, pf[qb][ks], oacc[qb][db]);
-            }
-        }
-    };
-
-    // One pipelined step: the next tile's scores, then this tile's softmax and PV.
-    auto step = [&](int t, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB]) {
-        if (t + 1 < nw) scores(nxt, t + 1);
-        const int k0 = t * BN;
-        if ((causal && k0 + BN - 1 > qw0) || k0 + BN > S)
-            softmax_pv(std::true_type{}, cur, t);
-        else
-            softmax_pv(std::false_type{}, cur, t);
+                for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32(vf[ks][db], pf[qb][ks], oacc[qb][db]);
     };
 
     // ---- prologue: K_0, V_0, K_1 in LDS; V_1 and K_2 in flight in registers
@@ -224,7 +247,14 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const uint16_t* __restric
     __syncthreads();
 
     f32x16 sa[QB][KB], sb[QB][KB];
-    if (nw > 0) scores(sa, 0);
+    if (nw > 0) {
+        bf16x8 kf[KB][D / 16];
+        load_k(kf, 0);
+        mma_scores(sa, kf);
+    }
+    // Iteration 0 overwrites K_0's buffer with K_2: every wave must have read
+    // K_0 first.
+    __syncthreads();
 
     // Iteration t: stage K_{t+2} (into K_t's buffer, consumed last iteration) and
     // V_{t+1} (into V_{t-1}'s buffer), start the loads of K_{t+3} and V_{t+2},
@@ -234,7 +264,10 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const uint16_t* __restric
         if (t + 1 < ntiles) vt.store(vbuf(t + 1), tid);
         if (t + 3 < ntiles) kt.load(Kh, (t + 3) * BN, S, tid);
         if (t + 2 < ntiles) vt.load(Vh, (t + 2) * BN, S, tid);
-        if (t < nw) step(t, cur, nxt);
+        if (t + 1 < nw)
+            step(std::false_type{}, std::true_type{}, cur, nxt, t);
+        else if (t + 1 == nw)
+            step(std::true_type{}, std::false_type{}, cur, nxt, t);
         __syncthreads();
     };
     for (int t = 0; t < ntiles; t += 2) {
@@ -265,21 +298,21 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const uint16_t* __restric
     }
 }
 
-template <int D, int QB>
+template <int D, int QB, int NW>
 static hipError_t launch_fwd(const LaunchArgs& a) {
-    using Cfg = FwdCfg<D, QB>;
+    using Cfg = FwdCfg<D, QB, NW>;
     const int nblk = (int)((a.S + Cfg::BM - 1) / Cfg::BM);
     const int64_t total = (int64_t)nblk * a.BH;
     if (total > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, QB>), dim3((unsigned)total), dim3(Cfg::NT), 0, a.stream,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW>), dim3((unsigned)total), dim3(Cfg::NT), 0, a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                       (int)a.S, nblk, (int)total, a.scale * kLog2e, a.causal);
+                       (int)a.S, nblk, (int)a.BH, a.scale * kLog2e, a.causal);
     return hipGetLastError();
 }
 
 hipError_t launch_fwd_bf16(const LaunchArgs& a) {
-    if (a.D == 64) return launch_fwd<64, 1>(a);
-    if (a.D == 128) return launch_fwd<128, 1>(a);
+    if (a.D == 64) return launch_fwd<64, 1, FWD_NW>(a);
+    if (a.D == 128) return launch_fwd<128, 1, FWD_NW>(a);
     return hipErrorInvalidValue;
 }
 
