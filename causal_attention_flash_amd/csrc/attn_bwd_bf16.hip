@@ -48,11 +48,12 @@ struct DkdvCfg {
     static constexpr int STR = QT::STR;
     static constexpr int QE = QT::ELEMS;
     static constexpr int BUF_ELEMS = 2 * QE;   // Q, dO
-    static constexpr int BUF_STATS = 2 * BMQ;  // lse2, delta (fp32)
+    static constexpr int BUF_STATS = 2 * BMQ;  // -LSE/scale, -delta (fp32)
+    static constexpr int WAVES_PER_SIMD = D == 64 ? 2 : 1;  // register budget: 256 VGPRs at D = 64
 };
 
 template <int D, int BMQ, int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_kernel(
+__global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) void bwd_dkdv_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int S, int nblk, int BH, float c, float scale,
@@ -101,6 +102,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_kernel(
             dvacc[db][r] = 0.f;
         }
 
+    const float rscale = 1.f / scale;
     const int t0 = causal ? n0 / BMQ : 0;
     const int ntiles = (S + BMQ - 1) / BMQ;
 
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_kernel(
     auto fetch = [&](int t) {
         qt.load(Qh, t * BMQ, S, tid);
         ot.load(dOh, t * BMQ, S, tid);
-        st.load(Lh, Dh, t * BMQ, S, tid);
+        st.load(Lh, Dh, t * BMQ, S, rscale, tid);
     };
 
     if (t0 < ntiles) {
@@ -129,42 +131,46 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_kernel(
 
     // One query tile against this wave's 32 keys; MASK instantiates the causal
     // mask for tiles that cross the diagonal (query rows past S need no mask:
-    // their lse2 is +inf, so P is exactly 0 there).
+    // their statistic is -inf, so P is exactly 0 there).
+    //
+    // The accumulators start from the per-row statistics instead of zero, so the
+    // MFMAs deliver S - LSE/scale and dP - delta directly (register r of a lane
+    // holds query row crow(r, h)); then P = exp2(c * acc) with c = scale*log2(e),
+    // and dS = P * acc.
     auto tile = [&](auto mask_tag, int b, int qt0) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const uint16_t* Qs = bufp(b);
         const uint16_t* dOs = Qs + Cfg::QE;
-        const float* L2s = stat(b);
-        const float* DLs = L2s + BMQ;
+        const float* SIs = stat(b);
+        const float* PIs = SIs + BMQ;
 #pragma unroll
         for (int qb = 0; qb < BMQ / 32; ++qb) {
-            // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
             f32x16 sacc, pacc;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                sacc[r] = 0.f;
-                pacc[r] = 0.f;
+            for (int g = 0; g < 4; ++g) {
+                const int rl = qb * 32 + 8 * g + 4 * h;
+                const f32x4 si = *reinterpret_cast<const f32x4*>(SIs + rl);
+                const f32x4 pi = *reinterpret_cast<const f32x4*>(PIs + rl);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    sacc[4 * g + i] = si[i];
+                    pacc[4 * g + i] = pi[i];
+                }
             }
+            // 32 queries x this wave's 32 keys: S - LSE/scale and dP - delta
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks) {
                 const int off = (qb * 32 + n) * STR + ks * 16 + 8 * h;
                 sacc = mfma32(as_bf16x8(lds16(Qs + off)), kf[ks], sacc);
                 pacc = mfma32(as_bf16x8(lds16(dOs + off)), vf[ks], pacc);
             }
-            // P and dS; query rows of register r are qb*32 + crow(r, h)
+            // P and dS
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int rl = qb * 32 + 8 * g + 4 * h;
-                const f32x4 l2 = *reinterpret_cast<const f32x4*>(L2s + rl);
-                const f32x4 dl = *reinterpret_cast<const f32x4*>(DLs + rl);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 4 * g + i;
-                    float p = fast_exp2(fmaf(sacc[r], c, -l2[i]));
-                    if constexpr (MASK) p = key > qt0 + rl + i ? 0.f : p;
-                    sacc[r] = p;
-                    pacc[r] = p * (pacc[r] - dl[i]);
-                }
+            for (int r = 0; r < 16; ++r) {
+                float p = fast_exp2(sacc[r] * c);
+                if constexpr (MASK) p = key > qt0 + qb * 32 + crow(r, h) ? 0.f : p;
+                sacc[r] = p;
+                pacc[r] *= p;
             }
             // dV^T += dO^T P ; dK^T += Q^T dS  (contraction over these 32 queries;
             // dO^T and Q^T read transposed from the row-major tiles)
@@ -248,10 +254,12 @@ struct DqCfg {
     static constexpr int STR = KT::STR;
     static constexpr int KE = KT::ELEMS;
     static constexpr int BUF_ELEMS = 2 * KE;  // K, V
+    // register budget: 168 VGPRs (3 waves per SIMD) fits D = 64 without spills
+    static constexpr int WAVES_PER_SIMD = D == 64 ? 3 : 1;
 };
 
 template <int D, int BNK, int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_kernel(
+__global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     uint16_t* __restrict__ dQ, int S, int nblk, int BH, float c, float scale, int causal) {

@@ -14,6 +14,14 @@
 
 namespace attn {
 
+// Buffer resource covering `bytes` bytes from `base`.  Raw buffer loads through
+// it are range-checked by the hardware: bytes at or beyond the end read as zero
+// and nothing outside the range is accessed.  Dword 3 = 0x00020000 selects the
+// 32-bit data format that untyped buffer loads require on gfx9-family parts.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
 template <int ROWS, int D, int NT = 256>
 struct RowTile {
     static constexpr int STR = D + 8;          // LDS row stride (elements)
@@ -25,16 +33,16 @@ struct RowTile {
 
     u32x4 r[PT];
 
+    // Rows row0 .. row0+ROWS-1 of the [S][D] matrix g; rows at or beyond S read
+    // as zero (the buffer range ends at row S).
     __device__ __forceinline__ void load(const uint16_t* __restrict__ g, int row0, int S, int tid) {
+        const int rows = max(0, min(S - row0, ROWS));
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(g + (size_t)row0 * D, rows * D * 2);
 #pragma unroll
         for (int i = 0; i < PT; ++i) {
             const int c = tid + i * NT;
-            u32x4 a = {0u, 0u, 0u, 0u};
-            if (CHUNKS % NT == 0 || c < CHUNKS) {
-                const int row = row0 + c / CPR;
-                if (row < S) a = ldg16(g + (size_t)row * D + (c % CPR) * 8);
-            }
-            r[i] = a;
+            if (CHUNKS % NT == 0 || c < CHUNKS)
+                r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, c * 16, 0, 0);
         }
     }
 
@@ -48,22 +56,22 @@ struct RowTile {
     }
 };
 
-// Per-row fp32 statistics (LSE in log2 units, delta) for a tile of query rows.
+// Per-row fp32 statistics of a tile of query rows, in the form the backward
+// accumulators start from: a = -LSE/scale (S - LSE/scale is the exponent of P
+// before the factor scale*log2(e)) and b = -delta.  Rows past S get a = -inf, so
+// P is exactly 0 there.
 template <int ROWS, int NT = 256>
 struct RowStats {
     float a, b;
-    // lse2 = LSE * log2(e); rows past S get +inf so exp2(s - lse2) is exactly 0.
     __device__ __forceinline__ void load(const float* __restrict__ lse, const float* __restrict__ delta,
-                                         int row0, int S, int tid) {
-        a = INFINITY;
-        b = 0.f;
-        if (tid < ROWS) {
-            const int row = row0 + tid;
-            if (row < S) {
-                a = lse[row] * kLog2e;
-                b = delta[row];
-            }
-        }
+                                         int row0, int S, float rscale, int tid) {
+        const int rows = max(0, min(S - row0, ROWS));
+        const __amdgpu_buffer_rsrc_t rl = buffer_rsrc(lse + row0, rows * 4);
+        const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(delta + row0, rows * 4);
+        const float l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, tid * 4, 0, 0));
+        const float d = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, tid * 4, 0, 0));
+        a = tid < rows ? -l * rscale : -INFINITY;
+        b = -d;
     }
     __device__ __forceinline__ void store(float* sa, float* sb, int tid) const {
         if (tid < ROWS) {
