@@ -30,12 +30,6 @@
 
 namespace attn {
 
-#ifndef DKDV_NW
-#define DKDV_NW 4
-#endif
-#ifndef DQ_NW
-#define DQ_NW 4
-#endif
 
 // ============================================================== dK / dV pass
 
@@ -238,8 +232,8 @@ static hipError_t launch_dkdv(const LaunchArgs& a) {
 }
 
 hipError_t launch_bwd_dkdv_bf16(const LaunchArgs& a) {
-    if (a.D == 64) return launch_dkdv<64, 64, DKDV_NW>(a);
-    if (a.D == 128) return launch_dkdv<128, 32, DKDV_NW>(a);
+    if (a.D == 64) return launch_dkdv<64, 64, 8>(a);
+    if (a.D == 128) return launch_dkdv<128, 32, 4>(a);
     return hipErrorInvalidValue;
 }
 
@@ -408,8 +402,8 @@ static hipError_t launch_dq(const LaunchArgs& a) {
 }
 
 hipError_t launch_bwd_dq_bf16(const LaunchArgs& a) {
-    if (a.D == 64) return launch_dq<64, 64, DQ_NW>(a);
-    if (a.D == 128) return launch_dq<128, 32, DQ_NW>(a);
+    if (a.D == 64) return launch_dq<64, 64, 4>(a);
+    if (a.D == 128) return launch_dq<128, 32, 4>(a);
     return hipErrorInvalidValue;
 }
 

@@ -28,8 +28,8 @@
 // * Software pipeline: K runs one tile ahead of V in LDS, so iteration t issues
 //   the MFMAs of S^T for tile t+1 next to the exp/max/sum VALU work of tile t
 //   (the MFMA unit works asynchronously from the VALU), then O += V_t P_t.
-//   Q stays in registers for the whole loop; the next tiles' global loads are in
-//   flight while the current one is multiplied; one barrier per tile.
+//   Q stays in registers for the whole loop; the global loads of a K/V tile are
+//   issued two iterations before it is stored to LDS; one barrier per tile.
 #include <type_traits>
 
 #include "attn_launch.h"
@@ -37,9 +37,6 @@
 
 namespace attn {
 
-#ifndef FWD_NW
-#define FWD_NW 4
-#endif
 
 constexpr float kRescaleSlack = 8.0f;
 
@@ -232,18 +229,23 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
                 for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32(vf[ks][db], pf[qb][ks], oacc[qb][db]);
     };
 
-    // ---- prologue: K_0, V_0, K_1 in LDS; V_1 and K_2 in flight in registers
-    typename Cfg::Tile kt, vt;
-    kt.load(Kh, 0, S, tid);
-    vt.load(Vh, 0, S, tid);
-    kt.store(kbuf(0), tid);
-    vt.store(vbuf(0), tid);
-    if (ntiles > 1) {
-        kt.load(Kh, BN, S, tid);
-        vt.load(Vh, BN, S, tid);
-        kt.store(kbuf(1), tid);
-        if (ntiles > 2) kt.load(Kh, 2 * BN, S, tid);
-    }
+    // ---- prologue: K_0, V_0, K_1 in LDS; register set 0 holds (K_2, V_1) and
+    // set 1 holds (K_3, V_2), both in flight.  A tile index at or past ntiles
+    // loads from row S: an empty buffer range, so nothing is read and the
+    // registers hold zeros (stores and loads stay unconditional, which keeps
+    // the count of loads in flight the same on every path).
+    auto row_of = [&](int t) { return t < ntiles ? t * BN : S; };
+    typename Cfg::Tile kt[2], vt[2];
+    kt[0].load(Kh, 0, S, tid);
+    vt[0].load(Vh, 0, S, tid);
+    kt[1].load(Kh, row_of(1), S, tid);
+    kt[0].store(kbuf(0), tid);
+    vt[0].store(vbuf(0), tid);
+    kt[1].store(kbuf(1), tid);
+    kt[0].load(Kh, row_of(2), S, tid);
+    vt[0].load(Vh, row_of(1), S, tid);
+    kt[1].load(Kh, row_of(3), S, tid);
+    vt[1].load(Vh, row_of(2), S, tid);
     __syncthreads();
 
     f32x16 sa[QB][KB], sb[QB][KB];
@@ -256,14 +258,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
     // K_0 first.
     __syncthreads();
 
-    // Iteration t: stage K_{t+2} (into K_t's buffer, consumed last iteration) and
-    // V_{t+1} (into V_{t-1}'s buffer), start the loads of K_{t+3} and V_{t+2},
-    // compute, then one barrier.
-    auto iteration = [&](int t, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB]) {
-        if (t + 2 < ntiles) kt.store(kbuf(t), tid);
-        if (t + 1 < ntiles) vt.store(vbuf(t + 1), tid);
-        if (t + 3 < ntiles) kt.load(Kh, (t + 3) * BN, S, tid);
-        if (t + 2 < ntiles) vt.load(Vh, (t + 2) * BN, S, tid);
+    // Iteration t, with register set t % 2 holding (K_{t+2}, V_{t+1}): stage them
+    // (into the buffers of K_t and V_{t-1}, both consumed last iteration), start
+    // the loads of K_{t+4} and V_{t+3} into the same set (two tiles of latency
+    // cover), compute, then one barrier.
+    auto iteration = [&](int t, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB], typename Cfg::Tile& kr,
+                         typename Cfg::Tile& vr) {
+        kr.store(kbuf(t), tid);
+        vr.store(vbuf(t + 1), tid);
+        kr.load(Kh, row_of(t + 4), S, tid);
+        vr.load(Vh, row_of(t + 3), S, tid);
         if (t + 1 < nw)
             step(std::false_type{}, std::true_type{}, cur, nxt, t);
         else if (t + 1 == nw)
@@ -271,8 +275,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
         __syncthreads();
     };
     for (int t = 0; t < ntiles; t += 2) {
-        iteration(t, sa, sb);
-        if (t + 1 < ntiles) iteration(t + 1, sb, sa);
+        iteration(t, sa, sb, kt[0], vt[0]);
+        if (t + 1 < ntiles) iteration(t + 1, sb, sa, kt[1], vt[1]);
     }
 
     // ---- epilogue: O = O / l (l == 0 -> 0), LSE = (m + log2 l) * ln 2
@@ -311,8 +315,8 @@ static hipError_t launch_fwd(const LaunchArgs& a) {
 }
 
 hipError_t launch_fwd_bf16(const LaunchArgs& a) {
-    if (a.D == 64) return launch_fwd<64, 1, FWD_NW>(a);
-    if (a.D == 128) return launch_fwd<128, 1, FWD_NW>(a);
+    if (a.D == 64) return launch_fwd<64, 1, 4>(a);
+    if (a.D == 128) return launch_fwd<128, 1, 4>(a);
     return hipErrorInvalidValue;
 }
 

@@ -18,8 +18,12 @@ namespace attn {
 // it are range-checked by the hardware: bytes at or beyond the end read as zero
 // and nothing outside the range is accessed.  Dword 3 = 0x00020000 selects the
 // 32-bit data format that untyped buffer loads require on gfx9-family parts.
+// `bytes` must be the same in every lane; it is read from the first lane so that
+// the descriptor lives in scalar registers (a clamp computed on the vector unit
+// would otherwise make the compiler wrap each load in a per-lane loop).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                             __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
 template <int ROWS, int D, int NT = 256>
