@@ -108,19 +108,23 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
         uint16_t* s = bufp(b);
         qt.store(s, tid);
         ot.store(s + Cfg::QE, tid);
-        st.store(stat(b), stat(b) + BMQ, tid);
+        st.store(stat(b), stat(b) + BMQ, rscale, tid);
     };
     auto fetch = [&](int t) {
         qt.load(Qh, t * BMQ, S, tid);
         ot.load(dOh, t * BMQ, S, tid);
-        st.load(Lh, Dh, t * BMQ, S, rscale, tid);
+        st.load(Lh, Dh, t * BMQ, S, tid);
     };
 
     if (t0 < ntiles) {
         fetch(t0);
         stage(0);
-        if (t0 + 1 < ntiles) fetch(t0 + 1);
     }
+    // The K and V operand loads have landed before the first prefetch is issued;
+    // otherwise they would still be outstanding where the loop starts and the
+    // wait for them there would cover every later prefetch as well.
+    wait_vmem_all();
+    if (t0 + 1 < ntiles) fetch(t0 + 1);
     __syncthreads();
 
     // One query tile against this wave's 32 keys; MASK instantiates the causal

@@ -122,6 +122,16 @@ __device__ __forceinline__ float half_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt vmcnt(0): every vector memory load issued so far has returned.
+// Encoding (gfx9): vmcnt in bits 3:0 and 15:14 (0), expcnt in bits 6:4 and
+// lgkmcnt in bits 11:8 at their maxima (no wait on those counters).  The
+// scheduling barriers keep loads from being moved across the wait.
+__device__ __forceinline__ void wait_vmem_all() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ u32x4 ldg16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }

@@ -80,15 +80,17 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
             sv[j] = vis ? d : -INFINITY;
             mx = fmaxf(mx, sv[j]);
         }
-        const float mn = fmaxf(m, mx * c);
-        const float f = exp2f(m - mn);
+        // m is kept in raw score units and the exponent is (s - m) * c, so the
+        // row maximum gets exactly exp2(0) = 1
+        const float mn = fmaxf(m, mx);
+        const float f = exp2f((m - mn) * c);
         m = mn;
         l *= f;
 #pragma unroll
         for (int e = 0; e < 32; ++e) ov[e] *= f;
 #pragma unroll
         for (int j = 0; j < kF32Tile; ++j) {
-            const float p = exp2f(fmaf(sv[j], c, -m));
+            const float p = exp2f((sv[j] - m) * c);
             l += p;
 #pragma unroll
             for (int e = 0; e < 32; ++e) ov[e] = fmaf(p, Vs[j * D + part * 32 + e], ov[e]);
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
         const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
         for (int e = 0; e < 32; ++e) O[base + (size_t)q * D + part * 32 + e] = ov[e] * inv;
-        if (part == 0) LSE[(size_t)head * S + q] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+        if (part == 0) LSE[(size_t)head * S + q] = l > 0.f ? (m * c + log2f(l)) * kLn2 : -INFINITY;
     }
 }
 

@@ -61,26 +61,27 @@ struct RowTile {
 };
 
 // Per-row fp32 statistics of a tile of query rows, in the form the backward
-// accumulators start from: a = -LSE/scale (S - LSE/scale is the exponent of P
-// before the factor scale*log2(e)) and b = -delta.  Rows past S get a = -inf, so
-// P is exactly 0 there.
+// accumulators start from: -LSE/scale (S - LSE/scale is the exponent of P
+// before the factor scale*log2(e)) and -delta.  Rows past S get -inf, so P is
+// exactly 0 there.  load() only issues the loads; the transform happens in
+// store(), so no wait for the loads is placed at the point of issue.
 template <int ROWS, int NT = 256>
 struct RowStats {
-    float a, b;
+    float l, d;
+    bool ok;
     __device__ __forceinline__ void load(const float* __restrict__ lse, const float* __restrict__ delta,
-                                         int row0, int S, float rscale, int tid) {
+                                         int row0, int S, int tid) {
         const int rows = max(0, min(S - row0, ROWS));
         const __amdgpu_buffer_rsrc_t rl = buffer_rsrc(lse + row0, rows * 4);
         const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(delta + row0, rows * 4);
-        const float l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, tid * 4, 0, 0));
-        const float d = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, tid * 4, 0, 0));
-        a = tid < rows ? -l * rscale : -INFINITY;
-        b = -d;
+        l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, tid * 4, 0, 0));
+        d = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, tid * 4, 0, 0));
+        ok = tid < rows;
     }
-    __device__ __forceinline__ void store(float* sa, float* sb, int tid) const {
+    __device__ __forceinline__ void store(float* sa, float* sb, float rscale, int tid) const {
         if (tid < ROWS) {
-            sa[tid] = a;
-            sb[tid] = b;
+            sa[tid] = ok ? -l * rscale : -INFINITY;
+            sb[tid] = -d;
         }
     }
 };
