@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-One step = attn_fwd + attn_bwd (delta preprocess, dK/dV pass, dQ pass) over one
+One step = attn_fwd + attn_bwd (dQ pass that also forms delta, dK/dV pass) over one
 batch of synthetic inputs already resident in HBM.  Prints ONE JSON line:
 forward+backward TFLOP/s under the 7*B*H*S^2*D causal convention, the roofline
 of the dominant kernel (algorithmic FLOPs / its average HIP-event duration over a
@@ -53,7 +53,8 @@ def kernel_units(w):
     B*H*S^2*D FLOPs (2 FLOPs per multiply-add, halved by causality).  The
     forward does 2 units (QK^T, PV); the backward's 5 units are S, dP, dV, dK in
     the dK/dV pass and dQ in the dQ pass (the dQ pass's recomputed S and dP are
-    not algorithmic work).
+    not algorithmic work).  The dQ pass also reads O to form delta = rowsum(dO o O)
+    and writes delta, which the dK/dV pass reads.
     """
     unit = w.B * w.H * w.S * w.S * w.D * (1.0 if w.causal else 2.0)
     elem = 2 if w.dtype == "bf16" else 4
@@ -61,9 +62,8 @@ def kernel_units(w):
     rows = w.B * w.H * w.S * 4
     return {
         "fwd": {"flops": 2 * unit, "bytes": 3 * tensor + tensor + rows},
-        "bwd_preprocess": {"flops": 0.0, "bytes": 2 * tensor + rows},
+        "bwd_dq": {"flops": 1 * unit, "bytes": 5 * tensor + rows + tensor + rows},
         "bwd_dkdv": {"flops": 4 * unit, "bytes": 4 * tensor + 2 * rows + 2 * tensor},
-        "bwd_dq": {"flops": 1 * unit, "bytes": 4 * tensor + 2 * rows + tensor},
     }
 
 
@@ -163,16 +163,14 @@ def main():
         chk(bd.c_attn_bwd(P["q"], P["k"], P["v"], P["o"], P["do"], P["lse"], P["dq"], P["dk"], P["dv"], P["ws"],
                           nws, B, H, S, D, scale, causal, dt, stream), "bwd")
 
-    def pre():
-        chk(bd.c_attn_bwd_preprocess(P["o"], P["do"], P["ws"], B, H, S, D, dt, stream), "pre")
+    def dq_delta():
+        chk(bd.c_attn_bwd_dq_delta(P["q"], P["k"], P["v"], P["o"], P["do"], P["lse"], P["ws"], P["dq"], B, H, S, D,
+                                   scale, causal, dt, stream), "dq_delta")
 
     def dkdv():
         chk(bd.c_attn_bwd_dkdv(P["q"], P["k"], P["v"], P["do"], P["lse"], P["ws"], P["dk"], P["dv"], B, H, S, D,
                                scale, causal, dt, stream), "dkdv")
 
-    def dqk():
-        chk(bd.c_attn_bwd_dq(P["q"], P["k"], P["v"], P["do"], P["lse"], P["ws"], P["dq"], B, H, S, D, scale,
-                             causal, dt, stream), "dq")
 
     if args.profile_steps:
         # A plain copy of known size first: the counters' reading for it calibrates
@@ -209,9 +207,10 @@ def main():
     gpu_ms = ev0.elapsed_time(ev1)
     ms_per_step = gpu_ms / args.steps
 
-    # ---- per-kernel durations: the same K steps, each kernel bracketed by events
-    names = ("fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq")
-    calls = (fwd, pre, dkdv, dqk)
+    # ---- per-kernel durations: the same K steps, each kernel attn_bwd launches
+    # (in its order) bracketed by events
+    names = ("fwd", "bwd_dq", "bwd_dkdv")
+    calls = (fwd, dq_delta, dkdv)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):

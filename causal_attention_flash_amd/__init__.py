@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     attn_bwd,
     attn_bwd_dkdv,
     attn_bwd_dq,
+    attn_bwd_dq_delta,
     attn_bwd_preprocess,
     attn_fwd,
     load_library,

@@ -41,6 +41,7 @@ SIGNATURES = {
     "attn_bwd_preprocess": (_INT, [_P, _P, _P, _I64, _I64, _I64, _I64, _INT, _P]),
     "attn_bwd_dkdv": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _INT, _INT, _P]),
     "attn_bwd_dq": (_INT, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _INT, _INT, _P]),
+    "attn_bwd_dq_delta": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _INT, _INT, _P]),
     "attn_status_string": (ctypes.c_char_p, [_INT]),
 }
 
@@ -104,6 +105,10 @@ def c_attn_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, B, H, S, D, scale, causal, 
 
 def c_attn_bwd_dq(q, k, v, do, lse, delta, dq, B, H, S, D, scale, causal, dtype, stream=0) -> int:
     return load_library().attn_bwd_dq(q, k, v, do, lse, delta, dq, B, H, S, D, scale, causal, dtype, stream)
+
+
+def c_attn_bwd_dq_delta(q, k, v, o, do, lse, delta, dq, B, H, S, D, scale, causal, dtype, stream=0) -> int:
+    return load_library().attn_bwd_dq_delta(q, k, v, o, do, lse, delta, dq, B, H, S, D, scale, causal, dtype, stream)
 
 
 # ------------------------------------------------------------- torch-tensor wrappers
@@ -218,3 +223,17 @@ def attn_bwd_dq(q, k, v, do, lse, delta, scale=None, causal=True, out=None):
           delta.data_ptr(), dq.data_ptr(), B, H, S, D, _scale(scale, D), int(bool(causal)), _dtype_code(q),
           _stream(q.device))
     return dq
+
+
+def attn_bwd_dq_delta(q, k, v, o, do, lse, scale=None, causal=True, out=None, delta_out=None):
+    """dQ pass that also forms delta = rowsum(dO o O); returns (dQ, delta)."""
+    torch = _torch()
+    B, H, S, D = q.shape
+    _check_tensors((("q", q), ("k", k), ("v", v), ("o", o), ("do", do)), q.shape, q.dtype, q.device)
+    _check_tensors((("lse", lse),), (B, H, S), torch.float32, q.device)
+    dq = out if out is not None else torch.empty_like(q)
+    delta = delta_out if delta_out is not None else torch.empty(B, H, S, dtype=torch.float32, device=q.device)
+    _call(c_attn_bwd_dq_delta, "attn_bwd_dq_delta", q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+          do.data_ptr(), lse.data_ptr(), delta.data_ptr(), dq.data_ptr(), B, H, S, D, _scale(scale, D),
+          int(bool(causal)), _dtype_code(q), _stream(q.device))
+    return dq, delta

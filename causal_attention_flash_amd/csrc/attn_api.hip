@@ -104,6 +104,9 @@ attn_status run_dkdv(const LaunchArgs& a, attn_dtype dt) {
 attn_status run_dq(const LaunchArgs& a, attn_dtype dt) {
     return from_hip(dt == ATTN_BF16 ? attn::launch_bwd_dq_bf16(a) : attn::launch_bwd_dq_f32(a));
 }
+attn_status run_dq_delta(const LaunchArgs& a, attn_dtype dt) {
+    return from_hip(dt == ATTN_BF16 ? attn::launch_bwd_dq_delta_bf16(a) : attn::launch_bwd_dq_delta_f32(a));
+}
 
 }  // namespace
 
@@ -219,6 +222,34 @@ attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const void*
     return run_dq(a, dtype);
 }
 
+attn_status attn_bwd_dq_delta(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                              const float* lse, float* delta, void* dq, int64_t B, int64_t H, int64_t S, int64_t D,
+                              float scale, int causal, attn_dtype dtype, void* stream) {
+    bool empty = false;
+    attn_status st = check_shape(B, H, S, D, dtype, &empty);
+    if (st == ATTN_OK) st = check_scale_causal(scale, causal);
+    if (st != ATTN_OK || empty) return st;
+    if ((st = check_ptrs({q, k, v, o, dout, lse, delta, dq})) != ATTN_OK) return st;
+    const Sizes z = sizes(B, H, S, D, dtype);
+    if ((st = check_alias({{dq, z.tensor}, {delta, z.rows}}, {{q, z.tensor},
+                                                               {k, z.tensor},
+                                                               {v, z.tensor},
+                                                               {o, z.tensor},
+                                                               {dout, z.tensor},
+                                                               {lse, z.rows}})) != ATTN_OK)
+        return st;
+    LaunchArgs a = base_args(B, H, S, D, scale, causal, stream);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o_in = o;
+    a.dout = dout;
+    a.lse_in = lse;
+    a.delta = delta;
+    a.dq = dq;
+    return run_dq_delta(a, dtype);
+}
+
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
                      int64_t S, int64_t D, float scale, int causal, attn_dtype dtype, void* stream) {
@@ -250,9 +281,9 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
-    if ((st = run_preprocess(a, dtype)) != ATTN_OK) return st;
-    if ((st = run_dkdv(a, dtype)) != ATTN_OK) return st;
-    return run_dq(a, dtype);
+    // dQ first: it forms delta, which the dK/dV pass reads
+    if ((st = run_dq_delta(a, dtype)) != ATTN_OK) return st;
+    return run_dkdv(a, dtype);
 }
 
 }  // extern "C"

@@ -256,11 +256,15 @@ struct DqCfg {
     static constexpr int WAVES_PER_SIMD = D == 64 ? 3 : 1;
 };
 
-template <int D, int BNK, int NW>
+// DELTA_FROM_O: delta = rowsum(dO o O) is formed here, from the O rows of this
+// wave's queries (fp32 sums of bf16 products), and written to DeltaOut for the
+// dK/dV pass; otherwise delta is read from Delta.
+template <int D, int BNK, int NW, bool DELTA_FROM_O>
 __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
-    uint16_t* __restrict__ dQ, int S, int nblk, int BH, float c, float scale, int causal) {
+    const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
+    const float* __restrict__ Delta, float* __restrict__ DeltaOut, uint16_t* __restrict__ dQ, int S, int nblk,
+    int BH, float c, float scale, int causal) {
     using Cfg = DqCfg<D, BNK, NW>;
     constexpr int BMQ = Cfg::BMQ;
     constexpr int STR = Cfg::STR;
@@ -292,7 +296,22 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
         of[ks] = as_bf16x8(b);
     }
     const float l2 = q < S ? LSE[(size_t)head * S + q] * kLog2e : INFINITY;
-    const float dl = q < S ? Delta[(size_t)head * S + q] : 0.f;
+    float dl;
+    if constexpr (DELTA_FROM_O) {
+        // this lane holds half of the row (d = 16ks + 8h .. +7); its partner
+        // lane l ^ 32 holds the other half
+        float part = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            u32x4 u = {0u, 0u, 0u, 0u};
+            if (q < S) u = ldg16(O + base + (size_t)q * D + ks * 16 + 8 * h);
+            part = dot_bf16x8(of[ks], as_bf16x8(u), part);
+        }
+        dl = half_sum(part);
+        if (h == 0 && q < S) DeltaOut[(size_t)head * S + q] = dl;
+    } else {
+        dl = q < S ? Delta[(size_t)head * S + q] : 0.f;
+    }
 
     f32x16 dqacc[D / 32];
 #pragma unroll
@@ -392,22 +411,28 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
     }
 }
 
-template <int D, int BNK, int NW>
+template <int D, int BNK, int NW, bool DELTA_FROM_O>
 static hipError_t launch_dq(const LaunchArgs& a) {
     using Cfg = DqCfg<D, BNK, NW>;
     const int nblk = (int)((a.S + Cfg::BMQ - 1) / Cfg::BMQ);
     const int64_t total = (int64_t)nblk * a.BH;
     if (total > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, BNK, NW>), dim3((unsigned)total), dim3(Cfg::NT), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, a.lse_in, a.delta_in, (uint16_t*)a.dq, (int)a.S, nblk,
-                       (int)a.BH, a.scale * kLog2e, a.scale, a.causal);
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, BNK, NW, DELTA_FROM_O>), dim3((unsigned)total), dim3(Cfg::NT), 0,
+                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.o_in, (const uint16_t*)a.dout, a.lse_in, a.delta_in, a.delta,
+                       (uint16_t*)a.dq, (int)a.S, nblk, (int)a.BH, a.scale * kLog2e, a.scale, a.causal);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq_bf16(const LaunchArgs& a) {
-    if (a.D == 64) return launch_dq<64, 64, 4>(a);
-    if (a.D == 128) return launch_dq<128, 32, 4>(a);
+    if (a.D == 64) return launch_dq<64, 64, 4, false>(a);
+    if (a.D == 128) return launch_dq<128, 32, 4, false>(a);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dq_delta_bf16(const LaunchArgs& a) {
+    if (a.D == 64) return launch_dq<64, 64, 4, true>(a);
+    if (a.D == 128) return launch_dq<128, 32, 4, true>(a);
     return hipErrorInvalidValue;
 }
 

@@ -104,6 +104,16 @@ __device__ __forceinline__ float sum_bf16x8(const bf16x8& x, float acc) {
     return acc;
 }
 
+// acc + the dot product of two bf16x8 vectors (fp32 accumulation, pairs built
+// element by element as in sum_bf16x8).
+__device__ __forceinline__ float dot_bf16x8(const bf16x8& x, const bf16x8& y, float acc) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{x[0], x[1]}, bf16x2{y[0], y[1]}, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{x[2], x[3]}, bf16x2{y[2], y[3]}, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{x[4], x[5]}, bf16x2{y[4], y[5]}, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{x[6], x[7]}, bf16x2{y[6], y[7]}, acc, false);
+    return acc;
+}
+
 // Reductions over the lane pair (l, l ^ 32).  v_permlane32_swap exchanges the
 // upper half of its first register with the lower half of its second; given x in
 // both, every lane ends up holding x[l % 32] in one result and x[l % 32 + 32] in

@@ -104,10 +104,13 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
     }
 }
 
-template <int D>
+// DELTA_FROM_O: delta = rowsum(dO o O) is formed here from the O rows and
+// written to DeltaOut; otherwise it is read from Delta.
+template <int D, bool DELTA_FROM_O>
 __global__ __launch_bounds__(256) void dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
-                                                     const float* __restrict__ V, const float* __restrict__ dO,
-                                                     const float* __restrict__ LSE, const float* __restrict__ Delta,
+                                                     const float* __restrict__ V, const float* __restrict__ O,
+                                                     const float* __restrict__ dO, const float* __restrict__ LSE,
+                                                     const float* __restrict__ Delta, float* __restrict__ DeltaOut,
                                                      float* __restrict__ dQ, int S, int nblk, int BH, float c,
                                                      float scale, int causal) {
     constexpr int G = D / 32, R = 256 / G;
@@ -131,7 +134,17 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(const float* __restrict__ Q
         acc[e] = 0.f;
     }
     const float l2 = q < S ? LSE[(size_t)head * S + q] * kLog2e : INFINITY;
-    const float dl = q < S ? Delta[(size_t)head * S + q] : 0.f;
+    float dl;
+    if constexpr (DELTA_FROM_O) {
+        float dsum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 32; ++e)
+            dsum = fmaf(dov[e], q < S ? O[base + (size_t)q * D + part * 32 + e] : 0.f, dsum);
+        dl = group_sum<G>(dsum);
+        if (part == 0 && q < S) DeltaOut[(size_t)head * S + q] = dl;
+    } else {
+        dl = q < S ? Delta[(size_t)head * S + q] : 0.f;
+    }
     const int kend = causal ? min(S, q0 + R) : S;
     for (int k0 = 0; k0 < kend; k0 += kF32Tile) {
         __syncthreads();
@@ -252,14 +265,15 @@ static hipError_t fwd_f32(const LaunchArgs& a) {
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool DELTA_FROM_O>
 static hipError_t dq_f32(const LaunchArgs& a) {
     int nblk;
     const int total = f32_blocks<D>(a, &nblk);
     if (total < 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((dq_f32_kernel<D>), dim3(total), dim3(256), 0, a.stream, (const float*)a.q,
-                       (const float*)a.k, (const float*)a.v, (const float*)a.dout, a.lse_in, a.delta_in,
-                       (float*)a.dq, (int)a.S, nblk, (int)a.BH, a.scale * kLog2e, a.scale, a.causal);
+    hipLaunchKernelGGL((dq_f32_kernel<D, DELTA_FROM_O>), dim3(total), dim3(256), 0, a.stream, (const float*)a.q,
+                       (const float*)a.k, (const float*)a.v, (const float*)a.o_in, (const float*)a.dout, a.lse_in,
+                       a.delta_in, a.delta, (float*)a.dq, (int)a.S, nblk, (int)a.BH, a.scale * kLog2e, a.scale,
+                       a.causal);
     return hipGetLastError();
 }
 
@@ -280,8 +294,14 @@ hipError_t launch_fwd_f32(const LaunchArgs& a) {
     return hipErrorInvalidValue;
 }
 hipError_t launch_bwd_dq_f32(const LaunchArgs& a) {
-    if (a.D == 64) return dq_f32<64>(a);
-    if (a.D == 128) return dq_f32<128>(a);
+    if (a.D == 64) return dq_f32<64, false>(a);
+    if (a.D == 128) return dq_f32<128, false>(a);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dq_delta_f32(const LaunchArgs& a) {
+    if (a.D == 64) return dq_f32<64, true>(a);
+    if (a.D == 128) return dq_f32<128, true>(a);
     return hipErrorInvalidValue;
 }
 hipError_t launch_bwd_dkdv_f32(const LaunchArgs& a) {

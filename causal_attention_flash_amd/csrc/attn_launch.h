@@ -12,13 +12,13 @@ struct LaunchArgs {
     const void* q = nullptr;
     const void* k = nullptr;
     const void* v = nullptr;
-    const void* o_in = nullptr;  // forward output read by the backward preprocess
+    const void* o_in = nullptr;  // forward output, read where delta = rowsum(dO o O) is formed
     const void* dout = nullptr;
     const float* lse_in = nullptr;
     const float* delta_in = nullptr;
     void* o = nullptr;
     float* lse = nullptr;
-    float* delta = nullptr;
+    float* delta = nullptr;  // delta written by the preprocess or the dQ-with-delta pass
     void* dq = nullptr;
     void* dk = nullptr;
     void* dv = nullptr;
@@ -33,10 +33,13 @@ struct LaunchArgs {
 hipError_t launch_fwd_bf16(const LaunchArgs& a);
 hipError_t launch_bwd_dkdv_bf16(const LaunchArgs& a);
 hipError_t launch_bwd_dq_bf16(const LaunchArgs& a);
+// dQ pass that also forms delta from O and dO and writes it to a.delta
+hipError_t launch_bwd_dq_delta_bf16(const LaunchArgs& a);
 
 hipError_t launch_fwd_f32(const LaunchArgs& a);
 hipError_t launch_bwd_dkdv_f32(const LaunchArgs& a);
 hipError_t launch_bwd_dq_f32(const LaunchArgs& a);
+hipError_t launch_bwd_dq_delta_f32(const LaunchArgs& a);
 
 // delta = rowsum(dO o O) for either element type (elem_bytes 2 = bf16, 4 = f32).
 hipError_t launch_bwd_preprocess(const LaunchArgs& a, int elem_bytes);

@@ -102,7 +102,8 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D, attn
  *   dq, dk, dv       : device, [B,H,S,D] of dtype, fully overwritten.
  *   workspace        : device, at least attn_bwd_workspace_bytes() bytes, owned by the
  *                      caller; clobbered; must not overlap any other argument.
- * Enqueues, in order: delta = rowsum(dO o O) (fp32), the dK/dV pass, the dQ pass.
+ * Enqueues, in order: the dQ pass, which also forms delta = rowsum(dO o O) (fp32)
+ * in the workspace, then the dK/dV pass, which reads it.
  * Source: Forge RESEARCH.md §6 (the "D term" paragraph and the two-kernel,
  * atomic-free backward that recomputes P = exp(S - L) per tile).
  */
@@ -114,10 +115,12 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      float scale, int causal, attn_dtype dtype, void* stream);
 
 /*
- * The three stages attn_bwd enqueues, exposed one by one (same argument rules).
- * attn_bwd is exactly attn_bwd_preprocess + attn_bwd_dkdv + attn_bwd_dq on one
- * stream.
- *   delta : device, [B,H,S] fp32; written by the preprocess, read by the others.
+ * The backward's stages, exposed one by one (same argument rules as attn_bwd).
+ * attn_bwd is exactly attn_bwd_dq_delta + attn_bwd_dkdv on one stream.
+ * attn_bwd_preprocess + attn_bwd_dkdv + attn_bwd_dq computes the same gradients
+ * with delta formed by a separate pass (its fp32 sums may differ in the last bits).
+ *   delta : device, [B,H,S] fp32; written by attn_bwd_preprocess and
+ *           attn_bwd_dq_delta, read by attn_bwd_dkdv and attn_bwd_dq.
  */
 attn_status attn_bwd_preprocess(const void* o, const void* dout, float* delta,
                                 int64_t B, int64_t H, int64_t S, int64_t D,
@@ -132,6 +135,16 @@ attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const void*
                         const float* lse, const float* delta, void* dq,
                         int64_t B, int64_t H, int64_t S, int64_t D,
                         float scale, int causal, attn_dtype dtype, void* stream);
+
+/*
+ * dQ pass that also forms delta = rowsum(dO o O) for every query row from o and
+ * dout (fp32 sums of the stored values) and writes it to delta (fully
+ * overwritten; must not overlap the other arguments).
+ */
+attn_status attn_bwd_dq_delta(const void* q, const void* k, const void* v, const void* o,
+                              const void* dout, const float* lse, float* delta, void* dq,
+                              int64_t B, int64_t H, int64_t S, int64_t D,
+                              float scale, int causal, attn_dtype dtype, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(attn_status status);

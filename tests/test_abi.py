@@ -43,7 +43,7 @@ def lib():
 def test_header_declares_the_boundary():
     decls = _declared_functions()
     assert set(decls) == {"attn_fwd", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_preprocess",
-                          "attn_bwd_dkdv", "attn_bwd_dq", "attn_status_string"}
+                          "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_delta", "attn_status_string"}
     for name, nargs in decls.items():
         assert len(bd.SIGNATURES[name][1]) == nargs, name
 
@@ -146,6 +146,13 @@ def test_stage_entry_points_validate(lib):
     assert bd.c_attn_bwd_dkdv(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], 2, 3, 100, 64, 0.1, 3, BF16) == UNSUP
     assert bd.c_attn_bwd_dq(P[0], P[1], P[2], P[3], P[4], 0, P[6], 2, 3, 100, 64, 0.1, 1, BF16) == NULL
     assert bd.c_attn_bwd_dq(P[0], P[1], P[2], P[3], P[4], P[5], P[4] + 32, 2, 3, 100, 64, 0.1, 1, BF16) == ALIAS
+    # attn_bwd_dq_delta(q, k, v, o, dout, lse, delta, dq, ...): delta and dq are outputs
+    assert bd.c_attn_bwd_dq_delta(P[0], P[1], P[2], P[3], P[4], P[5], 0, P[7], 2, 3, 100, 64, 0.1, 1, BF16) == NULL
+    assert bd.c_attn_bwd_dq_delta(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[3], 2, 3, 100, 64, 0.1, 1, BF16) == ALIAS
+    assert bd.c_attn_bwd_dq_delta(P[0], P[1], P[2], P[3], P[4], P[5], P[5] + 64, P[7], 2, 3, 100, 64, 0.1, 1,
+                                  BF16) == ALIAS
+    assert bd.c_attn_bwd_dq_delta(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], 2, 3, 100, 64, 0.0, 1, BF16) == UNSUP
+    assert bd.c_attn_bwd_dq_delta(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], 0, 3, 100, 64, 0.1, 1, BF16) == OK
 
 
 def test_torch_wrapper_rejects_cpu_tensors(lib):
