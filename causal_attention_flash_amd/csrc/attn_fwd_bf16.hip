@@ -205,6 +205,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
             for (int db = 0; db < D / 32; ++db) vf[ks][db] = lds_tr_operand<STR>(Vs, ks * 16, db * 32, lane);
 
         if (resc) {
+            // rare (the reference point moves only past the slack): keep it a
+            // branch; the empty volatile asm stops the compiler from executing
+            // the rescale unconditionally
+            asm volatile("");
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 const float f = fast_exp2(m[qb] - mn[qb]);
