@@ -31,10 +31,19 @@ excluded exactly: they contribute 0 to every sum, which is what a finite mask
 value on the GPU reaches whenever a row has at least one visible key (always
 true for causal self-attention: key i is visible to query i).
 
+Grouped key/value heads (GQA): with H query heads and H_kv key/value heads
+(H a multiple of H_kv, G = H / H_kv), query head h reads key/value head h // G
+of the same batch entry -- the index map of Forge RESEARCH.md §6 ("GQA",
+kv_head = q_head / (n_heads / n_kv_heads)), with no copies of K and V.  Each
+query head is then plain attention on its key/value head, and because a
+key/value head feeds G query heads, its dK and dV are the sums of the G heads'
+contributions (the chain rule through the shared input).
+
 Parity status: pinned.  Each function here is checked in tests/test_oracle_pins.py
 against closed forms, invariants, central finite differences, torch's float64
-scaled_dot_product_attention on tiny shapes, and the one numeric cell the pages
-print (Rigel §6, the 455.9375 accumulator probe).
+scaled_dot_product_attention on tiny shapes (with enable_gqa for the grouped
+form), and the one numeric cell the pages print (Rigel §6, the 455.9375
+accumulator probe).
 """
 from __future__ import annotations
 
@@ -46,6 +55,8 @@ __all__ = [
     "attention_forward",
     "attention_backward",
     "attention_head",
+    "gqa_forward",
+    "gqa_backward",
 ]
 
 
@@ -130,4 +141,41 @@ def attention_backward(q, k, v, do, scale: float, causal: bool = True):
     for b, h in _heads(q):
         dq[b, h], dk[b, h], dv[b, h], _, _ = head_backward(
             q[b, h], k[b, h], v[b, h], do[b, h], scale, causal)
+    return dq, dk, dv
+
+
+def _group(q, k):
+    """G = H / H_kv for q [B, H, S, D] and k [B, H_kv, S, D]."""
+    H, Hkv = q.shape[1], k.shape[1]
+    if Hkv < 1 or H % Hkv != 0 or q.shape[0] != k.shape[0]:
+        raise ValueError(f"query heads {H} must be a multiple of key/value heads {Hkv}")
+    return H // Hkv
+
+
+def gqa_forward(q, k, v, scale: float, causal: bool = True):
+    """q [B, H, S, D], k and v [B, H_kv, S, D] -> (o [B, H, S, D], lse [B, H, S]).
+
+    Query head h attends with key/value head h // (H / H_kv); float64, head by head.
+    """
+    G = _group(q, k)
+    B, H, S, _ = q.shape
+    o = np.empty(q.shape[:3] + (v.shape[3],), dtype=np.float64)
+    lse = np.empty((B, H, S), dtype=np.float64)
+    for b, h in _heads(q):
+        o[b, h], lse[b, h] = head_forward(q[b, h], k[b, h // G], v[b, h // G], scale, causal)
+    return o, lse
+
+
+def gqa_backward(q, k, v, do, scale: float, causal: bool = True):
+    """Gradients for the grouped form: dq [B, H, S, D]; dk, dv [B, H_kv, S, D], each
+    key/value head's gradient summed over the G query heads that read it."""
+    G = _group(q, k)
+    dq = np.empty(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    for b, h in _heads(q):
+        dq_h, dk_h, dv_h, _, _ = head_backward(q[b, h], k[b, h // G], v[b, h // G], do[b, h], scale, causal)
+        dq[b, h] = dq_h
+        dk[b, h // G] += dk_h
+        dv[b, h // G] += dv_h
     return dq, dk, dv

@@ -15,7 +15,12 @@ log2-vs-ln LSE, a missing delta term) fails at least one of them:
   routine the attention guide's Core AI section uses as the definition) on
   tiny shapes;
 * the one numeric cell the pages print: Rigel §6's accumulator-width probe,
-  448 + 127 * 0.0625 = 455.9375 (tests/golden/accumulator_width.json).
+  448 + 127 * 0.0625 = 455.9375 (tests/golden/accumulator_width.json);
+* grouped key/value heads: torch's float64 scaled_dot_product_attention with
+  enable_gqa and autograd; central finite differences through a shared key/value
+  head (pins the summation of dK/dV over the group); the index map h -> h // G
+  (a tiled or mis-ordered map fails the repeat identity against the pinned
+  per-head oracle).
 """
 import json
 import os
@@ -23,7 +28,8 @@ import os
 import numpy as np
 import pytest
 
-from oracle import attention_backward, attention_forward, attention_head, head_backward, head_forward
+from oracle import (attention_backward, attention_forward, attention_head, gqa_backward, gqa_forward, head_backward,
+                    head_forward)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -299,3 +305,85 @@ def test_accumulator_width_cell():
     o, lse = head_forward(q, k, np.ones((1, 2)), g["scale"], True)
     assert lse[0] == g["lse"]  # exact: every term and partial sum is a dyadic rational
     assert g["lse_with_narrow_accumulator"] != g["lse"]
+
+
+# ------------------------------------------------------ grouped key/value heads
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (6, 1), (4, 4)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_gqa_against_torch_sdpa_float64(H, Hkv, causal):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(300 + H + Hkv)
+    B, S, D = 2, 9, 4
+    scale = 1.0 / np.sqrt(D)
+    q, do = _rand(rng, B, H, S, D), _rand(rng, B, H, S, D)
+    k, v = _rand(rng, B, Hkv, S, D), _rand(rng, B, Hkv, S, D)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale, enable_gqa=True)
+    to.backward(torch.tensor(do, dtype=torch.float64))
+    o, lse = gqa_forward(q, k, v, scale, causal)
+    dq, dk, dv = gqa_backward(q, k, v, do, scale, causal)
+    np.testing.assert_allclose(o, to.detach().numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_gqa_repeat_identity_and_index_map():
+    """Grouped attention equals per-head attention on K/V repeated G times along the
+    head axis (query head h reads key/value head h // G); its dK/dV are the per-head
+    gradients summed over each group."""
+    rng = np.random.default_rng(31)
+    B, H, Hkv, S, D = 2, 6, 2, 7, 5
+    G = H // Hkv
+    scale = 0.4
+    q, do = _rand(rng, B, H, S, D), _rand(rng, B, H, S, D)
+    k, v = _rand(rng, B, Hkv, S, D), _rand(rng, B, Hkv, S, D)
+    kr, vr = np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)
+    o, lse = gqa_forward(q, k, v, scale)
+    o_ref, lse_ref = attention_forward(q, kr, vr, scale)
+    np.testing.assert_array_equal(o, o_ref)
+    np.testing.assert_array_equal(lse, lse_ref)
+    dq, dk, dv = gqa_backward(q, k, v, do, scale)
+    dq_ref, dk_ref, dv_ref = attention_backward(q, kr, vr, do, scale)
+    np.testing.assert_array_equal(dq, dq_ref)
+    np.testing.assert_allclose(dk, dk_ref.reshape(B, Hkv, G, S, D).sum(axis=2), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(dv, dv_ref.reshape(B, Hkv, G, S, D).sum(axis=2), rtol=1e-13, atol=1e-14)
+    # a tiled map (h -> h % Hkv) is a different function on these inputs
+    o_tiled, _ = attention_forward(q, np.tile(k, (1, G, 1, 1)), np.tile(v, (1, G, 1, 1)), scale)
+    assert np.abs(o_tiled - o).max() > 1e-3
+
+
+def test_gqa_finite_differences_through_shared_heads():
+    rng = np.random.default_rng(32)
+    B, H, Hkv, S, D = 1, 4, 2, 5, 3
+    scale = 0.6
+    q, do = _rand(rng, B, H, S, D), _rand(rng, B, H, S, D)
+    k, v = _rand(rng, B, Hkv, S, D), _rand(rng, B, Hkv, S, D)
+    dq, dk, dv = gqa_backward(q, k, v, do, scale)
+
+    def loss():
+        o, _ = gqa_forward(q, k, v, scale)
+        return float((do * o).sum())
+
+    h = 1e-5
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + h
+            lp = loss()
+            x[idx] = old - h
+            lm = loss()
+            x[idx] = old
+            fd[idx] = (lp - lm) / (2 * h)
+        err = np.abs(fd - g).max() / np.abs(g).max()
+        assert err <= 1e-6, (name, err)
+
+
+def test_gqa_rejects_non_divisible_heads():
+    q = np.zeros((1, 5, 3, 2))
+    k = np.zeros((1, 2, 3, 2))
+    with pytest.raises(ValueError):
+        gqa_forward(q, k, k, 1.0)
