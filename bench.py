@@ -38,7 +38,8 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="gpt205m_bf16", choices=sorted(si.WORKLOADS))
+    ap.add_argument("--workload", default="gpt205m_bf16", choices=sorted(si.WORKLOADS) + sorted(si.GQA_WORKLOADS),
+                    help="grouped key/value head workloads run attn_fwd_gqa / attn_bwd_gqa")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--profile-steps", type=int, default=0,
@@ -54,16 +55,20 @@ def kernel_units(w):
     forward does 2 units (QK^T, PV); the backward's 5 units are S, dP, dV, dK in
     the dK/dV pass and dQ in the dQ pass (the dQ pass's recomputed S and dP are
     not algorithmic work).  The dQ pass also reads O to form delta = rowsum(dO o O)
-    and writes delta, which the dK/dV pass reads.
+    and writes delta, which the dK/dV pass reads.  With grouped key/value heads the
+    units count query heads (the work is the same); K, V, dK, dV are H_kv/H the size,
+    and "bwd" is the whole backward (both passes).
     """
     unit = w.B * w.H * w.S * w.S * w.D * (1.0 if w.causal else 2.0)
     elem = 2 if w.dtype == "bf16" else 4
     tensor = w.B * w.H * w.S * w.D * elem
+    kvt = tensor // w.H * w.kv_heads
     rows = w.B * w.H * w.S * 4
     return {
-        "fwd": {"flops": 2 * unit, "bytes": 3 * tensor + tensor + rows},
-        "bwd_dq": {"flops": 1 * unit, "bytes": 5 * tensor + rows + tensor + rows},
-        "bwd_dkdv": {"flops": 4 * unit, "bytes": 4 * tensor + 2 * rows + 2 * tensor},
+        "fwd": {"flops": 2 * unit, "bytes": tensor + 2 * kvt + tensor + rows},
+        "bwd_dq": {"flops": 1 * unit, "bytes": 3 * tensor + 2 * kvt + rows + tensor + rows},
+        "bwd_dkdv": {"flops": 4 * unit, "bytes": 2 * tensor + 2 * kvt + 2 * rows + 2 * kvt},
+        "bwd": {"flops": 5 * unit, "bytes": 3 * tensor + 2 * kvt + rows + tensor + 2 * kvt},
     }
 
 
@@ -96,10 +101,11 @@ def cpu_baseline(w, x, target_s: float):
         cores = os.cpu_count() or 1
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     per_head = w.flops / len(heads)
+    G = w.H // w.kv_heads  # query head h reads key/value head h // G
     done = 0
     t0 = time.perf_counter()
     for b, h in heads:
-        attention_head(x["q"][b, h], x["k"][b, h], x["v"][b, h], x["do"][b, h], w.scale, w.causal)
+        attention_head(x["q"][b, h], x["k"][b, h // G], x["v"][b, h // G], x["do"][b, h], w.scale, w.causal)
         done += 1
         if time.perf_counter() - t0 >= target_s:
             break
@@ -130,7 +136,8 @@ def main():
         sys.exit(1)
     caf.load_library()
     dev = torch.device("cuda:0")
-    w = si.WORKLOADS[args.workload]
+    w = si.WORKLOADS[args.workload] if args.workload in si.WORKLOADS else si.GQA_WORKLOADS[args.workload]
+    grouped = w.kv_heads != w.H
     x = si.make_inputs(w, seed=0)
 
     def dev_t(name):
@@ -146,8 +153,10 @@ def main():
     bd = caf._binding
     o = torch.empty_like(q)
     lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    nws = bd.c_attn_bwd_workspace_bytes(B, H, S, D, dt)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
+    Hkv = k.shape[1]
+    nws = (bd.c_attn_bwd_gqa_workspace_bytes(B, H, Hkv, S, D, dt) if grouped
+           else bd.c_attn_bwd_workspace_bytes(B, H, S, D, dt))
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     P = {n: t.data_ptr() for n, t in dict(q=q, k=k, v=v, o=o, lse=lse, do=do, dq=dq, dk=dk, dv=dv, ws=ws).items()}
@@ -157,11 +166,19 @@ def main():
             raise caf.AttnError(st, where)
 
     def fwd():
-        chk(bd.c_attn_fwd(P["q"], P["k"], P["v"], P["o"], P["lse"], B, H, S, D, scale, causal, dt, stream), "fwd")
+        if grouped:
+            chk(bd.c_attn_fwd_gqa(P["q"], P["k"], P["v"], P["o"], P["lse"], B, H, Hkv, S, D, scale, causal, dt, stream),
+                "fwd_gqa")
+        else:
+            chk(bd.c_attn_fwd(P["q"], P["k"], P["v"], P["o"], P["lse"], B, H, S, D, scale, causal, dt, stream), "fwd")
 
     def bwd():
-        chk(bd.c_attn_bwd(P["q"], P["k"], P["v"], P["o"], P["do"], P["lse"], P["dq"], P["dk"], P["dv"], P["ws"],
-                          nws, B, H, S, D, scale, causal, dt, stream), "bwd")
+        if grouped:
+            chk(bd.c_attn_bwd_gqa(P["q"], P["k"], P["v"], P["o"], P["do"], P["lse"], P["dq"], P["dk"], P["dv"],
+                                  P["ws"], nws, B, H, Hkv, S, D, scale, causal, dt, stream), "bwd_gqa")
+        else:
+            chk(bd.c_attn_bwd(P["q"], P["k"], P["v"], P["o"], P["do"], P["lse"], P["dq"], P["dk"], P["dv"], P["ws"],
+                              nws, B, H, S, D, scale, causal, dt, stream), "bwd")
 
     def dq_delta():
         chk(bd.c_attn_bwd_dq_delta(P["q"], P["k"], P["v"], P["o"], P["do"], P["lse"], P["ws"], P["dq"], B, H, S, D,
@@ -208,9 +225,14 @@ def main():
     ms_per_step = gpu_ms / args.steps
 
     # ---- per-kernel durations: the same K steps, each kernel attn_bwd launches
-    # (in its order) bracketed by events
-    names = ("fwd", "bwd_dq", "bwd_dkdv")
-    calls = (fwd, dq_delta, dkdv)
+    # (in its order) bracketed by events; the grouped form has no stage entry
+    # points, so there the backward is timed as one (its dQ and dK/dV passes)
+    if grouped:
+        names = ("fwd", "bwd")
+        calls = (fwd, bwd)
+    else:
+        names = ("fwd", "bwd_dq", "bwd_dkdv")
+        calls = (fwd, dq_delta, dkdv)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
@@ -225,7 +247,7 @@ def main():
     per_kernel_mean = {n: sum(d) / len(d) for n, d in durations.items()}
 
     units = kernel_units(w)
-    dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: per_kernel_mean[n])
+    dom = max(names, key=lambda n: per_kernel_mean[n])
     dom_ms = per_kernel_mean[dom]
     mfma_peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = units[dom]["flops"] / (dom_ms * 1e-3) / 1e12
@@ -245,7 +267,8 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "D": w.D, "causal": bool(w.causal),
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "S": w.S, "D": w.D,
+                   "causal": bool(w.causal),
                    "global_batch": w.B, "seq_len": w.S, "parallelism": "none (1 GPU)"},
         "pct_of_mfma_peak": round(100.0 * value / mfma_peak, 3),
         "wall_s_timed": round(wall, 4),

@@ -6,6 +6,8 @@ stream; all computation runs in the library's kernels.
 
     o, lse = attn_fwd(q, k, v, scale=None, causal=True)
     dq, dk, dv = attn_bwd(q, k, v, o, do, lse, scale=None, causal=True)
+    o, lse = attn_fwd_gqa(q, k, v)          # K, V with fewer (grouped) heads
+    dq, dk, dv = attn_bwd_gqa(q, k, v, o, do, lse)
 """
 from ._binding import (  # noqa: F401
     ATTN_BF16,
@@ -18,8 +20,10 @@ from ._binding import (  # noqa: F401
     attn_bwd_dkdv,
     attn_bwd_dq,
     attn_bwd_dq_delta,
+    attn_bwd_gqa,
     attn_bwd_preprocess,
     attn_fwd,
+    attn_fwd_gqa,
     load_library,
     status_string,
 )

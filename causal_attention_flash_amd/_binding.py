@@ -36,8 +36,12 @@ _INT = ctypes.c_int
 _SZ = ctypes.c_size_t
 SIGNATURES = {
     "attn_fwd": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _INT, _INT, _P]),
+    "attn_fwd_gqa": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _INT, _INT, _P]),
     "attn_bwd_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _INT]),
+    "attn_bwd_gqa_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64, _INT]),
     "attn_bwd": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64, _I64, _I64, _F, _INT, _INT, _P]),
+    "attn_bwd_gqa": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64, _I64, _I64, _I64, _F, _INT, _INT,
+                            _P]),
     "attn_bwd_preprocess": (_INT, [_P, _P, _P, _I64, _I64, _I64, _I64, _INT, _P]),
     "attn_bwd_dkdv": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _INT, _INT, _P]),
     "attn_bwd_dq": (_INT, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _INT, _INT, _P]),
@@ -86,13 +90,27 @@ def c_attn_fwd(q, k, v, o, lse, B, H, S, D, scale, causal, dtype, stream=0) -> i
     return load_library().attn_fwd(q, k, v, o, lse, B, H, S, D, scale, causal, dtype, stream)
 
 
+def c_attn_fwd_gqa(q, k, v, o, lse, B, H, H_kv, S, D, scale, causal, dtype, stream=0) -> int:
+    return load_library().attn_fwd_gqa(q, k, v, o, lse, B, H, H_kv, S, D, scale, causal, dtype, stream)
+
+
 def c_attn_bwd_workspace_bytes(B, H, S, D, dtype) -> int:
     return load_library().attn_bwd_workspace_bytes(B, H, S, D, dtype)
+
+
+def c_attn_bwd_gqa_workspace_bytes(B, H, H_kv, S, D, dtype) -> int:
+    return load_library().attn_bwd_gqa_workspace_bytes(B, H, H_kv, S, D, dtype)
 
 
 def c_attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, H, S, D, scale, causal, dtype, stream=0) -> int:
     return load_library().attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, H, S, D, scale, causal,
                                    dtype, stream)
+
+
+def c_attn_bwd_gqa(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, H, H_kv, S, D, scale, causal, dtype,
+                   stream=0) -> int:
+    return load_library().attn_bwd_gqa(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, H, H_kv, S, D, scale, causal,
+                                       dtype, stream)
 
 
 def c_attn_bwd_preprocess(o, do, delta, B, H, S, D, dtype, stream=0) -> int:
@@ -185,6 +203,49 @@ def attn_bwd(q, k, v, o, do, lse, scale=None, causal=True):
     _call(c_attn_bwd, "attn_bwd", q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
           lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(),
           B, H, S, D, _scale(scale, D), int(bool(causal)), dt, _stream(q.device))
+    return dq, dk, dv
+
+
+def _kv_heads(q, k):
+    """H_kv from K's shape [B, H_kv, S, D] next to Q's [B, H, S, D]."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, H, S, D] and [B, H_kv, S, D]")
+    B, H, S, D = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, S, D) or Hkv < 1 or H % Hkv != 0:
+        raise ValueError(f"k has shape {tuple(k.shape)}; expected [B, H_kv, S, D] with H_kv dividing H = {H}")
+    return Hkv
+
+
+def attn_fwd_gqa(q, k, v, scale=None, causal=True):
+    """O, LSE = attn_fwd_gqa(Q, K, V): Q [B,H,S,D]; K, V [B,H_kv,S,D] (grouped heads)."""
+    torch = _torch()
+    Hkv = _kv_heads(q, k)
+    B, H, S, D = q.shape
+    _check_tensors((("q", q),), q.shape, q.dtype, q.device)
+    _check_tensors((("k", k), ("v", v)), k.shape, q.dtype, q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    _call(c_attn_fwd_gqa, "attn_fwd_gqa", q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+          B, H, Hkv, S, D, _scale(scale, D), int(bool(causal)), _dtype_code(q), _stream(q.device))
+    return o, lse
+
+
+def attn_bwd_gqa(q, k, v, o, do, lse, scale=None, causal=True):
+    """dQ, dK, dV = attn_bwd_gqa(Q, K, V, O, dO, LSE); dK, dV are [B,H_kv,S,D]."""
+    torch = _torch()
+    Hkv = _kv_heads(q, k)
+    B, H, S, D = q.shape
+    _check_tensors((("q", q), ("o", o), ("do", do)), q.shape, q.dtype, q.device)
+    _check_tensors((("k", k), ("v", v)), k.shape, q.dtype, q.device)
+    _check_tensors((("lse", lse),), (B, H, S), torch.float32, q.device)
+    dt = _dtype_code(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
+    nws = c_attn_bwd_gqa_workspace_bytes(B, H, Hkv, S, D, dt)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=q.device)
+    _call(c_attn_bwd_gqa, "attn_bwd_gqa", q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+          lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(),
+          B, H, Hkv, S, D, _scale(scale, D), int(bool(causal)), dt, _stream(q.device))
     return dq, dk, dv
 
 

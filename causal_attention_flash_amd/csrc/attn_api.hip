@@ -74,6 +74,14 @@ attn_status check_alias(std::initializer_list<Span> outs, std::initializer_list<
 
 attn_status from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
+// Grouped key/value heads: H_kv >= 1 dividing H (negative always rejected; any
+// non-negative value is accepted for an empty problem).
+attn_status check_groups(int64_t H, int64_t H_kv, bool empty) {
+    if (H_kv < 0) return ATTN_ERR_SHAPE;
+    if (empty) return ATTN_OK;
+    return (H_kv >= 1 && H % H_kv == 0) ? ATTN_OK : ATTN_ERR_SHAPE;
+}
+
 struct Sizes {
     size_t tensor;  // bytes of one [B,H,S,D] tensor
     size_t rows;    // bytes of one [B,H,S] fp32 vector
@@ -87,6 +95,8 @@ Sizes sizes(int64_t B, int64_t H, int64_t S, int64_t D, attn_dtype dt) {
 LaunchArgs base_args(int64_t B, int64_t H, int64_t S, int64_t D, float scale, int causal, void* stream) {
     LaunchArgs a;
     a.BH = B * H;
+    a.H = H;
+    a.Hkv = H;
     a.S = S;
     a.D = D;
     a.scale = scale;
@@ -104,6 +114,17 @@ attn_status run_dkdv(const LaunchArgs& a, attn_dtype dt) {
 attn_status run_dq(const LaunchArgs& a, attn_dtype dt) {
     return from_hip(dt == ATTN_BF16 ? attn::launch_bwd_dq_bf16(a) : attn::launch_bwd_dq_f32(a));
 }
+// Workspace of the grouped backward: delta (B*H*S fp32), then for bf16 with more
+// than one query head per key/value head the per-query-head fp32 dK and dV
+// ([B,H,S,D] each), each region starting on a 256-byte boundary.
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+size_t gqa_workspace(int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D, attn_dtype dt) {
+    const Sizes z = sizes(B, H, S, D, dt);
+    if (dt != ATTN_BF16 || H_kv == H) return z.rows;
+    const size_t part = (size_t)B * (size_t)H * (size_t)S * (size_t)D * sizeof(float);
+    return round256(z.rows) + 2 * round256(part);
+}
+attn_status run_group_sum(const LaunchArgs& a) { return from_hip(attn::launch_group_sum_bf16(a)); }
 attn_status run_dq_delta(const LaunchArgs& a, attn_dtype dt) {
     return from_hip(dt == ATTN_BF16 ? attn::launch_bwd_dq_delta_bf16(a) : attn::launch_bwd_dq_delta_f32(a));
 }
@@ -116,7 +137,8 @@ const char* attn_status_string(attn_status s) {
     switch (s) {
         case ATTN_OK: return "ok";
         case ATTN_ERR_NULL: return "a required pointer is NULL";
-        case ATTN_ERR_SHAPE: return "negative size, or sizes beyond B*H*S < 2^31 and S*D < 2^31";
+        case ATTN_ERR_SHAPE:
+            return "negative size, sizes beyond B*H*S < 2^31 and S*D < 2^31, or H_kv < 1 or not dividing H";
         case ATTN_ERR_UNSUPPORTED:
             return "unsupported: D must be 64 or 128, dtype ATTN_F32 or ATTN_BF16, causal 0 or 1, scale finite and > 0";
         case ATTN_ERR_ALIGNMENT: return "a device pointer is not 16-byte aligned";
@@ -129,15 +151,24 @@ const char* attn_status_string(attn_status s) {
 
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                      int64_t S, int64_t D, float scale, int causal, attn_dtype dtype, void* stream) {
+    return attn_fwd_gqa(q, k, v, o, lse, B, H, H, S, D, scale, causal, dtype, stream);
+}
+
+attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                         int64_t H_kv, int64_t S, int64_t D, float scale, int causal, attn_dtype dtype,
+                         void* stream) {
     bool empty = false;
     attn_status st = check_shape(B, H, S, D, dtype, &empty);
+    if (st == ATTN_OK) st = check_groups(H, H_kv, empty);
     if (st == ATTN_OK) st = check_scale_causal(scale, causal);
     if (st != ATTN_OK || empty) return st;
     if ((st = check_ptrs({q, k, v, o, lse})) != ATTN_OK) return st;
     const Sizes z = sizes(B, H, S, D, dtype);
-    if ((st = check_alias({{o, z.tensor}, {lse, z.rows}}, {{q, z.tensor}, {k, z.tensor}, {v, z.tensor}})) != ATTN_OK)
+    const size_t zkv = z.tensor / (size_t)H * (size_t)H_kv;
+    if ((st = check_alias({{o, z.tensor}, {lse, z.rows}}, {{q, z.tensor}, {k, zkv}, {v, zkv}})) != ATTN_OK)
         return st;
     LaunchArgs a = base_args(B, H, S, D, scale, causal, stream);
+    a.Hkv = H_kv;
     a.q = q;
     a.k = k;
     a.v = v;
@@ -253,23 +284,35 @@ attn_status attn_bwd_dq_delta(const void* q, const void* k, const void* v, const
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
                      int64_t S, int64_t D, float scale, int causal, attn_dtype dtype, void* stream) {
+    return attn_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, S, D, scale, causal,
+                        dtype, stream);
+}
+
+attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                         int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D, float scale, int causal,
+                         attn_dtype dtype, void* stream) {
     bool empty = false;
     attn_status st = check_shape(B, H, S, D, dtype, &empty);
+    if (st == ATTN_OK) st = check_groups(H, H_kv, empty);
     if (st == ATTN_OK) st = check_scale_causal(scale, causal);
     if (st != ATTN_OK || empty) return st;
     if ((st = check_ptrs({q, k, v, o, dout, lse, dq, dk, dv})) != ATTN_OK) return st;
     const Sizes z = sizes(B, H, S, D, dtype);
-    if (!workspace || workspace_bytes < z.rows) return ATTN_ERR_WORKSPACE;
+    const size_t zkv = z.tensor / (size_t)H * (size_t)H_kv;
+    const size_t wsz = gqa_workspace(B, H, H_kv, S, D, dtype);
+    if (!workspace || workspace_bytes < wsz) return ATTN_ERR_WORKSPACE;
     if (!aligned16(workspace)) return ATTN_ERR_ALIGNMENT;
-    if ((st = check_alias({{dq, z.tensor}, {dk, z.tensor}, {dv, z.tensor}, {workspace, z.rows}},
+    if ((st = check_alias({{dq, z.tensor}, {dk, zkv}, {dv, zkv}, {workspace, wsz}},
                           {{q, z.tensor},
-                           {k, z.tensor},
-                           {v, z.tensor},
+                           {k, zkv},
+                           {v, zkv},
                            {o, z.tensor},
                            {dout, z.tensor},
                            {lse, z.rows}})) != ATTN_OK)
         return st;
     LaunchArgs a = base_args(B, H, S, D, scale, causal, stream);
+    a.Hkv = H_kv;
     a.q = q;
     a.k = k;
     a.v = v;
@@ -281,9 +324,25 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
-    // dQ first: it forms delta, which the dK/dV pass reads
+    const bool partials = dtype == ATTN_BF16 && H_kv != H;
+    if (partials) {
+        char* w = (char*)workspace;
+        const size_t part = (size_t)B * (size_t)H * (size_t)S * (size_t)D * sizeof(float);
+        a.dk_part = (float*)(w + round256(z.rows));
+        a.dv_part = (float*)(w + round256(z.rows) + round256(part));
+    }
+    // dQ first: it forms delta, which the dK/dV pass reads; with grouped heads in
+    // bf16 the dK/dV pass leaves per-query-head partials that the group sum adds
     if ((st = run_dq_delta(a, dtype)) != ATTN_OK) return st;
-    return run_dkdv(a, dtype);
+    if ((st = run_dkdv(a, dtype)) != ATTN_OK) return st;
+    return partials ? run_group_sum(a) : ATTN_OK;
+}
+
+size_t attn_bwd_gqa_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D, attn_dtype dtype) {
+    bool empty = false;
+    if (check_shape(B, H, S, D, dtype, &empty) != ATTN_OK || empty) return 0;
+    if (check_groups(H, H_kv, empty) != ATTN_OK) return 0;
+    return gqa_workspace(B, H, H_kv, S, D, dtype);
 }
 
 }  // extern "C"

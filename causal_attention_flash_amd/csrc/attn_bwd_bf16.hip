@@ -46,12 +46,18 @@ struct DkdvCfg {
     static constexpr int WAVES_PER_SIMD = D == 64 ? 2 : 1;  // register budget: 256 VGPRs at D = 64
 };
 
-template <int D, int BMQ, int NW>
+// One workgroup per (query head, key block): the query head's Q/dO/LSE/delta
+// against the keys of its key/value head.  With one query head per key/value
+// head (PARTIAL = false) dK and dV are final and stored as bf16.  With grouped
+// key/value heads (PARTIAL = true) each query head's contribution is stored as
+// fp32 at its own [query head] slot of dKp/dVp, and the sum over the G query
+// heads of a key/value head is formed by bwd_group_sum_kernel.
+template <int D, int BMQ, int NW, bool PARTIAL>
 __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) void bwd_dkdv_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int S, int nblk, int BH, float c, float scale,
-    int causal) {
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ dKp, float* __restrict__ dVp, int S,
+    int nblk, int BH, int H, int GQ, float c, float scale, int causal) {
     using Cfg = DkdvCfg<D, BMQ, NW>;
     constexpr int NT = Cfg::NT, BNK = Cfg::BNK;
     constexpr int STR = Cfg::STR;
@@ -63,6 +69,7 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
     const int kblk = wi.rank;  // low key blocks see the most queries: first
     const int n0 = kblk * BNK;
     const size_t base = (size_t)head * S * D;
+    const size_t kvbase = (size_t)kv_head_of(head, H, GQ) * S * D;
     const uint16_t* Qh = Q + base;
     const uint16_t* dOh = dO + base;
     const float* Lh = LSE + (size_t)head * S;
@@ -80,8 +87,8 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
     for (int ks = 0; ks < D / 16; ++ks) {
         u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
         if (key < S) {
-            a = ldg16(K + base + (size_t)key * D + ks * 16 + 8 * h);
-            b = ldg16(V + base + (size_t)key * D + ks * 16 + 8 * h);
+            a = ldg16(K + kvbase + (size_t)key * D + ks * 16 + 8 * h);
+            b = ldg16(V + kvbase + (size_t)key * D + ks * 16 + 8 * h);
         }
         kf[ks] = as_bf16x8(a);
         vf[ks] = as_bf16x8(b);
@@ -203,9 +210,27 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
         __syncthreads();
     }
 
-    if (key < S) {
-        uint16_t* dKr = dK + base + (size_t)key * D;
-        uint16_t* dVr = dV + base + (size_t)key * D;
+    if (PARTIAL && key < S) {
+        float* dKr = dKp + base + (size_t)key * D;
+        float* dVr = dVp + base + (size_t)key * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = db * 32 + 8 * g + 4 * h;
+                f32x4 fk, fv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    fk[i] = dkacc[db][4 * g + i] * scale;
+                    fv[i] = dvacc[db][4 * g + i];
+                }
+                *reinterpret_cast<f32x4*>(dKr + d) = fk;
+                *reinterpret_cast<f32x4*>(dVr + d) = fv;
+            }
+    }
+    if (!PARTIAL && key < S) {
+        uint16_t* dKr = dK + kvbase + (size_t)key * D;
+        uint16_t* dVr = dV + kvbase + (size_t)key * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -228,10 +253,18 @@ static hipError_t launch_dkdv(const LaunchArgs& a) {
     const int nblk = (int)((a.S + Cfg::BNK - 1) / Cfg::BNK);
     const int64_t total = (int64_t)nblk * a.BH;
     if (total > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, BMQ, NW>), dim3((unsigned)total), dim3(Cfg::NT), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, a.lse_in, a.delta_in, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                       (int)a.S, nblk, (int)a.BH, a.scale * kLog2e, a.scale, a.causal);
+    const int GQ = (int)(a.H / a.Hkv);
+    if (GQ == 1)
+        hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, BMQ, NW, false>), dim3((unsigned)total), dim3(Cfg::NT), 0,
+                           a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                           (const uint16_t*)a.dout, a.lse_in, a.delta_in, (uint16_t*)a.dk, (uint16_t*)a.dv,
+                           nullptr, nullptr, (int)a.S, nblk, (int)a.BH, (int)a.H, 1, a.scale * kLog2e, a.scale,
+                           a.causal);
+    else
+        hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, BMQ, NW, true>), dim3((unsigned)total), dim3(Cfg::NT), 0,
+                           a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                           (const uint16_t*)a.dout, a.lse_in, a.delta_in, nullptr, nullptr, a.dk_part, a.dv_part,
+                           (int)a.S, nblk, (int)a.BH, (int)a.H, GQ, a.scale * kLog2e, a.scale, a.causal);
     return hipGetLastError();
 }
 
@@ -239,6 +272,52 @@ hipError_t launch_bwd_dkdv_bf16(const LaunchArgs& a) {
     if (a.D == 64) return launch_dkdv<64, 64, 8>(a);
     if (a.D == 128) return launch_dkdv<128, 32, 4>(a);
     return hipErrorInvalidValue;
+}
+
+// ====================================================== grouped key/value heads
+//
+// dK[b, j] = sum over g < GQ of dKp[b, j*GQ + g] (likewise dV), fp32 sums of the
+// per-query-head contributions, rounded once to bf16.  Grid-stride over groups
+// of 8 elements of [batch, key/value head, S, D].
+__global__ __launch_bounds__(256) void bwd_group_sum_kernel(const float* __restrict__ dKp,
+                                                            const float* __restrict__ dVp,
+                                                            uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+                                                            int64_t n8, int64_t head_elems, int GQ) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t e = i * 8;                // element of the [B, H_kv, S, D] output
+        const int64_t kvh = e / head_elems;     // batch x key/value head
+        const int64_t off = e - kvh * head_elems;
+        const int64_t src0 = kvh * GQ * head_elems + off;  // query head kvh*GQ of the same batch entry
+        f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = k0, v0 = k0, v1 = k0;
+        for (int g = 0; g < GQ; ++g) {
+            const int64_t src = src0 + (int64_t)g * head_elems;
+            k0 += *reinterpret_cast<const f32x4*>(dKp + src);
+            k1 += *reinterpret_cast<const f32x4*>(dKp + src + 4);
+            v0 += *reinterpret_cast<const f32x4*>(dVp + src);
+            v1 += *reinterpret_cast<const f32x4*>(dVp + src + 4);
+        }
+        u32x4 uk, uv;
+        uk[0] = pack_bf16x2(k0[0], k0[1]);
+        uk[1] = pack_bf16x2(k0[2], k0[3]);
+        uk[2] = pack_bf16x2(k1[0], k1[1]);
+        uk[3] = pack_bf16x2(k1[2], k1[3]);
+        uv[0] = pack_bf16x2(v0[0], v0[1]);
+        uv[1] = pack_bf16x2(v0[2], v0[3]);
+        uv[2] = pack_bf16x2(v1[0], v1[1]);
+        uv[3] = pack_bf16x2(v1[2], v1[3]);
+        *reinterpret_cast<u32x4*>(dK + e) = uk;
+        *reinterpret_cast<u32x4*>(dV + e) = uv;
+    }
+}
+
+hipError_t launch_group_sum_bf16(const LaunchArgs& a) {
+    const int64_t head_elems = a.S * a.D;
+    const int64_t n8 = a.BH / a.H * a.Hkv * head_elems / 8;
+    const int64_t want = (n8 + 255) / 256;
+    const unsigned grid = (unsigned)(want < 8192 ? (want > 0 ? want : 1) : 8192);
+    hipLaunchKernelGGL(bwd_group_sum_kernel, dim3(grid), dim3(256), 0, a.stream, a.dk_part, a.dv_part,
+                       (uint16_t*)a.dk, (uint16_t*)a.dv, n8, head_elems, (int)(a.H / a.Hkv));
+    return hipGetLastError();
 }
 
 // ================================================================== dQ pass
@@ -264,7 +343,7 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
     const float* __restrict__ Delta, float* __restrict__ DeltaOut, uint16_t* __restrict__ dQ, int S, int nblk,
-    int BH, float c, float scale, int causal) {
+    int BH, int H, int GQ, float c, float scale, int causal) {
     using Cfg = DqCfg<D, BNK, NW>;
     constexpr int BMQ = Cfg::BMQ;
     constexpr int STR = Cfg::STR;
@@ -275,8 +354,9 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
     const int qblk = nblk - 1 - wi.rank;  // high query blocks see the most keys: first
     const int q0 = qblk * BMQ;
     const size_t base = (size_t)head * S * D;
-    const uint16_t* Kh = K + base;
-    const uint16_t* Vh = V + base;
+    const size_t kvbase = (size_t)kv_head_of(head, H, GQ) * S * D;
+    const uint16_t* Kh = K + kvbase;
+    const uint16_t* Vh = V + kvbase;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -420,7 +500,8 @@ static hipError_t launch_dq(const LaunchArgs& a) {
     hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, BNK, NW, DELTA_FROM_O>), dim3((unsigned)total), dim3(Cfg::NT), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.o_in, (const uint16_t*)a.dout, a.lse_in, a.delta_in, a.delta,
-                       (uint16_t*)a.dq, (int)a.S, nblk, (int)a.BH, a.scale * kLog2e, a.scale, a.causal);
+                       (uint16_t*)a.dq, (int)a.S, nblk, (int)a.BH, (int)a.H, (int)(a.H / a.Hkv), a.scale * kLog2e,
+                       a.scale, a.causal);
     return hipGetLastError();
 }
 

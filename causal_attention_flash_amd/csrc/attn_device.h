@@ -176,4 +176,10 @@ struct WorkItem {
 };
 __device__ __forceinline__ WorkItem heavy_first(int bid, int BH) { return {bid % BH, bid / BH}; }
 
+// Grouped key/value heads: with H query heads per batch entry sharing H / GQ
+// key/value heads, query head qh (index over batch x H) reads key/value head
+// (qh / H) * (H / GQ) + (qh % H) / GQ (index over batch x H / GQ).  GQ = 1 is
+// one key/value head per query head.
+__device__ __forceinline__ int kv_head_of(int qh, int H, int GQ) { return (qh / H) * (H / GQ) + (qh % H) / GQ; }
+
 }  // namespace attn

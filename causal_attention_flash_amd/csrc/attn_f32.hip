@@ -40,7 +40,8 @@ __device__ __forceinline__ void stage_rows_f32(float* dst, const float* __restri
 template <int D>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                       const float* __restrict__ V, float* __restrict__ O,
-                                                      float* __restrict__ LSE, int S, int nblk, int BH, float c,
+                                                      float* __restrict__ LSE, int S, int nblk, int BH, int H, int GQ,
+                                                      float c,
                                                       int causal) {
     constexpr int G = D / 32, R = 256 / G;
     __shared__ __attribute__((aligned(16))) float Ks[kF32Tile * D];
@@ -50,6 +51,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
     const int blk = nblk - 1 - wi.rank;
     const int q0 = blk * R;
     const size_t base = (size_t)head * S * D;
+    const size_t kvbase = (size_t)kv_head_of(head, H, GQ) * S * D;
     const int tid = threadIdx.x;
     const int part = tid % G;
     const int q = q0 + tid / G;
@@ -64,8 +66,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
     const int kend = causal ? min(S, q0 + R) : S;
     for (int k0 = 0; k0 < kend; k0 += kF32Tile) {
         __syncthreads();
-        stage_rows_f32<D>(Ks, K + base, k0, S, tid);
-        stage_rows_f32<D>(Vs, V + base, k0, S, tid);
+        stage_rows_f32<D>(Ks, K + kvbase, k0, S, tid);
+        stage_rows_f32<D>(Vs, V + kvbase, k0, S, tid);
         __syncthreads();
         float sv[kF32Tile];
         float mx = -INFINITY;
@@ -111,7 +113,8 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(const float* __restrict__ Q
                                                      const float* __restrict__ V, const float* __restrict__ O,
                                                      const float* __restrict__ dO, const float* __restrict__ LSE,
                                                      const float* __restrict__ Delta, float* __restrict__ DeltaOut,
-                                                     float* __restrict__ dQ, int S, int nblk, int BH, float c,
+                                                     float* __restrict__ dQ, int S, int nblk, int BH, int H, int GQ,
+                                                     float c,
                                                      float scale, int causal) {
     constexpr int G = D / 32, R = 256 / G;
     __shared__ __attribute__((aligned(16))) float Ks[kF32Tile * D];
@@ -121,6 +124,7 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(const float* __restrict__ Q
     const int blk = nblk - 1 - wi.rank;
     const int q0 = blk * R;
     const size_t base = (size_t)head * S * D;
+    const size_t kvbase = (size_t)kv_head_of(head, H, GQ) * S * D;
     const int tid = threadIdx.x;
     const int part = tid % G;
     const int q = q0 + tid / G;
@@ -148,8 +152,8 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(const float* __restrict__ Q
     const int kend = causal ? min(S, q0 + R) : S;
     for (int k0 = 0; k0 < kend; k0 += kF32Tile) {
         __syncthreads();
-        stage_rows_f32<D>(Ks, K + base, k0, S, tid);
-        stage_rows_f32<D>(Vs, V + base, k0, S, tid);
+        stage_rows_f32<D>(Ks, K + kvbase, k0, S, tid);
+        stage_rows_f32<D>(Vs, V + kvbase, k0, S, tid);
         __syncthreads();
 #pragma unroll 4
         for (int j = 0; j < kF32Tile; ++j) {
@@ -180,7 +184,8 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(const float* __restrict__
                                                        const float* __restrict__ V, const float* __restrict__ dO,
                                                        const float* __restrict__ LSE,
                                                        const float* __restrict__ Delta, float* __restrict__ dK,
-                                                       float* __restrict__ dV, int S, int nblk, int BH, float c,
+                                                       float* __restrict__ dV, int S, int nblk, int BH, int H, int GQ,
+                                                       float c,
                                                        float scale, int causal) {
     constexpr int G = D / 32, R = 256 / G;
     __shared__ __attribute__((aligned(16))) float Qs[kF32Tile * D];
@@ -205,14 +210,21 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(const float* __restrict__
         dv[e] = 0.f;
     }
     const int qstart = causal ? n0 : 0;
+    // BH counts key/value heads here; the GQ query heads that read this one
+    // all add into dk and dv
+    const int Hkv = H / GQ;
+    const int qh0 = (head / Hkv) * H + (head % Hkv) * GQ;
+    for (int g = 0; g < GQ; ++g)
     for (int qt0 = qstart; qt0 < S; qt0 += kF32Tile) {
+        const int qh = qh0 + g;
+        const size_t qbase = (size_t)qh * S * D;
         __syncthreads();
-        stage_rows_f32<D>(Qs, Q + base, qt0, S, tid);
-        stage_rows_f32<D>(Os, dO + base, qt0, S, tid);
+        stage_rows_f32<D>(Qs, Q + qbase, qt0, S, tid);
+        stage_rows_f32<D>(Os, dO + qbase, qt0, S, tid);
         if (tid < kF32Tile) {
             const int qq = qt0 + tid;
-            L2s[tid] = qq < S ? LSE[(size_t)head * S + qq] * kLog2e : INFINITY;
-            DLs[tid] = qq < S ? Delta[(size_t)head * S + qq] : 0.f;
+            L2s[tid] = qq < S ? LSE[(size_t)qh * S + qq] * kLog2e : INFINITY;
+            DLs[tid] = qq < S ? Delta[(size_t)qh * S + qq] : 0.f;
         }
         __syncthreads();
 #pragma unroll 4
@@ -260,7 +272,8 @@ static hipError_t fwd_f32(const LaunchArgs& a) {
     const int total = f32_blocks<D>(a, &nblk);
     if (total < 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3(total), dim3(256), 0, a.stream, (const float*)a.q,
-                       (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, (int)a.S, nblk, (int)a.BH,
+                       (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, (int)a.S, nblk, (int)a.BH, (int)a.H,
+                       (int)(a.H / a.Hkv),
                        a.scale * kLog2e, a.causal);
     return hipGetLastError();
 }
@@ -272,7 +285,8 @@ static hipError_t dq_f32(const LaunchArgs& a) {
     if (total < 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL((dq_f32_kernel<D, DELTA_FROM_O>), dim3(total), dim3(256), 0, a.stream, (const float*)a.q,
                        (const float*)a.k, (const float*)a.v, (const float*)a.o_in, (const float*)a.dout, a.lse_in,
-                       a.delta_in, a.delta, (float*)a.dq, (int)a.S, nblk, (int)a.BH, a.scale * kLog2e, a.scale,
+                       a.delta_in, a.delta, (float*)a.dq, (int)a.S, nblk, (int)a.BH, (int)a.H, (int)(a.H / a.Hkv),
+                       a.scale * kLog2e, a.scale,
                        a.causal);
     return hipGetLastError();
 }
@@ -280,11 +294,14 @@ static hipError_t dq_f32(const LaunchArgs& a) {
 template <int D>
 static hipError_t dkdv_f32(const LaunchArgs& a) {
     int nblk;
-    const int total = f32_blocks<D>(a, &nblk);
-    if (total < 0) return hipErrorInvalidValue;
+    // one block per key block of each key/value head
+    const int64_t bhkv = a.BH / a.H * a.Hkv;
+    if (f32_blocks<D>(a, &nblk) < 0) return hipErrorInvalidValue;
+    const int total = nblk * (int)bhkv;
     hipLaunchKernelGGL((dkdv_f32_kernel<D>), dim3(total), dim3(256), 0, a.stream, (const float*)a.q,
                        (const float*)a.k, (const float*)a.v, (const float*)a.dout, a.lse_in, a.delta_in,
-                       (float*)a.dk, (float*)a.dv, (int)a.S, nblk, (int)a.BH, a.scale * kLog2e, a.scale, a.causal);
+                       (float*)a.dk, (float*)a.dv, (int)a.S, nblk, (int)bhkv, (int)a.H, (int)(a.H / a.Hkv),
+                       a.scale * kLog2e, a.scale, a.causal);
     return hipGetLastError();
 }
 

@@ -56,7 +56,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
                                                        const uint16_t* __restrict__ K,
                                                        const uint16_t* __restrict__ V,
                                                        uint16_t* __restrict__ O, float* __restrict__ LSE,
-                                                       int S, int nblk, int BH, float c, int causal) {
+                                                       int S, int nblk, int BH, int H, int GQ, float c,
+                                                       int causal) {
     using Cfg = FwdCfg<D, QB, NW>;
     constexpr int BM = Cfg::BM, BN = Cfg::BN, STR = Cfg::STR, TE = Cfg::TE;
     constexpr int KB = BN / 32;  // 32-key blocks per tile
@@ -67,9 +68,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
     const int qblk = nblk - 1 - wi.rank;  // most work first
     const int q0 = qblk * BM;
     const size_t base = (size_t)head * S * D;
+    const size_t kvbase = (size_t)kv_head_of(head, H, GQ) * S * D;
     const uint16_t* Qh = Q + base;
-    const uint16_t* Kh = K + base;
-    const uint16_t* Vh = V + base;
+    const uint16_t* Kh = K + kvbase;
+    const uint16_t* Vh = V + kvbase;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -314,7 +316,7 @@ static hipError_t launch_fwd(const LaunchArgs& a) {
     if (total > INT32_MAX) return hipErrorInvalidValue;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW>), dim3((unsigned)total), dim3(Cfg::NT), 0, a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                       (int)a.S, nblk, (int)a.BH, a.scale * kLog2e, a.causal);
+                       (int)a.S, nblk, (int)a.BH, (int)a.H, (int)(a.H / a.Hkv), a.scale * kLog2e, a.causal);
     return hipGetLastError();
 }
 

@@ -22,7 +22,11 @@ struct LaunchArgs {
     void* dq = nullptr;
     void* dk = nullptr;
     void* dv = nullptr;
-    int64_t BH = 0;  // batch * heads
+    float* dk_part = nullptr;  // grouped key/value heads: per-query-head fp32 dK, dV ([B,H,S,D])
+    float* dv_part = nullptr;
+    int64_t BH = 0;  // batch * query heads
+    int64_t H = 0;   // query heads per batch entry
+    int64_t Hkv = 0; // key/value heads per batch entry (H is a multiple of Hkv)
     int64_t S = 0;
     int64_t D = 0;
     float scale = 0.f;
@@ -35,6 +39,8 @@ hipError_t launch_bwd_dkdv_bf16(const LaunchArgs& a);
 hipError_t launch_bwd_dq_bf16(const LaunchArgs& a);
 // dQ pass that also forms delta from O and dO and writes it to a.delta
 hipError_t launch_bwd_dq_delta_bf16(const LaunchArgs& a);
+// dK, dV of each key/value head = sum of its query heads' fp32 partials (bf16 out)
+hipError_t launch_group_sum_bf16(const LaunchArgs& a);
 
 hipError_t launch_fwd_f32(const LaunchArgs& a);
 hipError_t launch_bwd_dkdv_f32(const LaunchArgs& a);

@@ -66,7 +66,8 @@ typedef enum attn_dtype {
 typedef enum attn_status {
     ATTN_OK = 0,
     ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
-    ATTN_ERR_SHAPE = 2,       /* a negative size, or sizes whose products overflow the limits */
+    ATTN_ERR_SHAPE = 2,       /* a negative size, sizes whose products overflow the limits, or a
+                                 key/value head count that does not divide the query heads */
     ATTN_ERR_UNSUPPORTED = 3, /* D, dtype, causal flag or scale outside the supported set */
     ATTN_ERR_ALIGNMENT = 4,   /* a device pointer not aligned to 16 bytes */
     ATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than attn_bwd_workspace_bytes() */
@@ -88,6 +89,21 @@ typedef enum attn_status {
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                      int64_t B, int64_t H, int64_t S, int64_t D,
                      float scale, int causal, attn_dtype dtype, void* stream);
+
+/*
+ * Forward pass with grouped key/value heads (GQA): H query heads per batch entry
+ * share H_kv key/value heads (H a multiple of H_kv, G = H / H_kv); query head h
+ * reads key/value head h / G.  Source: Forge RESEARCH.md §6, the "GQA" index map
+ * (kv_head = q_head / (n_heads / n_kv_heads), no repeated copies).
+ *   q, o    : device, [B,H,S,D] of dtype.
+ *   k, v    : device, [B,H_kv,S,D] of dtype, read only.
+ *   lse     : device, [B,H,S] fp32.
+ * attn_fwd is this call with H_kv = H.  Other rules as attn_fwd; H_kv < 1 or not
+ * dividing H -> ATTN_ERR_SHAPE.
+ */
+attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D,
+                         float scale, int causal, attn_dtype dtype, void* stream);
 
 /*
  * Bytes of device workspace attn_bwd needs: the fp32 delta vector, B*H*S*4 bytes.
@@ -113,6 +129,30 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      void* workspace, size_t workspace_bytes,
                      int64_t B, int64_t H, int64_t S, int64_t D,
                      float scale, int causal, attn_dtype dtype, void* stream);
+
+/*
+ * Backward pass with grouped key/value heads: dQ as attn_bwd; dK and dV of each
+ * key/value head are the sums over the G query heads that read it (the chain
+ * rule through the shared input).  bf16 with G > 1: the dK/dV pass runs per query
+ * head and leaves fp32 partials in the workspace, and a group-sum pass adds them
+ * (no atomics; deterministic).  q, o, dout, dq: [B,H,S,D]; k, v, dk, dv:
+ * [B,H_kv,S,D]; lse: [B,H,S]; workspace: attn_bwd_gqa_workspace_bytes() bytes.
+ * attn_bwd is this call with H_kv = H.  Source: Forge RESEARCH.md §6 ("GQA").
+ */
+/*
+ * Bytes of device workspace attn_bwd_gqa needs: B*H*S*4 (delta), plus, for bf16
+ * with H_kv < H, 2*B*H*S*D*4 (the per-query-head fp32 dK and dV), each region
+ * rounded up to 256 bytes.  Returns 0 for an empty or invalid problem.
+ */
+size_t attn_bwd_gqa_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D,
+                                    attn_dtype dtype);
+
+attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse,
+                         void* dq, void* dk, void* dv,
+                         void* workspace, size_t workspace_bytes,
+                         int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D,
+                         float scale, int causal, attn_dtype dtype, void* stream);
 
 /*
  * The backward's stages, exposed one by one (same argument rules as attn_bwd).

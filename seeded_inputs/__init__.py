@@ -7,7 +7,9 @@ bfloat16 rounding that turns a draw into a bf16 tensor.
 Draw recipe (one recipe for every workload):
 
 * one numpy ``PCG64(seed)`` generator per call;
-* float32 standard normals drawn in the order Q, K, V, dO, each of shape [B, H, S, D];
+* float32 standard normals drawn in the order Q, K, V, dO; Q and dO of shape
+  [B, H, S, D], K and V of shape [B, H_kv, S, D] (H_kv = H unless the workload
+  groups its key/value heads);
 * each draw multiplied by its standard deviation in float32;
 * for bf16 workloads, every value rounded to the nearest bfloat16, ties to even.
 
@@ -24,6 +26,7 @@ import numpy as np
 __all__ = [
     "Workload",
     "WORKLOADS",
+    "GQA_WORKLOADS",
     "make_inputs",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
@@ -45,6 +48,11 @@ class Workload:
     sigma_v: float = 1.0
     sigma_do: float = 1.0
     causal: bool = True
+    Hkv: int = 0  # key/value heads; 0 = H (one per query head)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv if self.Hkv else self.H
 
     @property
     def scale(self) -> float:
@@ -76,6 +84,14 @@ WORKLOADS = {
     "gpt125m_bf16": Workload("gpt125m_bf16", 8, 12, 1024, 64, "bf16", 1.0, 1.0, 0.1),
     "gpt205m_bf16": Workload("gpt205m_bf16", 4, 16, 2048, 64, "bf16", 1.0, 1.0, 0.1),
     "long8191_bf16": Workload("long8191_bf16", 1, 16, 8191, 128, "bf16", 4.0, 1.0, 0.1),
+}
+
+# Grouped key/value heads (GQA) at the shapes of common decoder models: the
+# headline workload with 4 query heads per key/value head, and a head_dim 128
+# model with 32 query and 8 key/value heads.  Same draw recipe and scales.
+GQA_WORKLOADS = {
+    "gqa4_gpt205m_bf16": Workload("gqa4_gpt205m_bf16", 4, 16, 2048, 64, "bf16", 1.0, 1.0, 0.1, Hkv=4),
+    "gqa8_d128_bf16": Workload("gqa8_d128_bf16", 1, 32, 4096, 128, "bf16", 1.0, 1.0, 0.1, Hkv=8),
 }
 
 
@@ -110,15 +126,16 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
 def make_inputs(w: Workload, seed: int = 0) -> dict:
     """Draw Q, K, V, dO for workload ``w`` from ``PCG64(seed)``.
 
-    Returns a dict with float32 arrays ``q, k, v, do`` of shape [B, H, S, D]
-    (bf16-exact for bf16 workloads) and, for bf16 workloads, their uint16 bit
-    patterns under ``q_bits, k_bits, v_bits, do_bits``.
+    Returns a dict with float32 arrays ``q, k, v, do`` (q and do [B, H, S, D], k and
+    v [B, H_kv, S, D]; bf16-exact for bf16 workloads) and, for bf16 workloads,
+    their uint16 bit patterns under ``q_bits, k_bits, v_bits, do_bits``.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
-    shape = (w.B, w.H, w.S, w.D)
+    qshape = (w.B, w.H, w.S, w.D)
+    kvshape = (w.B, w.kv_heads, w.S, w.D)
     out = {}
     for name, sigma in (("q", w.sigma_qk), ("k", w.sigma_qk), ("v", w.sigma_v), ("do", w.sigma_do)):
-        x = rng.standard_normal(size=shape, dtype=np.float32)
+        x = rng.standard_normal(size=kvshape if name in ("k", "v") else qshape, dtype=np.float32)
         x *= np.float32(sigma)
         if w.dtype == "bf16":
             bits = f32_to_bf16_bits(x)

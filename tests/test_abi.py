@@ -43,7 +43,8 @@ def lib():
 def test_header_declares_the_boundary():
     decls = _declared_functions()
     assert set(decls) == {"attn_fwd", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_preprocess",
-                          "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_delta", "attn_status_string"}
+                          "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_delta", "attn_status_string",
+                          "attn_fwd_gqa", "attn_bwd_gqa", "attn_bwd_gqa_workspace_bytes"}
     for name, nargs in decls.items():
         assert len(bd.SIGNATURES[name][1]) == nargs, name
 
@@ -170,3 +171,61 @@ def test_missing_library_fails_loudly(tmp_path):
             bd.load_library(str(tmp_path / "nope.so"))
     finally:
         bd._lib = saved
+
+
+# ------------------------------------------------------ grouped key/value heads
+
+
+def fwd_gqa(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=2, H=8, Hkv=2, S=100, D=64, scale=0.125, causal=1,
+             dtype=BF16)
+    a.update(kw)
+    return bd.c_attn_fwd_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["S"], a["D"],
+                             a["scale"], a["causal"], a["dtype"], 0)
+
+
+GQA_WS = 6400 + 2 * 409600  # delta 2*8*100*4 bytes, then fp32 dK and dV partials 2*8*100*64*4 bytes each
+
+
+def bwd_gqa(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], do=P[4], lse=P[5], dq=P[6], dk=P[7], dv=P[8], ws=P[9],
+             ws_bytes=GQA_WS, B=2, H=8, Hkv=2, S=100, D=64, scale=0.125, causal=1, dtype=BF16)
+    a.update(kw)
+    return bd.c_attn_bwd_gqa(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["ws"],
+                             a["ws_bytes"], a["B"], a["H"], a["Hkv"], a["S"], a["D"], a["scale"], a["causal"],
+                             a["dtype"], 0)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(Hkv=0), SHAPE), (dict(Hkv=3), SHAPE), (dict(Hkv=16), SHAPE), (dict(Hkv=-1), SHAPE),
+    (dict(k=0), NULL), (dict(D=96), UNSUP), (dict(scale=0.0), UNSUP),
+    # o overlapping the tail of k: K spans B*Hkv*S*D*2 = 51200 bytes (a call that
+    # passes validation would launch, so only overlaps are checked here)
+    (dict(o=P[1] + 51200 - 16), ALIAS), (dict(lse=P[2] + 51200 - 16), ALIAS),
+])
+def test_fwd_gqa_validation(lib, kw, expect):
+    assert fwd_gqa(**kw) == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(Hkv=0), SHAPE), (dict(Hkv=5), SHAPE), (dict(dk=0), NULL),
+    (dict(ws_bytes=GQA_WS - 1), WS), (dict(ws=0), WS), (dict(ws=P[4] + 16), ALIAS),
+    # dk overlapping dv: each spans B*Hkv*S*D*2 = 51200 bytes
+    (dict(dv=P[7] + 51200 - 16), ALIAS), (dict(dk=P[5]), ALIAS),
+])
+def test_bwd_gqa_validation(lib, kw, expect):
+    assert bwd_gqa(**kw) == expect
+
+
+def test_gqa_workspace_bytes(lib):
+    assert bd.c_attn_bwd_gqa_workspace_bytes(2, 8, 2, 100, 64, BF16) == GQA_WS
+    assert bd.c_attn_bwd_gqa_workspace_bytes(2, 8, 8, 100, 64, BF16) == 2 * 8 * 100 * 4  # one per query head
+    assert bd.c_attn_bwd_gqa_workspace_bytes(2, 8, 2, 100, 64, F32) == 2 * 8 * 100 * 4   # fp32 sums in-kernel
+    assert bd.c_attn_bwd_gqa_workspace_bytes(2, 8, 3, 100, 64, BF16) == 0                # 3 does not divide 8
+    assert bd.c_attn_bwd_gqa_workspace_bytes(0, 8, 2, 100, 64, BF16) == 0
+
+
+def test_gqa_empty_problems_are_ok(lib):
+    assert fwd_gqa(B=0, Hkv=0) == OK
+    assert bwd_gqa(S=0) == OK
+    assert fwd_gqa(B=0, Hkv=-1) == SHAPE
