@@ -37,7 +37,7 @@ int elem_bytes(attn_dtype dt) { return dt == ATTN_BF16 ? 2 : 4; }
 attn_status check_shape(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, bool* empty) {
     if (B < 0 || H < 0 || S < 0 || D < 0) return ATTN_ERR_SHAPE;
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    if (D != 64 && D != 80 && D != 96 && D != 128) return ATTN_ERR_UNSUPPORTED;
     *empty = (B == 0 || H == 0 || S == 0);
     if (*empty) return ATTN_OK;
     // B*H*S < 2^31 and S*D < 2^31, checked without overflow.
@@ -140,7 +140,7 @@ const char* attn_status_string(attn_status s) {
         case ATTN_ERR_SHAPE:
             return "negative size, sizes beyond B*H*S < 2^31 and S*D < 2^31, or H_kv < 1 or not dividing H";
         case ATTN_ERR_UNSUPPORTED:
-            return "unsupported: D must be 64 or 128, dtype ATTN_F32 or ATTN_BF16, causal 0 or 1, scale finite and > 0";
+            return "unsupported: D must be 64, 80, 96 or 128, dtype ATTN_F32 or ATTN_BF16, causal 0 or 1, scale finite and > 0";
         case ATTN_ERR_ALIGNMENT: return "a device pointer is not 16-byte aligned";
         case ATTN_ERR_WORKSPACE: return "workspace is NULL or smaller than attn_bwd_workspace_bytes()";
         case ATTN_ERR_HIP: return "the HIP runtime reported an error at launch";

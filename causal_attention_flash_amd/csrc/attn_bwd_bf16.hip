@@ -43,7 +43,10 @@ struct DkdvCfg {
     static constexpr int QE = QT::ELEMS;
     static constexpr int BUF_ELEMS = 2 * QE;   // Q, dO
     static constexpr int BUF_STATS = 2 * BMQ;  // -LSE/scale, -delta (fp32)
-    static constexpr int WAVES_PER_SIMD = D == 64 ? 2 : 1;  // register budget: 256 VGPRs at D = 64
+    // register budget: 256 VGPRs (two waves per SIMD) up to D = 96
+    static constexpr int WAVES_PER_SIMD = D <= 96 ? 2 : 1;
+    static constexpr int KS = HeadDim<D>::KSTEPS;
+    static constexpr int DB = HeadDim<D>::DB;
 };
 
 // One workgroup per (query head, key block): the query head's Q/dO/LSE/delta
@@ -61,7 +64,9 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
     using Cfg = DkdvCfg<D, BMQ, NW>;
     constexpr int NT = Cfg::NT, BNK = Cfg::BNK;
     constexpr int STR = Cfg::STR;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Cfg::BUF_ELEMS];
+    constexpr int KS = Cfg::KS, DB = Cfg::DB;
+    // [Q, dO][2]; both are read transposed, so the last carries the slack
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Cfg::BUF_ELEMS + Cfg::QT::TR_SLACK];
     __shared__ __attribute__((aligned(16))) float sstat[2 * Cfg::BUF_STATS];
 
     const WorkItem wi = heavy_first(blockIdx.x, BH);
@@ -82,9 +87,9 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
     const int key = kw0 + n;  // the key this lane's C columns belong to
 
     // K and V as B operands (keys on the lanes), d = 16ks+8h..+7.
-    bf16x8 kf[D / 16], vf[D / 16];
+    bf16x8 kf[KS], vf[KS];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
         u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
         if (key < S) {
             a = ldg16(K + kvbase + (size_t)key * D + ks * 16 + 8 * h);
@@ -94,9 +99,9 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
         vf[ks] = as_bf16x8(b);
     }
 
-    f32x16 dkacc[D / 32], dvacc[D / 32];
+    f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             dkacc[db][r] = 0.f;
@@ -164,7 +169,7 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
             }
             // 32 queries x this wave's 32 keys: S - LSE/scale and dP - delta
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
+            for (int ks = 0; ks < KS; ++ks) {
                 const int off = (qb * 32 + n) * STR + ks * 16 + 8 * h;
                 sacc = mfma32(as_bf16x8(lds16(Qs + off)), kf[ks], sacc);
                 pacc = mfma32(as_bf16x8(lds16(dOs + off)), vf[ks], pacc);
@@ -184,7 +189,7 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
                 const bf16x8 pb = pack_operand(sacc, c2);
                 const bf16x8 sb = pack_operand(pacc, c2);
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
+                for (int db = 0; db < DB; ++db) {
                     const int r0 = (qb * 2 + c2) * 16;
                     dvacc[db] = mfma32(lds_tr_operand<STR>(dOs, r0, db * 32, lane), pb, dvacc[db]);
                     dkacc[db] = mfma32(lds_tr_operand<STR>(Qs, r0, db * 32, lane), sb, dkacc[db]);
@@ -214,9 +219,10 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
         float* dKr = dKp + base + (size_t)key * D;
         float* dVr = dVp + base + (size_t)key * D;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
+                if (!HeadDim<D>::live(db, g)) continue;
                 const int d = db * 32 + 8 * g + 4 * h;
                 f32x4 fk, fv;
 #pragma unroll
@@ -232,9 +238,10 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
         uint16_t* dKr = dK + kvbase + (size_t)key * D;
         uint16_t* dVr = dV + kvbase + (size_t)key * D;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
+                if (!HeadDim<D>::live(db, g)) continue;
                 const int d = db * 32 + 8 * g + 4 * h;
                 u32x2 uk, uv;
                 uk[0] = pack_bf16x2(dkacc[db][4 * g + 0] * scale, dkacc[db][4 * g + 1] * scale);
@@ -270,6 +277,8 @@ static hipError_t launch_dkdv(const LaunchArgs& a) {
 
 hipError_t launch_bwd_dkdv_bf16(const LaunchArgs& a) {
     if (a.D == 64) return launch_dkdv<64, 64, 8>(a);
+    if (a.D == 80) return launch_dkdv<80, 64, 8>(a);
+    if (a.D == 96) return launch_dkdv<96, 64, 8>(a);
     if (a.D == 128) return launch_dkdv<128, 32, 4>(a);
     return hipErrorInvalidValue;
 }
@@ -331,8 +340,11 @@ struct DqCfg {
     static constexpr int STR = KT::STR;
     static constexpr int KE = KT::ELEMS;
     static constexpr int BUF_ELEMS = 2 * KE;  // K, V
-    // register budget: 168 VGPRs (3 waves per SIMD) fits D = 64 without spills
-    static constexpr int WAVES_PER_SIMD = D == 64 ? 3 : 1;
+    // register budget: 168 VGPRs (3 waves per SIMD) fits D = 64 without spills,
+    // 256 (two) fits D = 80 and 96
+    static constexpr int WAVES_PER_SIMD = D == 64 ? 3 : (D <= 96 ? 2 : 1);
+    static constexpr int KS = HeadDim<D>::KSTEPS;
+    static constexpr int DB = HeadDim<D>::DB;
 };
 
 // DELTA_FROM_O: delta = rowsum(dO o O) is formed here, from the O rows of this
@@ -347,7 +359,10 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
     using Cfg = DqCfg<D, BNK, NW>;
     constexpr int BMQ = Cfg::BMQ;
     constexpr int STR = Cfg::STR;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Cfg::BUF_ELEMS];
+    constexpr int KS = Cfg::KS, DB = Cfg::DB;
+    // [K, V][2]; K is read transposed (a V tile follows each K tile; the slack
+    // keeps the layout rule uniform)
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Cfg::BUF_ELEMS + Cfg::KT::TR_SLACK];
 
     const WorkItem wi = heavy_first(blockIdx.x, BH);
     const int head = wi.head;
@@ -364,9 +379,9 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
     const int qw0 = q0 + wave * 32;
     const int q = qw0 + n;  // the query this lane's C columns belong to
 
-    bf16x8 qf[D / 16], of[D / 16];
+    bf16x8 qf[KS], of[KS];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
         u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
         if (q < S) {
             a = ldg16(Q + base + (size_t)q * D + ks * 16 + 8 * h);
@@ -382,7 +397,7 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
         // lane l ^ 32 holds the other half
         float part = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
             u32x4 u = {0u, 0u, 0u, 0u};
             if (q < S) u = ldg16(O + base + (size_t)q * D + ks * 16 + 8 * h);
             part = dot_bf16x8(of[ks], as_bf16x8(u), part);
@@ -393,9 +408,9 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
         dl = q < S ? Delta[(size_t)head * S + q] : 0.f;
     }
 
-    f32x16 dqacc[D / 32];
+    f32x16 dqacc[DB];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
 
@@ -435,7 +450,7 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
                 pacc[r] = 0.f;
             }
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
+            for (int ks = 0; ks < KS; ++ks) {
                 const int off = (kb * 32 + n) * STR + ks * 16 + 8 * h;
                 sacc = mfma32(as_bf16x8(lds16(Ks + off)), qf[ks], sacc);
                 pacc = mfma32(as_bf16x8(lds16(Vs + off)), of[ks], pacc);
@@ -455,7 +470,7 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
             for (int c2 = 0; c2 < 2; ++c2) {
                 const bf16x8 sb = pack_operand(pacc, c2);
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db)
+                for (int db = 0; db < DB; ++db)
                     dqacc[db] = mfma32(lds_tr_operand<STR>(Ks, (kb * 2 + c2) * 16, db * 32, lane), sb, dqacc[db]);
             }
         }
@@ -480,9 +495,10 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
     if (q < S) {
         uint16_t* dQr = dQ + base + (size_t)q * D;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
+                if (!HeadDim<D>::live(db, g)) continue;
                 u32x2 u;
                 u[0] = pack_bf16x2(dqacc[db][4 * g + 0] * scale, dqacc[db][4 * g + 1] * scale);
                 u[1] = pack_bf16x2(dqacc[db][4 * g + 2] * scale, dqacc[db][4 * g + 3] * scale);
@@ -507,12 +523,16 @@ static hipError_t launch_dq(const LaunchArgs& a) {
 
 hipError_t launch_bwd_dq_bf16(const LaunchArgs& a) {
     if (a.D == 64) return launch_dq<64, 64, 4, false>(a);
+    if (a.D == 80) return launch_dq<80, 64, 4, false>(a);
+    if (a.D == 96) return launch_dq<96, 64, 4, false>(a);
     if (a.D == 128) return launch_dq<128, 32, 4, false>(a);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_dq_delta_bf16(const LaunchArgs& a) {
     if (a.D == 64) return launch_dq<64, 64, 4, true>(a);
+    if (a.D == 80) return launch_dq<80, 64, 4, true>(a);
+    if (a.D == 96) return launch_dq<96, 64, 4, true>(a);
     if (a.D == 128) return launch_dq<128, 32, 4, true>(a);
     return hipErrorInvalidValue;
 }

@@ -50,6 +50,21 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 // Row of the 32x32 C tile held by register r of a lane in half h.
 __device__ __forceinline__ int crow(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
+// Head dimensions.  Contractions over d run in 16-deep MFMA steps (D / 16 of
+// them, D a multiple of 16); outputs over d are built in 32-wide C tiles, so D =
+// 80 uses three tiles of which the last has 16 live columns.  The dead columns
+// are computed from whatever the operand reads return and never stored: in an
+// MFMA, output row i depends on row i of A alone.
+template <int D>
+struct HeadDim {
+    static_assert(D % 16 == 0 && D >= 32, "head dimension");
+    static constexpr int KSTEPS = D / 16;        // 16-deep contraction steps over d
+    static constexpr int DB = (D + 31) / 32;     // 32-wide output tiles over d
+    // C registers 4g .. 4g+3 of output tile db hold d = 32 db + 8 g + 4 h + 0..3;
+    // the whole group of 8 (both halves) is live or dead together.
+    static constexpr bool live(int db, int g) { return db * 32 + 8 * g < D; }
+};
+
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;

@@ -2,10 +2,10 @@
 //
 // Same method as the bf16 MFMA path (Forge RESEARCH.md §6: online softmax with a
 // saved LSE; atomic-free backward recomputing P from the LSE; delta from the
-// preprocess), laid out for exact fp32 products instead of matrix cores: G = D/32
-// lanes share one row (a query, or a key for the dK/dV pass), each lane holding 32
-// consecutive columns, and dot products are finished with cross-lane xors inside
-// the G-lane group.  The streamed rows are staged in LDS, where all groups read
+// preprocess), laid out for exact fp32 products instead of matrix cores: G lanes
+// share one row (a query, or a key for the dK/dV pass), each lane holding E = D/G
+// consecutive columns (G = 2 at D = 64, else 4), and dot products are finished
+// with cross-lane xors inside the G-lane group.  The streamed rows are staged in LDS, where all groups read
 // the same row (a broadcast).  This path serves fp32 callers and small problems;
 // the bf16 kernels carry the throughput.
 #include "attn_launch.h"
@@ -14,6 +14,15 @@
 namespace attn {
 
 constexpr int kF32Tile = 32;  // streamed rows per LDS tile
+
+// Row split: G lanes per row, E columns per lane, R rows per 256-thread block.
+template <int D>
+struct F32Split {
+    static constexpr int G = D <= 64 ? 2 : 4;
+    static constexpr int E = D / G;
+    static constexpr int R = 256 / G;
+    static_assert(D % G == 0 && E % 4 == 0, "head dimension");
+};
 
 template <int G>
 __device__ __forceinline__ float group_sum(float x) {
@@ -43,7 +52,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
                                                       float* __restrict__ LSE, int S, int nblk, int BH, int H, int GQ,
                                                       float c,
                                                       int causal) {
-    constexpr int G = D / 32, R = 256 / G;
+    constexpr int G = F32Split<D>::G, R = F32Split<D>::R, E = F32Split<D>::E;
     __shared__ __attribute__((aligned(16))) float Ks[kF32Tile * D];
     __shared__ __attribute__((aligned(16))) float Vs[kF32Tile * D];
     const WorkItem wi = heavy_first(blockIdx.x, BH);
@@ -56,10 +65,10 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
     const int part = tid % G;
     const int q = q0 + tid / G;
 
-    float qv[32], ov[32];
+    float qv[E], ov[E];
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-        qv[e] = q < S ? Q[base + (size_t)q * D + part * 32 + e] : 0.f;
+    for (int e = 0; e < E; ++e) {
+        qv[e] = q < S ? Q[base + (size_t)q * D + part * E + e] : 0.f;
         ov[e] = 0.f;
     }
     float m = -FLT_MAX, l = 0.f;
@@ -75,7 +84,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
         for (int j = 0; j < kF32Tile; ++j) {
             float d = 0.f;
 #pragma unroll
-            for (int e = 0; e < 32; ++e) d = fmaf(qv[e], Ks[j * D + part * 32 + e], d);
+            for (int e = 0; e < E; ++e) d = fmaf(qv[e], Ks[j * D + part * E + e], d);
             d = group_sum<G>(d);
             const int key = k0 + j;
             const bool vis = key < S && (!causal || key <= q);
@@ -89,19 +98,19 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
         m = mn;
         l *= f;
 #pragma unroll
-        for (int e = 0; e < 32; ++e) ov[e] *= f;
+        for (int e = 0; e < E; ++e) ov[e] *= f;
 #pragma unroll
         for (int j = 0; j < kF32Tile; ++j) {
             const float p = exp2f((sv[j] - m) * c);
             l += p;
 #pragma unroll
-            for (int e = 0; e < 32; ++e) ov[e] = fmaf(p, Vs[j * D + part * 32 + e], ov[e]);
+            for (int e = 0; e < E; ++e) ov[e] = fmaf(p, Vs[j * D + part * E + e], ov[e]);
         }
     }
     if (q < S) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-        for (int e = 0; e < 32; ++e) O[base + (size_t)q * D + part * 32 + e] = ov[e] * inv;
+        for (int e = 0; e < E; ++e) O[base + (size_t)q * D + part * E + e] = ov[e] * inv;
         if (part == 0) LSE[(size_t)head * S + q] = l > 0.f ? (m * c + log2f(l)) * kLn2 : -INFINITY;
     }
 }
@@ -116,7 +125,7 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(const float* __restrict__ Q
                                                      float* __restrict__ dQ, int S, int nblk, int BH, int H, int GQ,
                                                      float c,
                                                      float scale, int causal) {
-    constexpr int G = D / 32, R = 256 / G;
+    constexpr int G = F32Split<D>::G, R = F32Split<D>::R, E = F32Split<D>::E;
     __shared__ __attribute__((aligned(16))) float Ks[kF32Tile * D];
     __shared__ __attribute__((aligned(16))) float Vs[kF32Tile * D];
     const WorkItem wi = heavy_first(blockIdx.x, BH);
@@ -129,10 +138,10 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(const float* __restrict__ Q
     const int part = tid % G;
     const int q = q0 + tid / G;
 
-    float qv[32], dov[32], acc[32];
+    float qv[E], dov[E], acc[E];
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-        const size_t off = base + (size_t)q * D + part * 32 + e;
+    for (int e = 0; e < E; ++e) {
+        const size_t off = base + (size_t)q * D + part * E + e;
         qv[e] = q < S ? Q[off] : 0.f;
         dov[e] = q < S ? dO[off] : 0.f;
         acc[e] = 0.f;
@@ -142,8 +151,8 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(const float* __restrict__ Q
     if constexpr (DELTA_FROM_O) {
         float dsum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 32; ++e)
-            dsum = fmaf(dov[e], q < S ? O[base + (size_t)q * D + part * 32 + e] : 0.f, dsum);
+        for (int e = 0; e < E; ++e)
+            dsum = fmaf(dov[e], q < S ? O[base + (size_t)q * D + part * E + e] : 0.f, dsum);
         dl = group_sum<G>(dsum);
         if (part == 0 && q < S) DeltaOut[(size_t)head * S + q] = dl;
     } else {
@@ -159,9 +168,9 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(const float* __restrict__ Q
         for (int j = 0; j < kF32Tile; ++j) {
             float s = 0.f, dp = 0.f;
 #pragma unroll
-            for (int e = 0; e < 32; ++e) {
-                s = fmaf(qv[e], Ks[j * D + part * 32 + e], s);
-                dp = fmaf(dov[e], Vs[j * D + part * 32 + e], dp);
+            for (int e = 0; e < E; ++e) {
+                s = fmaf(qv[e], Ks[j * D + part * E + e], s);
+                dp = fmaf(dov[e], Vs[j * D + part * E + e], dp);
             }
             s = group_sum<G>(s);
             dp = group_sum<G>(dp);
@@ -170,12 +179,12 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(const float* __restrict__ Q
             const float p = vis ? exp2f(fmaf(s, c, -l2)) : 0.f;
             const float ds = p * (dp - dl);
 #pragma unroll
-            for (int e = 0; e < 32; ++e) acc[e] = fmaf(ds, Ks[j * D + part * 32 + e], acc[e]);
+            for (int e = 0; e < E; ++e) acc[e] = fmaf(ds, Ks[j * D + part * E + e], acc[e]);
         }
     }
     if (q < S) {
 #pragma unroll
-        for (int e = 0; e < 32; ++e) dQ[base + (size_t)q * D + part * 32 + e] = acc[e] * scale;
+        for (int e = 0; e < E; ++e) dQ[base + (size_t)q * D + part * E + e] = acc[e] * scale;
     }
 }
 
@@ -187,7 +196,7 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(const float* __restrict__
                                                        float* __restrict__ dV, int S, int nblk, int BH, int H, int GQ,
                                                        float c,
                                                        float scale, int causal) {
-    constexpr int G = D / 32, R = 256 / G;
+    constexpr int G = F32Split<D>::G, R = F32Split<D>::R, E = F32Split<D>::E;
     __shared__ __attribute__((aligned(16))) float Qs[kF32Tile * D];
     __shared__ __attribute__((aligned(16))) float Os[kF32Tile * D];
     __shared__ float L2s[kF32Tile], DLs[kF32Tile];
@@ -200,10 +209,10 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(const float* __restrict__
     const int part = tid % G;
     const int key = n0 + tid / G;
 
-    float kv[32], vv[32], dk[32], dv[32];
+    float kv[E], vv[E], dk[E], dv[E];
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-        const size_t off = base + (size_t)key * D + part * 32 + e;
+    for (int e = 0; e < E; ++e) {
+        const size_t off = base + (size_t)key * D + part * E + e;
         kv[e] = key < S ? K[off] : 0.f;
         vv[e] = key < S ? V[off] : 0.f;
         dk[e] = 0.f;
@@ -231,9 +240,9 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(const float* __restrict__
         for (int j = 0; j < kF32Tile; ++j) {
             float s = 0.f, dp = 0.f;
 #pragma unroll
-            for (int e = 0; e < 32; ++e) {
-                s = fmaf(kv[e], Qs[j * D + part * 32 + e], s);
-                dp = fmaf(vv[e], Os[j * D + part * 32 + e], dp);
+            for (int e = 0; e < E; ++e) {
+                s = fmaf(kv[e], Qs[j * D + part * E + e], s);
+                dp = fmaf(vv[e], Os[j * D + part * E + e], dp);
             }
             s = group_sum<G>(s);
             dp = group_sum<G>(dp);
@@ -242,16 +251,16 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(const float* __restrict__
             const float p = vis ? exp2f(fmaf(s, c, -L2s[j])) : 0.f;
             const float ds = p * (dp - DLs[j]);
 #pragma unroll
-            for (int e = 0; e < 32; ++e) {
-                dv[e] = fmaf(p, Os[j * D + part * 32 + e], dv[e]);
-                dk[e] = fmaf(ds, Qs[j * D + part * 32 + e], dk[e]);
+            for (int e = 0; e < E; ++e) {
+                dv[e] = fmaf(p, Os[j * D + part * E + e], dv[e]);
+                dk[e] = fmaf(ds, Qs[j * D + part * E + e], dk[e]);
             }
         }
     }
     if (key < S) {
 #pragma unroll
-        for (int e = 0; e < 32; ++e) {
-            const size_t off = base + (size_t)key * D + part * 32 + e;
+        for (int e = 0; e < E; ++e) {
+            const size_t off = base + (size_t)key * D + part * E + e;
             dK[off] = dk[e] * scale;
             dV[off] = dv[e];
         }
@@ -260,7 +269,7 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(const float* __restrict__
 
 template <int D>
 static int f32_blocks(const LaunchArgs& a, int* nblk) {
-    constexpr int R = 256 / (D / 32);
+    constexpr int R = F32Split<D>::R;
     *nblk = (int)((a.S + R - 1) / R);
     const int64_t total = (int64_t)(*nblk) * a.BH;
     return total > INT32_MAX ? -1 : (int)total;
@@ -307,22 +316,30 @@ static hipError_t dkdv_f32(const LaunchArgs& a) {
 
 hipError_t launch_fwd_f32(const LaunchArgs& a) {
     if (a.D == 64) return fwd_f32<64>(a);
+    if (a.D == 80) return fwd_f32<80>(a);
+    if (a.D == 96) return fwd_f32<96>(a);
     if (a.D == 128) return fwd_f32<128>(a);
     return hipErrorInvalidValue;
 }
 hipError_t launch_bwd_dq_f32(const LaunchArgs& a) {
     if (a.D == 64) return dq_f32<64, false>(a);
+    if (a.D == 80) return dq_f32<80, false>(a);
+    if (a.D == 96) return dq_f32<96, false>(a);
     if (a.D == 128) return dq_f32<128, false>(a);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_dq_delta_f32(const LaunchArgs& a) {
     if (a.D == 64) return dq_f32<64, true>(a);
+    if (a.D == 80) return dq_f32<80, true>(a);
+    if (a.D == 96) return dq_f32<96, true>(a);
     if (a.D == 128) return dq_f32<128, true>(a);
     return hipErrorInvalidValue;
 }
 hipError_t launch_bwd_dkdv_f32(const LaunchArgs& a) {
     if (a.D == 64) return dkdv_f32<64>(a);
+    if (a.D == 80) return dkdv_f32<80>(a);
+    if (a.D == 96) return dkdv_f32<96>(a);
     if (a.D == 128) return dkdv_f32<128>(a);
     return hipErrorInvalidValue;
 }

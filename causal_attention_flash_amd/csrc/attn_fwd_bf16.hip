@@ -49,6 +49,8 @@ struct FwdCfg {
     using Tile = RowTile<BN, D, NT>;
     static constexpr int STR = Tile::STR;
     static constexpr int TE = Tile::ELEMS;   // one K or V tile in LDS (elements)
+    static constexpr int KS = HeadDim<D>::KSTEPS;
+    static constexpr int DB = HeadDim<D>::DB;
 };
 
 template <int D, int QB, int NW>
@@ -61,7 +63,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
     using Cfg = FwdCfg<D, QB, NW>;
     constexpr int BM = Cfg::BM, BN = Cfg::BN, STR = Cfg::STR, TE = Cfg::TE;
     constexpr int KB = BN / 32;  // 32-key blocks per tile
-    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TE];  // K[2], V[2]
+    constexpr int KS = Cfg::KS, DB = Cfg::DB;
+    // K[2], V[2]; V is read transposed, so the last buffer carries the slack
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TE + Cfg::Tile::TR_SLACK];
 
     const WorkItem wi = heavy_first(blockIdx.x, BH);
     const int head = wi.head;
@@ -87,45 +91,45 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
     auto vbuf = [&](int t) { return smem + (2 + (t & 1)) * TE; };
 
     // Q as the B operand of S^T = K Q^T: lane holds query qw0+32qb+n, d = 16ks+8h..+7.
-    bf16x8 qf[QB][D / 16];
+    bf16x8 qf[QB][KS];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int q = qw0 + qb * 32 + n;
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
             u32x4 u = {0u, 0u, 0u, 0u};
             if (q < S) u = ldg16(Qh + (size_t)q * D + ks * 16 + 8 * h);
             qf[qb][ks] = as_bf16x8(u);
         }
     }
 
-    f32x16 oacc[QB][D / 32];
+    f32x16 oacc[QB][DB];
     float m[QB], l[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         m[qb] = -FLT_MAX;
         l[qb] = 0.f;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
     }
 
     // K rows of tile t as A operands of S^T = K Q^T:
     // kf[kb][ks] = K[t*BN + 32kb + n][16ks + 8h .. +7].
-    auto load_k = [&](bf16x8 (&kf)[KB][D / 16], int t) {
+    auto load_k = [&](bf16x8 (&kf)[KB][KS], int t) {
         const uint16_t* Ks = kbuf(t);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks)
+            for (int ks = 0; ks < KS; ++ks)
                 kf[kb][ks] = as_bf16x8(lds16(Ks + (kb * 32 + n) * STR + ks * 16 + 8 * h));
     };
     // S^T tile from K operands already in registers; the first contraction step
     // starts from a zero accumulator.
-    auto mma_scores = [&](f32x16 (&sacc)[QB][KB], const bf16x8 (&kf)[KB][D / 16]) {
+    auto mma_scores = [&](f32x16 (&sacc)[QB][KB], const bf16x8 (&kf)[KB][KS]) {
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -142,7 +146,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
     auto step = [&](auto mask_tag, auto next_tag, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB], int t) {
         constexpr bool MASK = decltype(mask_tag)::value;
         constexpr bool NEXT = decltype(next_tag)::value;
-        bf16x8 kf[KB][D / 16];
+        bf16x8 kf[KB][KS];
         if constexpr (NEXT) load_k(kf, t + 1);
 
         // ---- mask, row max (raw scores; c > 0 so max commutes with scaling)
@@ -200,11 +204,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
         }
         // V^T operands, read transposed from the row-major V tile
         const uint16_t* Vs = vbuf(t);
-        bf16x8 vf[BN / 16][D / 32];
+        bf16x8 vf[BN / 16][DB];
 #pragma unroll
         for (int ks = 0; ks < BN / 16; ++ks)
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) vf[ks][db] = lds_tr_operand<STR>(Vs, ks * 16, db * 32, lane);
+            for (int db = 0; db < DB; ++db) vf[ks][db] = lds_tr_operand<STR>(Vs, ks * 16, db * 32, lane);
 
         if (resc) {
             // rare (the reference point moves only past the slack): keep it a
@@ -216,7 +220,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
                 const float f = fast_exp2(m[qb] - mn[qb]);
                 l[qb] *= f;
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db)
+                for (int db = 0; db < DB; ++db)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= f;
             }
@@ -230,7 +234,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
 #pragma unroll
         for (int ks = 0; ks < BN / 16; ++ks)
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32(vf[ks][db], pf[qb][ks], oacc[qb][db]);
     };
@@ -256,7 +260,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
 
     f32x16 sa[QB][KB], sb[QB][KB];
     if (nw > 0) {
-        bf16x8 kf[KB][D / 16];
+        bf16x8 kf[KB][KS];
         load_k(kf, 0);
         mma_scores(sa, kf);
     }
@@ -295,9 +299,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         if (q < S) {
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
+                    if (!HeadDim<D>::live(db, g)) continue;
                     u32x2 u;
                     u[0] = pack_bf16x2(oacc[qb][db][4 * g + 0] * inv, oacc[qb][db][4 * g + 1] * inv);
                     u[1] = pack_bf16x2(oacc[qb][db][4 * g + 2] * inv, oacc[qb][db][4 * g + 3] * inv);
@@ -322,6 +327,8 @@ static hipError_t launch_fwd(const LaunchArgs& a) {
 
 hipError_t launch_fwd_bf16(const LaunchArgs& a) {
     if (a.D == 64) return launch_fwd<64, 1, 4>(a);
+    if (a.D == 80) return launch_fwd<80, 1, 4>(a);
+    if (a.D == 96) return launch_fwd<96, 1, 4>(a);
     if (a.D == 128) return launch_fwd<128, 1, 4>(a);
     return hipErrorInvalidValue;
 }

@@ -5,23 +5,28 @@
 // instead of per (query, key) pair (the hoist the page measures at 3.1x on a
 // training step).  O here is the forward output as stored (bf16 or fp32).
 //
-// Memory-bound: each lane reads 16 bytes of O and of dO per row slice; the
-// D*elem/16 lanes of a row reduce their partial dots with cross-lane xors.
+// Memory-bound: each lane reads 16 bytes of O and of dO per row slice.  A row
+// gets G lanes, the power of two at or above its D*elem/16 slices (lanes past
+// the last slice contribute zero), which reduce their partial dots with
+// cross-lane xors.
 #include "attn_launch.h"
 #include "attn_device.h"
 
 namespace attn {
 
+constexpr int pow2_at_least(int x) { return x <= 1 ? 1 : 2 * pow2_at_least((x + 1) / 2); }
+
 template <int ELEM_BYTES, int D>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const void* __restrict__ O, const void* __restrict__ dO,
                                                              float* __restrict__ delta, int64_t rows) {
-    constexpr int G = D * ELEM_BYTES / 16;  // lanes per row (4 .. 32)
-    constexpr int RPB = 256 / G;            // rows per block
+    constexpr int SL = D * ELEM_BYTES / 16;  // 16-byte slices per row (8 .. 32)
+    constexpr int G = pow2_at_least(SL);     // lanes per row
+    constexpr int RPB = 256 / G;             // rows per block
     const int tid = threadIdx.x;
     const int64_t row = (int64_t)blockIdx.x * RPB + tid / G;
     const int part = tid % G;
     float acc = 0.f;
-    if (row < rows) {
+    if (row < rows && part < SL) {
         const size_t off = (size_t)row * D * ELEM_BYTES + (size_t)part * 16;
         const u32x4 a = ldg16((const char*)O + off);
         const u32x4 b = ldg16((const char*)dO + off);
@@ -43,8 +48,7 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const void* __restr
 
 template <int ELEM_BYTES, int D>
 static hipError_t launch_pre(const LaunchArgs& a) {
-    constexpr int G = D * ELEM_BYTES / 16;
-    constexpr int RPB = 256 / G;
+    constexpr int RPB = 256 / pow2_at_least(D * ELEM_BYTES / 16);
     const int64_t rows = a.BH * a.S;
     const int64_t blocks = (rows + RPB - 1) / RPB;
     if (blocks > INT32_MAX) return hipErrorInvalidValue;
@@ -55,8 +59,12 @@ static hipError_t launch_pre(const LaunchArgs& a) {
 
 hipError_t launch_bwd_preprocess(const LaunchArgs& a, int elem_bytes) {
     if (elem_bytes == 2 && a.D == 64) return launch_pre<2, 64>(a);
+    if (elem_bytes == 2 && a.D == 80) return launch_pre<2, 80>(a);
+    if (elem_bytes == 2 && a.D == 96) return launch_pre<2, 96>(a);
     if (elem_bytes == 2 && a.D == 128) return launch_pre<2, 128>(a);
     if (elem_bytes == 4 && a.D == 64) return launch_pre<4, 64>(a);
+    if (elem_bytes == 4 && a.D == 80) return launch_pre<4, 80>(a);
+    if (elem_bytes == 4 && a.D == 96) return launch_pre<4, 96>(a);
     if (elem_bytes == 4 && a.D == 128) return launch_pre<4, 128>(a);
     return hipErrorInvalidValue;
 }

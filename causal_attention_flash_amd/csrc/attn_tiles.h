@@ -33,7 +33,12 @@ struct RowTile {
     static constexpr int CPR = D / 8;          // 16-byte chunks per row
     static constexpr int CHUNKS = ROWS * CPR;
     static constexpr int PT = (CHUNKS + NT - 1) / NT;
-    static_assert(ROWS % 32 == 0 && D % 32 == 0, "tile shape");
+    // Transposing reads cover whole 32-column output tiles (HeadDim::DB of
+    // them), so when 32*DB > STR the last row's read runs past the tile by the
+    // difference; a buffer holding tiles reserves this many elements after its
+    // last tile.
+    static constexpr int TR_SLACK = HeadDim<D>::DB * 32 > STR ? HeadDim<D>::DB * 32 - STR : 0;
+    static_assert(ROWS % 32 == 0 && D % 16 == 0, "tile shape");
 
     u32x4 r[PT];
 

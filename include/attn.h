@@ -34,8 +34,10 @@
  * softmax statistics are fp32 whatever the input type.  Outputs are written in
  * the input type, rounded to nearest even.
  *
- * Supported set: D in {64, 128}; dtype in {ATTN_F32, ATTN_BF16}; causal in {0, 1};
- * finite scale; any S >= 1 (no tile-multiple requirement); B*H*S*D < 2^62 and
+ * Supported set: D in {64, 80, 96, 128} (the head dimensions of GPT-style
+ * models; Forge RESEARCH.md §6 "Fused attention design" lists 64, 80 and 128 as
+ * the tuned set and its pitfalls section compares backward variants up to
+ * D = 96); dtype in {ATTN_F32, ATTN_BF16}; causal in {0, 1}; finite scale; any S >= 1 (no tile-multiple requirement); B*H*S*D < 2^62 and
  * S*D < 2^31.  B, H or S equal to 0 is an empty problem: ATTN_OK, nothing
  * enqueued, pointers not read.
  *

@@ -85,7 +85,7 @@ def bwd(**kw):
     (dict(S=-1), SHAPE), (dict(B=-2), SHAPE), (dict(H=-1), SHAPE),
     (dict(B=1 << 20, H=1 << 11, S=1), SHAPE),          # B*H*S = 2^31
     (dict(B=1, H=1, S=1 << 25, D=64), SHAPE),           # S*D = 2^31
-    (dict(D=96), UNSUP), (dict(D=32), UNSUP), (dict(D=256), UNSUP),
+    (dict(D=112), UNSUP), (dict(D=48), UNSUP), (dict(D=32), UNSUP), (dict(D=256), UNSUP),
     (dict(dtype=2), UNSUP), (dict(dtype=-1), UNSUP),
     (dict(causal=2), UNSUP), (dict(causal=-1), UNSUP),
     (dict(scale=0.0), UNSUP), (dict(scale=-0.5), UNSUP), (dict(scale=float("nan")), UNSUP),
@@ -103,7 +103,7 @@ def test_fwd_empty_problem_is_ok_without_pointers(lib, kw):
 
 
 def test_fwd_empty_still_checks_the_supported_set(lib):
-    assert fwd(B=0, D=96) == UNSUP
+    assert fwd(B=0, D=112) == UNSUP
     assert fwd(B=0, dtype=7) == UNSUP
     assert fwd(B=0, S=-1) == SHAPE
 
@@ -120,7 +120,7 @@ def test_fwd_adjacent_buffers_do_not_alias(lib):
     (dict(ws=P[9] + 4), ALIGN),
     (dict(ws=P[0]), ALIAS), (dict(dq=P[1]), ALIAS), (dict(dk=P[6]), ALIAS), (dict(dv=P[5]), ALIAS),
     (dict(o=0), NULL), (dict(do=0), NULL), (dict(dq=0), NULL),
-    (dict(D=80), UNSUP), (dict(S=-3), SHAPE), (dict(scale=-1.0), UNSUP),
+    (dict(D=72), UNSUP), (dict(S=-3), SHAPE), (dict(scale=-1.0), UNSUP),
 ])
 def test_bwd_validation(lib, kw, expect):
     assert bwd(**kw) == expect
@@ -135,7 +135,8 @@ def test_workspace_bytes(lib):
     assert bd.c_attn_bwd_workspace_bytes(1, 16, 8191, 128, BF16) == 16 * 8191 * 4
     assert bd.c_attn_bwd_workspace_bytes(1, 4, 128, 64, F32) == 4 * 128 * 4
     assert bd.c_attn_bwd_workspace_bytes(0, 3, 100, 64, BF16) == 0
-    assert bd.c_attn_bwd_workspace_bytes(2, 3, 100, 96, BF16) == 0
+    assert bd.c_attn_bwd_workspace_bytes(2, 3, 100, 80, BF16) == 2 * 3 * 100 * 4
+    assert bd.c_attn_bwd_workspace_bytes(2, 3, 100, 112, BF16) == 0
     assert bd.c_attn_bwd_workspace_bytes(2, 3, -1, 64, BF16) == 0
 
 
@@ -198,7 +199,7 @@ def bwd_gqa(**kw):
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(Hkv=0), SHAPE), (dict(Hkv=3), SHAPE), (dict(Hkv=16), SHAPE), (dict(Hkv=-1), SHAPE),
-    (dict(k=0), NULL), (dict(D=96), UNSUP), (dict(scale=0.0), UNSUP),
+    (dict(k=0), NULL), (dict(D=112), UNSUP), (dict(scale=0.0), UNSUP),
     # o overlapping the tail of k: K spans B*Hkv*S*D*2 = 51200 bytes (a call that
     # passes validation would launch, so only overlaps are checked here)
     (dict(o=P[1] + 51200 - 16), ALIAS), (dict(lse=P[2] + 51200 - 16), ALIAS),

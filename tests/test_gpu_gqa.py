@@ -57,6 +57,9 @@ def check_groups(x, w, gpu, groups, causal=True, label=""):
     (1, 4, 2, 129, 128, "f32", False),
     (1, 4, 2, 1, 64, "bf16", True),
     (3, 16, 4, 200, 64, "bf16", True),
+    (2, 8, 2, 300, 80, "bf16", True),
+    (1, 6, 3, 130, 96, "bf16", False),
+    (1, 4, 2, 70, 80, "f32", True),
 ])
 def test_gqa_small_shapes_every_head(device, B, H, Hkv, S, D, dtype, causal):
     w = si.Workload("gqa", B, H, S, D, dtype, 1.0, 1.0, 0.1 if dtype == "bf16" else 1.0, causal, Hkv=Hkv)

@@ -74,6 +74,20 @@ def test_edge_shapes(device, S, D, dtype, causal):
     gu.check(gu.errors(gpu, ref, all_heads(w)), dtype, f"S={S} D={D} {dtype} causal={causal}")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [80, 96])
+@pytest.mark.parametrize("S", [1, 33, 64, 65, 129, 257, 600])
+def test_head_dims_80_96(device, S, D, dtype, causal):
+    """Head dimensions that are not a multiple of the 32-wide output tiles (80) or are (96)."""
+    w = si.Workload("hd", 2, 3, S, D, dtype, 1.0, 1.0, 0.1 if dtype == "bf16" else 1.0, causal)
+    print(f"\n[head dim] S={S} D={D} {dtype} causal={causal}", flush=True)
+    x = si.make_inputs(w, seed=S * 11 + D)
+    gpu = gu.run_gpu(x, w, device, causal=causal)
+    ref = oracle_heads(x, w, all_heads(w), causal=causal)
+    gu.check(gu.errors(gpu, ref, all_heads(w)), dtype, f"S={S} D={D} {dtype} causal={causal}")
+
+
 @pytest.mark.parametrize("S", [300, 1000])
 def test_ragged_tails_long_d128_large_logits(device, S):
     """Tails that are not a tile multiple with the sigma=4 query/key draw of the long workload."""
