@@ -38,7 +38,8 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="gpt205m_bf16", choices=sorted(si.WORKLOADS) + sorted(si.GQA_WORKLOADS),
+    ap.add_argument("--workload", default="gpt205m_bf16",
+                    choices=sorted(si.WORKLOADS) + sorted(si.GQA_WORKLOADS) + sorted(si.F16_WORKLOADS),
                     help="grouped key/value head workloads run attn_fwd_gqa / attn_bwd_gqa")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -60,7 +61,7 @@ def kernel_units(w):
     and "bwd" is the whole backward (both passes).
     """
     unit = w.B * w.H * w.S * w.S * w.D * (1.0 if w.causal else 2.0)
-    elem = 2 if w.dtype == "bf16" else 4
+    elem = 4 if w.dtype == "f32" else 2
     tensor = w.B * w.H * w.S * w.D * elem
     kvt = tensor // w.H * w.kv_heads
     rows = w.B * w.H * w.S * 4
@@ -136,18 +137,19 @@ def main():
         sys.exit(1)
     caf.load_library()
     dev = torch.device("cuda:0")
-    w = si.WORKLOADS[args.workload] if args.workload in si.WORKLOADS else si.GQA_WORKLOADS[args.workload]
+    w = {**si.WORKLOADS, **si.GQA_WORKLOADS, **si.F16_WORKLOADS}[args.workload]
     grouped = w.kv_heads != w.H
     x = si.make_inputs(w, seed=0)
 
     def dev_t(name):
-        if w.dtype == "bf16":
-            return torch.from_numpy(x[name + "_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+        if w.dtype in ("bf16", "f16"):
+            tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+            return torch.from_numpy(x[name + "_bits"].view(np.int16)).to(dev).view(tdt)
         return torch.from_numpy(x[name]).to(dev)
 
     q, k, v, do = (dev_t(n) for n in ("q", "k", "v", "do"))
     B, H, S, D = q.shape
-    dt = caf.ATTN_BF16 if w.dtype == "bf16" else caf.ATTN_F32
+    dt = {"bf16": caf.ATTN_BF16, "f16": caf.ATTN_F16, "f32": caf.ATTN_F32}[w.dtype]
     causal = int(w.causal)
     scale = w.scale
     bd = caf._binding
@@ -249,7 +251,7 @@ def main():
     units = kernel_units(w)
     dom = max(names, key=lambda n: per_kernel_mean[n])
     dom_ms = per_kernel_mean[dom]
-    mfma_peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    mfma_peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS  # fp16 dense MFMA peak = bf16
     achieved = units[dom]["flops"] / (dom_ms * 1e-3) / 1e12
     traffic = read_traffic(dom, w.name)
 

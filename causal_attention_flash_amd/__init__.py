@@ -11,6 +11,7 @@ stream; all computation runs in the library's kernels.
 """
 from ._binding import (  # noqa: F401
     ATTN_BF16,
+    ATTN_F16,
     ATTN_F32,
     LIB_PATH,
     SIGNATURES,

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libcausal_attn.so")
 
 ATTN_F32 = 0
 ATTN_BF16 = 1
+ATTN_F16 = 2
 
 STATUS_NAMES = {
     0: "ATTN_OK",
@@ -140,9 +141,11 @@ def _dtype_code(t) -> int:
     torch = _torch()
     if t.dtype == torch.bfloat16:
         return ATTN_BF16
+    if t.dtype == torch.float16:
+        return ATTN_F16
     if t.dtype == torch.float32:
         return ATTN_F32
-    raise ValueError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+    raise ValueError(f"unsupported dtype {t.dtype}: use torch.bfloat16, torch.float16 or torch.float32")
 
 
 def _check_tensors(names_and_tensors, shape, dtype, device):
@@ -174,7 +177,7 @@ def _call(fn, where, *args):
 
 
 def attn_fwd(q, k, v, scale=None, causal=True):
-    """O, LSE = attn_fwd(Q, K, V): [B,H,S,D] tensors (bf16 or fp32) on one GPU."""
+    """O, LSE = attn_fwd(Q, K, V): [B,H,S,D] tensors (bf16, fp16 or fp32) on one GPU."""
     torch = _torch()
     if q.dim() != 4:
         raise ValueError("q must be [B, H, S, D]")

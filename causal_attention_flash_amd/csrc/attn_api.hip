@@ -31,12 +31,14 @@ bool overlaps(const Span& a, const Span& b) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-int elem_bytes(attn_dtype dt) { return dt == ATTN_BF16 ? 2 : 4; }
+int elem_bytes(attn_dtype dt) { return dt == ATTN_F32 ? 4 : 2; }
+// bf16 and fp16 run the MFMA kernels; fp32 the vector-ALU kernels
+bool is16(attn_dtype dt) { return dt == ATTN_BF16 || dt == ATTN_F16; }
 
 // Sizes, D, dtype.  Sets *empty when there is nothing to compute.
 attn_status check_shape(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, bool* empty) {
     if (B < 0 || H < 0 || S < 0 || D < 0) return ATTN_ERR_SHAPE;
-    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
     if (D != 64 && D != 80 && D != 96 && D != 128) return ATTN_ERR_UNSUPPORTED;
     *empty = (B == 0 || H == 0 || S == 0);
     if (*empty) return ATTN_OK;
@@ -106,27 +108,35 @@ LaunchArgs base_args(int64_t B, int64_t H, int64_t S, int64_t D, float scale, in
 }
 
 attn_status run_preprocess(LaunchArgs a, attn_dtype dt) {
-    return from_hip(attn::launch_bwd_preprocess(a, elem_bytes(dt)));
+    return from_hip(attn::launch_bwd_preprocess(a, (int)dt));
 }
 attn_status run_dkdv(const LaunchArgs& a, attn_dtype dt) {
-    return from_hip(dt == ATTN_BF16 ? attn::launch_bwd_dkdv_bf16(a) : attn::launch_bwd_dkdv_f32(a));
+    return from_hip(dt == ATTN_BF16  ? attn::launch_bwd_dkdv_bf16(a)
+                    : dt == ATTN_F16 ? attn::launch_bwd_dkdv_f16(a)
+                                     : attn::launch_bwd_dkdv_f32(a));
 }
 attn_status run_dq(const LaunchArgs& a, attn_dtype dt) {
-    return from_hip(dt == ATTN_BF16 ? attn::launch_bwd_dq_bf16(a) : attn::launch_bwd_dq_f32(a));
+    return from_hip(dt == ATTN_BF16  ? attn::launch_bwd_dq_bf16(a)
+                    : dt == ATTN_F16 ? attn::launch_bwd_dq_f16(a)
+                                     : attn::launch_bwd_dq_f32(a));
 }
-// Workspace of the grouped backward: delta (B*H*S fp32), then for bf16 with more
+// Workspace of the grouped backward: delta (B*H*S fp32), then for bf16/fp16 with more
 // than one query head per key/value head the per-query-head fp32 dK and dV
 // ([B,H,S,D] each), each region starting on a 256-byte boundary.
 size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 size_t gqa_workspace(int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D, attn_dtype dt) {
     const Sizes z = sizes(B, H, S, D, dt);
-    if (dt != ATTN_BF16 || H_kv == H) return z.rows;
+    if (!is16(dt) || H_kv == H) return z.rows;
     const size_t part = (size_t)B * (size_t)H * (size_t)S * (size_t)D * sizeof(float);
     return round256(z.rows) + 2 * round256(part);
 }
-attn_status run_group_sum(const LaunchArgs& a) { return from_hip(attn::launch_group_sum_bf16(a)); }
+attn_status run_group_sum(const LaunchArgs& a, attn_dtype dt) {
+    return from_hip(dt == ATTN_F16 ? attn::launch_group_sum_f16(a) : attn::launch_group_sum_bf16(a));
+}
 attn_status run_dq_delta(const LaunchArgs& a, attn_dtype dt) {
-    return from_hip(dt == ATTN_BF16 ? attn::launch_bwd_dq_delta_bf16(a) : attn::launch_bwd_dq_delta_f32(a));
+    return from_hip(dt == ATTN_BF16  ? attn::launch_bwd_dq_delta_bf16(a)
+                    : dt == ATTN_F16 ? attn::launch_bwd_dq_delta_f16(a)
+                                     : attn::launch_bwd_dq_delta_f32(a));
 }
 
 }  // namespace
@@ -140,7 +150,7 @@ const char* attn_status_string(attn_status s) {
         case ATTN_ERR_SHAPE:
             return "negative size, sizes beyond B*H*S < 2^31 and S*D < 2^31, or H_kv < 1 or not dividing H";
         case ATTN_ERR_UNSUPPORTED:
-            return "unsupported: D must be 64, 80, 96 or 128, dtype ATTN_F32 or ATTN_BF16, causal 0 or 1, scale finite and > 0";
+            return "unsupported: D must be 64, 80, 96 or 128, dtype ATTN_F32, ATTN_BF16 or ATTN_F16, causal 0 or 1, scale finite and > 0";
         case ATTN_ERR_ALIGNMENT: return "a device pointer is not 16-byte aligned";
         case ATTN_ERR_WORKSPACE: return "workspace is NULL or smaller than attn_bwd_workspace_bytes()";
         case ATTN_ERR_HIP: return "the HIP runtime reported an error at launch";
@@ -174,7 +184,9 @@ attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, f
     a.v = v;
     a.o = o;
     a.lse = lse;
-    return from_hip(dtype == ATTN_BF16 ? attn::launch_fwd_bf16(a) : attn::launch_fwd_f32(a));
+    return from_hip(dtype == ATTN_BF16  ? attn::launch_fwd_bf16(a)
+                    : dtype == ATTN_F16 ? attn::launch_fwd_f16(a)
+                                        : attn::launch_fwd_f32(a));
 }
 
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D, attn_dtype dtype) {
@@ -324,7 +336,7 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
-    const bool partials = dtype == ATTN_BF16 && H_kv != H;
+    const bool partials = is16(dtype) && H_kv != H;
     if (partials) {
         char* w = (char*)workspace;
         const size_t part = (size_t)B * (size_t)H * (size_t)S * (size_t)D * sizeof(float);
@@ -332,10 +344,10 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void
         a.dv_part = (float*)(w + round256(z.rows) + round256(part));
     }
     // dQ first: it forms delta, which the dK/dV pass reads; with grouped heads in
-    // bf16 the dK/dV pass leaves per-query-head partials that the group sum adds
+    // bf16/fp16 the dK/dV pass leaves per-query-head partials that the group sum adds
     if ((st = run_dq_delta(a, dtype)) != ATTN_OK) return st;
     if ((st = run_dkdv(a, dtype)) != ATTN_OK) return st;
-    return partials ? run_group_sum(a) : ATTN_OK;
+    return partials ? run_group_sum(a, dtype) : ATTN_OK;
 }
 
 size_t attn_bwd_gqa_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D, attn_dtype dtype) {

@@ -55,13 +55,14 @@ struct DkdvCfg {
 // key/value heads (PARTIAL = true) each query head's contribution is stored as
 // fp32 at its own [query head] slot of dKp/dVp, and the sum over the G query
 // heads of a key/value head is formed by bwd_group_sum_kernel.
-template <int D, int BMQ, int NW, bool PARTIAL>
-__global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) void bwd_dkdv_bf16_kernel(
+template <class E, int D, int BMQ, int NW, bool PARTIAL>
+__global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) void bwd_dkdv_mfma_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ dKp, float* __restrict__ dVp, int S,
     int nblk, int BH, int H, int GQ, float c, float scale, int causal) {
     using Cfg = DkdvCfg<D, BMQ, NW>;
+    using V8 = typename E::V8;
     constexpr int NT = Cfg::NT, BNK = Cfg::BNK;
     constexpr int STR = Cfg::STR;
     constexpr int KS = Cfg::KS, DB = Cfg::DB;
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
     const int key = kw0 + n;  // the key this lane's C columns belong to
 
     // K and V as B operands (keys on the lanes), d = 16ks+8h..+7.
-    bf16x8 kf[KS], vf[KS];
+    V8 kf[KS], vf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
@@ -95,8 +96,8 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
             a = ldg16(K + kvbase + (size_t)key * D + ks * 16 + 8 * h);
             b = ldg16(V + kvbase + (size_t)key * D + ks * 16 + 8 * h);
         }
-        kf[ks] = as_bf16x8(a);
-        vf[ks] = as_bf16x8(b);
+        kf[ks] = as_op<E>(a);
+        vf[ks] = as_op<E>(b);
     }
 
     f32x16 dkacc[DB], dvacc[DB];
@@ -171,8 +172,8 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int off = (qb * 32 + n) * STR + ks * 16 + 8 * h;
-                sacc = mfma32(as_bf16x8(lds16(Qs + off)), kf[ks], sacc);
-                pacc = mfma32(as_bf16x8(lds16(dOs + off)), vf[ks], pacc);
+                sacc = E::mma(as_op<E>(lds16(Qs + off)), kf[ks], sacc);
+                pacc = E::mma(as_op<E>(lds16(dOs + off)), vf[ks], pacc);
             }
             // P and dS
 #pragma unroll
@@ -186,13 +187,13 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
             // dO^T and Q^T read transposed from the row-major tiles)
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
-                const bf16x8 pb = pack_operand(sacc, c2);
-                const bf16x8 sb = pack_operand(pacc, c2);
+                const V8 pb = pack_op<E>(sacc, c2);
+                const V8 sb = pack_op<E>(pacc, c2);
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     const int r0 = (qb * 2 + c2) * 16;
-                    dvacc[db] = mfma32(lds_tr_operand<STR>(dOs, r0, db * 32, lane), pb, dvacc[db]);
-                    dkacc[db] = mfma32(lds_tr_operand<STR>(Qs, r0, db * 32, lane), sb, dkacc[db]);
+                    dvacc[db] = E::mma(lds_tr_op<E, STR>(dOs, r0, db * 32, lane), pb, dvacc[db]);
+                    dkacc[db] = E::mma(lds_tr_op<E, STR>(Qs, r0, db * 32, lane), sb, dkacc[db]);
                 }
             }
         }
@@ -244,17 +245,17 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
                 if (!HeadDim<D>::live(db, g)) continue;
                 const int d = db * 32 + 8 * g + 4 * h;
                 u32x2 uk, uv;
-                uk[0] = pack_bf16x2(dkacc[db][4 * g + 0] * scale, dkacc[db][4 * g + 1] * scale);
-                uk[1] = pack_bf16x2(dkacc[db][4 * g + 2] * scale, dkacc[db][4 * g + 3] * scale);
-                uv[0] = pack_bf16x2(dvacc[db][4 * g + 0], dvacc[db][4 * g + 1]);
-                uv[1] = pack_bf16x2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]);
+                uk[0] = E::pack2(dkacc[db][4 * g + 0] * scale, dkacc[db][4 * g + 1] * scale);
+                uk[1] = E::pack2(dkacc[db][4 * g + 2] * scale, dkacc[db][4 * g + 3] * scale);
+                uv[0] = E::pack2(dvacc[db][4 * g + 0], dvacc[db][4 * g + 1]);
+                uv[1] = E::pack2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]);
                 *reinterpret_cast<u32x2*>(dKr + d) = uk;
                 *reinterpret_cast<u32x2*>(dVr + d) = uv;
             }
     }
 }
 
-template <int D, int BMQ, int NW>
+template <class E, int D, int BMQ, int NW>
 static hipError_t launch_dkdv(const LaunchArgs& a) {
     using Cfg = DkdvCfg<D, BMQ, NW>;
     const int nblk = (int)((a.S + Cfg::BNK - 1) / Cfg::BNK);
@@ -262,32 +263,37 @@ static hipError_t launch_dkdv(const LaunchArgs& a) {
     if (total > INT32_MAX) return hipErrorInvalidValue;
     const int GQ = (int)(a.H / a.Hkv);
     if (GQ == 1)
-        hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, BMQ, NW, false>), dim3((unsigned)total), dim3(Cfg::NT), 0,
+        hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D, BMQ, NW, false>), dim3((unsigned)total), dim3(Cfg::NT), 0,
                            a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                            (const uint16_t*)a.dout, a.lse_in, a.delta_in, (uint16_t*)a.dk, (uint16_t*)a.dv,
                            nullptr, nullptr, (int)a.S, nblk, (int)a.BH, (int)a.H, 1, a.scale * kLog2e, a.scale,
                            a.causal);
     else
-        hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, BMQ, NW, true>), dim3((unsigned)total), dim3(Cfg::NT), 0,
+        hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D, BMQ, NW, true>), dim3((unsigned)total), dim3(Cfg::NT), 0,
                            a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                            (const uint16_t*)a.dout, a.lse_in, a.delta_in, nullptr, nullptr, a.dk_part, a.dv_part,
                            (int)a.S, nblk, (int)a.BH, (int)a.H, GQ, a.scale * kLog2e, a.scale, a.causal);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkdv_bf16(const LaunchArgs& a) {
-    if (a.D == 64) return launch_dkdv<64, 64, 8>(a);
-    if (a.D == 80) return launch_dkdv<80, 64, 8>(a);
-    if (a.D == 96) return launch_dkdv<96, 64, 8>(a);
-    if (a.D == 128) return launch_dkdv<128, 32, 4>(a);
+template <class E>
+static hipError_t launch_dkdv_type(const LaunchArgs& a) {
+    if (a.D == 64) return launch_dkdv<E, 64, 64, 8>(a);
+    if (a.D == 80) return launch_dkdv<E, 80, 64, 8>(a);
+    if (a.D == 96) return launch_dkdv<E, 96, 64, 8>(a);
+    if (a.D == 128) return launch_dkdv<E, 128, 32, 4>(a);
     return hipErrorInvalidValue;
 }
+
+hipError_t launch_bwd_dkdv_bf16(const LaunchArgs& a) { return launch_dkdv_type<Bf16>(a); }
+hipError_t launch_bwd_dkdv_f16(const LaunchArgs& a) { return launch_dkdv_type<F16>(a); }
 
 // ====================================================== grouped key/value heads
 //
 // dK[b, j] = sum over g < GQ of dKp[b, j*GQ + g] (likewise dV), fp32 sums of the
-// per-query-head contributions, rounded once to bf16.  Grid-stride over groups
+// per-query-head contributions, rounded once to the output type.  Grid-stride over groups
 // of 8 elements of [batch, key/value head, S, D].
+template <class E>
 __global__ __launch_bounds__(256) void bwd_group_sum_kernel(const float* __restrict__ dKp,
                                                             const float* __restrict__ dVp,
                                                             uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
@@ -306,28 +312,32 @@ __global__ __launch_bounds__(256) void bwd_group_sum_kernel(const float* __restr
             v1 += *reinterpret_cast<const f32x4*>(dVp + src + 4);
         }
         u32x4 uk, uv;
-        uk[0] = pack_bf16x2(k0[0], k0[1]);
-        uk[1] = pack_bf16x2(k0[2], k0[3]);
-        uk[2] = pack_bf16x2(k1[0], k1[1]);
-        uk[3] = pack_bf16x2(k1[2], k1[3]);
-        uv[0] = pack_bf16x2(v0[0], v0[1]);
-        uv[1] = pack_bf16x2(v0[2], v0[3]);
-        uv[2] = pack_bf16x2(v1[0], v1[1]);
-        uv[3] = pack_bf16x2(v1[2], v1[3]);
+        uk[0] = E::pack2(k0[0], k0[1]);
+        uk[1] = E::pack2(k0[2], k0[3]);
+        uk[2] = E::pack2(k1[0], k1[1]);
+        uk[3] = E::pack2(k1[2], k1[3]);
+        uv[0] = E::pack2(v0[0], v0[1]);
+        uv[1] = E::pack2(v0[2], v0[3]);
+        uv[2] = E::pack2(v1[0], v1[1]);
+        uv[3] = E::pack2(v1[2], v1[3]);
         *reinterpret_cast<u32x4*>(dK + e) = uk;
         *reinterpret_cast<u32x4*>(dV + e) = uv;
     }
 }
 
-hipError_t launch_group_sum_bf16(const LaunchArgs& a) {
+template <class E>
+static hipError_t launch_group_sum(const LaunchArgs& a) {
     const int64_t head_elems = a.S * a.D;
     const int64_t n8 = a.BH / a.H * a.Hkv * head_elems / 8;
     const int64_t want = (n8 + 255) / 256;
     const unsigned grid = (unsigned)(want < 8192 ? (want > 0 ? want : 1) : 8192);
-    hipLaunchKernelGGL(bwd_group_sum_kernel, dim3(grid), dim3(256), 0, a.stream, a.dk_part, a.dv_part,
+    hipLaunchKernelGGL(bwd_group_sum_kernel<E>, dim3(grid), dim3(256), 0, a.stream, a.dk_part, a.dv_part,
                        (uint16_t*)a.dk, (uint16_t*)a.dv, n8, head_elems, (int)(a.H / a.Hkv));
     return hipGetLastError();
 }
+
+hipError_t launch_group_sum_bf16(const LaunchArgs& a) { return launch_group_sum<Bf16>(a); }
+hipError_t launch_group_sum_f16(const LaunchArgs& a) { return launch_group_sum<F16>(a); }
 
 // ================================================================== dQ pass
 
@@ -350,13 +360,14 @@ struct DqCfg {
 // DELTA_FROM_O: delta = rowsum(dO o O) is formed here, from the O rows of this
 // wave's queries (fp32 sums of bf16 products), and written to DeltaOut for the
 // dK/dV pass; otherwise delta is read from Delta.
-template <int D, int BNK, int NW, bool DELTA_FROM_O>
-__global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void bwd_dq_bf16_kernel(
+template <class E, int D, int BNK, int NW, bool DELTA_FROM_O>
+__global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void bwd_dq_mfma_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
     const float* __restrict__ Delta, float* __restrict__ DeltaOut, uint16_t* __restrict__ dQ, int S, int nblk,
     int BH, int H, int GQ, float c, float scale, int causal) {
     using Cfg = DqCfg<D, BNK, NW>;
+    using V8 = typename E::V8;
     constexpr int BMQ = Cfg::BMQ;
     constexpr int STR = Cfg::STR;
     constexpr int KS = Cfg::KS, DB = Cfg::DB;
@@ -379,7 +390,7 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
     const int qw0 = q0 + wave * 32;
     const int q = qw0 + n;  // the query this lane's C columns belong to
 
-    bf16x8 qf[KS], of[KS];
+    V8 qf[KS], of[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
@@ -387,8 +398,8 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
             a = ldg16(Q + base + (size_t)q * D + ks * 16 + 8 * h);
             b = ldg16(dO + base + (size_t)q * D + ks * 16 + 8 * h);
         }
-        qf[ks] = as_bf16x8(a);
-        of[ks] = as_bf16x8(b);
+        qf[ks] = as_op<E>(a);
+        of[ks] = as_op<E>(b);
     }
     const float l2 = q < S ? LSE[(size_t)head * S + q] * kLog2e : INFINITY;
     float dl;
@@ -400,7 +411,7 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 u = {0u, 0u, 0u, 0u};
             if (q < S) u = ldg16(O + base + (size_t)q * D + ks * 16 + 8 * h);
-            part = dot_bf16x8(of[ks], as_bf16x8(u), part);
+            part = dot8<E>(of[ks], as_op<E>(u), part);
         }
         dl = half_sum(part);
         if (h == 0 && q < S) DeltaOut[(size_t)head * S + q] = dl;
@@ -452,8 +463,8 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int off = (kb * 32 + n) * STR + ks * 16 + 8 * h;
-                sacc = mfma32(as_bf16x8(lds16(Ks + off)), qf[ks], sacc);
-                pacc = mfma32(as_bf16x8(lds16(Vs + off)), of[ks], pacc);
+                sacc = E::mma(as_op<E>(lds16(Ks + off)), qf[ks], sacc);
+                pacc = E::mma(as_op<E>(lds16(Vs + off)), of[ks], pacc);
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -468,10 +479,10 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
             // transposed from the row-major K tile)
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
-                const bf16x8 sb = pack_operand(pacc, c2);
+                const V8 sb = pack_op<E>(pacc, c2);
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
-                    dqacc[db] = mfma32(lds_tr_operand<STR>(Ks, (kb * 2 + c2) * 16, db * 32, lane), sb, dqacc[db]);
+                    dqacc[db] = E::mma(lds_tr_op<E, STR>(Ks, (kb * 2 + c2) * 16, db * 32, lane), sb, dqacc[db]);
             }
         }
     };
@@ -500,20 +511,20 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
             for (int g = 0; g < 4; ++g) {
                 if (!HeadDim<D>::live(db, g)) continue;
                 u32x2 u;
-                u[0] = pack_bf16x2(dqacc[db][4 * g + 0] * scale, dqacc[db][4 * g + 1] * scale);
-                u[1] = pack_bf16x2(dqacc[db][4 * g + 2] * scale, dqacc[db][4 * g + 3] * scale);
+                u[0] = E::pack2(dqacc[db][4 * g + 0] * scale, dqacc[db][4 * g + 1] * scale);
+                u[1] = E::pack2(dqacc[db][4 * g + 2] * scale, dqacc[db][4 * g + 3] * scale);
                 *reinterpret_cast<u32x2*>(dQr + db * 32 + 8 * g + 4 * h) = u;
             }
     }
 }
 
-template <int D, int BNK, int NW, bool DELTA_FROM_O>
+template <class E, int D, int BNK, int NW, bool DELTA_FROM_O>
 static hipError_t launch_dq(const LaunchArgs& a) {
     using Cfg = DqCfg<D, BNK, NW>;
     const int nblk = (int)((a.S + Cfg::BMQ - 1) / Cfg::BMQ);
     const int64_t total = (int64_t)nblk * a.BH;
     if (total > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, BNK, NW, DELTA_FROM_O>), dim3((unsigned)total), dim3(Cfg::NT), 0,
+    hipLaunchKernelGGL((bwd_dq_mfma_kernel<E, D, BNK, NW, DELTA_FROM_O>), dim3((unsigned)total), dim3(Cfg::NT), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.o_in, (const uint16_t*)a.dout, a.lse_in, a.delta_in, a.delta,
                        (uint16_t*)a.dq, (int)a.S, nblk, (int)a.BH, (int)a.H, (int)(a.H / a.Hkv), a.scale * kLog2e,
@@ -521,20 +532,18 @@ static hipError_t launch_dq(const LaunchArgs& a) {
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq_bf16(const LaunchArgs& a) {
-    if (a.D == 64) return launch_dq<64, 64, 4, false>(a);
-    if (a.D == 80) return launch_dq<80, 64, 4, false>(a);
-    if (a.D == 96) return launch_dq<96, 64, 4, false>(a);
-    if (a.D == 128) return launch_dq<128, 32, 4, false>(a);
+template <class E, bool DELTA_FROM_O>
+static hipError_t launch_dq_type(const LaunchArgs& a) {
+    if (a.D == 64) return launch_dq<E, 64, 64, 4, DELTA_FROM_O>(a);
+    if (a.D == 80) return launch_dq<E, 80, 64, 4, DELTA_FROM_O>(a);
+    if (a.D == 96) return launch_dq<E, 96, 64, 4, DELTA_FROM_O>(a);
+    if (a.D == 128) return launch_dq<E, 128, 32, 4, DELTA_FROM_O>(a);
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_dq_delta_bf16(const LaunchArgs& a) {
-    if (a.D == 64) return launch_dq<64, 64, 4, true>(a);
-    if (a.D == 80) return launch_dq<80, 64, 4, true>(a);
-    if (a.D == 96) return launch_dq<96, 64, 4, true>(a);
-    if (a.D == 128) return launch_dq<128, 32, 4, true>(a);
-    return hipErrorInvalidValue;
-}
+hipError_t launch_bwd_dq_bf16(const LaunchArgs& a) { return launch_dq_type<Bf16, false>(a); }
+hipError_t launch_bwd_dq_delta_bf16(const LaunchArgs& a) { return launch_dq_type<Bf16, true>(a); }
+hipError_t launch_bwd_dq_f16(const LaunchArgs& a) { return launch_dq_type<F16, false>(a); }
+hipError_t launch_bwd_dq_delta_f16(const LaunchArgs& a) { return launch_dq_type<F16, true>(a); }
 
 }  // namespace attn

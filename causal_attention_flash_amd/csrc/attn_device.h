@@ -129,6 +129,86 @@ __device__ __forceinline__ float dot_bf16x8(const bf16x8& x, const bf16x8& y, fl
     return acc;
 }
 
+// 16-bit element types of the MFMA kernels.  A kernel templated on E uses
+// E::V8 for its operand quads and E's MFMA, pack, dot and transposing-read
+// helpers; everything else (fp32 accumulation, fp32 softmax statistics, the
+// lane layouts above) is the same for both types.  Conversions from fp32 round
+// to nearest even.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+struct Bf16 {
+    using V8 = bf16x8;
+    using V2 = bf16x2;
+    static __device__ __forceinline__ f32x16 mma(const V8& a, const V8& b, const f32x16& c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
+    // acc + a.lo*b.lo + a.hi*b.hi in fp32, on packed pairs
+    static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(V2, a), __builtin_bit_cast(V2, b), acc, false);
+    }
+    static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+    static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+};
+
+struct F16 {
+    using V8 = f16x8;
+    using V2 = f16x2;
+    static __device__ __forceinline__ f32x16 mma(const V8& a, const V8& b, const f32x16& c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+        const f16x2 r = {(_Float16)a, (_Float16)b};
+        return __builtin_bit_cast(uint32_t, r);
+    }
+    static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(V2, a), __builtin_bit_cast(V2, b), acc, false);
+    }
+    static __device__ __forceinline__ float lo(uint32_t w) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+    }
+    static __device__ __forceinline__ float hi(uint32_t w) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    }
+};
+
+// Generic forms of the helpers above for an element type E.
+template <class E>
+__device__ __forceinline__ typename E::V8 as_op(const u32x4& u) {
+    return __builtin_bit_cast(typename E::V8, u);
+}
+template <class E>
+__device__ __forceinline__ typename E::V8 pack_op(const f32x16& acc, int c) {
+    u32x4 u;
+    u[0] = E::pack2(acc[8 * c + 0], acc[8 * c + 1]);
+    u[1] = E::pack2(acc[8 * c + 2], acc[8 * c + 3]);
+    u[2] = E::pack2(acc[8 * c + 4], acc[8 * c + 5]);
+    u[3] = E::pack2(acc[8 * c + 6], acc[8 * c + 7]);
+    return __builtin_bit_cast(typename E::V8, u);
+}
+// acc + the sum of the eight values of x (fp32 accumulation)
+template <class E>
+__device__ __forceinline__ float sum8(const typename E::V8& x, float acc) {
+    const u32x4 u = __builtin_bit_cast(u32x4, x);
+    const uint32_t one = E::pack2(1.0f, 1.0f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = E::dot2(u[i], one, acc);
+    return acc;
+}
+// acc + the dot product of x and y (fp32 accumulation)
+template <class E>
+__device__ __forceinline__ float dot8(const typename E::V8& x, const typename E::V8& y, float acc) {
+    const u32x4 u = __builtin_bit_cast(u32x4, x), w = __builtin_bit_cast(u32x4, y);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = E::dot2(u[i], w[i], acc);
+    return acc;
+}
+template <class E, int STR>
+__device__ __forceinline__ typename E::V8 lds_tr_op(const uint16_t* T, int r0, int c0, int lane) {
+    return __builtin_bit_cast(typename E::V8, lds_tr_operand<STR>(T, r0, c0, lane));
+}
+
 // Reductions over the lane pair (l, l ^ 32).  v_permlane32_swap exchanges the
 // upper half of its first register with the lower half of its second; given x in
 // both, every lane ends up holding x[l % 32] in one result and x[l % 32 + 32] in

@@ -53,14 +53,15 @@ struct FwdCfg {
     static constexpr int DB = HeadDim<D>::DB;
 };
 
-template <int D, int QB, int NW>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __restrict__ Q,
+template <class E, int D, int QB, int NW>
+__global__ __launch_bounds__(NW * 64) void fwd_mfma_kernel(const uint16_t* __restrict__ Q,
                                                        const uint16_t* __restrict__ K,
                                                        const uint16_t* __restrict__ V,
                                                        uint16_t* __restrict__ O, float* __restrict__ LSE,
                                                        int S, int nblk, int BH, int H, int GQ, float c,
                                                        int causal) {
     using Cfg = FwdCfg<D, QB, NW>;
+    using V8 = typename E::V8;
     constexpr int BM = Cfg::BM, BN = Cfg::BN, STR = Cfg::STR, TE = Cfg::TE;
     constexpr int KB = BN / 32;  // 32-key blocks per tile
     constexpr int KS = Cfg::KS, DB = Cfg::DB;
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
     auto vbuf = [&](int t) { return smem + (2 + (t & 1)) * TE; };
 
     // Q as the B operand of S^T = K Q^T: lane holds query qw0+32qb+n, d = 16ks+8h..+7.
-    bf16x8 qf[QB][KS];
+    V8 qf[QB][KS];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int q = qw0 + qb * 32 + n;
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 u = {0u, 0u, 0u, 0u};
             if (q < S) u = ldg16(Qh + (size_t)q * D + ks * 16 + 8 * h);
-            qf[qb][ks] = as_bf16x8(u);
+            qf[qb][ks] = as_op<E>(u);
         }
     }
 
@@ -117,24 +118,24 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
 
     // K rows of tile t as A operands of S^T = K Q^T:
     // kf[kb][ks] = K[t*BN + 32kb + n][16ks + 8h .. +7].
-    auto load_k = [&](bf16x8 (&kf)[KB][KS], int t) {
+    auto load_k = [&](V8 (&kf)[KB][KS], int t) {
         const uint16_t* Ks = kbuf(t);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                kf[kb][ks] = as_bf16x8(lds16(Ks + (kb * 32 + n) * STR + ks * 16 + 8 * h));
+                kf[kb][ks] = as_op<E>(lds16(Ks + (kb * 32 + n) * STR + ks * 16 + 8 * h));
     };
     // S^T tile from K operands already in registers; the first contraction step
     // starts from a zero accumulator.
-    auto mma_scores = [&](f32x16 (&sacc)[QB][KB], const bf16x8 (&kf)[KB][KS]) {
+    auto mma_scores = [&](f32x16 (&sacc)[QB][KB], const V8 (&kf)[KB][KS]) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
-                    sacc[qb][kb] = mfma32(kf[kb][ks], qf[qb][ks], ks == 0 ? f32x16{} : sacc[qb][kb]);
+                    sacc[qb][kb] = E::mma(kf[kb][ks], qf[qb][ks], ks == 0 ? f32x16{} : sacc[qb][kb]);
     };
 
     // One key tile t: softmax of its scores `cur` and O += V_t P_t.  With NEXT,
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
     auto step = [&](auto mask_tag, auto next_tag, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB], int t) {
         constexpr bool MASK = decltype(mask_tag)::value;
         constexpr bool NEXT = decltype(next_tag)::value;
-        bf16x8 kf[KB][KS];
+        V8 kf[KB][KS];
         if constexpr (NEXT) load_k(kf, t + 1);
 
         // ---- mask, row max (raw scores; c > 0 so max commutes with scaling)
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
         // rounded values the PV product multiplies, so numerator and
         // denominator of O = (P V) / l carry the same rounding (a row whose
         // weight sits on one key reproduces that key's V row).
-        bf16x8 pf[QB][BN / 16];
+        V8 pf[QB][BN / 16];
         float ls[QB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
@@ -196,19 +197,19 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
             for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) cur[qb][kb][r] = fast_exp2(fmaf(cur[qb][kb][r], c, -mn[qb]));
-                pf[qb][2 * kb] = pack_operand(cur[qb][kb], 0);
-                pf[qb][2 * kb + 1] = pack_operand(cur[qb][kb], 1);
-                ls[qb] = sum_bf16x8(pf[qb][2 * kb], ls[qb]);
-                ls[qb] = sum_bf16x8(pf[qb][2 * kb + 1], ls[qb]);
+                pf[qb][2 * kb] = pack_op<E>(cur[qb][kb], 0);
+                pf[qb][2 * kb + 1] = pack_op<E>(cur[qb][kb], 1);
+                ls[qb] = sum8<E>(pf[qb][2 * kb], ls[qb]);
+                ls[qb] = sum8<E>(pf[qb][2 * kb + 1], ls[qb]);
             }
         }
         // V^T operands, read transposed from the row-major V tile
         const uint16_t* Vs = vbuf(t);
-        bf16x8 vf[BN / 16][DB];
+        V8 vf[BN / 16][DB];
 #pragma unroll
         for (int ks = 0; ks < BN / 16; ++ks)
 #pragma unroll
-            for (int db = 0; db < DB; ++db) vf[ks][db] = lds_tr_operand<STR>(Vs, ks * 16, db * 32, lane);
+            for (int db = 0; db < DB; ++db) vf[ks][db] = lds_tr_op<E, STR>(Vs, ks * 16, db * 32, lane);
 
         if (resc) {
             // rare (the reference point moves only past the slack): keep it a
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32(vf[ks][db], pf[qb][ks], oacc[qb][db]);
+                for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = E::mma(vf[ks][db], pf[qb][ks], oacc[qb][db]);
     };
 
     // ---- prologue: K_0, V_0, K_1 in LDS; register set 0 holds (K_2, V_1) and
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
 
     f32x16 sa[QB][KB], sb[QB][KB];
     if (nw > 0) {
-        bf16x8 kf[KB][KS];
+        V8 kf[KB][KS];
         load_k(kf, 0);
         mma_scores(sa, kf);
     }
@@ -304,8 +305,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
                 for (int g = 0; g < 4; ++g) {
                     if (!HeadDim<D>::live(db, g)) continue;
                     u32x2 u;
-                    u[0] = pack_bf16x2(oacc[qb][db][4 * g + 0] * inv, oacc[qb][db][4 * g + 1] * inv);
-                    u[1] = pack_bf16x2(oacc[qb][db][4 * g + 2] * inv, oacc[qb][db][4 * g + 3] * inv);
+                    u[0] = E::pack2(oacc[qb][db][4 * g + 0] * inv, oacc[qb][db][4 * g + 1] * inv);
+                    u[1] = E::pack2(oacc[qb][db][4 * g + 2] * inv, oacc[qb][db][4 * g + 3] * inv);
                     *reinterpret_cast<u32x2*>(Oh + (size_t)q * D + db * 32 + 8 * g + 4 * h) = u;
                 }
             if (h == 0) Lh[q] = lt > 0.f ? (m[qb] + __log2f(lt)) * kLn2 : -INFINITY;
@@ -313,24 +314,28 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const uint16_t* __res
     }
 }
 
-template <int D, int QB, int NW>
+template <class E, int D, int QB, int NW>
 static hipError_t launch_fwd(const LaunchArgs& a) {
     using Cfg = FwdCfg<D, QB, NW>;
     const int nblk = (int)((a.S + Cfg::BM - 1) / Cfg::BM);
     const int64_t total = (int64_t)nblk * a.BH;
     if (total > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, NW>), dim3((unsigned)total), dim3(Cfg::NT), 0, a.stream,
+    hipLaunchKernelGGL((fwd_mfma_kernel<E, D, QB, NW>), dim3((unsigned)total), dim3(Cfg::NT), 0, a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
                        (int)a.S, nblk, (int)a.BH, (int)a.H, (int)(a.H / a.Hkv), a.scale * kLog2e, a.causal);
     return hipGetLastError();
 }
 
-hipError_t launch_fwd_bf16(const LaunchArgs& a) {
-    if (a.D == 64) return launch_fwd<64, 1, 4>(a);
-    if (a.D == 80) return launch_fwd<80, 1, 4>(a);
-    if (a.D == 96) return launch_fwd<96, 1, 4>(a);
-    if (a.D == 128) return launch_fwd<128, 1, 4>(a);
+template <class E>
+static hipError_t launch_fwd_type(const LaunchArgs& a) {
+    if (a.D == 64) return launch_fwd<E, 64, 1, 4>(a);
+    if (a.D == 80) return launch_fwd<E, 80, 1, 4>(a);
+    if (a.D == 96) return launch_fwd<E, 96, 1, 4>(a);
+    if (a.D == 128) return launch_fwd<E, 128, 1, 4>(a);
     return hipErrorInvalidValue;
 }
+
+hipError_t launch_fwd_bf16(const LaunchArgs& a) { return launch_fwd_type<Bf16>(a); }
+hipError_t launch_fwd_f16(const LaunchArgs& a) { return launch_fwd_type<F16>(a); }
 
 }  // namespace attn

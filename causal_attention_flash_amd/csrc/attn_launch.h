@@ -39,15 +39,23 @@ hipError_t launch_bwd_dkdv_bf16(const LaunchArgs& a);
 hipError_t launch_bwd_dq_bf16(const LaunchArgs& a);
 // dQ pass that also forms delta from O and dO and writes it to a.delta
 hipError_t launch_bwd_dq_delta_bf16(const LaunchArgs& a);
-// dK, dV of each key/value head = sum of its query heads' fp32 partials (bf16 out)
+// dK, dV of each key/value head = sum of its query heads' fp32 partials (16-bit out)
 hipError_t launch_group_sum_bf16(const LaunchArgs& a);
+
+// The same kernels for fp16 tensors.
+hipError_t launch_fwd_f16(const LaunchArgs& a);
+hipError_t launch_bwd_dkdv_f16(const LaunchArgs& a);
+hipError_t launch_bwd_dq_f16(const LaunchArgs& a);
+hipError_t launch_bwd_dq_delta_f16(const LaunchArgs& a);
+hipError_t launch_group_sum_f16(const LaunchArgs& a);
 
 hipError_t launch_fwd_f32(const LaunchArgs& a);
 hipError_t launch_bwd_dkdv_f32(const LaunchArgs& a);
 hipError_t launch_bwd_dq_f32(const LaunchArgs& a);
 hipError_t launch_bwd_dq_delta_f32(const LaunchArgs& a);
 
-// delta = rowsum(dO o O) for either element type (elem_bytes 2 = bf16, 4 = f32).
-hipError_t launch_bwd_preprocess(const LaunchArgs& a, int elem_bytes);
+// delta = rowsum(dO o O) for any element type (0 = f32, 1 = bf16, 2 = f16: the
+// attn_dtype codes).
+hipError_t launch_bwd_preprocess(const LaunchArgs& a, int dtype);
 
 }  // namespace attn

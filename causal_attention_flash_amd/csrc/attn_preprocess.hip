@@ -3,7 +3,7 @@
 // Forge RESEARCH.md §6, the "D term" paragraph: rowsum(dP o P) equals dO_i . O_i
 // exactly, so it is computed once per row outside the two main backward kernels
 // instead of per (query, key) pair (the hoist the page measures at 3.1x on a
-// training step).  O here is the forward output as stored (bf16 or fp32).
+// training step).  O here is the forward output as stored (fp32, bf16 or fp16).
 //
 // Memory-bound: each lane reads 16 bytes of O and of dO per row slice.  A row
 // gets G lanes, the power of two at or above its D*elem/16 slices (lanes past
@@ -16,9 +16,10 @@ namespace attn {
 
 constexpr int pow2_at_least(int x) { return x <= 1 ? 1 : 2 * pow2_at_least((x + 1) / 2); }
 
-template <int ELEM_BYTES, int D>
+template <int DT, int D>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const void* __restrict__ O, const void* __restrict__ dO,
                                                              float* __restrict__ delta, int64_t rows) {
+    constexpr int ELEM_BYTES = DT == 0 ? 4 : 2;  // attn_dtype: 0 f32, 1 bf16, 2 f16
     constexpr int SL = D * ELEM_BYTES / 16;  // 16-byte slices per row (8 .. 32)
     constexpr int G = pow2_at_least(SL);     // lanes per row
     constexpr int RPB = 256 / G;             // rows per block
@@ -30,11 +31,17 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const void* __restr
         const size_t off = (size_t)row * D * ELEM_BYTES + (size_t)part * 16;
         const u32x4 a = ldg16((const char*)O + off);
         const u32x4 b = ldg16((const char*)dO + off);
-        if (ELEM_BYTES == 2) {
+        if constexpr (DT == 1) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                acc = fmaf(bf16_lo(a[e]), bf16_lo(b[e]), acc);
-                acc = fmaf(bf16_hi(a[e]), bf16_hi(b[e]), acc);
+                acc = fmaf(Bf16::lo(a[e]), Bf16::lo(b[e]), acc);
+                acc = fmaf(Bf16::hi(a[e]), Bf16::hi(b[e]), acc);
+            }
+        } else if constexpr (DT == 2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc = fmaf(F16::lo(a[e]), F16::lo(b[e]), acc);
+                acc = fmaf(F16::hi(a[e]), F16::hi(b[e]), acc);
             }
         } else {
 #pragma unroll
@@ -46,26 +53,30 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const void* __restr
     if (row < rows && part == 0) delta[row] = acc;
 }
 
-template <int ELEM_BYTES, int D>
+template <int DT, int D>
 static hipError_t launch_pre(const LaunchArgs& a) {
-    constexpr int RPB = 256 / pow2_at_least(D * ELEM_BYTES / 16);
+    constexpr int RPB = 256 / pow2_at_least(D * (DT == 0 ? 4 : 2) / 16);
     const int64_t rows = a.BH * a.S;
     const int64_t blocks = (rows + RPB - 1) / RPB;
     if (blocks > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_preprocess_kernel<ELEM_BYTES, D>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL((bwd_preprocess_kernel<DT, D>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
                        a.o_in, a.dout, a.delta, rows);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_preprocess(const LaunchArgs& a, int elem_bytes) {
-    if (elem_bytes == 2 && a.D == 64) return launch_pre<2, 64>(a);
-    if (elem_bytes == 2 && a.D == 80) return launch_pre<2, 80>(a);
-    if (elem_bytes == 2 && a.D == 96) return launch_pre<2, 96>(a);
-    if (elem_bytes == 2 && a.D == 128) return launch_pre<2, 128>(a);
-    if (elem_bytes == 4 && a.D == 64) return launch_pre<4, 64>(a);
-    if (elem_bytes == 4 && a.D == 80) return launch_pre<4, 80>(a);
-    if (elem_bytes == 4 && a.D == 96) return launch_pre<4, 96>(a);
-    if (elem_bytes == 4 && a.D == 128) return launch_pre<4, 128>(a);
+template <int DT>
+static hipError_t launch_pre_type(const LaunchArgs& a) {
+    if (a.D == 64) return launch_pre<DT, 64>(a);
+    if (a.D == 80) return launch_pre<DT, 80>(a);
+    if (a.D == 96) return launch_pre<DT, 96>(a);
+    if (a.D == 128) return launch_pre<DT, 128>(a);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_preprocess(const LaunchArgs& a, int dtype) {
+    if (dtype == 0) return launch_pre_type<0>(a);
+    if (dtype == 1) return launch_pre_type<1>(a);
+    if (dtype == 2) return launch_pre_type<2>(a);
     return hipErrorInvalidValue;
 }
 

@@ -30,14 +30,19 @@
  *
  * Layout: Q, K, V, O, dO, dQ, dK, dV are contiguous [B, H, S, D] (D innermost);
  * LSE and delta are contiguous [B, H, S] fp32.  Tensor element type is `dtype`
- * (ATTN_F32: float, ATTN_BF16: bfloat16 bit patterns); accumulation and all
+ * (ATTN_F32: float, ATTN_BF16: bfloat16 bit patterns, ATTN_F16: IEEE binary16
+ * bit patterns); accumulation and all
  * softmax statistics are fp32 whatever the input type.  Outputs are written in
  * the input type, rounded to nearest even.
  *
  * Supported set: D in {64, 80, 96, 128} (the head dimensions of GPT-style
  * models; Forge RESEARCH.md §6 "Fused attention design" lists 64, 80 and 128 as
  * the tuned set and its pitfalls section compares backward variants up to
- * D = 96); dtype in {ATTN_F32, ATTN_BF16}; causal in {0, 1}; finite scale; any S >= 1 (no tile-multiple requirement); B*H*S*D < 2^62 and
+ * D = 96); dtype in {ATTN_F32, ATTN_BF16, ATTN_F16} (fp16 operands with fp32
+ * accumulation and statistics are the form of the assembled kernel in §9 of
+ * "Cooperative tensors, reductions, and building a fused attention kernel", and
+ * the Forge paper measures its matmul2d with half operands); causal in {0, 1};
+ * finite scale; any S >= 1 (no tile-multiple requirement); B*H*S*D < 2^62 and
  * S*D < 2^31.  B, H or S equal to 0 is an empty problem: ATTN_OK, nothing
  * enqueued, pointers not read.
  *
@@ -62,7 +67,8 @@ extern "C" {
 
 typedef enum attn_dtype {
     ATTN_F32 = 0,  /* float32 tensors */
-    ATTN_BF16 = 1  /* bfloat16 tensors (uint16 bit patterns) */
+    ATTN_BF16 = 1, /* bfloat16 tensors (uint16 bit patterns) */
+    ATTN_F16 = 2   /* IEEE fp16 tensors (uint16 bit patterns) */
 } attn_dtype;
 
 typedef enum attn_status {
@@ -135,14 +141,14 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
 /*
  * Backward pass with grouped key/value heads: dQ as attn_bwd; dK and dV of each
  * key/value head are the sums over the G query heads that read it (the chain
- * rule through the shared input).  bf16 with G > 1: the dK/dV pass runs per query
+ * rule through the shared input).  bf16 or fp16 with G > 1: the dK/dV pass runs per query
  * head and leaves fp32 partials in the workspace, and a group-sum pass adds them
  * (no atomics; deterministic).  q, o, dout, dq: [B,H,S,D]; k, v, dk, dv:
  * [B,H_kv,S,D]; lse: [B,H,S]; workspace: attn_bwd_gqa_workspace_bytes() bytes.
  * attn_bwd is this call with H_kv = H.  Source: Forge RESEARCH.md §6 ("GQA").
  */
 /*
- * Bytes of device workspace attn_bwd_gqa needs: B*H*S*4 (delta), plus, for bf16
+ * Bytes of device workspace attn_bwd_gqa needs: B*H*S*4 (delta), plus, for bf16 or fp16
  * with H_kv < H, 2*B*H*S*D*4 (the per-query-head fp32 dK and dV), each region
  * rounded up to 256 bytes.  Returns 0 for an empty or invalid problem.
  */

@@ -2,7 +2,7 @@
 
 This module is shared by the oracle side and the GPU side of every test and of the
 bench.  It holds no attention arithmetic, only random draws and the float32 ->
-bfloat16 rounding that turns a draw into a bf16 tensor.
+bfloat16 / float16 roundings that turn a draw into a 16-bit tensor.
 
 Draw recipe (one recipe for every workload):
 
@@ -11,7 +11,9 @@ Draw recipe (one recipe for every workload):
   [B, H, S, D], K and V of shape [B, H_kv, S, D] (H_kv = H unless the workload
   groups its key/value heads);
 * each draw multiplied by its standard deviation in float32;
-* for bf16 workloads, every value rounded to the nearest bfloat16, ties to even.
+* for bf16 workloads, every value rounded to the nearest bfloat16, ties to even;
+  for f16 workloads, to the nearest IEEE binary16 (the standard float32 ->
+  float16 conversion, ties to even, overflow to infinity).
 
 The returned arrays are float32 holding exactly the values the GPU consumes, so
 the oracle and the GPU path read identical numbers.
@@ -27,10 +29,13 @@ __all__ = [
     "Workload",
     "WORKLOADS",
     "GQA_WORKLOADS",
+    "F16_WORKLOADS",
     "make_inputs",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
     "round_to_bf16",
+    "f32_to_f16_bits",
+    "f16_bits_to_f32",
 ]
 
 
@@ -43,7 +48,7 @@ class Workload:
     H: int
     S: int
     D: int
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "f16"
     sigma_qk: float = 1.0
     sigma_v: float = 1.0
     sigma_do: float = 1.0
@@ -94,6 +99,13 @@ GQA_WORKLOADS = {
     "gqa8_d128_bf16": Workload("gqa8_d128_bf16", 1, 32, 4096, 128, "bf16", 1.0, 1.0, 0.1, Hkv=8),
 }
 
+# fp16 inputs: the headline shape and the long-sequence stress shape with the
+# same draws, rounded to IEEE binary16 instead of bfloat16.
+F16_WORKLOADS = {
+    "gpt205m_f16": Workload("gpt205m_f16", 4, 16, 2048, 64, "f16", 1.0, 1.0, 0.1),
+    "long8191_f16": Workload("long8191_f16", 1, 16, 8191, 128, "f16", 4.0, 1.0, 0.1),
+}
+
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (nearest, ties to even); return the uint16 bit patterns.
@@ -123,12 +135,27 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     return bf16_bits_to_f32(f32_to_bf16_bits(x))
 
 
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE binary16 (nearest, ties to even); return the uint16 bit patterns.
+
+    Values beyond the binary16 range round to infinity (IEEE overflow).
+    """
+    with np.errstate(over="ignore"):
+        return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen binary16 bit patterns to float32 (exact)."""
+    return np.ascontiguousarray(b, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
 def make_inputs(w: Workload, seed: int = 0) -> dict:
     """Draw Q, K, V, dO for workload ``w`` from ``PCG64(seed)``.
 
     Returns a dict with float32 arrays ``q, k, v, do`` (q and do [B, H, S, D], k and
-    v [B, H_kv, S, D]; bf16-exact for bf16 workloads) and, for bf16 workloads,
-    their uint16 bit patterns under ``q_bits, k_bits, v_bits, do_bits``.
+    v [B, H_kv, S, D]; exact in the workload's 16-bit type for bf16 and f16
+    workloads) and, for those, their uint16 bit patterns under ``q_bits, k_bits,
+    v_bits, do_bits``.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     qshape = (w.B, w.H, w.S, w.D)
@@ -141,6 +168,10 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
             bits = f32_to_bf16_bits(x)
             out[name + "_bits"] = bits
             x = bf16_bits_to_f32(bits)
+        elif w.dtype == "f16":
+            bits = f32_to_f16_bits(x)
+            out[name + "_bits"] = bits
+            x = f16_bits_to_f32(bits)
         elif w.dtype != "f32":
             raise ValueError(f"unknown dtype {w.dtype!r}")
         out[name] = x

@@ -2,6 +2,12 @@
 
 Tolerances (written here, applied per output tensor):
 * bf16 inputs: max |gpu - oracle| <= 2e-2 for O, LSE, dQ, dK, dV;
+* fp16 inputs: max |gpu - oracle| <= 5e-3 for the same outputs.  Derivation: the
+  error terms are the 16-bit roundings of the outputs, of P and dS before the
+  MFMAs and of O where delta is formed; binary16 carries 3 more fraction bits
+  than bfloat16, so each shrinks by 2^-3 against the bf16 case (2e-2 -> 2.5e-3),
+  and the output rounding alone reaches 2^-9 ~ 2e-3 for |x| in [4, 8), which
+  the long workload's O attains; 5e-3 covers both with a factor of ~2;
 * fp32 inputs: max |gpu - oracle| / max |oracle| <= 1e-4 per tensor (the relative
   error is taken against the tensor's largest magnitude because dQ's first row
   is exactly zero, where an elementwise relative error is undefined); a tensor
@@ -10,6 +16,7 @@ Tolerances (written here, applied per output tensor):
 import numpy as np
 
 BF16_ABS_TOL = 2e-2
+F16_ABS_TOL = 5e-3
 F32_REL_TOL = 1e-4
 OUTPUTS = ("o", "lse", "dq", "dk", "dv")
 
@@ -31,9 +38,9 @@ def require_gpu():
 
 def to_device(x: dict, name: str, dtype: str, device):
     torch = torch_mod()
-    if dtype == "bf16":
+    if dtype in ("bf16", "f16"):
         bits = np.ascontiguousarray(x[name + "_bits"]).view(np.int16)
-        return torch.from_numpy(bits).to(device).view(torch.bfloat16)
+        return torch.from_numpy(bits).to(device).view(torch.bfloat16 if dtype == "bf16" else torch.float16)
     return torch.from_numpy(np.ascontiguousarray(x[name], dtype=np.float32)).to(device)
 
 
@@ -72,9 +79,10 @@ def check(errs: dict, dtype: str, label: str = ""):
     lines = []
     bad = []
     for n, (e, mref) in errs.items():
-        if dtype == "bf16":
-            ok = e <= BF16_ABS_TOL
-            lines.append(f"{n}: max|err| {e:.3e} (tol {BF16_ABS_TOL}) max|ref| {mref:.3g}")
+        if dtype in ("bf16", "f16"):
+            tol = BF16_ABS_TOL if dtype == "bf16" else F16_ABS_TOL
+            ok = e <= tol
+            lines.append(f"{n}: max|err| {e:.3e} (tol {tol}) max|ref| {mref:.3g}")
         else:
             # an identically zero reference (e.g. dQ, dK at S = 1) has no relative
             # error; there the bound is absolute, on the unit scale of the inputs

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
 
 OK, NULL, SHAPE, UNSUP, ALIGN, WS, HIP, ALIAS = range(8)
-BF16, F32 = bd.ATTN_BF16, bd.ATTN_F32
+BF16, F32, F16 = bd.ATTN_BF16, bd.ATTN_F32, bd.ATTN_F16
 
 # distinct, 16-byte aligned, far apart fake device addresses
 P = [0x10_0000_0000 * (i + 1) for i in range(12)]
@@ -86,7 +86,7 @@ def bwd(**kw):
     (dict(B=1 << 20, H=1 << 11, S=1), SHAPE),          # B*H*S = 2^31
     (dict(B=1, H=1, S=1 << 25, D=64), SHAPE),           # S*D = 2^31
     (dict(D=112), UNSUP), (dict(D=48), UNSUP), (dict(D=32), UNSUP), (dict(D=256), UNSUP),
-    (dict(dtype=2), UNSUP), (dict(dtype=-1), UNSUP),
+    (dict(dtype=3), UNSUP), (dict(dtype=-1), UNSUP),
     (dict(causal=2), UNSUP), (dict(causal=-1), UNSUP),
     (dict(scale=0.0), UNSUP), (dict(scale=-0.5), UNSUP), (dict(scale=float("nan")), UNSUP),
     (dict(scale=float("inf")), UNSUP),
@@ -136,6 +136,8 @@ def test_workspace_bytes(lib):
     assert bd.c_attn_bwd_workspace_bytes(1, 4, 128, 64, F32) == 4 * 128 * 4
     assert bd.c_attn_bwd_workspace_bytes(0, 3, 100, 64, BF16) == 0
     assert bd.c_attn_bwd_workspace_bytes(2, 3, 100, 80, BF16) == 2 * 3 * 100 * 4
+    assert bd.c_attn_bwd_workspace_bytes(2, 3, 100, 64, F16) == 2 * 3 * 100 * 4
+    assert bd.c_attn_bwd_workspace_bytes(2, 3, 100, 64, 3) == 0
     assert bd.c_attn_bwd_workspace_bytes(2, 3, 100, 112, BF16) == 0
     assert bd.c_attn_bwd_workspace_bytes(2, 3, -1, 64, BF16) == 0
 

@@ -47,6 +47,41 @@ def test_bf16_matches_torch_conversion():
     np.testing.assert_array_equal(ours, theirs)
 
 
+def test_f16_round_to_nearest_even_ties():
+    # binary16 has 10 fraction bits: 1 + 2^-11 is halfway between 1 and 1 + 2^-10
+    # and goes to the even neighbour 1; 1 + 3*2^-11 lies between 1 + 2^-10 (odd)
+    # and 1 + 2^-9 (even) and goes to 1 + 2^-9; 65520 is the tie between 65504 and
+    # the next step (65536, beyond the range) and overflows to infinity.
+    x = np.array([1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, -(1.0 + 2.0 ** -11),
+                  1.0 + 2.0 ** -11 + 2.0 ** -20, 65504.0, 65519.0, 65520.0, 2.0 ** -24, 2.0 ** -26],
+                 dtype=np.float32)
+    r = si.f16_bits_to_f32(si.f32_to_f16_bits(x))
+    assert r[0] == 1.0
+    assert r[1] == 1.0 + 2.0 ** -9
+    assert r[2] == -1.0
+    assert r[3] == 1.0 + 2.0 ** -10
+    assert r[4] == 65504.0 and r[5] == 65504.0
+    assert r[6] == np.inf
+    assert r[7] == 2.0 ** -24            # smallest subnormal, exact
+    assert r[8] == 0.0                   # a quarter of it rounds to zero
+    # bit patterns of a few exact values
+    np.testing.assert_array_equal(si.f32_to_f16_bits(np.array([1.0, -2.0, 0.5], np.float32)),
+                                  np.array([0x3C00, 0xC000, 0x3800], np.uint16))
+
+
+def test_values_are_f16_exact_and_scaled():
+    w = si.WORKLOADS["long8191_bf16"].with_shape(S=512, dtype="f16")
+    x = si.make_inputs(w, seed=0)
+    for n, sigma in (("q", 4.0), ("k", 4.0), ("v", 1.0), ("do", 0.1)):
+        np.testing.assert_array_equal(si.f16_bits_to_f32(si.f32_to_f16_bits(x[n])), x[n])
+        np.testing.assert_array_equal(si.f32_to_f16_bits(x[n]), x[n + "_bits"])
+        assert abs(x[n].std() / sigma - 1.0) < 0.01
+    # the same draw as the bf16 workload before rounding: values agree to bf16 precision
+    xb = si.make_inputs(w.with_shape(dtype="bf16"), seed=0)
+    # (binary16 subnormals below 2^-14 hold absolute, not relative, precision)
+    np.testing.assert_allclose(x["q"], xb["q"], rtol=2 ** -8, atol=2 ** -24)
+
+
 def test_values_are_bf16_exact_and_scaled():
     w = si.WORKLOADS["long8191_bf16"].with_shape(S=512)
     x = si.make_inputs(w, seed=0)
