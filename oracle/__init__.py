@@ -7,6 +7,8 @@ from .attention import (  # noqa: F401
     attention_backward,
     attention_forward,
     attention_head,
+    decode,
+    decode_head,
     gqa_backward,
     gqa_forward,
     head_backward,

@@ -39,6 +39,14 @@ query head is then plain attention on its key/value head, and because a
 key/value head feeds G query heads, its dK and dV are the sums of the G heads'
 contributions (the chain rule through the shared input).
 
+Decode (one new query row per head against a key/value cache): the query is the
+newest position, appended after its own key and value, so under the causal rule
+it sees every cached row; it is plain attention of one row over the first n
+cache rows (Forge RESEARCH.md §6, the decode path of "forge generate": one query
+row against a long cache).  With per-sequence cache lengths, batch entry b uses
+its first kv_lens[b] rows; a length of 0 leaves no visible key, and the result
+is o = 0, LSE = -inf (the convention of a row whose exponential sum is 0).
+
 Parity status: pinned.  Each function here is checked in tests/test_oracle_pins.py
 against closed forms, invariants, central finite differences, torch's float64
 scaled_dot_product_attention on tiny shapes (with enable_gqa for the grouped
@@ -57,6 +65,8 @@ __all__ = [
     "attention_head",
     "gqa_forward",
     "gqa_backward",
+    "decode_head",
+    "decode",
 ]
 
 
@@ -179,3 +189,36 @@ def gqa_backward(q, k, v, do, scale: float, causal: bool = True):
         dk[b, h // G] += dk_h
         dv[b, h // G] += dv_h
     return dq, dk, dv
+
+
+def decode_head(q, k, v, scale: float):
+    """One query row q [D] against cache rows k [n, D], v [n, Dv], all visible ->
+    (o [Dv], lse), float64.  n = 0 gives (zeros, -inf)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if k.shape[0] == 0:
+        return np.zeros(v.shape[1], dtype=np.float64), -np.inf
+    s = scale * (k @ q)
+    m = s.max()
+    lse = m + np.log(np.exp(s - m).sum())
+    p = np.exp(s - lse)
+    return p @ v, lse
+
+
+def decode(q, k, v, scale: float, kv_lens=None):
+    """q [B, H, D]; k, v [B, H_kv, L, D] caches; kv_lens [B] rows in use (None = L)
+    -> (o [B, H, D], lse [B, H]), float64.  Query head h reads cache head
+    h // (H / H_kv); batch entry b reads its first kv_lens[b] rows."""
+    B, H, _ = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    if Hkv < 1 or H % Hkv != 0 or k.shape[0] != B:
+        raise ValueError(f"query heads {H} must be a multiple of key/value heads {Hkv}")
+    G = H // Hkv
+    o = np.empty((B, H, v.shape[3]), dtype=np.float64)
+    lse = np.empty((B, H), dtype=np.float64)
+    for b in range(B):
+        n = L if kv_lens is None else int(kv_lens[b])
+        for h in range(H):
+            o[b, h], lse[b, h] = decode_head(q[b, h], k[b, h // G, :n], v[b, h // G, :n], scale)
+    return o, lse

@@ -28,8 +28,8 @@ import os
 import numpy as np
 import pytest
 
-from oracle import (attention_backward, attention_forward, attention_head, gqa_backward, gqa_forward, head_backward,
-                    head_forward)
+from oracle import (attention_backward, attention_forward, attention_head, decode, decode_head, gqa_backward,
+                    gqa_forward, head_backward, head_forward)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -387,3 +387,82 @@ def test_gqa_rejects_non_divisible_heads():
     k = np.zeros((1, 2, 3, 2))
     with pytest.raises(ValueError):
         gqa_forward(q, k, k, 1.0)
+
+
+# ------------------------------------------------------------------- decode
+
+
+def test_decode_is_last_row_of_causal_attention():
+    """The newest position under the causal rule sees every cached key: decode of
+    q_{n-1} over rows 0..n-1 is the last row of the (independently pinned) causal
+    forward on the same sequence."""
+    rng = np.random.default_rng(400)
+    for n, D in ((1, 8), (5, 4), (40, 16)):
+        q, k, v = (_rand(rng, n, D) for _ in range(3))
+        scale = 1.0 / np.sqrt(D)
+        o_full, lse_full = head_forward(q, k, v, scale, True)
+        o, lse = decode_head(q[-1], k, v, scale)
+        np.testing.assert_allclose(o, o_full[-1], rtol=1e-13, atol=1e-14)
+        assert abs(lse - lse_full[-1]) < 1e-13
+
+
+def test_decode_closed_forms():
+    rng = np.random.default_rng(401)
+    D = 8
+    q, k0, v0 = _rand(rng, D), _rand(rng, D), _rand(rng, D)
+    # one cached row: o = v_0, lse = scale q.k_0
+    o, lse = decode_head(q, k0[None], v0[None], 0.5)
+    np.testing.assert_array_equal(o, v0)
+    assert lse == pytest.approx(0.5 * q @ k0, abs=1e-15)
+    # identical keys: uniform weights, o = mean of the values, lse = s + ln n
+    n = 7
+    vals = _rand(rng, n, D)
+    o, lse = decode_head(q, np.repeat(k0[None], n, axis=0), vals, 0.5)
+    np.testing.assert_allclose(o, vals.mean(axis=0), rtol=1e-14, atol=1e-15)
+    assert lse == pytest.approx(0.5 * q @ k0 + np.log(n), abs=1e-14)
+    # no cached row: o = 0, lse = -inf
+    o, lse = decode_head(q, np.zeros((0, D)), np.zeros((0, D)), 0.5)
+    np.testing.assert_array_equal(o, np.zeros(D))
+    assert lse == -np.inf
+
+
+def test_decode_ignores_cache_order_and_rows_past_length():
+    """No position dependence among visible rows (a consistent permutation of keys
+    and values changes nothing), and rows at or past a sequence's length are never
+    read (NaN there leaves the result finite and unchanged)."""
+    rng = np.random.default_rng(402)
+    B, H, Hkv, L, D = 3, 4, 2, 12, 8
+    q = _rand(rng, B, H, D)
+    k, v = _rand(rng, B, Hkv, L, D), _rand(rng, B, Hkv, L, D)
+    lens = np.array([12, 5, 1])
+    o, lse = decode(q, k, v, 0.3, lens)
+    perm = rng.permutation(5)
+    k2, v2 = k.copy(), v.copy()
+    k2[1, :, :5], v2[1, :, :5] = k[1][:, perm], v[1][:, perm]
+    k2[1, :, 5:], v2[1, :, 5:] = np.nan, np.nan
+    k2[2, :, 1:], v2[2, :, 1:] = np.nan, np.nan
+    o2, lse2 = decode(q, k2, v2, 0.3, lens)
+    np.testing.assert_allclose(o2, o, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-13, atol=1e-14)
+    # batch entry 2 with one row: its query heads return that row's values
+    np.testing.assert_array_equal(o[2, 0], v[2, 0, 0])
+    np.testing.assert_array_equal(o[2, 3], v[2, 1, 0])
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (6, 1), (4, 4)])
+def test_decode_against_torch_sdpa_float64(H, Hkv):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(403 + H * Hkv)
+    B, L, D = 2, 11, 8
+    scale = 1.0 / np.sqrt(D)
+    q = _rand(rng, B, H, D)
+    k, v = _rand(rng, B, Hkv, L, D), _rand(rng, B, Hkv, L, D)
+    tq = torch.tensor(q[:, :, None, :])
+    to = torch.nn.functional.scaled_dot_product_attention(tq, torch.tensor(k), torch.tensor(v), scale=scale,
+                                                          enable_gqa=True)
+    o, lse = decode(q, k, v, scale)
+    np.testing.assert_allclose(o, to[:, :, 0].numpy(), rtol=1e-12, atol=1e-13)
+    G = H // Hkv
+    kr = torch.tensor(k).repeat_interleave(G, dim=1)
+    ref_lse = torch.logsumexp(scale * (tq @ kr.transpose(-1, -2))[:, :, 0], dim=-1).numpy()
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-13, atol=1e-13)
