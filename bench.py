@@ -39,7 +39,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gpt205m_bf16",
-                    choices=sorted(si.WORKLOADS) + sorted(si.GQA_WORKLOADS) + sorted(si.F16_WORKLOADS),
+                    choices=sorted(si.WORKLOADS) + sorted(si.GQA_WORKLOADS) + sorted(si.F16_WORKLOADS)
+                    + sorted(si.DECODE_WORKLOADS),
                     help="grouped key/value head workloads run attn_fwd_gqa / attn_bwd_gqa")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -120,6 +121,115 @@ def cpu_baseline(w, x, target_s: float):
     }
 
 
+def decode_bench(args, dev):
+    """One decode step per iteration (attn_decode: the split pass and, for several
+    chunks, the merge pass) over a resident cache; value = algorithmic HBM bytes
+    per second: each sequence's cache rows in use (K and V), plus q, O and LSE."""
+    import torch
+
+    import causal_attention_flash_amd as caf
+
+    w = si.DECODE_WORKLOADS[args.workload]
+    x = si.make_decode_inputs(w, seed=0)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
+
+    def dev_t(name):
+        if w.dtype == "f32":
+            return torch.from_numpy(x[name]).to(dev)
+        return torch.from_numpy(x[name + "_bits"].view(np.int16)).to(dev).view(tdt)
+
+    q, k, v = (dev_t(n) for n in ("q", "k", "v"))
+    lens = x["kv_lens"] if x["kv_lens"] is not None else np.full(w.B, w.L, np.int32)
+    kl = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    dt = {"bf16": caf.ATTN_BF16, "f16": caf.ATTN_F16, "f32": caf.ATTN_F32}[w.dtype]
+    bd = caf._binding
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+    nws = bd.c_attn_decode_workspace_bytes(w.B, w.H, w.Hkv, w.L, w.D, dt)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def step():
+        st = bd.c_attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), kl.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                              ws.data_ptr(), nws, w.B, w.H, w.Hkv, w.L, w.D, w.scale, dt, stream)
+        if st != 0:
+            raise caf.AttnError(st, "decode")
+
+    elem = q.element_size()
+    nbytes = float(lens.sum()) * w.Hkv * w.D * elem * 2 + 2 * w.B * w.H * w.D * elem + w.B * w.H * 4
+    if args.profile_steps:
+        for _ in range(args.profile_steps):
+            step()
+        torch.cuda.synchronize()
+        print(f"profile run: {args.profile_steps} steps of {w.name}", flush=True)
+        return
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    # per-call durations (events around each call on the launch stream)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record()
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    durs = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    mean_ms = sum(durs) / len(durs)
+    value = nbytes * args.steps / (gpu_ms * 1e-3) / 1e9
+    achieved = nbytes / (mean_ms * 1e-3) / 1e9
+    result = {
+        "metric": "decode attention step, algorithmic HBM GB/s on 1 GPU",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(gpu_ms / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.Hkv, "L": w.L, "D": w.D,
+                   "kv_lens": [int(n) for n in lens], "parallelism": "none (1 GPU)"},
+        "tokens_per_s": round(w.B * args.steps / (gpu_ms * 1e-3), 1),
+        "wall_s_timed": round(wall, 4),
+        "kernel_ms": {"decode": round(mean_ms, 5)},
+        "roofline": {"kernel": "decode (split + merge passes)", "bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 5),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import decode
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        except Exception:  # pragma: no cover
+            cores = os.cpu_count() or 1
+        t0 = time.perf_counter()
+        nb = 0
+        done_bytes = 0.0
+        while nb < w.B and time.perf_counter() - t0 < args.cpu_seconds:
+            b = slice(nb, nb + 1)
+            decode(x["q"][b], x["k"][b], x["v"][b], w.scale, lens[b])
+            done_bytes += float(lens[nb]) * w.Hkv * w.D * elem * 2 + 2 * w.H * w.D * elem + w.H * 4
+            nb += 1
+        dtc = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(done_bytes / dtc / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+                                  "kind": "oracle",
+                                  "sample": f"{nb} of {w.B} sequences, fp64 decode, {dtc:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -137,6 +247,9 @@ def main():
         sys.exit(1)
     caf.load_library()
     dev = torch.device("cuda:0")
+    if args.workload in si.DECODE_WORKLOADS:
+        decode_bench(args, dev)
+        return
     w = {**si.WORKLOADS, **si.GQA_WORKLOADS, **si.F16_WORKLOADS}[args.workload]
     grouped = w.kv_heads != w.H
     x = si.make_inputs(w, seed=0)

@@ -8,6 +8,7 @@ stream; all computation runs in the library's kernels.
     dq, dk, dv = attn_bwd(q, k, v, o, do, lse, scale=None, causal=True)
     o, lse = attn_fwd_gqa(q, k, v)          # K, V with fewer (grouped) heads
     dq, dk, dv = attn_bwd_gqa(q, k, v, o, do, lse)
+    o, lse = attn_decode(q, k_cache, v_cache, kv_lens=None)  # one query row per head
 """
 from ._binding import (  # noqa: F401
     ATTN_BF16,
@@ -23,6 +24,7 @@ from ._binding import (  # noqa: F401
     attn_bwd_dq_delta,
     attn_bwd_gqa,
     attn_bwd_preprocess,
+    attn_decode,
     attn_fwd,
     attn_fwd_gqa,
     load_library,

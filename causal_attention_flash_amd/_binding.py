@@ -47,6 +47,8 @@ SIGNATURES = {
     "attn_bwd_dkdv": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _INT, _INT, _P]),
     "attn_bwd_dq": (_INT, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _INT, _INT, _P]),
     "attn_bwd_dq_delta": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _INT, _INT, _P]),
+    "attn_decode_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64, _INT]),
+    "attn_decode": (_INT, [_P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64, _I64, _I64, _I64, _F, _INT, _P]),
     "attn_status_string": (ctypes.c_char_p, [_INT]),
 }
 
@@ -128,6 +130,14 @@ def c_attn_bwd_dq(q, k, v, do, lse, delta, dq, B, H, S, D, scale, causal, dtype,
 
 def c_attn_bwd_dq_delta(q, k, v, o, do, lse, delta, dq, B, H, S, D, scale, causal, dtype, stream=0) -> int:
     return load_library().attn_bwd_dq_delta(q, k, v, o, do, lse, delta, dq, B, H, S, D, scale, causal, dtype, stream)
+
+
+def c_attn_decode_workspace_bytes(B, H, H_kv, L, D, dtype) -> int:
+    return load_library().attn_decode_workspace_bytes(B, H, H_kv, L, D, dtype)
+
+
+def c_attn_decode(q, k, v, kv_lens, o, lse, ws, ws_bytes, B, H, H_kv, L, D, scale, dtype, stream=0) -> int:
+    return load_library().attn_decode(q, k, v, kv_lens, o, lse, ws, ws_bytes, B, H, H_kv, L, D, scale, dtype, stream)
 
 
 # ------------------------------------------------------------- torch-tensor wrappers
@@ -301,3 +311,32 @@ def attn_bwd_dq_delta(q, k, v, o, do, lse, scale=None, causal=True, out=None, de
           do.data_ptr(), lse.data_ptr(), delta.data_ptr(), dq.data_ptr(), B, H, S, D, _scale(scale, D),
           int(bool(causal)), _dtype_code(q), _stream(q.device))
     return dq, delta
+
+
+def attn_decode(q, k_cache, v_cache, kv_lens=None, scale=None):
+    """O, LSE = attn_decode(q [B,H,D], k_cache, v_cache [B,H_kv,L,D], kv_lens int32 [B] or None).
+
+    One new query row per (batch entry, query head) against its cache; sequence b
+    uses its first kv_lens[b] cache rows (all L when kv_lens is None).
+    """
+    torch = _torch()
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, H, D] and the caches [B, H_kv, L, D]")
+    B, H, D = q.shape
+    Hkv, L = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Hkv, L, D) or Hkv < 1 or H % Hkv != 0:
+        raise ValueError(f"k_cache has shape {tuple(k_cache.shape)}; expected [B, H_kv, L, D] with H_kv dividing {H}")
+    _check_tensors((("q", q),), q.shape, q.dtype, q.device)
+    _check_tensors((("k_cache", k_cache), ("v_cache", v_cache)), k_cache.shape, q.dtype, q.device)
+    lens_ptr = 0
+    if kv_lens is not None:
+        _check_tensors((("kv_lens", kv_lens),), (B,), torch.int32, q.device)
+        lens_ptr = kv_lens.data_ptr()
+    dt = _dtype_code(q)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    nws = c_attn_decode_workspace_bytes(B, H, Hkv, L, D, dt)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=q.device)
+    _call(c_attn_decode, "attn_decode", q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), lens_ptr, o.data_ptr(),
+          lse.data_ptr(), ws.data_ptr(), ws.numel(), B, H, Hkv, L, D, _scale(scale, D), dt, _stream(q.device))
+    return o, lse

@@ -350,6 +350,56 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void
     return partials ? run_group_sum(a, dtype) : ATTN_OK;
 }
 
+// Decode shapes: B, H >= 0; H_kv >= 1 dividing H; L >= 1; B*H*L and L*D below
+// 2^31 (B or H = 0 is an empty problem).
+attn_status check_decode(int64_t B, int64_t H, int64_t H_kv, int64_t L, int64_t D, int dtype, bool* empty) {
+    attn_status st = check_shape(B, H, L, D, dtype, empty);
+    if (st != ATTN_OK) return st;
+    if (H_kv < 0) return ATTN_ERR_SHAPE;
+    if (*empty) return L == 0 ? ATTN_ERR_SHAPE : ATTN_OK;
+    if (H_kv < 1 || H % H_kv != 0) return ATTN_ERR_SHAPE;
+    return ATTN_OK;
+}
+
+size_t attn_decode_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t L, int64_t D, attn_dtype dtype) {
+    bool empty = false;
+    if (check_decode(B, H, H_kv, L, D, dtype, &empty) != ATTN_OK || empty) return 0;
+    return attn::decode_plan(B, H, H_kv, L, D).workspace_bytes;
+}
+
+attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_lens, void* o,
+                        float* lse, void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t H_kv,
+                        int64_t L, int64_t D, float scale, attn_dtype dtype, void* stream) {
+    bool empty = false;
+    attn_status st = check_decode(B, H, H_kv, L, D, dtype, &empty);
+    if (st == ATTN_OK) st = check_scale_causal(scale, 1);
+    if (st != ATTN_OK || empty) return st;
+    if ((st = check_ptrs({q, k_cache, v_cache, o, lse})) != ATTN_OK) return st;
+    if (kv_lens && ((uintptr_t)kv_lens & 3u) != 0) return ATTN_ERR_ALIGNMENT;
+    const size_t eb = (size_t)elem_bytes(dtype);
+    const size_t zq = (size_t)B * (size_t)H * (size_t)D * eb;
+    const size_t zkv = (size_t)B * (size_t)H_kv * (size_t)L * (size_t)D * eb;
+    const size_t zl = (size_t)B * (size_t)H * sizeof(float);
+    const size_t wsz = attn::decode_plan(B, H, H_kv, L, D).workspace_bytes;
+    if (wsz > 0) {
+        if (!workspace || workspace_bytes < wsz) return ATTN_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return ATTN_ERR_ALIGNMENT;
+    }
+    if ((st = check_alias({{o, zq}, {lse, zl}, {wsz > 0 ? workspace : nullptr, wsz}},
+                          {{q, zq}, {k_cache, zkv}, {v_cache, zkv}, {kv_lens, kv_lens ? (size_t)B * 4 : 0}})) !=
+        ATTN_OK)
+        return st;
+    LaunchArgs a = base_args(B, H, L, D, scale, 1, stream);
+    a.Hkv = H_kv;
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.kv_lens = kv_lens;
+    a.o = o;
+    a.lse = lse;
+    return from_hip(attn::launch_decode(a, (int)dtype, (float*)workspace));
+}
+
 size_t attn_bwd_gqa_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D, attn_dtype dtype) {
     bool empty = false;
     if (check_shape(B, H, S, D, dtype, &empty) != ATTN_OK || empty) return 0;

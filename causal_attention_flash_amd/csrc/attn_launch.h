@@ -24,10 +24,11 @@ struct LaunchArgs {
     void* dv = nullptr;
     float* dk_part = nullptr;  // grouped key/value heads: per-query-head fp32 dK, dV ([B,H,S,D])
     float* dv_part = nullptr;
+    const int* kv_lens = nullptr;  // decode: rows in use of each sequence's cache ([B]), or null
     int64_t BH = 0;  // batch * query heads
     int64_t H = 0;   // query heads per batch entry
     int64_t Hkv = 0; // key/value heads per batch entry (H is a multiple of Hkv)
-    int64_t S = 0;
+    int64_t S = 0;   // sequence length (decode: cache rows L)
     int64_t D = 0;
     float scale = 0.f;
     int causal = 1;
@@ -53,6 +54,17 @@ hipError_t launch_fwd_f32(const LaunchArgs& a);
 hipError_t launch_bwd_dkdv_f32(const LaunchArgs& a);
 hipError_t launch_bwd_dq_f32(const LaunchArgs& a);
 hipError_t launch_bwd_dq_delta_f32(const LaunchArgs& a);
+
+// Decode: q [B,H,D] against caches k, v [B,H_kv,L,D] (L in a.S); o [B,H,D], lse
+// [B,H].  The cache is read in nsplit chunks of `chunk` rows by workgroups that
+// each serve gt query heads of one key/value head; with nsplit > 1 the partials
+// go to a workspace of workspace_bytes and a second pass merges them.
+struct DecodePlan {
+    int gt = 1, nsplit = 1, chunk = 0;
+    size_t workspace_bytes = 0;
+};
+DecodePlan decode_plan(int64_t B, int64_t H, int64_t Hkv, int64_t L, int64_t D);
+hipError_t launch_decode(const LaunchArgs& a, int dtype, float* workspace);
 
 // delta = rowsum(dO o O) for any element type (0 = f32, 1 = bf16, 2 = f16: the
 // attn_dtype codes).

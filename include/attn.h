@@ -195,6 +195,36 @@ attn_status attn_bwd_dq_delta(const void* q, const void* k, const void* v, const
                               float scale, int causal, attn_dtype dtype, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
+/*
+ * Decode attention: one new query row per (batch entry, query head) against a
+ * key/value cache.  The query is the newest position, appended after its own key
+ * and value, so it sees every cached row of its sequence: plain attention of one
+ * row over the first n rows of the cache (Forge RESEARCH.md §6, the decode path
+ * of "forge generate": one query row, a strided walk of the cache with an online
+ * softmax, split into chunks over a long cache and merged in a second pass).
+ *   q        : device, [B,H,D] of dtype, read only.
+ *   k_cache,
+ *   v_cache  : device, [B,H_kv,L,D] of dtype, read only; query head h of batch
+ *              entry b reads cache head h / (H / H_kv) of b (grouped heads).
+ *   kv_lens  : device int32 [B], rows in use of each sequence's cache (values
+ *              are clamped to [0, L]); NULL = every sequence uses all L rows.
+ *              A sequence with 0 rows gives O = 0 and LSE = -inf.
+ *   o        : device, [B,H,D] of dtype, fully overwritten.
+ *   lse      : device, [B,H] fp32, natural-log log-sum-exp of the scaled scores.
+ *   workspace: device, attn_decode_workspace_bytes() bytes (may be NULL when
+ *              that is 0); holds the per-chunk partial results.
+ * Supported set: as attn_fwd for D, dtype and scale; H_kv >= 1 dividing H; L >= 1.
+ * Deterministic (no atomics).
+ */
+size_t attn_decode_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t L, int64_t D,
+                                   attn_dtype dtype);
+
+attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* kv_lens, void* o, float* lse,
+                        void* workspace, size_t workspace_bytes,
+                        int64_t B, int64_t H, int64_t H_kv, int64_t L, int64_t D,
+                        float scale, attn_dtype dtype, void* stream);
+
 const char* attn_status_string(attn_status status);
 
 #ifdef __cplusplus

@@ -17,6 +17,12 @@ Draw recipe (one recipe for every workload):
 
 The returned arrays are float32 holding exactly the values the GPU consumes, so
 the oracle and the GPU path read identical numbers.
+
+Decode workloads (one new query row per head against a key/value cache) draw, from
+one ``PCG64(seed)`` stream, float32 normals for q [B, H, D], then the caches K and V
+[B, H_kv, L, D], rounded like the other workloads; with ragged lengths the
+per-sequence cache lengths follow as integers uniform in [L/2, L] (numpy's
+``Generator.integers``, endpoint included).
 """
 from __future__ import annotations
 
@@ -30,6 +36,9 @@ __all__ = [
     "WORKLOADS",
     "GQA_WORKLOADS",
     "F16_WORKLOADS",
+    "DecodeWorkload",
+    "DECODE_WORKLOADS",
+    "make_decode_inputs",
     "make_inputs",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
@@ -175,4 +184,67 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
         elif w.dtype != "f32":
             raise ValueError(f"unknown dtype {w.dtype!r}")
         out[name] = x
+    return out
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """One decode step: B sequences, H query heads (one row each) over caches of up
+    to L rows of H_kv key/value heads."""
+
+    name: str
+    B: int
+    H: int
+    Hkv: int
+    L: int
+    D: int
+    dtype: str  # "f32", "bf16" or "f16"
+    ragged: bool = True
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    def with_shape(self, **kw) -> "DecodeWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+# Decode steps at the shapes of the headline model (16 heads of 64, 4K context)
+# and of a grouped-head model with head_dim 128 (32 query / 8 key/value heads, 8K
+# context); eight sequences each, with a mix of cache lengths.
+DECODE_WORKLOADS = {
+    "decode_gpt205m_bf16": DecodeWorkload("decode_gpt205m_bf16", 8, 16, 16, 4096, 64, "bf16"),
+    "decode_gqa8_d128_bf16": DecodeWorkload("decode_gqa8_d128_bf16", 8, 32, 8, 8192, 128, "bf16"),
+}
+
+
+def _round(x: np.ndarray, dtype: str):
+    """float32 draw -> (values exact in dtype as float32, uint16 bits or None)."""
+    if dtype == "bf16":
+        bits = f32_to_bf16_bits(x)
+        return bf16_bits_to_f32(bits), bits
+    if dtype == "f16":
+        bits = f32_to_f16_bits(x)
+        return f16_bits_to_f32(bits), bits
+    if dtype != "f32":
+        raise ValueError(f"unknown dtype {dtype!r}")
+    return x, None
+
+
+def make_decode_inputs(w: DecodeWorkload, seed: int = 0) -> dict:
+    """Draw q, k, v (and kv_lens when ragged) for decode workload ``w``.
+
+    Returns float32 arrays ``q`` [B, H, D], ``k`` and ``v`` [B, H_kv, L, D] (exact in
+    the workload's type; uint16 bit patterns under ``*_bits`` for 16-bit types) and
+    ``kv_lens`` (int32 [B], or None when every sequence uses all L rows).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {}
+    for name, shape in (("q", (w.B, w.H, w.D)), ("k", (w.B, w.Hkv, w.L, w.D)), ("v", (w.B, w.Hkv, w.L, w.D))):
+        x = rng.standard_normal(size=shape, dtype=np.float32)
+        x, bits = _round(x, w.dtype)
+        out[name] = x
+        if bits is not None:
+            out[name + "_bits"] = bits
+    out["kv_lens"] = rng.integers(w.L // 2, w.L, size=w.B, endpoint=True).astype(np.int32) if w.ragged else None
     return out

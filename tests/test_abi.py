@@ -44,7 +44,8 @@ def test_header_declares_the_boundary():
     decls = _declared_functions()
     assert set(decls) == {"attn_fwd", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_preprocess",
                           "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_delta", "attn_status_string",
-                          "attn_fwd_gqa", "attn_bwd_gqa", "attn_bwd_gqa_workspace_bytes"}
+                          "attn_fwd_gqa", "attn_bwd_gqa", "attn_bwd_gqa_workspace_bytes",
+                          "attn_decode", "attn_decode_workspace_bytes"}
     for name, nargs in decls.items():
         assert len(bd.SIGNATURES[name][1]) == nargs, name
 
@@ -232,3 +233,41 @@ def test_gqa_empty_problems_are_ok(lib):
     assert fwd_gqa(B=0, Hkv=0) == OK
     assert bwd_gqa(S=0) == OK
     assert fwd_gqa(B=0, Hkv=-1) == SHAPE
+
+
+# ------------------------------------------------------------------- decode
+
+
+def dec(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], lens=P[3], o=P[4], lse=P[5], ws=P[6], ws_bytes=1 << 30,
+             B=8, H=16, Hkv=4, L=4096, D=64, scale=0.125, dtype=BF16)
+    a.update(kw)
+    return bd.c_attn_decode(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"], a["ws"], a["ws_bytes"], a["B"],
+                            a["H"], a["Hkv"], a["L"], a["D"], a["scale"], a["dtype"], 0)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=0), NULL), (dict(k=0), NULL), (dict(v=0), NULL), (dict(o=0), NULL), (dict(lse=0), NULL),
+    (dict(Hkv=3), SHAPE), (dict(Hkv=0), SHAPE), (dict(Hkv=-1), SHAPE), (dict(L=0), SHAPE), (dict(L=-1), SHAPE),
+    (dict(B=-1), SHAPE), (dict(D=72), UNSUP), (dict(dtype=3), UNSUP), (dict(scale=0.0), UNSUP),
+    (dict(q=P[0] + 8), ALIGN), (dict(lens=P[3] + 2), ALIGN), (dict(ws=P[6] + 8), ALIGN),
+    (dict(ws=0), WS), (dict(ws_bytes=16), WS),
+    (dict(o=P[1]), ALIAS), (dict(lse=P[0] + 64), ALIAS), (dict(ws=P[2] + 4096), ALIAS), (dict(o=P[3]), ALIAS),
+])
+def test_decode_validation(lib, kw, expect):
+    assert dec(**kw) == expect
+
+
+def test_decode_empty_and_workspace(lib):
+    assert dec(B=0, q=0, k=0, v=0, o=0, lse=0, ws=0, ws_bytes=0) == OK
+    assert dec(H=0, Hkv=0, ws=0, ws_bytes=0) == OK
+    assert dec(B=0, L=0) == SHAPE
+    # the workspace holds (D + 2) fp32 per query head and chunk; one chunk needs none
+    nws = bd.c_attn_decode_workspace_bytes(8, 16, 4, 4096, 64, BF16)
+    assert nws > 0 and nws % (8 * 16 * (64 + 2) * 4) == 0
+    assert bd.c_attn_decode_workspace_bytes(8, 16, 4, 200, 64, BF16) == 0
+    assert bd.c_attn_decode_workspace_bytes(8, 16, 3, 4096, 64, BF16) == 0
+    assert bd.c_attn_decode_workspace_bytes(8, 16, 4, 4096, 72, BF16) == 0
+    # with no workspace needed, a NULL workspace is accepted (the call then fails only
+    # at launch, which the fake pointers would make unsafe: stop at validation)
+    assert dec(L=200, ws=0, ws_bytes=0, q=P[0] + 8) == ALIGN
