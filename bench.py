@@ -124,7 +124,8 @@ def cpu_baseline(w, x, target_s: float):
 def decode_bench(args, dev):
     """One decode step per iteration (attn_decode: the split pass and, for several
     chunks, the merge pass) over a resident cache; value = algorithmic HBM bytes
-    per second: each sequence's cache rows in use (K and V), plus q, O and LSE."""
+    per second: each sequence's cache rows in use (K and V), plus q, O and LSE.
+    Steps rotate over copies of the cache totalling >= 1 GiB (cold MALL)."""
     import torch
 
     import causal_attention_flash_amd as caf
@@ -139,6 +140,12 @@ def decode_bench(args, dev):
         return torch.from_numpy(x[name + "_bits"].view(np.int16)).to(dev).view(tdt)
 
     q, k, v = (dev_t(n) for n in ("q", "k", "v"))
+    # Consecutive steps read different copies of the cache (as a model's layers
+    # do), at least 1 GiB in all, so no step finds its cache in the 256 MB MALL.
+    cache_bytes = 2 * k.numel() * k.element_size()
+    ncopy = max(1, -(-(1 << 30) // cache_bytes))
+    kcs = [k] + [k.clone() for _ in range(ncopy - 1)]
+    vcs = [v] + [v.clone() for _ in range(ncopy - 1)]
     lens = x["kv_lens"] if x["kv_lens"] is not None else np.full(w.B, w.L, np.int32)
     kl = torch.from_numpy(lens.astype(np.int32)).to(dev)
     dt = {"bf16": caf.ATTN_BF16, "f16": caf.ATTN_F16, "f32": caf.ATTN_F32}[w.dtype]
@@ -149,9 +156,13 @@ def decode_bench(args, dev):
     ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
 
+    it = [0]
+
     def step():
-        st = bd.c_attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), kl.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                              ws.data_ptr(), nws, w.B, w.H, w.Hkv, w.L, w.D, w.scale, dt, stream)
+        i = it[0] % ncopy
+        it[0] += 1
+        st = bd.c_attn_decode(q.data_ptr(), kcs[i].data_ptr(), vcs[i].data_ptr(), kl.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), ws.data_ptr(), nws, w.B, w.H, w.Hkv, w.L, w.D, w.scale, dt, stream)
         if st != 0:
             raise caf.AttnError(st, "decode")
 
@@ -200,7 +211,7 @@ def decode_bench(args, dev):
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.Hkv, "L": w.L, "D": w.D,
-                   "kv_lens": [int(n) for n in lens], "parallelism": "none (1 GPU)"},
+                   "kv_lens": [int(n) for n in lens], "cache_copies": ncopy, "parallelism": "none (1 GPU)"},
         "tokens_per_s": round(w.B * args.steps / (gpu_ms * 1e-3), 1),
         "wall_s_timed": round(wall, 4),
         "kernel_ms": {"decode": round(mean_ms, 5)},

@@ -87,6 +87,43 @@ __device__ __forceinline__ void merge(Run<E>& a, float m2, float l2, const float
     for (int e = 0; e < E; ++e) a.o[e] = a.o[e] * f1 + o2[e] * f2;
 }
 
+// Sum over aligned groups of DG lanes (DG a power of two <= 32), the result in
+// every lane of the group: DPP adds within rows of 16 lanes (pairs, quads, the
+// two halves of a row, the two halves of 16), then one cross-row exchange.
+template <int CTRL>
+__device__ __forceinline__ float plus_dpp(float x) {
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+template <int DG>
+__device__ __forceinline__ float group_sum(float x) {
+    if constexpr (DG >= 2) x = plus_dpp<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+    if constexpr (DG >= 4) x = plus_dpp<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (DG >= 8) x = plus_dpp<0x141>(x);  // row_half_mirror: the other quad of 8
+    if constexpr (DG >= 16) x = plus_dpp<0x140>(x); // row_mirror: the other 8 of 16
+    if constexpr (DG >= 32) x += __shfl_xor(x, 16);
+    return x;
+}
+
+// q . k over one lane's 16-byte slices (q pre-widened for fp32, packed for 16-bit)
+template <class T>
+struct SliceDot {
+    static __device__ __forceinline__ float dot(const u32x4& q, const u32x4& k) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s = T::dot2(q[i], k[i], s);
+        return s;
+    }
+};
+template <>
+struct SliceDot<float> {
+    static __device__ __forceinline__ float dot(const u32x4& q, const u32x4& k) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s = fmaf(__uint_as_float(q[i]), __uint_as_float(k[i]), s);
+        return s;
+    }
+};
+
 }  // namespace
 
 // Grid: B * H_kv * (G / GT) * nsplit workgroups, block index = ((b * H_kv + j) *
@@ -122,20 +159,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const void* __restric
     const char* Kb = (const char*)K + ((size_t)b * Hkv + j) * (size_t)L * D * EB + (size_t)part * 16;
     const char* Vb = (const char*)V + ((size_t)b * Hkv + j) * (size_t)L * D * EB + (size_t)part * 16;
 
-    // query slices, scaled into log2 units
-    float qv[GT][E];
+    // query slices as stored (the dot runs on the stored type with fp32
+    // accumulation; scale*log2(e) multiplies the dot)
+    u32x4 qs[GT];
     Run<E> run[GT];
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
         const int h = j * G + gt * GT + g;
-        u32x4 u = {0u, 0u, 0u, 0u};
-        if (act) u = ldg16((const char*)Q + ((size_t)b * H + h) * D * EB + (size_t)part * 16);
-        Chunk<T>::widen(u, qv[g]);
+        qs[g] = u32x4{0u, 0u, 0u, 0u};
+        if (act) qs[g] = ldg16((const char*)Q + ((size_t)b * H + h) * D * EB + (size_t)part * 16);
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            qv[g][e] *= c;
-            run[g].o[e] = 0.f;
-        }
+        for (int e = 0; e < E; ++e) run[g].o[e] = 0.f;
         run[g].m = -INFINITY;
         run[g].l = 0.f;
     }
@@ -157,34 +191,40 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const void* __restric
     fetch(kc, vc, r);
     while (r < k_end) {  // uniform within a lane group
         fetch(kn, vn, r + U * R);
+        // scores of the batch (rows past the chunk end: -inf, weight 0)
+        float sc[U][GT];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int key = r + u * R;
-            float kf[E], vf[E];
-            Chunk<T>::widen(kc[u], kf);
-            Chunk<T>::widen(vc[u], vf);
+            const bool valid = r + u * R < k_end;
 #pragma unroll
             for (int g = 0; g < GT; ++g) {
-                float s = 0.f;
-#pragma unroll
-                for (int e = 0; e < E; ++e) s = fmaf(qv[g][e], kf[e], s);
-#pragma unroll
-                for (int x = 1; x < DG; x <<= 1) s += __shfl_xor(s, x);
-                if (key < k_end) {
-                    Run<E>& st = run[g];
-                    if (s > st.m) {
-                        const float f = fast_exp2(st.m - s);  // 0 for the first row
-                        st.l *= f;
-#pragma unroll
-                        for (int e = 0; e < E; ++e) st.o[e] *= f;
-                        st.m = s;
-                    }
-                    const float p = fast_exp2(s - st.m);
-                    st.l += p;
-#pragma unroll
-                    for (int e = 0; e < E; ++e) st.o[e] = fmaf(p, vf[e], st.o[e]);
-                }
+                const float s = group_sum<DG>(SliceDot<T>::dot(qs[g], kc[u])) * c;
+                sc[u][g] = valid ? s : -INFINITY;
             }
+        }
+        float vf[U][E];
+#pragma unroll
+        for (int u = 0; u < U; ++u) Chunk<T>::widen(vc[u], vf[u]);
+        // one rescale per batch: the new reference is the max over the batch and
+        // the running max (finite: the batch's first row is always in range)
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+            Run<E>& st = run[g];
+            float mn = st.m;
+#pragma unroll
+            for (int u = 0; u < U; ++u) mn = fmaxf(mn, sc[u][g]);
+            const float f = fast_exp2(st.m - mn);  // 0 while the state is empty
+            st.l *= f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) st.o[e] *= f;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float p = fast_exp2(sc[u][g] - mn);
+                st.l += p;
+#pragma unroll
+                for (int e = 0; e < E; ++e) st.o[e] = fmaf(p, vf[u][e], st.o[e]);
+            }
+            st.m = mn;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
