@@ -78,19 +78,33 @@ def read_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed counter summary, if it still matches the kernel source."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
-    import hashlib
     text = open(TRAFFIC_FILE).read()
     m = re.search(rf"^{re.escape(kernel)}\s+{re.escape(workload)}\s+(\S+)\s+(\S+)\s+(\S+)\s*$", text, flags=re.M)
     if not m:
         return None
     src_hash, fetch_b, write_b = m.group(1), float(m.group(2)), float(m.group(3))
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "causal_attention_flash_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        h.update(open(os.path.join(csrc, f), "rb").read())
-    if h.hexdigest()[:16] != src_hash:
+    if kernel_sources_hash(kernel) != src_hash:
         return None
     return fetch_b + write_b
+
+
+# The sources each timed kernel is compiled from: its traffic figures stay valid
+# while these are unchanged.
+KERNEL_SOURCES = {
+    "fwd": ("attn_fwd_mfma.hip", "attn_tiles.h", "attn_device.h", "attn_launch.h"),
+    "bwd_dq": ("attn_bwd_mfma.hip", "attn_tiles.h", "attn_device.h", "attn_launch.h"),
+    "bwd_dkdv": ("attn_bwd_mfma.hip", "attn_tiles.h", "attn_device.h", "attn_launch.h"),
+}
+
+
+def kernel_sources_hash(kernel: str) -> str:
+    """sha256 (first 16 hex digits) of the kernel's source files, in the order listed."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "causal_attention_flash_amd", "csrc")
+    for f in KERNEL_SOURCES.get(kernel, ()):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def cpu_baseline(w, x, target_s: float):

@@ -299,28 +299,37 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const void* __restric
     }
 }
 
-// Second pass: one wave per (b, h) merges its nsplit partials.
+// Second pass: one wave per (b, h) merges its nsplit <= 64 partials.  Lane s
+// reads partial s's (m, l); the reference M and the total L are wave reductions;
+// the weights 2^(m_s - M) go through LDS to the lanes that own the output
+// elements, which then read the partial outputs with independent loads.
 template <class T, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_ml, void* __restrict__ O,
                                                           float* __restrict__ LSE, int nsplit) {
     constexpr int EB = 16 / Chunk<T>::E;
+    __shared__ float wgt[64];
     const size_t bh = blockIdx.x;
     const int lane = threadIdx.x;
-    const float* ml = part_ml + bh * nsplit * 2;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[2 * s]);
-    float Ls = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-        const float m = ml[2 * s];
-        Ls += m == -INFINITY ? 0.f : ml[2 * s + 1] * fast_exp2(m - M);
+    float m = -INFINITY, l = 0.f;
+    if (lane < nsplit) {
+        m = part_ml[(bh * nsplit + lane) * 2];
+        l = part_ml[(bh * nsplit + lane) * 2 + 1];
     }
+    float M = m;
+#pragma unroll
+    for (int x = 1; x < 64; x <<= 1) M = fmaxf(M, __shfl_xor(M, x));
+    const float f = m == -INFINITY ? 0.f : fast_exp2(m - M);
+    float Ls = l * f;
+#pragma unroll
+    for (int x = 1; x < 64; x <<= 1) Ls += __shfl_xor(Ls, x);
+    wgt[lane] = f;
+    __syncthreads();
+    const float* po = part_o + bh * nsplit * D;
     for (int d = lane; d < D; d += 64) {
         float od = 0.f;
-        for (int s = 0; s < nsplit; ++s) {
-            const float m = ml[2 * s];
-            if (m != -INFINITY) od = fmaf(part_o[(bh * nsplit + s) * D + d], fast_exp2(m - M), od);
-        }
+#pragma unroll 8
+        for (int sp = 0; sp < nsplit; ++sp) od = fmaf(po[(size_t)sp * D + d], wgt[sp], od);
         const float x = Ls > 0.f ? od / Ls : 0.f;
         if constexpr (EB == 4)
             reinterpret_cast<float*>(O)[bh * D + d] = x;
@@ -331,7 +340,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
 }
 
 // Chunking of the cache: at least 256 rows per chunk, enough chunks that the
-// first pass has about 1024 workgroups.
+// first pass has about 1024 workgroups, at most 64 chunks.
 DecodePlan decode_plan(int64_t B, int64_t H, int64_t Hkv, int64_t L, int64_t D) {
     const int64_t G = H / Hkv;
     const int64_t gt = G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
@@ -339,6 +348,7 @@ DecodePlan decode_plan(int64_t B, int64_t H, int64_t Hkv, int64_t L, int64_t D) 
     int64_t nsplit = (1024 + units - 1) / units;
     const int64_t max_split = (L + 255) / 256;
     if (nsplit > max_split) nsplit = max_split;
+    if (nsplit > 64) nsplit = 64;  // the merge pass reads one partial per lane
     if (nsplit < 1) nsplit = 1;
     int64_t chunk = (L + nsplit - 1) / nsplit;
     chunk = (chunk + 63) / 64 * 64;
