@@ -1,0 +1,137 @@
+// Direct global -> LDS staging of 16-bit row tiles ([rows][D], D contiguous) for
+// the gfx950 attention kernels: buffer_load_dwordx4 ... lds writes each lane's 16
+// bytes straight into LDS (at the wave's base + 16 * lane), with no register
+// round trip and no ds_write.  The loads are asynchronous: a tile is usable once
+// every wave's loads for it have drained (s_waitcnt vmcnt) and a barrier has
+// passed; the kernels count their own loads for that.
+//
+// LDS layout: row r of a tile holds RP 16-byte slots (RP = D/8 rounded up to a
+// power of two); logical 16-byte chunk c of the row sits in slot c ^ swz(r).  A
+// wave's load fills 64 consecutive slots, and each lane fetches the logical chunk
+// that belongs in its slot, so the swizzle costs nothing at load time.  Slots past
+// the row's D/8 chunks are loaded from an offset beyond the buffer range and read
+// as zero.  Rows at or beyond S also read as zero: the buffer range of a tile ends
+// at row S.
+//
+// swz(r) = 2*(r % 4) + (r / 4) % 2 makes both operand reads conflict-free (rows
+// of 128 or 256 bytes start on the same bank; a 16-byte slot covers 4 of the 32
+// four-byte banks):
+// * 16-byte row reads (8 consecutive rows, one logical chunk): swz takes 8
+//   distinct values over 8 consecutive rows, so the 8 slots are distinct;
+// * transposing reads (groups of 4 consecutive rows r..r+3, r % 4 == 0, each
+//   reading a pair of adjacent chunks 2p, 2p+1): swz / 2 = r % 4 differs across
+//   the 4 rows and swz keeps pairs together, so the 4 pairs occupy distinct slot
+//   pairs.
+#pragma once
+
+#include "attn_tiles.h"
+
+namespace attn {
+
+constexpr int pow2_up(int x) { return x <= 1 ? 1 : 2 * pow2_up((x + 1) / 2); }
+
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+// s_waitcnt vmcnt(n): at most n vector-memory operations of this wave still in
+// flight (expcnt and lgkmcnt unconstrained).  n < 64.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Barrier without the memory fence __syncthreads carries (the fence would wait
+// for every load in flight, including prefetches of later tiles).  LDS reads
+// issued before it have been consumed by the time a wave reaches it.
+__device__ __forceinline__ void bare_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int ROWS, int D, int NW>
+struct DTile {
+    static constexpr int CPR = D / 8;              // logical 16-byte chunks per row
+    static constexpr int RP = pow2_up(CPR);        // slots per LDS row
+    static constexpr int RS = RP * 8;              // LDS row stride (elements)
+    static constexpr int ELEMS = ROWS * RS;        // LDS footprint (elements)
+    static constexpr int LOADS = ROWS * RP / (64 * NW);  // load instructions per wave per tile
+    static_assert(ROWS * RP % (64 * NW) == 0, "tile must split evenly over the waves");
+    static_assert(RP <= 16, "swizzle covers up to 16 slots");
+
+    // Byte offsets (within the tile's global rows) each lane fetches, one per
+    // load instruction; slots with no logical chunk get an offset past any range.
+    struct Src {
+        int off[LOADS];
+        __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                const int p = (i * NW + wave) * 64 + lane;  // slot this lane fills
+                const int row = p / RP, slot = p % RP;
+                const int c = slot ^ swz(row);
+                off[i] = c < CPR ? (row * D + c * 8) * 2 : 0x7fffff00;
+            }
+        }
+    };
+
+    // Issue the loads of rows row0 .. row0+ROWS-1 of the [S][D] matrix g into the
+    // LDS tile t; rows at or beyond S read as zero.
+    __device__ static __forceinline__ void load(const uint16_t* __restrict__ g, int row0, int S, uint16_t* t,
+                                                const Src& src, int wave) {
+        const int rows = max(0, min(S - row0, ROWS));
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(g + (size_t)row0 * D, rows * D * 2);
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void*)(t + (i * NW + wave) * 512), 16, src.off[i], 0, 0,
+                0);
+    }
+
+    // element offset of logical (row, col), col % 4 == 0
+    __device__ static __forceinline__ int at(int r, int col) {
+        return r * RS + ((((col >> 3) ^ swz(r)) << 3) | (col & 7));
+    }
+};
+
+// Per-lane LDS offsets for the two operand reads of a DTile, computed once (the
+// swizzle depends on the row modulo 8 only, and every row step the kernels add
+// is a multiple of 8).
+//   row[ks]   : 16-byte row operand, row n, columns 16ks + 8h .. +7
+//   tr[db][e] : transposing read (the lds_tr_operand lane map) for columns
+//               32db.., rows +0 (e = 0) and +8 (e = 1) of a 16-row step
+template <class TILE, int D>
+struct DOffsets {
+    static constexpr int KS = HeadDim<D>::KSTEPS;
+    static constexpr int DB = HeadDim<D>::DB;
+    int row[KS];
+    int tr[DB][2];
+    __device__ __forceinline__ void init(int lane) {
+        const int n = lane & 31, h = lane >> 5, g = lane >> 4, j = lane & 15;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) row[ks] = TILE::at(n, ks * 16 + 8 * h);
+        const int rr = 4 * (g >> 1) + (j >> 2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int col = db * 32 + 16 * (g & 1) + 4 * (j & 3);
+            tr[db][0] = TILE::at(rr, col);
+            tr[db][1] = TILE::at(rr + 8, col);
+        }
+    }
+    // row operand of row r0 + n (r0 a multiple of 8)
+    template <class E>
+    __device__ __forceinline__ typename E::V8 row_op(const uint16_t* T, int r0, int ks) const {
+        return as_op<E>(lds16(T + r0 * TILE::RS + row[ks]));
+    }
+    // operand contracting over rows r0 .. r0+15 (r0 a multiple of 16), columns 32db + n
+    template <class E>
+    __device__ __forceinline__ typename E::V8 tr_op(const uint16_t* T, int r0, int db) const {
+        const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(T + r0 * TILE::RS + tr[db][0]));
+        const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(T + r0 * TILE::RS + tr[db][1]));
+        const i16x8 r = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(typename E::V8, r);
+    }
+};
+
+}  // namespace attn

@@ -28,12 +28,13 @@
 // * Software pipeline: K runs one tile ahead of V in LDS, so iteration t issues
 //   the MFMAs of S^T for tile t+1 next to the exp/max/sum VALU work of tile t
 //   (the MFMA unit works asynchronously from the VALU), then O += V_t P_t.
-//   Q stays in registers for the whole loop; the global loads of a K/V tile are
-//   issued two iterations before it is stored to LDS; one barrier per tile.
+//   Q stays in registers for the whole loop; K/V tiles go from HBM straight to
+//   LDS (buffer loads with the lds flag, swizzled rows) one tile ahead of their
+//   use; one barrier per tile.
 #include <type_traits>
 
 #include "attn_launch.h"
-#include "attn_tiles.h"
+#include "attn_direct.h"
 
 namespace attn {
 
@@ -46,9 +47,14 @@ struct FwdCfg {
     static constexpr int NT = NW * 64;
     static constexpr int BM = NW * 32 * QB;  // queries per workgroup
     static constexpr int BN = 64;            // keys per tile
-    using Tile = RowTile<BN, D, NT>;
-    static constexpr int STR = Tile::STR;
+    using Tile = DTile<BN, D, NW>;
     static constexpr int TE = Tile::ELEMS;   // one K or V tile in LDS (elements)
+    // LDS buffers per operand: a tile is fetched during the iteration before its
+    // use.  (An iteration issues its operand reads before its loads: the compiler
+    // cannot tell the transposing LDS read from a write of an in-flight load and
+    // waits for all loads before it, which then finds none outstanding.)
+    static constexpr int NB = 2;
+    static constexpr int P = NB - 1;
     static constexpr int KS = HeadDim<D>::KSTEPS;
     static constexpr int DB = HeadDim<D>::DB;
 };
@@ -62,11 +68,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma_kernel(const uint16_t* __res
                                                        int causal) {
     using Cfg = FwdCfg<D, QB, NW>;
     using V8 = typename E::V8;
-    constexpr int BM = Cfg::BM, BN = Cfg::BN, STR = Cfg::STR, TE = Cfg::TE;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, TE = Cfg::TE, NB = Cfg::NB, P = Cfg::P;
+    constexpr int LOADS = Cfg::Tile::LOADS;
     constexpr int KB = BN / 32;  // 32-key blocks per tile
     constexpr int KS = Cfg::KS, DB = Cfg::DB;
-    // K[2], V[2]; V is read transposed, so the last buffer carries the slack
-    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TE + Cfg::Tile::TR_SLACK];
+    // K[NB], V[NB]
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * NB * TE];
 
     const WorkItem wi = heavy_first(blockIdx.x, BH);
     const int head = wi.head;
@@ -88,8 +95,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma_kernel(const uint16_t* __res
     // tiles this wave multiplies: the causal ones up to its last query
     const int nw = causal ? min(ntiles, (qw0 + 32 * QB - 1) / BN + 1) : ntiles;
 
-    auto kbuf = [&](int t) { return smem + (t & 1) * TE; };
-    auto vbuf = [&](int t) { return smem + (2 + (t & 1)) * TE; };
+    auto kbuf = [&](int t) { return smem + (t % NB) * TE; };
+    auto vbuf = [&](int t) { return smem + (NB + t % NB) * TE; };
+    typename Cfg::Tile::Src src;
+    src.init(wave, lane);
+    DOffsets<typename Cfg::Tile, D> lo;
+    lo.init(lane);
 
     // Q as the B operand of S^T = K Q^T: lane holds query qw0+32qb+n, d = 16ks+8h..+7.
     V8 qf[QB][KS];
@@ -124,7 +135,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma_kernel(const uint16_t* __res
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                kf[kb][ks] = as_op<E>(lds16(Ks + (kb * 32 + n) * STR + ks * 16 + 8 * h));
+                kf[kb][ks] = lo.template row_op<E>(Ks, kb * 32, ks);
     };
     // S^T tile from K operands already in registers; the first contraction step
     // starts from a zero accumulator.
@@ -144,11 +155,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma_kernel(const uint16_t* __res
     // MASK instantiates the per-element causal / sequence-end mask; only a
     // wave's last tile can need it (its earlier tiles lie entirely below the
     // diagonal and before S), and the last tile has no successor.
-    auto step = [&](auto mask_tag, auto next_tag, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB], int t) {
+    auto step = [&](auto mask_tag, auto next_tag, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB], int t,
+                    const V8 (&kf)[KB][KS], const V8 (&vf)[BN / 16][DB]) {
         constexpr bool MASK = decltype(mask_tag)::value;
         constexpr bool NEXT = decltype(next_tag)::value;
-        V8 kf[KB][KS];
-        if constexpr (NEXT) load_k(kf, t + 1);
 
         // ---- mask, row max (raw scores; c > 0 so max commutes with scaling)
         const int k0 = t * BN;
@@ -203,14 +213,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma_kernel(const uint16_t* __res
                 ls[qb] = sum8<E>(pf[qb][2 * kb + 1], ls[qb]);
             }
         }
-        // V^T operands, read transposed from the row-major V tile
-        const uint16_t* Vs = vbuf(t);
-        V8 vf[BN / 16][DB];
-#pragma unroll
-        for (int ks = 0; ks < BN / 16; ++ks)
-#pragma unroll
-            for (int db = 0; db < DB; ++db) vf[ks][db] = lds_tr_op<E, STR>(Vs, ks * 16, db * 32, lane);
-
         if (resc) {
             // rare (the reference point moves only past the slack): keep it a
             // branch; the empty volatile asm stops the compiler from executing
@@ -240,24 +242,25 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma_kernel(const uint16_t* __res
                 for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = E::mma(vf[ks][db], pf[qb][ks], oacc[qb][db]);
     };
 
-    // ---- prologue: K_0, V_0, K_1 in LDS; register set 0 holds (K_2, V_1) and
-    // set 1 holds (K_3, V_2), both in flight.  A tile index at or past ntiles
-    // loads from row S: an empty buffer range, so nothing is read and the
-    // registers hold zeros (stores and loads stay unconditional, which keeps
-    // the count of loads in flight the same on every path).
+    // ---- prologue: loads of K_0, then (K_{i+1}, V_i) for i < P, straight into
+    // LDS.  Iteration t reads K_{t+1} and V_t and issues K_{t+1+P} and V_{t+P}
+    // into the buffers of K_t and V_{t-1} (read in the previous iteration, so
+    // free once the iteration's barrier has passed).  Each wave then finds the
+    // tiles it needs complete once at most 2 (P - 1) tiles of its own loads are
+    // outstanding: that count is the same in every iteration.  A tile index at
+    // or past ntiles loads from row S: an empty buffer range, so the tile reads
+    // as zeros and the count of loads stays the same on every path.
     auto row_of = [&](int t) { return t < ntiles ? t * BN : S; };
-    typename Cfg::Tile kt[2], vt[2];
-    kt[0].load(Kh, 0, S, tid);
-    vt[0].load(Vh, 0, S, tid);
-    kt[1].load(Kh, row_of(1), S, tid);
-    kt[0].store(kbuf(0), tid);
-    vt[0].store(vbuf(0), tid);
-    kt[1].store(kbuf(1), tid);
-    kt[0].load(Kh, row_of(2), S, tid);
-    vt[0].load(Vh, row_of(1), S, tid);
-    kt[1].load(Kh, row_of(3), S, tid);
-    vt[1].load(Vh, row_of(2), S, tid);
-    __syncthreads();
+    auto load_kt = [&](int t) { Cfg::Tile::load(Kh, row_of(t), S, kbuf(t), src, wave); };
+    auto load_vt = [&](int t) { Cfg::Tile::load(Vh, row_of(t), S, vbuf(t), src, wave); };
+    load_kt(0);
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        load_kt(i + 1);
+        load_vt(i);
+    }
+    wait_vmcnt<2 * P * LOADS>();  // K_0 landed
+    bare_barrier();
 
     f32x16 sa[QB][KB], sb[QB][KB];
     if (nw > 0) {
@@ -265,30 +268,37 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma_kernel(const uint16_t* __res
         load_k(kf, 0);
         mma_scores(sa, kf);
     }
-    // Iteration 0 overwrites K_0's buffer with K_2: every wave must have read
-    // K_0 first.
-    __syncthreads();
 
-    // Iteration t, with register set t % 2 holding (K_{t+2}, V_{t+1}): stage them
-    // (into the buffers of K_t and V_{t-1}, both consumed last iteration), start
-    // the loads of K_{t+4} and V_{t+3} into the same set (two tiles of latency
-    // cover), compute, then one barrier.
-    auto iteration = [&](int t, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB], typename Cfg::Tile& kr,
-                         typename Cfg::Tile& vr) {
-        kr.store(kbuf(t), tid);
-        vr.store(vbuf(t + 1), tid);
-        kr.load(Kh, row_of(t + 4), S, tid);
-        vr.load(Vh, row_of(t + 3), S, tid);
+    // Iteration t: wait for K_{t+1} and V_t (own loads, then everyone's), issue
+    // the loads of K_{t+1+P} and V_{t+P}, compute.
+    auto iteration = [&](int t, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB]) {
+        wait_vmcnt<2 * (P - 1) * LOADS>();
+        bare_barrier();
+        // this iteration's operand reads: K_{t+1} rows and V_t transposed
+        V8 kf[KB][KS], vf[BN / 16][DB];
+        if (t + 1 < nw) load_k(kf, t + 1);
+        if (t < nw) {
+            const uint16_t* Vs = vbuf(t);
+#pragma unroll
+            for (int ks = 0; ks < BN / 16; ++ks)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) vf[ks][db] = lo.template tr_op<E>(Vs, ks * 16, db);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        load_kt(t + 1 + P);
+        load_vt(t + P);
+        __builtin_amdgcn_sched_barrier(0);
         if (t + 1 < nw)
-            step(std::false_type{}, std::true_type{}, cur, nxt, t);
+            step(std::false_type{}, std::true_type{}, cur, nxt, t, kf, vf);
         else if (t + 1 == nw)
-            step(std::true_type{}, std::false_type{}, cur, nxt, t);
-        __syncthreads();
+            step(std::true_type{}, std::false_type{}, cur, nxt, t, kf, vf);
     };
     for (int t = 0; t < ntiles; t += 2) {
-        iteration(t, sa, sb, kt[0], vt[0]);
-        if (t + 1 < ntiles) iteration(t + 1, sb, sa, kt[1], vt[1]);
+        iteration(t, sa, sb);
+        if (t + 1 < ntiles) iteration(t + 1, sb, sa);
     }
+    // no load may still be writing this workgroup's LDS when it exits
+    wait_vmcnt<0>();
 
     // ---- epilogue: O = O / l (l == 0 -> 0), LSE = (m + log2 l) * ln 2
     uint16_t* Oh = O + base;
