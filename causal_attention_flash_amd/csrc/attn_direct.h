@@ -32,6 +32,28 @@ constexpr int pow2_up(int x) { return x <= 1 ? 1 : 2 * pow2_up((x + 1) / 2); }
 
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
+// Byte address within LDS of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Wait for every LDS read issued so far (s_waitcnt lgkmcnt(0)) and tie the raw
+// halves of asynchronous reads to it, so that nothing (a use, a copy) reads them
+// before the wait.  N counts 64-bit halves.
+template <int N>
+__device__ __forceinline__ void lds_wait(i16x4 (&x)[N]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(x[i]));
+}
+
+// Operand from the two halves of a transposing read.
+template <class E>
+__device__ __forceinline__ typename E::V8 tr_join(const i16x4 (&h)[2]) {
+    const i16x8 r = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(typename E::V8, r);
+}
+
 // s_waitcnt vmcnt(n): at most n vector-memory operations of this wave still in
 // flight (expcnt and lgkmcnt unconstrained).  n < 64.
 template <int N>
@@ -124,13 +146,19 @@ struct DOffsets {
     __device__ __forceinline__ typename E::V8 row_op(const uint16_t* T, int r0, int ks) const {
         return as_op<E>(lds16(T + r0 * TILE::RS + row[ks]));
     }
-    // operand contracting over rows r0 .. r0+15 (r0 a multiple of 16), columns 32db + n
-    template <class E>
-    __device__ __forceinline__ typename E::V8 tr_op(const uint16_t* T, int r0, int db) const {
-        const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(T + r0 * TILE::RS + tr[db][0]));
-        const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(T + r0 * TILE::RS + tr[db][1]));
-        const i16x8 r = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-        return __builtin_bit_cast(typename E::V8, r);
+    // Transposing read of the operand contracting over rows r0 .. r0+15 (r0 a
+    // multiple of 16), columns 32db + n, issued as inline assembly into two raw
+    // halves.  The compiler does not see an LDS read there, so it adds no wait for
+    // the loads in flight (which it would otherwise do before every transposing
+    // read, unable to tell it from a load's LDS write).  The halves hold data only
+    // after lds_wait() has taken them; tr_join() then forms the operand.  LDS
+    // operations complete in order, so the compiler's own lgkmcnt waits for its
+    // reads stay correct (only stricter) with these in flight.
+    __device__ __forceinline__ void tr_async(const uint16_t* T, int r0, int db, i16x4 (&h)[2]) const {
+        const uint32_t a0 = lds_addr(T + r0 * TILE::RS + tr[db][0]);
+        const uint32_t a1 = lds_addr(T + r0 * TILE::RS + tr[db][1]);
+        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(h[0]) : "v"(a0));
+        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(h[1]) : "v"(a1));
     }
 };
 

@@ -155,10 +155,20 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma_kernel(const uint16_t* __res
     // MASK instantiates the per-element causal / sequence-end mask; only a
     // wave's last tile can need it (its earlier tiles lie entirely below the
     // diagonal and before S), and the last tile has no successor.
-    auto step = [&](auto mask_tag, auto next_tag, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB], int t,
-                    const V8 (&kf)[KB][KS], const V8 (&vf)[BN / 16][DB]) {
+    auto step = [&](auto mask_tag, auto next_tag, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB], int t) {
         constexpr bool MASK = decltype(mask_tag)::value;
         constexpr bool NEXT = decltype(next_tag)::value;
+        V8 kf[KB][KS];
+        if constexpr (NEXT) load_k(kf, t + 1);
+        // V^T operands, read transposed from the V tile (asynchronous: used after lds_wait)
+        i16x4 vr[BN / 16][DB][2];
+        {
+            const uint16_t* Vs = vbuf(t);
+#pragma unroll
+            for (int ks = 0; ks < BN / 16; ++ks)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) lo.tr_async(Vs, ks * 16, db, vr[ks][db]);
+        }
 
         // ---- mask, row max (raw scores; c > 0 so max commutes with scaling)
         const int k0 = t * BN;
@@ -233,6 +243,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma_kernel(const uint16_t* __res
             m[qb] = mn[qb];
             l[qb] += ls[qb];
         }
+        lds_wait(reinterpret_cast<i16x4 (&)[(BN / 16) * DB * 2]>(vr));
+        V8 vf[BN / 16][DB];
+#pragma unroll
+        for (int ks = 0; ks < BN / 16; ++ks)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) vf[ks][db] = tr_join<E>(vr[ks][db]);
         // ---- O^T += V^T P^T
 #pragma unroll
         for (int ks = 0; ks < BN / 16; ++ks)
@@ -274,24 +290,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma_kernel(const uint16_t* __res
     auto iteration = [&](int t, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB]) {
         wait_vmcnt<2 * (P - 1) * LOADS>();
         bare_barrier();
-        // this iteration's operand reads: K_{t+1} rows and V_t transposed
-        V8 kf[KB][KS], vf[BN / 16][DB];
-        if (t + 1 < nw) load_k(kf, t + 1);
-        if (t < nw) {
-            const uint16_t* Vs = vbuf(t);
-#pragma unroll
-            for (int ks = 0; ks < BN / 16; ++ks)
-#pragma unroll
-                for (int db = 0; db < DB; ++db) vf[ks][db] = lo.template tr_op<E>(Vs, ks * 16, db);
-        }
-        __builtin_amdgcn_sched_barrier(0);
         load_kt(t + 1 + P);
         load_vt(t + P);
-        __builtin_amdgcn_sched_barrier(0);
         if (t + 1 < nw)
-            step(std::false_type{}, std::true_type{}, cur, nxt, t, kf, vf);
+            step(std::false_type{}, std::true_type{}, cur, nxt, t);
         else if (t + 1 == nw)
-            step(std::true_type{}, std::false_type{}, cur, nxt, t, kf, vf);
+            step(std::true_type{}, std::false_type{}, cur, nxt, t);
     };
     for (int t = 0; t < ntiles; t += 2) {
         iteration(t, sa, sb);
