@@ -92,8 +92,8 @@ def read_traffic(kernel: str, workload: str):
 # while these are unchanged.
 KERNEL_SOURCES = {
     "fwd": ("attn_fwd_mfma.hip", "attn_direct.h", "attn_tiles.h", "attn_device.h", "attn_launch.h"),
-    "bwd_dq": ("attn_bwd_mfma.hip", "attn_tiles.h", "attn_device.h", "attn_launch.h"),
-    "bwd_dkdv": ("attn_bwd_mfma.hip", "attn_tiles.h", "attn_device.h", "attn_launch.h"),
+    "bwd_dq": ("attn_bwd_mfma.hip", "attn_direct.h", "attn_tiles.h", "attn_device.h", "attn_launch.h"),
+    "bwd_dkdv": ("attn_bwd_mfma.hip", "attn_direct.h", "attn_tiles.h", "attn_device.h", "attn_launch.h"),
 }
 
 

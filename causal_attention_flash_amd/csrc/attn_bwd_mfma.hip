@@ -22,11 +22,13 @@
 // Q and dO (dQ pass) as MFMA operands in registers, plus two fp32 accumulators
 // of 32 rows x D; the streamed operand tiles are double-buffered in LDS,
 // row-major only: the contractions over their rows read them through the
-// transposing LDS read (lds_tr_operand).
+// transposing LDS read.  The dK/dV pass stages its Q and dO tiles through
+// registers into padded rows; the dQ pass loads its K and V tiles straight from
+// HBM into swizzled rows (attn_direct.h).
 #include <type_traits>
 
 #include "attn_launch.h"
-#include "attn_tiles.h"
+#include "attn_direct.h"
 
 namespace attn {
 
@@ -346,10 +348,13 @@ struct DqCfg {
     static constexpr int NW = NW_;
     static constexpr int NT = NW * 64;
     static constexpr int BMQ = NW * 32;  // queries per workgroup (32 per wave)
-    using KT = RowTile<BNK, D, NT>;      // K and V tiles, row-major
-    static constexpr int STR = KT::STR;
-    static constexpr int KE = KT::ELEMS;
-    static constexpr int BUF_ELEMS = 2 * KE;  // K, V
+    using Tile = DTile<BNK, D, NW>;      // K and V tiles, swizzled rows
+    static constexpr int TE = Tile::ELEMS;
+    static constexpr int LOADS = Tile::LOADS;
+    // two buffers per matrix, tiles fetched one iteration ahead (three buffers,
+    // two ahead, measured slower: less occupancy at D = 64, no gain elsewhere)
+    static constexpr int NB = 2;
+    static constexpr int P = NB - 1;
     // register budget: 168 VGPRs (3 waves per SIMD) fits D = 64 without spills,
     // 256 (two) fits D = 80 and 96
     static constexpr int WAVES_PER_SIMD = D == 64 ? 3 : (D <= 96 ? 2 : 1);
@@ -369,11 +374,10 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
     using Cfg = DqCfg<D, BNK, NW>;
     using V8 = typename E::V8;
     constexpr int BMQ = Cfg::BMQ;
-    constexpr int STR = Cfg::STR;
     constexpr int KS = Cfg::KS, DB = Cfg::DB;
-    // [K, V][2]; K is read transposed (a V tile follows each K tile; the slack
-    // keeps the layout rule uniform)
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Cfg::BUF_ELEMS + Cfg::KT::TR_SLACK];
+    constexpr int TE = Cfg::TE, NB = Cfg::NB, P = Cfg::P, LOADS = Cfg::LOADS;
+    // K[NB], V[NB]
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * NB * TE];
 
     const WorkItem wi = heavy_first(blockIdx.x, BH);
     const int head = wi.head;
@@ -389,6 +393,29 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
     const int h = lane >> 5, n = lane & 31;
     const int qw0 = q0 + wave * 32;
     const int q = qw0 + n;  // the query this lane's C columns belong to
+
+    const int kend = causal ? min(S, q0 + BMQ) : S;
+    const int ntiles = (kend + BNK - 1) / BNK;
+
+    // Tile t goes to buffer t % NB, straight from HBM.  Iteration t issues tile
+    // t + P into the buffers of tile t - 1 (read in the previous iteration, free
+    // once the iteration's barrier has passed); a wave then finds tile t complete
+    // once at most P - 1 tiles of its own loads are outstanding, a count that is
+    // the same in every iteration because tiles at or past ntiles load from row S
+    // (an empty buffer range: zeros, and the same number of loads).
+    auto kbuf = [&](int t) { return smem + (t % NB) * TE; };
+    auto vbuf = [&](int t) { return smem + (NB + t % NB) * TE; };
+    typename Cfg::Tile::Src src;
+    src.init(wave, lane);
+    DOffsets<typename Cfg::Tile, D> lo;
+    lo.init(lane);
+    auto load_t = [&](int t) {
+        const int row = t < ntiles ? t * BNK : S;
+        Cfg::Tile::load(Kh, row, S, kbuf(t), src, wave);
+        Cfg::Tile::load(Vh, row, S, vbuf(t), src, wave);
+    };
+#pragma unroll
+    for (int i = 0; i < P; ++i) load_t(i);
 
     V8 qf[KS], of[KS];
 #pragma unroll
@@ -425,32 +452,13 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
 #pragma unroll
         for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
 
-    const int kend = causal ? min(S, q0 + BMQ) : S;
-    const int ntiles = (kend + BNK - 1) / BNK;
-
-    typename Cfg::KT kt, vt;
-    auto bufp = [&](int b) { return smem + b * Cfg::BUF_ELEMS; };
-    auto stage = [&](int b) {
-        uint16_t* s = bufp(b);
-        kt.store(s, tid);
-        vt.store(s + Cfg::KE, tid);
-    };
-    auto fetch = [&](int t) {
-        kt.load(Kh, t * BNK, S, tid);
-        vt.load(Vh, t * BNK, S, tid);
-    };
-
-    fetch(0);
-    stage(0);
-    if (ntiles > 1) fetch(1);
-    __syncthreads();
 
     // One key tile against this wave's 32 queries; MASK instantiates the causal
     // and sequence-end mask for tiles that cross the diagonal or the end.
-    auto tile = [&](auto mask_tag, int b, int k0) {
+    auto tile = [&](auto mask_tag, int t, int k0) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        const uint16_t* Ks = bufp(b);
-        const uint16_t* Vs = Ks + Cfg::KE;
+        const uint16_t* Ks = kbuf(t);
+        const uint16_t* Vs = vbuf(t);
 #pragma unroll
         for (int kb = 0; kb < BNK / 32; ++kb) {
             // S^T = K Q^T and dP^T = V dO^T: 32 keys x this wave's 32 queries
@@ -462,10 +470,16 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
             }
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const int off = (kb * 32 + n) * STR + ks * 16 + 8 * h;
-                sacc = E::mma(as_op<E>(lds16(Ks + off)), qf[ks], sacc);
-                pacc = E::mma(as_op<E>(lds16(Vs + off)), of[ks], pacc);
+                sacc = E::mma(lo.template row_op<E>(Ks, kb * 32, ks), qf[ks], sacc);
+                pacc = E::mma(lo.template row_op<E>(Vs, kb * 32, ks), of[ks], pacc);
             }
+            // K^T operands of this block's dQ product, read transposed from the
+            // K tile (asynchronous: used after lds_wait)
+            i16x4 kr[2][DB][2];
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) lo.tr_async(Ks, (kb * 2 + c2) * 16, db, kr[c2][db]);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float p = fast_exp2(fmaf(sacc[r], c, -l2));
@@ -475,33 +489,31 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
                 }
                 pacc[r] = p * (pacc[r] - dl);
             }
-            // dQ^T += K^T dS^T (contraction over these 32 keys; K^T read
-            // transposed from the row-major K tile)
+            // dQ^T += K^T dS^T (contraction over these 32 keys)
+            lds_wait(reinterpret_cast<i16x4 (&)[2 * DB * 2]>(kr));
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
                 const V8 sb = pack_op<E>(pacc, c2);
 #pragma unroll
-                for (int db = 0; db < DB; ++db)
-                    dqacc[db] = E::mma(lds_tr_op<E, STR>(Ks, (kb * 2 + c2) * 16, db * 32, lane), sb, dqacc[db]);
+                for (int db = 0; db < DB; ++db) dqacc[db] = E::mma(tr_join<E>(kr[c2][db]), sb, dqacc[db]);
             }
         }
     };
 
     for (int t = 0; t < ntiles; ++t) {
+        wait_vmcnt<2 * (P - 1) * LOADS>();  // own loads of tile t
+        bare_barrier();                       // everyone's; tile t - 1 no longer read
+        load_t(t + P);
         const int k0 = t * BNK;
         // wave-uniform: skip key tiles entirely after this wave's last query
         if (!causal || k0 <= qw0 + 31) {
             if ((causal && k0 + BNK - 1 > qw0) || k0 + BNK > S)
-                tile(std::true_type{}, t & 1, k0);
+                tile(std::true_type{}, t, k0);
             else
-                tile(std::false_type{}, t & 1, k0);
+                tile(std::false_type{}, t, k0);
         }
-        if (t + 1 < ntiles) {
-            stage((t + 1) & 1);
-            if (t + 2 < ntiles) fetch(t + 2);
-        }
-        __syncthreads();
     }
+    wait_vmcnt<0>();  // no load into LDS outlives the workgroup
 
     if (q < S) {
         uint16_t* dQr = dQ + base + (size_t)q * D;

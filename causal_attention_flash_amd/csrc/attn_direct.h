@@ -99,9 +99,12 @@ struct DTile {
     };
 
     // Issue the loads of rows row0 .. row0+ROWS-1 of the [S][D] matrix g into the
-    // LDS tile t; rows at or beyond S read as zero.
-    __device__ static __forceinline__ void load(const uint16_t* __restrict__ g, int row0, int S, uint16_t* t,
+    // LDS tile t; rows at or beyond S read as zero.  row0 must be the same across
+    // the wave (it is taken from the first lane, so the buffer descriptor stays in
+    // scalar registers whatever the compiler concludes about its uniformity).
+    __device__ static __forceinline__ void load(const uint16_t* __restrict__ g, int row0_, int S, uint16_t* t,
                                                 const Src& src, int wave) {
+        const int row0 = __builtin_amdgcn_readfirstlane(row0_);
         const int rows = max(0, min(S - row0, ROWS));
         const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(g + (size_t)row0 * D, rows * D * 2);
 #pragma unroll
