@@ -5,6 +5,10 @@
 Every HIP source under csrc/ is compiled to an object in parallel, then linked
 into causal_attention_flash_amd/libcausal_attn.so.  Objects go to _build/ at the
 repository root (not committed).  The library always rebuilds when asked to.
+
+Sources that use the asynchronous transposing LDS read (tr_async) are also
+compiled to device assembly, which asm_check verifies (no use or copy of such a
+read's registers before its wait); a violation fails the build.
 """
 from __future__ import annotations
 
@@ -62,13 +66,46 @@ def _compile(src: str, extra: list) -> str:
     return obj
 
 
+def uses_async_reads(src: str) -> bool:
+    with open(src) as f:
+        return "tr_async" in f.read()
+
+
+def device_asm(src: str, extra: list | None = None) -> str:
+    """Compile src to gfx950 device assembly under _build/; return its path."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    out = os.path.join(OBJDIR, os.path.basename(src) + ".s")
+    cmd = [hipcc(), *CFLAGS, *(extra or []), "--cuda-device-only", "-S", src, "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return out
+
+
+def check_async_reads(src: str, extra: list | None = None) -> int:
+    """Verify the asynchronous LDS reads in src's device code; return their count."""
+    from causal_attention_flash_amd import asm_check
+
+    with open(device_asm(src, extra)) as f:
+        asm = f.read()
+    bad = asm_check.check_text(asm)
+    n = asm_check.count_reads(asm)
+    if bad or n == 0:
+        head = "\n".join(bad[:10]) if bad else "no asynchronous reads found (assembly format changed?)"
+        raise RuntimeError(f"asynchronous LDS read check failed for {src} ({len(bad)} violations):\n{head}")
+    return n
+
+
 def build(verbose: bool = False, extra_flags: list | None = None) -> str:
     """Compile and link the library; return its path."""
     os.makedirs(OBJDIR, exist_ok=True)
     extra = list(extra_flags or [])
     srcs = sources()
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+    checked = [s for s in srcs if uses_async_reads(s)]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=8) as ex:
+        checks = [ex.submit(check_async_reads, s, extra) for s in checked]
         objs = list(ex.map(lambda s: _compile(s, extra), srcs))
+        nreads = sum(c.result() for c in checks)
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -76,6 +113,7 @@ def build(verbose: bool = False, extra_flags: list | None = None) -> str:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
     if verbose:
+        print(f"checked {nreads} asynchronous LDS reads in {len(checked)} sources")
         print(f"built {LIB}")
     return LIB
 
