@@ -348,13 +348,21 @@ struct DqCfg {
     static constexpr int NW = NW_;
     static constexpr int NT = NW * 64;
     static constexpr int BMQ = NW * 32;  // queries per workgroup (32 per wave)
-    using Tile = DTile<BNK, D, NW>;      // K and V tiles, swizzled rows
+    // K and V tiles, two buffers each, fetched one iteration ahead.  At D = 64
+    // they are staged through registers into padded rows; wider heads load them
+    // straight from HBM into swizzled rows (measured: the direct path is 1-2%
+    // slower at D = 64 and 5-7% faster at D = 128; fetching two tiles ahead was
+    // slower at every size)
+    static constexpr bool DIRECT = D != 64;
+    using KT = RowTile<BNK, D, NT>;  // register-staged: [rows][D + 8]
+    static constexpr int STR = KT::STR;
+    static constexpr int KE = KT::ELEMS;
+    using Tile = DTile<BNK, D, NW>;  // direct: swizzled rows
     static constexpr int TE = Tile::ELEMS;
     static constexpr int LOADS = Tile::LOADS;
-    // two buffers per matrix, tiles fetched one iteration ahead (three buffers,
-    // two ahead, measured slower: less occupancy at D = 64, no gain elsewhere)
-    static constexpr int NB = 2;
-    static constexpr int P = NB - 1;
+    // direct: K[2], V[2]; staged: [K, V][2] (K is read transposed: a V tile
+    // follows each K tile, and the slack keeps the layout rule uniform)
+    static constexpr int SMEM_ELEMS = DIRECT ? 4 * TE : 4 * KE + KT::TR_SLACK;
     // register budget: 168 VGPRs (3 waves per SIMD) fits D = 64 without spills,
     // 256 (two) fits D = 80 and 96
     static constexpr int WAVES_PER_SIMD = D == 64 ? 3 : (D <= 96 ? 2 : 1);
@@ -375,9 +383,9 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
     using V8 = typename E::V8;
     constexpr int BMQ = Cfg::BMQ;
     constexpr int KS = Cfg::KS, DB = Cfg::DB;
-    constexpr int TE = Cfg::TE, NB = Cfg::NB, P = Cfg::P, LOADS = Cfg::LOADS;
-    // K[NB], V[NB]
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * NB * TE];
+    constexpr bool DIRECT = Cfg::DIRECT;
+    constexpr int STR = Cfg::STR, KE = Cfg::KE, TE = Cfg::TE;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[Cfg::SMEM_ELEMS];
 
     const WorkItem wi = heavy_first(blockIdx.x, BH);
     const int head = wi.head;
@@ -397,25 +405,36 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
     const int kend = causal ? min(S, q0 + BMQ) : S;
     const int ntiles = (kend + BNK - 1) / BNK;
 
-    // Tile t goes to buffer t % NB, straight from HBM.  Iteration t issues tile
-    // t + P into the buffers of tile t - 1 (read in the previous iteration, free
-    // once the iteration's barrier has passed); a wave then finds tile t complete
-    // once at most P - 1 tiles of its own loads are outstanding, a count that is
-    // the same in every iteration because tiles at or past ntiles load from row S
-    // (an empty buffer range: zeros, and the same number of loads).
-    auto kbuf = [&](int t) { return smem + (t % NB) * TE; };
-    auto vbuf = [&](int t) { return smem + (NB + t % NB) * TE; };
+    // Tile t uses buffer t % 2.
+    // Direct: iteration t issues tile t + 1 into the buffers of tile t - 1 (read in
+    // the previous iteration, free once the iteration's barrier has passed), and
+    // waits for all of its own loads before that barrier.  Tiles at or past ntiles
+    // load from row S (an empty buffer range) so every path issues the same loads.
+    // Staged: after its tile, iteration t stores tile t + 1 from registers and
+    // fetches tile t + 2 into them.
+    auto kbuf = [&](int t) { return DIRECT ? smem + (t & 1) * TE : smem + (t & 1) * 2 * KE; };
+    auto vbuf = [&](int t) { return DIRECT ? smem + (2 + (t & 1)) * TE : smem + (t & 1) * 2 * KE + KE; };
     typename Cfg::Tile::Src src;
-    src.init(wave, lane);
     DOffsets<typename Cfg::Tile, D> lo;
-    lo.init(lane);
     auto load_t = [&](int t) {
         const int row = t < ntiles ? t * BNK : S;
         Cfg::Tile::load(Kh, row, S, kbuf(t), src, wave);
         Cfg::Tile::load(Vh, row, S, vbuf(t), src, wave);
     };
-#pragma unroll
-    for (int i = 0; i < P; ++i) load_t(i);
+    typename Cfg::KT kt, vt;
+    auto stage = [&](int t) {
+        kt.store(kbuf(t), tid);
+        vt.store(vbuf(t), tid);
+    };
+    auto fetch = [&](int t) {
+        kt.load(Kh, t * BNK, S, tid);
+        vt.load(Vh, t * BNK, S, tid);
+    };
+    if constexpr (DIRECT) {
+        src.init(wave, lane);
+        lo.init(lane);
+        load_t(0);
+    }
 
     V8 qf[KS], of[KS];
 #pragma unroll
@@ -452,6 +471,12 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
 #pragma unroll
         for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
 
+    if constexpr (!DIRECT) {
+        fetch(0);
+        stage(0);
+        if (ntiles > 1) fetch(1);
+        __syncthreads();
+    }
 
     // One key tile against this wave's 32 queries; MASK instantiates the causal
     // and sequence-end mask for tiles that cross the diagonal or the end.
@@ -470,16 +495,24 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
             }
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                sacc = E::mma(lo.template row_op<E>(Ks, kb * 32, ks), qf[ks], sacc);
-                pacc = E::mma(lo.template row_op<E>(Vs, kb * 32, ks), of[ks], pacc);
+                if constexpr (DIRECT) {
+                    sacc = E::mma(lo.template row_op<E>(Ks, kb * 32, ks), qf[ks], sacc);
+                    pacc = E::mma(lo.template row_op<E>(Vs, kb * 32, ks), of[ks], pacc);
+                } else {
+                    const int off = (kb * 32 + n) * STR + ks * 16 + 8 * h;
+                    sacc = E::mma(as_op<E>(lds16(Ks + off)), qf[ks], sacc);
+                    pacc = E::mma(as_op<E>(lds16(Vs + off)), of[ks], pacc);
+                }
             }
-            // K^T operands of this block's dQ product, read transposed from the
-            // K tile (asynchronous: used after lds_wait)
+            // direct: K^T operands of this block's dQ product, read transposed from
+            // the K tile (asynchronous: used after lds_wait)
             i16x4 kr[2][DB][2];
+            if constexpr (DIRECT) {
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2)
+                for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-                for (int db = 0; db < DB; ++db) lo.tr_async(Ks, (kb * 2 + c2) * 16, db, kr[c2][db]);
+                    for (int db = 0; db < DB; ++db) lo.tr_async(Ks, (kb * 2 + c2) * 16, db, kr[c2][db]);
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float p = fast_exp2(fmaf(sacc[r], c, -l2));
@@ -490,20 +523,27 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
                 pacc[r] = p * (pacc[r] - dl);
             }
             // dQ^T += K^T dS^T (contraction over these 32 keys)
-            lds_wait(reinterpret_cast<i16x4 (&)[2 * DB * 2]>(kr));
+            if constexpr (DIRECT) lds_wait(reinterpret_cast<i16x4 (&)[2 * DB * 2]>(kr));
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
                 const V8 sb = pack_op<E>(pacc, c2);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) dqacc[db] = E::mma(tr_join<E>(kr[c2][db]), sb, dqacc[db]);
+                for (int db = 0; db < DB; ++db) {
+                    if constexpr (DIRECT)
+                        dqacc[db] = E::mma(tr_join<E>(kr[c2][db]), sb, dqacc[db]);
+                    else
+                        dqacc[db] = E::mma(lds_tr_op<E, STR>(Ks, (kb * 2 + c2) * 16, db * 32, lane), sb, dqacc[db]);
+                }
             }
         }
     };
 
     for (int t = 0; t < ntiles; ++t) {
-        wait_vmcnt<2 * (P - 1) * LOADS>();  // own loads of tile t
-        bare_barrier();                       // everyone's; tile t - 1 no longer read
-        load_t(t + P);
+        if constexpr (DIRECT) {
+            wait_vmcnt<0>();  // own loads of tile t
+            bare_barrier();   // everyone's; tile t - 1 no longer read
+            load_t(t + 1);
+        }
         const int k0 = t * BNK;
         // wave-uniform: skip key tiles entirely after this wave's last query
         if (!causal || k0 <= qw0 + 31) {
@@ -512,8 +552,15 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
             else
                 tile(std::false_type{}, t, k0);
         }
+        if constexpr (!DIRECT) {
+            if (t + 1 < ntiles) {
+                stage(t + 1);
+                if (t + 2 < ntiles) fetch(t + 2);
+            }
+            __syncthreads();
+        }
     }
-    wait_vmcnt<0>();  // no load into LDS outlives the workgroup
+    if constexpr (DIRECT) wait_vmcnt<0>();  // no load into LDS outlives the workgroup
 
     if (q < S) {
         uint16_t* dQr = dQ + base + (size_t)q * D;
