@@ -9,6 +9,8 @@ from .attention import (  # noqa: F401
     attention_head,
     decode,
     decode_head,
+    e4m3_decode,
+    fp8qk_forward,
     gqa_backward,
     gqa_forward,
     head_backward,

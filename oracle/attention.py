@@ -47,6 +47,17 @@ row against a long cache).  With per-sequence cache lengths, batch entry b uses
 its first kv_lens[b] rows; a length of 0 leaves no visible key, and the result
 is o = 0, LSE = -inf (the convention of a row whose exponential sum is 0).
 
+fp8 query and key (inference forward): Q and K arrive as OCP FP8 E4M3 codes with
+one dequantisation factor each.  The Rigel paper (§6 on the low-precision
+formats) states that the E4M3 values are the OCP grid, with no infinity (overflow
+saturates to 448 on encoding; codes 0x7F and 0xFF are NaN), and (same section,
+the accumulator-width probe) that fp8 products are accumulated in at least fp32.
+Each code is decoded exactly to float64 from the format's definition (sign bit,
+4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 gives the
+subnormals m * 2^-9), multiplied by its factor, and the result is plain
+attention on those values: the oracle sums the exact products in float64, the
+definition the GPU's fp32 matrix-instruction sums approximate.
+
 Parity status: pinned.  Each function here is checked in tests/test_oracle_pins.py
 against closed forms, invariants, central finite differences, torch's float64
 scaled_dot_product_attention on tiny shapes (with enable_gqa for the grouped
@@ -67,6 +78,8 @@ __all__ = [
     "gqa_backward",
     "decode_head",
     "decode",
+    "e4m3_decode",
+    "fp8qk_forward",
 ]
 
 
@@ -222,3 +235,30 @@ def decode(q, k, v, scale: float, kv_lens=None):
         for h in range(H):
             o[b, h], lse[b, h] = decode_head(q[b, h], k[b, h // G, :n], v[b, h // G, :n], scale)
     return o, lse
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """OCP FP8 E4M3 codes (uint8) -> float64 values, exactly.
+
+    Bit 7 is the sign, bits 6..3 the exponent field e (bias 7), bits 2..0 the
+    mantissa m: e = 0 gives the subnormal m / 8 * 2^-6, otherwise (1 + m / 8) * 2^(e - 7);
+    the two codes with e = 15 and m = 7 (0x7F, 0xFF) are NaN, and there is no
+    infinity, so e = 15 with m < 7 are ordinary values up to 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    out = sign * mag
+    return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+def fp8qk_forward(q8, k8, v, q_descale: float, k_descale: float, scale: float, causal: bool = True):
+    """q8 [B, H, S, D] and k8 [B, H_kv, S, D] E4M3 codes, v [B, H_kv, S, D] values
+    -> (o [B, H, S, D], lse [B, H, S]), float64: plain attention on
+    q = decode(q8) * q_descale and k = decode(k8) * k_descale (grouped heads as
+    gqa_forward)."""
+    q = e4m3_decode(q8) * float(q_descale)
+    k = e4m3_decode(k8) * float(k_descale)
+    return gqa_forward(q, k, np.asarray(v, dtype=np.float64), scale, causal)

@@ -45,6 +45,10 @@ __all__ = [
     "round_to_bf16",
     "f32_to_f16_bits",
     "f16_bits_to_f32",
+    "f32_to_e4m3_codes",
+    "Fp8Workload",
+    "FP8_WORKLOADS",
+    "make_fp8_inputs",
 ]
 
 
@@ -156,6 +160,95 @@ def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
 def f16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     """Widen binary16 bit patterns to float32 (exact)."""
     return np.ascontiguousarray(b, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def f32_to_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """Round values to OCP FP8 E4M3 (nearest, ties to even, saturating at +-448);
+    return the uint8 codes.  NaN -> 0x7F (sign kept); infinities saturate to 448.
+
+    E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; the quantum is
+    2^(E - 3) for a value in [2^E, 2^(E+1)), E >= -6, and 2^-9 below 2^-6.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    sign = np.signbit(x).astype(np.uint8) << 7
+    nan = np.isnan(x)
+    a = np.minimum(np.abs(np.where(nan, 0.0, x)), 448.0)
+    _, ex = np.frexp(np.maximum(a, 2.0 ** -6))  # a' = f * 2^ex, f in [0.5, 1)
+    quantum = np.ldexp(1.0, ex - 1 - 3)
+    r = np.minimum(np.round(a / quantum) * quantum, 448.0)  # np.round: ties to even
+    sub = r < 2.0 ** -6
+    m_sub = np.round(r / 2.0 ** -9).astype(np.int64)
+    _, er = np.frexp(np.where(sub, 1.0, r))
+    E = er - 1
+    m_norm = np.round((np.where(sub, 1.0, r) / np.ldexp(1.0, E) - 1.0) * 8.0).astype(np.int64)
+    code = np.where(sub, m_sub, ((E + 7) << 3) | m_norm).astype(np.uint8)
+    code = np.where(nan, np.uint8(0x7F), code)
+    return (code | sign).astype(np.uint8)
+
+
+@dataclasses.dataclass(frozen=True)
+class Fp8Workload:
+    """Forward with fp8 (E4M3) Q and K: shape, V's type and the draw scales."""
+
+    name: str
+    B: int
+    H: int
+    Hkv: int
+    S: int
+    D: int
+    v_dtype: str  # "bf16" or "f16"
+    sigma_qk: float = 1.0
+    sigma_v: float = 1.0
+    causal: bool = True
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def fwd_flops(self) -> float:
+        """Algorithmic forward FLOPs, 4*B*H*S^2*D, halved for causal."""
+        dense = 4.0 * self.B * self.H * self.S * self.S * self.D
+        return dense / 2.0 if self.causal else dense
+
+    def with_shape(self, **kw) -> "Fp8Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# fp8 Q/K at the headline shape and at the long-sequence stress shape (sigma 4
+# on Q and K: logits of sigma ~16), V in bf16.
+FP8_WORKLOADS = {
+    "gpt205m_fp8qk": Fp8Workload("gpt205m_fp8qk", 4, 16, 16, 2048, 64, "bf16", 1.0, 1.0),
+    "long8191_fp8qk": Fp8Workload("long8191_fp8qk", 1, 16, 16, 8191, 128, "bf16", 4.0, 1.0),
+}
+
+
+def make_fp8_inputs(w: Fp8Workload, seed: int = 0) -> dict:
+    """Draw Q, K, V from ``PCG64(seed)`` (standard normals times the sigmas) and
+    quantise Q and K per tensor: descale = the power of two at or above
+    max|x| / 448, codes = E4M3(x / descale).
+
+    Returns ``q8, k8`` (uint8 codes, [B, H, S, D] and [B, H_kv, S, D]),
+    ``q_descale, k_descale`` (floats), ``v`` (float32, exact in v_dtype) and ``v_bits``.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {}
+    for name, shape in (("q", (w.B, w.H, w.S, w.D)), ("k", (w.B, w.Hkv, w.S, w.D))):
+        x = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(w.sigma_qk)
+        amax = float(np.abs(x).max()) if x.size else 1.0
+        descale = 2.0 ** math.ceil(math.log2(amax / 448.0)) if amax > 0 else 1.0
+        out[name + "8"] = f32_to_e4m3_codes(x.astype(np.float64) / descale)
+        out[name + "_descale"] = descale
+    v = rng.standard_normal(size=(w.B, w.Hkv, w.S, w.D), dtype=np.float32) * np.float32(w.sigma_v)
+    if w.v_dtype == "bf16":
+        out["v_bits"] = f32_to_bf16_bits(v)
+        out["v"] = bf16_bits_to_f32(out["v_bits"])
+    elif w.v_dtype == "f16":
+        out["v_bits"] = f32_to_f16_bits(v)
+        out["v"] = f16_bits_to_f32(out["v_bits"])
+    else:
+        raise ValueError(f"unknown v dtype {w.v_dtype!r}")
+    return out
 
 
 def make_inputs(w: Workload, seed: int = 0) -> dict:

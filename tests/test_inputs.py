@@ -103,3 +103,45 @@ def test_flop_convention():
     w = si.WORKLOADS["gpt205m_bf16"]
     assert w.flops == pytest.approx(120.26e9, rel=1e-3)
     assert w.fwd_flops == pytest.approx(34.36e9, rel=1e-3)
+
+
+# --------------------------------------------------------------- fp8 (E4M3)
+
+
+def test_e4m3_encoder_matches_torch_in_range():
+    """Round to nearest even onto the OCP E4M3 grid: torch's float8_e4m3fn
+    conversion is an independent implementation of the same rounding (within
+    +-448; beyond it torch gives NaN where this encoder saturates)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(4)
+    x = np.concatenate([rng.standard_normal(100000) * s for s in (1e-3, 3e-2, 1.0, 40.0, 200.0)])
+    x = np.clip(x, -448.0, 448.0).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(si.f32_to_e4m3_codes(x), ref)
+
+
+def test_e4m3_encoder_edges():
+    # ties to even on the grid: 1 + 1/16 lies halfway between 1 (m=0) and 1.125 (m=1)
+    assert si.f32_to_e4m3_codes(np.array([1.0625]))[0] == 0x38
+    assert si.f32_to_e4m3_codes(np.array([1.1875]))[0] == 0x3A  # halfway 1.125 / 1.25 -> m=2
+    # subnormals: quantum 2^-9; half of it ties to 0, 1.5 quanta to 2
+    assert list(si.f32_to_e4m3_codes(np.array([2.0 ** -10, 1.5 * 2.0 ** -9, 2.0 ** -9, 2.0 ** -6]))) == [0, 2, 1, 8]
+    # saturation at 448 (the Rigel paper, §6: E4M3 has no infinity and clamps to +-448)
+    sat = si.f32_to_e4m3_codes(np.array([449.0, 464.0, 1e9, np.inf, -np.inf, -500.0]))
+    assert list(sat) == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE]
+    assert si.f32_to_e4m3_codes(np.array([np.nan]))[0] & 0x7F == 0x7F
+    assert si.f32_to_e4m3_codes(np.array([-0.0]))[0] == 0x80
+
+
+def test_fp8_inputs():
+    w = si.FP8_WORKLOADS["long8191_fp8qk"].with_shape(S=300)
+    x = si.make_fp8_inputs(w, seed=3)
+    for n in ("q", "k"):
+        c, d = x[n + "8"], x[n + "_descale"]
+        assert c.dtype == np.uint8 and c.shape == (1, 16 if n == "q" else w.Hkv, 300, 128)
+        assert d == 2.0 ** round(np.log2(d))  # a power of two
+        assert not ((c & 0x7F) == 0x7F).any()  # no NaN codes
+        # the largest magnitude lands in the top binade of the grid
+        assert (c & 0x7F).max() >= 0x70
+    np.testing.assert_array_equal(si.bf16_bits_to_f32(x["v_bits"]), x["v"])
+    assert si.FP8_WORKLOADS["gpt205m_fp8qk"].fwd_flops == pytest.approx(34.36e9, rel=1e-3)

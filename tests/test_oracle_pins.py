@@ -466,3 +466,67 @@ def test_decode_against_torch_sdpa_float64(H, Hkv):
     kr = torch.tensor(k).repeat_interleave(G, dim=1)
     ref_lse = torch.logsumexp(scale * (tq @ kr.transpose(-1, -2))[:, :, 0], dim=-1).numpy()
     np.testing.assert_allclose(lse, ref_lse, rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------------------------------------ fp8 Q, K
+
+
+def test_e4m3_decode_matches_torch_on_every_code():
+    """All 256 codes against torch's float8_e4m3fn (an independent implementation
+    of the OCP E4M3 format), NaN codes included."""
+    torch = pytest.importorskip("torch")
+    from oracle import e4m3_decode
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = e4m3_decode(codes)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    np.testing.assert_array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+
+
+def test_e4m3_grid_facts():
+    """The Rigel paper, §6: the E4M3 grid is the OCP one, 448 is its largest value,
+    there is no infinity; 0x7F/0xFF are the only NaNs; sign symmetric; strictly
+    increasing over the positive codes; smallest subnormal 2^-9, smallest normal 2^-6."""
+    from oracle import e4m3_decode
+    v = e4m3_decode(np.arange(256, dtype=np.uint8))
+    nan = np.isnan(v)
+    assert list(np.nonzero(nan)[0]) == [0x7F, 0xFF]
+    assert not np.isinf(v).any()
+    assert np.nanmax(v) == 448.0 and np.nanmin(v) == -448.0
+    np.testing.assert_array_equal(v[0x80:0xFF], -v[0x00:0x7F])
+    assert (np.diff(v[0x00:0x7F]) > 0).all()
+    assert v[0x01] == 2.0 ** -9 and v[0x08] == 2.0 ** -6 and v[0x38] == 1.0
+
+
+def test_fp8qk_accumulator_width_cell():
+    """Rigel §6's cell through the fp8 oracle: one 448 and 127 terms 0.0625, all E4M3
+    values (tests/golden/accumulator_width.json)."""
+    import seeded_inputs as si
+    from oracle import fp8qk_forward
+    with open(os.path.join(GOLDEN, "accumulator_width.json")) as f:
+        g = json.load(f)
+    D = g["D"]
+    q = np.full((1, 1, 1, D), g["q"]["rest"])
+    q[..., 0] = g["q"]["first"]
+    k = np.full((1, 1, 1, D), g["k"]["rest"])
+    k[..., 0] = g["k"]["first"]
+    q8, k8 = si.f32_to_e4m3_codes(q), si.f32_to_e4m3_codes(k)
+    _, lse = fp8qk_forward(q8, k8, np.ones((1, 1, 1, D)), 1.0, 1.0, g["scale"], True)
+    assert lse[0, 0, 0] == g["lse"]
+
+
+def test_fp8qk_descales_and_grouping():
+    """The descale factors multiply the scores (q_descale * k_descale * scale enters
+    only as a product), and heads group as in gqa_forward."""
+    from oracle import e4m3_decode, fp8qk_forward
+    rng = np.random.default_rng(8)
+    q8 = rng.integers(0, 0x70, size=(2, 4, 9, 64), dtype=np.uint8) | (rng.integers(0, 2, (2, 4, 9, 64)) << 7).astype(np.uint8)
+    k8 = rng.integers(0, 0x70, size=(2, 2, 9, 64), dtype=np.uint8)
+    v = rng.standard_normal((2, 2, 9, 64))
+    o1, l1 = fp8qk_forward(q8, k8, v, 0.25, 0.5, 0.125, True)
+    o2, l2 = fp8qk_forward(q8, k8, v, 1.0, 1.0, 0.125 * 0.125, True)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, rtol=1e-12, atol=1e-12)
+    o3, l3 = gqa_forward(e4m3_decode(q8) * 0.25, e4m3_decode(k8) * 0.5, v, 0.125, True)
+    np.testing.assert_array_equal(o1, o3)
+    np.testing.assert_array_equal(l1, l3)
