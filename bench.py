@@ -30,6 +30,10 @@ import seeded_inputs as si  # noqa: E402
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
 PEAK_F32_TFLOPS = 157.3    # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5033.2   # MI355X dense fp8 MFMA: twice the bf16 rate
+# The fp8-QK forward runs half its FLOPs (Q K^T) at the fp8 rate and half (P V) at
+# the bf16 rate: its MFMA-time bound is the harmonic combination of the two.
+PEAK_FP8QK_FWD_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
 
 
@@ -40,7 +44,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gpt205m_bf16",
                     choices=sorted(si.WORKLOADS) + sorted(si.GQA_WORKLOADS) + sorted(si.F16_WORKLOADS)
-                    + sorted(si.DECODE_WORKLOADS),
+                    + sorted(si.DECODE_WORKLOADS) + sorted(si.FP8_WORKLOADS),
                     help="grouped key/value head workloads run attn_fwd_gqa / attn_bwd_gqa")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -255,6 +259,127 @@ def decode_bench(args, dev):
     print(json.dumps(result), flush=True)
 
 
+def fp8_bench(args, dev):
+    """Forward with fp8 (E4M3) Q and K (attn_fwd_fp8qk); value = algorithmic forward
+    TFLOP/s (4*B*H*S^2*D, halved for causal).  The bf16 forward on the same
+    (bf16-exact) values is timed beside it."""
+    import torch
+
+    import causal_attention_flash_amd as caf
+    from oracle import e4m3_decode
+
+    w = si.FP8_WORKLOADS[args.workload]
+    x = si.make_fp8_inputs(w, seed=0)
+    bd = caf._binding
+    q8 = torch.from_numpy(x["q8"]).to(dev)
+    k8 = torch.from_numpy(x["k8"]).to(dev)
+    v = torch.from_numpy(x["v_bits"].view(np.int16)).to(dev).view(torch.bfloat16 if w.v_dtype == "bf16" else torch.float16)
+    dt = caf.ATTN_BF16 if w.v_dtype == "bf16" else caf.ATTN_F16
+    o = torch.empty((w.B, w.H, w.S, w.D), dtype=v.dtype, device=dev)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def step():
+        st = bd.c_attn_fwd_fp8qk(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.H,
+                                 w.Hkv, w.S, w.D, w.scale, x["q_descale"], x["k_descale"], int(w.causal), dt, stream)
+        if st != 0:
+            raise caf.AttnError(st, "fwd_fp8qk")
+
+    if args.profile_steps:
+        for _ in range(args.profile_steps):
+            step()
+        torch.cuda.synchronize()
+        print(f"profile run: {args.profile_steps} steps of {w.name}", flush=True)
+        return
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record()
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    mean_ms = sum(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)) / args.steps
+    # the bf16 forward on the decoded values (exact in bf16: power-of-two descales)
+    qb = torch.from_numpy(si.f32_to_bf16_bits((e4m3_decode(x["q8"]) * x["q_descale"]).astype(np.float32))
+                          .view(np.int16)).to(dev).view(torch.bfloat16)
+    kb = torch.from_numpy(si.f32_to_bf16_bits((e4m3_decode(x["k8"]) * x["k_descale"]).astype(np.float32))
+                          .view(np.int16)).to(dev).view(torch.bfloat16)
+    vb = v if w.v_dtype == "bf16" else v.to(torch.bfloat16)
+
+    def step_bf16():
+        st = bd.c_attn_fwd_gqa(qb.data_ptr(), kb.data_ptr(), vb.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.H,
+                               w.Hkv, w.S, w.D, w.scale, int(w.causal), caf.ATTN_BF16, stream)
+        if st != 0:
+            raise caf.AttnError(st, "fwd_gqa")
+
+    for _ in range(args.warmup):
+        step_bf16()
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        step_bf16()
+    ev1.record()
+    torch.cuda.synchronize()
+    bf16_ms = ev0.elapsed_time(ev1) / args.steps
+    value = w.fwd_flops * args.steps / (gpu_ms * 1e-3) / 1e12
+    achieved = w.fwd_flops / (mean_ms * 1e-3) / 1e12
+    result = {
+        "metric": "causal attention forward TFLOP/s, fp8 (E4M3) Q and K, on 1 GPU",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(gpu_ms / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 (Q, K) / " + w.v_dtype + " (V, P, O)",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.Hkv, "S": w.S, "D": w.D, "causal": w.causal,
+                   "q_descale": x["q_descale"], "k_descale": x["k_descale"], "parallelism": "none (1 GPU)"},
+        "wall_s_timed": round(wall, 4),
+        "kernel_ms": {"fwd_fp8qk": round(mean_ms, 5), "fwd_bf16_same_values": round(bf16_ms, 5)},
+        "roofline": {"kernel": "fwd_fp8qk", "bound": "mfma", "achieved": round(achieved, 3),
+                     "peak": round(PEAK_FP8QK_FWD_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP8QK_FWD_TFLOPS, 5), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import fp8qk_forward
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        except Exception:  # pragma: no cover
+            cores = os.cpu_count() or 1
+        G = w.H // w.Hkv
+        heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+        t0 = time.perf_counter()
+        done = 0
+        for b, h in heads:
+            fp8qk_forward(x["q8"][b:b + 1, h:h + 1], x["k8"][b:b + 1, h // G:h // G + 1],
+                          x["v"][b:b + 1, h // G:h // G + 1], x["q_descale"], x["k_descale"], w.scale, w.causal)
+            done += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        dtc = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(done * w.fwd_flops / len(heads) / dtc / 1e12, 6),
+                                  "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+                                  "sample": f"{done} of {len(heads)} heads (S={w.S}, D={w.D}), fp64 forward, "
+                                            f"{dtc:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -272,6 +397,9 @@ def main():
         sys.exit(1)
     caf.load_library()
     dev = torch.device("cuda:0")
+    if args.workload in si.FP8_WORKLOADS:
+        fp8_bench(args, dev)
+        return
     if args.workload in si.DECODE_WORKLOADS:
         decode_bench(args, dev)
         return

@@ -9,6 +9,7 @@ stream; all computation runs in the library's kernels.
     o, lse = attn_fwd_gqa(q, k, v)          # K, V with fewer (grouped) heads
     dq, dk, dv = attn_bwd_gqa(q, k, v, o, do, lse)
     o, lse = attn_decode(q, k_cache, v_cache, kv_lens=None)  # one query row per head
+    o, lse = attn_fwd_fp8qk(q8, k8, v, q_descale, k_descale)  # fp8 (E4M3) Q and K
 """
 from ._binding import (  # noqa: F401
     ATTN_BF16,
@@ -26,6 +27,7 @@ from ._binding import (  # noqa: F401
     attn_bwd_preprocess,
     attn_decode,
     attn_fwd,
+    attn_fwd_fp8qk,
     attn_fwd_gqa,
     load_library,
     status_string,

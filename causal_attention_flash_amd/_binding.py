@@ -38,6 +38,7 @@ _SZ = ctypes.c_size_t
 SIGNATURES = {
     "attn_fwd": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _INT, _INT, _P]),
     "attn_fwd_gqa": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _INT, _INT, _P]),
+    "attn_fwd_fp8qk": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _F, _F, _INT, _INT, _P]),
     "attn_bwd_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _INT]),
     "attn_bwd_gqa_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64, _INT]),
     "attn_bwd": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64, _I64, _I64, _F, _INT, _INT, _P]),
@@ -95,6 +96,12 @@ def c_attn_fwd(q, k, v, o, lse, B, H, S, D, scale, causal, dtype, stream=0) -> i
 
 def c_attn_fwd_gqa(q, k, v, o, lse, B, H, H_kv, S, D, scale, causal, dtype, stream=0) -> int:
     return load_library().attn_fwd_gqa(q, k, v, o, lse, B, H, H_kv, S, D, scale, causal, dtype, stream)
+
+
+def c_attn_fwd_fp8qk(q, k, v, o, lse, B, H, H_kv, S, D, scale, q_descale, k_descale, causal, dtype,
+                     stream=0) -> int:
+    return load_library().attn_fwd_fp8qk(q, k, v, o, lse, B, H, H_kv, S, D, scale, q_descale, k_descale, causal,
+                                         dtype, stream)
 
 
 def c_attn_bwd_workspace_bytes(B, H, S, D, dtype) -> int:
@@ -241,6 +248,29 @@ def attn_fwd_gqa(q, k, v, scale=None, causal=True):
     lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     _call(c_attn_fwd_gqa, "attn_fwd_gqa", q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
           B, H, Hkv, S, D, _scale(scale, D), int(bool(causal)), _dtype_code(q), _stream(q.device))
+    return o, lse
+
+
+def attn_fwd_fp8qk(q8, k8, v, q_descale, k_descale, scale=None, causal=True):
+    """O, LSE = attn_fwd_fp8qk(Q8, K8, V, q_descale, k_descale): Q8 [B,H,S,D] and K8
+    [B,H_kv,S,D] hold OCP E4M3 codes (torch.uint8 or torch.float8_e4m3fn) whose
+    values are code * descale; V [B,H_kv,S,D] is bf16 or fp16 and sets O's type."""
+    torch = _torch()
+    fp8 = getattr(torch, "float8_e4m3fn", None)
+    for name, t in (("q8", q8), ("k8", k8)):
+        if t.dtype not in (torch.uint8, fp8):
+            raise ValueError(f"{name} must hold E4M3 codes (torch.uint8 or torch.float8_e4m3fn), not {t.dtype}")
+    Hkv = _kv_heads(q8, k8)
+    B, H, S, D = q8.shape
+    _check_tensors((("q8", q8),), q8.shape, q8.dtype, q8.device)
+    _check_tensors((("k8", k8),), k8.shape, k8.dtype, q8.device)
+    _check_tensors((("v", v),), k8.shape, v.dtype, q8.device)
+    dt = _dtype_code(v)
+    o = torch.empty((B, H, S, D), dtype=v.dtype, device=q8.device)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q8.device)
+    _call(c_attn_fwd_fp8qk, "attn_fwd_fp8qk", q8.data_ptr(), k8.data_ptr(), v.data_ptr(), o.data_ptr(),
+          lse.data_ptr(), B, H, Hkv, S, D, _scale(scale, D), float(q_descale), float(k_descale),
+          int(bool(causal)), dt, _stream(q8.device))
     return o, lse
 
 

@@ -150,7 +150,8 @@ const char* attn_status_string(attn_status s) {
         case ATTN_ERR_SHAPE:
             return "negative size, sizes beyond B*H*S < 2^31 and S*D < 2^31, or H_kv < 1 or not dividing H";
         case ATTN_ERR_UNSUPPORTED:
-            return "unsupported: D must be 64, 80, 96 or 128, dtype ATTN_F32, ATTN_BF16 or ATTN_F16, causal 0 or 1, scale finite and > 0";
+            return "unsupported: D must be 64, 80, 96 or 128 (64 or 128 with fp8 Q and K), dtype ATTN_F32, ATTN_BF16 "
+                   "or ATTN_F16 (16-bit with fp8 Q and K), causal 0 or 1, scale and fp8 descale factors finite and > 0";
         case ATTN_ERR_ALIGNMENT: return "a device pointer is not 16-byte aligned";
         case ATTN_ERR_WORKSPACE: return "workspace is NULL or smaller than attn_bwd_workspace_bytes()";
         case ATTN_ERR_HIP: return "the HIP runtime reported an error at launch";
@@ -187,6 +188,36 @@ attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, f
     return from_hip(dtype == ATTN_BF16  ? attn::launch_fwd_bf16(a)
                     : dtype == ATTN_F16 ? attn::launch_fwd_f16(a)
                                         : attn::launch_fwd_f32(a));
+}
+
+attn_status attn_fwd_fp8qk(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                           int64_t H, int64_t H_kv, int64_t S, int64_t D, float scale, float q_descale,
+                           float k_descale, int causal, attn_dtype dtype, void* stream) {
+    bool empty = false;
+    attn_status st = check_shape(B, H, S, D, dtype, &empty);
+    // the fp8 product contracts 64 values per instruction; V and O are 16-bit
+    if (st == ATTN_OK && ((D != 64 && D != 128) || !is16(dtype))) st = ATTN_ERR_UNSUPPORTED;
+    if (st == ATTN_OK) st = check_groups(H, H_kv, empty);
+    if (st == ATTN_OK) st = check_scale_causal(scale, causal);
+    if (st == ATTN_OK && (!(q_descale > 0.f) || !isfinite(q_descale) || !(k_descale > 0.f) ||
+                          !isfinite(k_descale) || !isfinite(scale * q_descale * k_descale) ||
+                          !(scale * q_descale * k_descale > 0.f)))
+        st = ATTN_ERR_UNSUPPORTED;
+    if (st != ATTN_OK || empty) return st;
+    if ((st = check_ptrs({q, k, v, o, lse})) != ATTN_OK) return st;
+    const Sizes z = sizes(B, H, S, D, dtype);
+    const size_t zkv = z.tensor / (size_t)H * (size_t)H_kv;  // V: 16-bit elements
+    if ((st = check_alias({{o, z.tensor}, {lse, z.rows}}, {{q, z.tensor / 2}, {k, zkv / 2}, {v, zkv}})) != ATTN_OK)
+        return st;
+    LaunchArgs a = base_args(B, H, S, D, scale, causal, stream);
+    a.Hkv = H_kv;
+    a.qk_descale = q_descale * k_descale;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    return from_hip(dtype == ATTN_BF16 ? attn::launch_fwd_fp8qk_bf16(a) : attn::launch_fwd_fp8qk_f16(a));
 }
 
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D, attn_dtype dtype) {

@@ -173,6 +173,27 @@ struct F16 {
     }
 };
 
+// fp8 (OCP E4M3) operands of v_mfma_f32_32x32x64_f8f6f4, for S^T = K Q^T only: a
+// lane holds 32 values of its row (row lane % 32), at the contraction indices
+// 32h .. 32h+31 of a 64-wide step, h = lane / 32 (the same map for both
+// operands, so the instruction pairs equal indices; checked on the device
+// against an fp64 dot product).  Format codes 0 select E4M3 for both operands;
+// zero scale operands leave the products unscaled.  The instruction sums the
+// exact fp8 products in fp32 with a narrower internal alignment than a serial
+// fp32 sum (relative differences up to ~6e-5 on random 64-term sums, measured;
+// one 448 and 63 terms of 0.0625 sum exactly).
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+struct Fp8E4M3 {
+    using Op = i32x8;
+    static __device__ __forceinline__ f32x16 mma(const Op& a, const Op& b, const f32x16& c) {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+    }
+    static __device__ __forceinline__ Op join(const u32x4& lo, const u32x4& hi) {
+        const u32x4 v[2] = {lo, hi};
+        return __builtin_bit_cast(Op, v);
+    }
+};
+
 // Generic forms of the helpers above for an element type E.
 template <class E>
 __device__ __forceinline__ typename E::V8 as_op(const u32x4& u) {

@@ -15,13 +15,17 @@
 //
 // swz(r) = 2*(r % 4) + (r / 4) % 2 makes both operand reads conflict-free (rows
 // of 128 or 256 bytes start on the same bank; a 16-byte slot covers 4 of the 32
-// four-byte banks):
+// four-byte banks a 16-byte read of 8 lanes spans):
 // * 16-byte row reads (8 consecutive rows, one logical chunk): swz takes 8
 //   distinct values over 8 consecutive rows, so the 8 slots are distinct;
 // * transposing reads (groups of 4 consecutive rows r..r+3, r % 4 == 0, each
 //   reading a pair of adjacent chunks 2p, 2p+1): swz / 2 = r % 4 differs across
 //   the 4 rows and swz keeps pairs together, so the 4 pairs occupy distinct slot
 //   pairs.
+// Rows of 64 bytes (4 slots; fp8 rows of 64 elements, read only as 16-byte row
+// operands) use swz4(r) = (r / 2) % 4: even and odd rows start 64 bytes apart,
+// and over 8 consecutive rows the 4 even (and the 4 odd) ones take 4 distinct
+// slots.
 #pragma once
 
 #include "attn_tiles.h"
@@ -31,6 +35,7 @@ namespace attn {
 constexpr int pow2_up(int x) { return x <= 1 ? 1 : 2 * pow2_up((x + 1) / 2); }
 
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+__device__ __forceinline__ int swz4(int r) { return (r >> 1) & 3; }
 
 // Byte address within LDS of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -81,7 +86,8 @@ struct DTile {
     static constexpr int ELEMS = ROWS * RS;        // LDS footprint (elements)
     static constexpr int LOADS = ROWS * RP / (64 * NW);  // load instructions per wave per tile
     static_assert(ROWS * RP % (64 * NW) == 0, "tile must split evenly over the waves");
-    static_assert(RP <= 16, "swizzle covers up to 16 slots");
+    static_assert(RP == 4 || RP == 8 || RP == 16, "swizzles cover rows of 4, 8 or 16 slots");
+    __device__ static __forceinline__ int sw(int r) { return RP == 4 ? swz4(r) : swz(r); }
 
     // Byte offsets (within the tile's global rows) each lane fetches, one per
     // load instruction; slots with no logical chunk get an offset past any range.
@@ -92,7 +98,7 @@ struct DTile {
             for (int i = 0; i < LOADS; ++i) {
                 const int p = (i * NW + wave) * 64 + lane;  // slot this lane fills
                 const int row = p / RP, slot = p % RP;
-                const int c = slot ^ swz(row);
+                const int c = slot ^ sw(row);
                 off[i] = c < CPR ? (row * D + c * 8) * 2 : 0x7fffff00;
             }
         }
@@ -116,7 +122,7 @@ struct DTile {
 
     // element offset of logical (row, col), col % 4 == 0
     __device__ static __forceinline__ int at(int r, int col) {
-        return r * RS + ((((col >> 3) ^ swz(r)) << 3) | (col & 7));
+        return r * RS + ((((col >> 3) ^ sw(r)) << 3) | (col & 7));
     }
 };
 

@@ -41,14 +41,36 @@ namespace attn {
 
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D, int QB, int NW_>
+// The S^T = K Q^T product: 16-bit Q and K of the element type E, or fp8 (E4M3)
+// Q and K.  Op is the MFMA operand, STEPS the MFMAs per 32x32 score block, KD the
+// 16-bit slots per K row in LDS (an fp8 row of D bytes is D/2 slots).
+template <class E, int D, bool QK8>
+struct QkOps {
+    using Op = typename E::V8;
+    static constexpr int STEPS = HeadDim<D>::KSTEPS;
+    static constexpr int KD = D;
+    static __device__ __forceinline__ f32x16 mma(const Op& a, const Op& b, const f32x16& c) { return E::mma(a, b, c); }
+};
+template <class E, int D>
+struct QkOps<E, D, true> {
+    using Op = Fp8E4M3::Op;
+    static constexpr int STEPS = D / 64;
+    static constexpr int KD = D / 2;
+    static __device__ __forceinline__ f32x16 mma(const Op& a, const Op& b, const f32x16& c) {
+        return Fp8E4M3::mma(a, b, c);
+    }
+};
+
+template <int D, int QB, int NW_, bool QK8 = false>
 struct FwdCfg {
     static constexpr int NW = NW_;
     static constexpr int NT = NW * 64;
     static constexpr int BM = NW * 32 * QB;  // queries per workgroup
     static constexpr int BN = 64;            // keys per tile
-    using Tile = DTile<BN, D, NW>;
-    static constexpr int TE = Tile::ELEMS;   // one K or V tile in LDS (elements)
+    using Tile = DTile<BN, D, NW>;           // V tile
+    static constexpr int TE = Tile::ELEMS;   // one V tile in LDS (elements)
+    using KTile = DTile<BN, QK8 ? D / 2 : D, NW>;  // K tile (fp8 rows: D bytes)
+    static constexpr int TK = KTile::ELEMS;
     // LDS buffers per operand: a tile is fetched during the iteration before its
     // use (fetching two ahead measured no faster)
     static constexpr int NB = 2;
@@ -57,21 +79,25 @@ struct FwdCfg {
     static constexpr int DB = HeadDim<D>::DB;
 };
 
-template <class E, int D, int QB, int NW>
-__global__ __launch_bounds__(NW * 64) void fwd_mfma_kernel(const uint16_t* __restrict__ Q,
-                                                       const uint16_t* __restrict__ K,
+// QK8: Q and K hold fp8 (E4M3) bytes and c carries their dequantisation factors.
+template <class E, int D, int QB, int NW, bool QK8>
+__global__ __launch_bounds__(NW * 64) void fwd_mfma_kernel(const void* __restrict__ Q,
+                                                       const void* __restrict__ K,
                                                        const uint16_t* __restrict__ V,
                                                        uint16_t* __restrict__ O, float* __restrict__ LSE,
                                                        int S, int nblk, int BH, int H, int GQ, float c,
                                                        int causal) {
-    using Cfg = FwdCfg<D, QB, NW>;
+    using Cfg = FwdCfg<D, QB, NW, QK8>;
     using V8 = typename E::V8;
-    constexpr int BM = Cfg::BM, BN = Cfg::BN, TE = Cfg::TE, NB = Cfg::NB, P = Cfg::P;
-    constexpr int LOADS = Cfg::Tile::LOADS;
+    using QK = QkOps<E, D, QK8>;
+    using QOp = typename QK::Op;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, TE = Cfg::TE, TK = Cfg::TK, NB = Cfg::NB, P = Cfg::P;
+    // loads per wave of one K tile plus one V tile
+    constexpr int LOADS2 = Cfg::KTile::LOADS + Cfg::Tile::LOADS;
     constexpr int KB = BN / 32;  // 32-key blocks per tile
-    constexpr int KS = Cfg::KS, DB = Cfg::DB;
+    constexpr int QS = QK::STEPS, DB = Cfg::DB;
     // K[NB], V[NB]
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * NB * TE];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NB * (TK + TE)];
 
     const WorkItem wi = heavy_first(blockIdx.x, BH);
     const int head = wi.head;
@@ -79,8 +105,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma_kernel(const uint16_t* __res
     const int q0 = qblk * BM;
     const size_t base = (size_t)head * S * D;
     const size_t kvbase = (size_t)kv_head_of(head, H, GQ) * S * D;
-    const uint16_t* Qh = Q + base;
-    const uint16_t* Kh = K + kvbase;
+    // Q and K rows as 16-bit slots (QK::KD per row; fp8 rows of D bytes are D / 2)
+    const uint16_t* Qh = (const uint16_t*)Q + (QK8 ? base / 2 : base);
+    const uint16_t* Kh = (const uint16_t*)K + (QK8 ? kvbase / 2 : kvbase);
     const uint16_t* Vh = V + kvbase;
 
     const int tid = threadIdx.x;
@@ -93,23 +120,46 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma_kernel(const uint16_t* __res
     // tiles this wave multiplies: the causal ones up to its last query
     const int nw = causal ? min(ntiles, (qw0 + 32 * QB - 1) / BN + 1) : ntiles;
 
-    auto kbuf = [&](int t) { return smem + (t % NB) * TE; };
-    auto vbuf = [&](int t) { return smem + (NB + t % NB) * TE; };
+    auto kbuf = [&](int t) { return smem + (t % NB) * TK; };
+    auto vbuf = [&](int t) { return smem + NB * TK + (t % NB) * TE; };
     typename Cfg::Tile::Src src;
     src.init(wave, lane);
+    typename Cfg::KTile::Src ksrc;
+    ksrc.init(wave, lane);
     DOffsets<typename Cfg::Tile, D> lo;
     lo.init(lane);
+    // K row operand offsets: 16-bit, the DOffsets row reads; fp8, two 16-byte
+    // chunks per step (indices 64s + 32h .. +31: slots 32s + 16h and +8)
+    int k8[QK8 ? QS : 1][2];
+    if constexpr (QK8) {
+#pragma unroll
+        for (int st = 0; st < QS; ++st) {
+            k8[st][0] = Cfg::KTile::at(n, st * 32 + 16 * h);
+            k8[st][1] = Cfg::KTile::at(n, st * 32 + 16 * h + 8);
+        }
+    }
 
-    // Q as the B operand of S^T = K Q^T: lane holds query qw0+32qb+n, d = 16ks+8h..+7.
-    V8 qf[QB][KS];
+    // Q as the B operand of S^T = K Q^T: lane holds query qw0+32qb+n; 16-bit:
+    // d = 16ks+8h..+7; fp8: d = 64s+32h..+31.
+    QOp qf[QB][QS];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int q = qw0 + qb * 32 + n;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            u32x4 u = {0u, 0u, 0u, 0u};
-            if (q < S) u = ldg16(Qh + (size_t)q * D + ks * 16 + 8 * h);
-            qf[qb][ks] = as_op<E>(u);
+        for (int st = 0; st < QS; ++st) {
+            const uint16_t* row = Qh + (size_t)q * QK::KD;
+            if constexpr (QK8) {
+                u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+                if (q < S) {
+                    a = ldg16(row + st * 32 + 16 * h);
+                    b = ldg16(row + st * 32 + 16 * h + 8);
+                }
+                qf[qb][st] = Fp8E4M3::join(a, b);
+            } else {
+                u32x4 u = {0u, 0u, 0u, 0u};
+                if (q < S) u = ldg16(row + st * 16 + 8 * h);
+                qf[qb][st] = as_op<E>(u);
+            }
         }
     }
 
@@ -125,26 +175,32 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma_kernel(const uint16_t* __res
             for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
     }
 
-    // K rows of tile t as A operands of S^T = K Q^T:
-    // kf[kb][ks] = K[t*BN + 32kb + n][16ks + 8h .. +7].
-    auto load_k = [&](V8 (&kf)[KB][KS], int t) {
+    // K rows of tile t as A operands of S^T = K Q^T: kf[kb][st] holds key
+    // t*BN + 32kb + n, at the contraction indices of the Q operand.
+    auto load_k = [&](QOp (&kf)[KB][QS], int t) {
         const uint16_t* Ks = kbuf(t);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                kf[kb][ks] = lo.template row_op<E>(Ks, kb * 32, ks);
+            for (int st = 0; st < QS; ++st) {
+                if constexpr (QK8) {
+                    const uint16_t* r = Ks + kb * 32 * Cfg::KTile::RS;
+                    kf[kb][st] = Fp8E4M3::join(lds16(r + k8[st][0]), lds16(r + k8[st][1]));
+                } else {
+                    kf[kb][st] = lo.template row_op<E>(Ks, kb * 32, st);
+                }
+            }
     };
     // S^T tile from K operands already in registers; the first contraction step
     // starts from a zero accumulator.
-    auto mma_scores = [&](f32x16 (&sacc)[QB][KB], const V8 (&kf)[KB][KS]) {
+    auto mma_scores = [&](f32x16 (&sacc)[QB][KB], const QOp (&kf)[KB][QS]) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int st = 0; st < QS; ++st)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
-                    sacc[qb][kb] = E::mma(kf[kb][ks], qf[qb][ks], ks == 0 ? f32x16{} : sacc[qb][kb]);
+                    sacc[qb][kb] = QK::mma(kf[kb][st], qf[qb][st], st == 0 ? f32x16{} : sacc[qb][kb]);
     };
 
     // One key tile t: softmax of its scores `cur` and O += V_t P_t.  With NEXT,
@@ -156,7 +212,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma_kernel(const uint16_t* __res
     auto step = [&](auto mask_tag, auto next_tag, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB], int t) {
         constexpr bool MASK = decltype(mask_tag)::value;
         constexpr bool NEXT = decltype(next_tag)::value;
-        V8 kf[KB][KS];
+        QOp kf[KB][QS];
         if constexpr (NEXT) load_k(kf, t + 1);
         // V^T operands, read transposed from the V tile (asynchronous: used after lds_wait)
         i16x4 vr[BN / 16][DB][2];
@@ -265,7 +321,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma_kernel(const uint16_t* __res
     // or past ntiles loads from row S: an empty buffer range, so the tile reads
     // as zeros and the count of loads stays the same on every path.
     auto row_of = [&](int t) { return t < ntiles ? t * BN : S; };
-    auto load_kt = [&](int t) { Cfg::Tile::load(Kh, row_of(t), S, kbuf(t), src, wave); };
+    auto load_kt = [&](int t) { Cfg::KTile::load(Kh, row_of(t), S, kbuf(t), ksrc, wave); };
     auto load_vt = [&](int t) { Cfg::Tile::load(Vh, row_of(t), S, vbuf(t), src, wave); };
     load_kt(0);
 #pragma unroll
@@ -273,12 +329,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma_kernel(const uint16_t* __res
         load_kt(i + 1);
         load_vt(i);
     }
-    wait_vmcnt<2 * P * LOADS>();  // K_0 landed
+    wait_vmcnt<P * LOADS2>();  // K_0 landed
     bare_barrier();
 
     f32x16 sa[QB][KB], sb[QB][KB];
     if (nw > 0) {
-        V8 kf[KB][KS];
+        QOp kf[KB][QS];
         load_k(kf, 0);
         mma_scores(sa, kf);
     }
@@ -286,7 +342,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma_kernel(const uint16_t* __res
     // Iteration t: wait for K_{t+1} and V_t (own loads, then everyone's), issue
     // the loads of K_{t+1+P} and V_{t+P}, compute.
     auto iteration = [&](int t, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB]) {
-        wait_vmcnt<2 * (P - 1) * LOADS>();
+        wait_vmcnt<(P - 1) * LOADS2>();
         bare_barrier();
         load_kt(t + 1 + P);
         load_vt(t + P);
@@ -326,28 +382,37 @@ __global__ __launch_bounds__(NW * 64) void fwd_mfma_kernel(const uint16_t* __res
     }
 }
 
-template <class E, int D, int QB, int NW>
+template <class E, int D, int QB, int NW, bool QK8>
 static hipError_t launch_fwd(const LaunchArgs& a) {
-    using Cfg = FwdCfg<D, QB, NW>;
+    using Cfg = FwdCfg<D, QB, NW, QK8>;
     const int nblk = (int)((a.S + Cfg::BM - 1) / Cfg::BM);
     const int64_t total = (int64_t)nblk * a.BH;
     if (total > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((fwd_mfma_kernel<E, D, QB, NW>), dim3((unsigned)total), dim3(Cfg::NT), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                       (int)a.S, nblk, (int)a.BH, (int)a.H, (int)(a.H / a.Hkv), a.scale * kLog2e, a.causal);
+    hipLaunchKernelGGL((fwd_mfma_kernel<E, D, QB, NW, QK8>), dim3((unsigned)total), dim3(Cfg::NT), 0, a.stream,
+                       a.q, a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, (int)a.S, nblk, (int)a.BH,
+                       (int)a.H, (int)(a.H / a.Hkv), a.scale * a.qk_descale * kLog2e, a.causal);
     return hipGetLastError();
 }
 
 template <class E>
 static hipError_t launch_fwd_type(const LaunchArgs& a) {
-    if (a.D == 64) return launch_fwd<E, 64, 1, 4>(a);
-    if (a.D == 80) return launch_fwd<E, 80, 1, 4>(a);
-    if (a.D == 96) return launch_fwd<E, 96, 1, 4>(a);
-    if (a.D == 128) return launch_fwd<E, 128, 1, 4>(a);
+    if (a.D == 64) return launch_fwd<E, 64, 1, 4, false>(a);
+    if (a.D == 80) return launch_fwd<E, 80, 1, 4, false>(a);
+    if (a.D == 96) return launch_fwd<E, 96, 1, 4, false>(a);
+    if (a.D == 128) return launch_fwd<E, 128, 1, 4, false>(a);
+    return hipErrorInvalidValue;
+}
+
+template <class E>
+static hipError_t launch_fwd_fp8qk_type(const LaunchArgs& a) {
+    if (a.D == 64) return launch_fwd<E, 64, 1, 4, true>(a);
+    if (a.D == 128) return launch_fwd<E, 128, 1, 4, true>(a);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd_bf16(const LaunchArgs& a) { return launch_fwd_type<Bf16>(a); }
 hipError_t launch_fwd_f16(const LaunchArgs& a) { return launch_fwd_type<F16>(a); }
+hipError_t launch_fwd_fp8qk_bf16(const LaunchArgs& a) { return launch_fwd_fp8qk_type<Bf16>(a); }
+hipError_t launch_fwd_fp8qk_f16(const LaunchArgs& a) { return launch_fwd_fp8qk_type<F16>(a); }
 
 }  // namespace attn

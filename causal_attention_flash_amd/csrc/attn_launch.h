@@ -31,11 +31,15 @@ struct LaunchArgs {
     int64_t S = 0;   // sequence length (decode: cache rows L)
     int64_t D = 0;
     float scale = 0.f;
+    float qk_descale = 1.f;  // fp8 Q/K: product of their dequantisation factors
     int causal = 1;
     hipStream_t stream = nullptr;
 };
 
 hipError_t launch_fwd_bf16(const LaunchArgs& a);
+// forward with fp8 (E4M3) Q and K, V and O of the named type
+hipError_t launch_fwd_fp8qk_bf16(const LaunchArgs& a);
+hipError_t launch_fwd_fp8qk_f16(const LaunchArgs& a);
 hipError_t launch_bwd_dkdv_bf16(const LaunchArgs& a);
 hipError_t launch_bwd_dq_bf16(const LaunchArgs& a);
 // dQ pass that also forms delta from O and dO and writes it to a.delta

@@ -114,6 +114,33 @@ attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, f
                          float scale, int causal, attn_dtype dtype, void* stream);
 
 /*
+ * Forward pass with fp8 Q and K (inference): the scores come from the fp8 matrix
+ * instructions, the rest is attn_fwd_gqa.
+ *   q          : device, [B,H,S,D] bytes, OCP FP8 E4M3 codes (sign, 4 exponent bits
+ *                with bias 7, 3 mantissa bits; subnormals; no infinities; 0x7F and
+ *                0xFF are NaN), read only; the values are code * q_descale.
+ *   k          : device, [B,H_kv,S,D] E4M3 codes, read only; values code * k_descale.
+ *   v          : device, [B,H_kv,S,D] of dtype (ATTN_BF16 or ATTN_F16), read only.
+ *   o, lse     : as attn_fwd_gqa (o of dtype).
+ *   q_descale, k_descale : finite, > 0 (per-tensor dequantisation factors).
+ * Computes S = scale * q_descale * k_descale * (codes of Q)(codes of K)^T: the
+ * products of two E4M3 values are exact and are summed in fp32 by
+ * v_mfma_f32_32x32x64_f8f6f4, whose internal alignment is narrower than a serial
+ * fp32 sum (relative differences up to ~6e-5 on random 64-term sums); then P, O
+ * and LSE exactly as attn_fwd_gqa.  The E4M3 grid, its saturation at 448 and the
+ * fp32 accumulation of fp8 products follow the Rigel paper (§5 "Is fp8
+ * accelerated or emulated?" and §6 on accumulator width and the low-precision
+ * formats); encoding to E4M3 (rounding, saturation, choice of the descale
+ * factors) is the caller's.
+ * Supported set: D in {64, 128}; dtype ATTN_BF16 or ATTN_F16; other rules as
+ * attn_fwd_gqa; anything else -> ATTN_ERR_UNSUPPORTED.  No backward.
+ */
+attn_status attn_fwd_fp8qk(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D,
+                           float scale, float q_descale, float k_descale, int causal,
+                           attn_dtype dtype, void* stream);
+
+/*
  * Bytes of device workspace attn_bwd needs: the fp32 delta vector, B*H*S*4 bytes.
  * Returns 0 for an empty or invalid problem.
  */

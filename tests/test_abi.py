@@ -45,7 +45,7 @@ def test_header_declares_the_boundary():
     assert set(decls) == {"attn_fwd", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_preprocess",
                           "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_delta", "attn_status_string",
                           "attn_fwd_gqa", "attn_bwd_gqa", "attn_bwd_gqa_workspace_bytes",
-                          "attn_decode", "attn_decode_workspace_bytes"}
+                          "attn_decode", "attn_decode_workspace_bytes", "attn_fwd_fp8qk"}
     for name, nargs in decls.items():
         assert len(bd.SIGNATURES[name][1]) == nargs, name
 
@@ -271,3 +271,35 @@ def test_decode_empty_and_workspace(lib):
     # with no workspace needed, a NULL workspace is accepted (the call then fails only
     # at launch, which the fake pointers would make unsafe: stop at validation)
     assert dec(L=200, ws=0, ws_bytes=0, q=P[0] + 8) == ALIGN
+
+
+# --------------------------------------------------------- fp8 Q and K forward
+
+
+def fwd8(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=2, H=8, Hkv=2, S=100, D=64, scale=0.125, qd=0.01,
+             kd=0.02, causal=1, dtype=BF16)
+    a.update(kw)
+    return bd.c_attn_fwd_fp8qk(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["S"], a["D"],
+                               a["scale"], a["qd"], a["kd"], a["causal"], a["dtype"], 0)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=0), NULL), (dict(k=0), NULL), (dict(v=0), NULL), (dict(o=0), NULL), (dict(lse=0), NULL),
+    (dict(D=80), UNSUP), (dict(D=96), UNSUP), (dict(D=112), UNSUP), (dict(dtype=F32), UNSUP), (dict(dtype=3), UNSUP),
+    (dict(scale=0.0), UNSUP), (dict(qd=0.0), UNSUP), (dict(kd=-1.0), UNSUP), (dict(qd=float("inf")), UNSUP),
+    (dict(kd=float("nan")), UNSUP), (dict(qd=1e30, kd=1e30), UNSUP), (dict(causal=2), UNSUP),
+    (dict(Hkv=3), SHAPE), (dict(Hkv=0), SHAPE), (dict(B=-1), SHAPE),
+    (dict(q=P[0] + 8), ALIGN), (dict(k=P[1] + 4), ALIGN), (dict(lse=P[4] + 4), ALIGN),
+    # K holds B*Hkv*S*D = 25600 bytes (one per code), V 51200 (bf16), O 102400
+    (dict(o=P[1] + 25600 - 16), ALIAS), (dict(lse=P[2] + 51200 - 16), ALIAS), (dict(o=P[0] + 51200 - 16), ALIAS),
+    (dict(lse=P[3] + 102400 - 16), ALIAS),
+])
+def test_fwd_fp8qk_validation(lib, kw, expect):
+    assert fwd8(**kw) == expect
+
+
+def test_fwd_fp8qk_empty_is_ok(lib):
+    assert fwd8(B=0, q=0, k=0, v=0, o=0, lse=0) == OK
+    assert fwd8(S=0) == OK
+    assert fwd8(B=0, D=80) == UNSUP  # the supported set is checked even with nothing to do
