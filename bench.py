@@ -46,6 +46,9 @@ def parse_args():
                     choices=sorted(si.WORKLOADS) + sorted(si.GQA_WORKLOADS) + sorted(si.F16_WORKLOADS)
                     + sorted(si.DECODE_WORKLOADS) + sorted(si.FP8_WORKLOADS),
                     help="grouped key/value head workloads run attn_fwd_gqa / attn_bwd_gqa")
+    ap.add_argument("--bwd", choices=("split", "atomic"), default="split",
+                    help="backward: attn_bwd (dQ pass + dK/dV pass, deterministic) or attn_bwd_atomic "
+                         "(dK/dV pass with fp32 atomic dQ; D = 64, one query head per key/value head)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--profile-steps", type=int, default=0,
@@ -405,6 +408,9 @@ def main():
         return
     w = {**si.WORKLOADS, **si.GQA_WORKLOADS, **si.F16_WORKLOADS}[args.workload]
     grouped = w.kv_heads != w.H
+    atomic = args.bwd == "atomic"
+    if atomic and (grouped or w.D != 64 or w.dtype == "f32"):
+        raise SystemExit("--bwd atomic needs D = 64, bf16 or fp16, one query head per key/value head")
     x = si.make_inputs(w, seed=0)
 
     def dev_t(name):
@@ -424,6 +430,7 @@ def main():
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
     Hkv = k.shape[1]
     nws = (bd.c_attn_bwd_gqa_workspace_bytes(B, H, Hkv, S, D, dt) if grouped
+           else bd.c_attn_bwd_atomic_workspace_bytes(B, H, S, D, dt) if atomic
            else bd.c_attn_bwd_workspace_bytes(B, H, S, D, dt))
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
@@ -441,7 +448,10 @@ def main():
             chk(bd.c_attn_fwd(P["q"], P["k"], P["v"], P["o"], P["lse"], B, H, S, D, scale, causal, dt, stream), "fwd")
 
     def bwd():
-        if grouped:
+        if atomic:
+            chk(bd.c_attn_bwd_atomic(P["q"], P["k"], P["v"], P["o"], P["do"], P["lse"], P["dq"], P["dk"], P["dv"],
+                                     P["ws"], nws, B, H, S, D, scale, causal, dt, stream), "bwd_atomic")
+        elif grouped:
             chk(bd.c_attn_bwd_gqa(P["q"], P["k"], P["v"], P["o"], P["do"], P["lse"], P["dq"], P["dk"], P["dv"],
                                   P["ws"], nws, B, H, Hkv, S, D, scale, causal, dt, stream), "bwd_gqa")
         else:
@@ -494,8 +504,9 @@ def main():
 
     # ---- per-kernel durations: the same K steps, each kernel attn_bwd launches
     # (in its order) bracketed by events; the grouped form has no stage entry
-    # points, so there the backward is timed as one (its dQ and dK/dV passes)
-    if grouped:
+    # points, so there the backward is timed as one (its dQ and dK/dV passes), and
+    # so is the atomic-dQ backward (delta, zero fill, fused pass, dQ conversion)
+    if grouped or atomic:
         names = ("fwd", "bwd")
         calls = (fwd, bwd)
     else:
@@ -536,7 +547,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "S": w.S, "D": w.D,
-                   "causal": bool(w.causal),
+                   "causal": bool(w.causal), "backward": "attn_bwd_atomic" if atomic else "attn_bwd",
                    "global_batch": w.B, "seq_len": w.S, "parallelism": "none (1 GPU)"},
         "pct_of_mfma_peak": round(100.0 * value / mfma_peak, 3),
         "wall_s_timed": round(wall, 4),

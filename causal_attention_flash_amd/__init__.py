@@ -6,6 +6,7 @@ stream; all computation runs in the library's kernels.
 
     o, lse = attn_fwd(q, k, v, scale=None, causal=True)
     dq, dk, dv = attn_bwd(q, k, v, o, do, lse, scale=None, causal=True)
+    dq, dk, dv = attn_bwd_atomic(q, k, v, o, do, lse)  # dQ by fp32 atomics (D = 64)
     o, lse = attn_fwd_gqa(q, k, v)          # K, V with fewer (grouped) heads
     dq, dk, dv = attn_bwd_gqa(q, k, v, o, do, lse)
     o, lse = attn_decode(q, k_cache, v_cache, kv_lens=None)  # one query row per head
@@ -20,6 +21,7 @@ from ._binding import (  # noqa: F401
     STATUS_NAMES,
     AttnError,
     attn_bwd,
+    attn_bwd_atomic,
     attn_bwd_dkdv,
     attn_bwd_dq,
     attn_bwd_dq_delta,

@@ -44,6 +44,9 @@ SIGNATURES = {
     "attn_bwd": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64, _I64, _I64, _F, _INT, _INT, _P]),
     "attn_bwd_gqa": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64, _I64, _I64, _I64, _F, _INT, _INT,
                             _P]),
+    "attn_bwd_atomic_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _INT]),
+    "attn_bwd_atomic": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64, _I64, _I64, _F, _INT, _INT,
+                               _P]),
     "attn_bwd_preprocess": (_INT, [_P, _P, _P, _I64, _I64, _I64, _I64, _INT, _P]),
     "attn_bwd_dkdv": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _INT, _INT, _P]),
     "attn_bwd_dq": (_INT, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _INT, _INT, _P]),
@@ -121,6 +124,16 @@ def c_attn_bwd_gqa(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, H, H_kv, S,
                    stream=0) -> int:
     return load_library().attn_bwd_gqa(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, H, H_kv, S, D, scale, causal,
                                        dtype, stream)
+
+
+def c_attn_bwd_atomic_workspace_bytes(B, H, S, D, dtype) -> int:
+    return load_library().attn_bwd_atomic_workspace_bytes(B, H, S, D, dtype)
+
+
+def c_attn_bwd_atomic(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, H, S, D, scale, causal, dtype,
+                      stream=0) -> int:
+    return load_library().attn_bwd_atomic(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, H, S, D, scale, causal,
+                                          dtype, stream)
 
 
 def c_attn_bwd_preprocess(o, do, delta, B, H, S, D, dtype, stream=0) -> int:
@@ -222,6 +235,25 @@ def attn_bwd(q, k, v, o, do, lse, scale=None, causal=True):
     ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=q.device)
     _call(c_attn_bwd, "attn_bwd", q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
           lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(),
+          B, H, S, D, _scale(scale, D), int(bool(causal)), dt, _stream(q.device))
+    return dq, dk, dv
+
+
+def attn_bwd_atomic(q, k, v, o, do, lse, scale=None, causal=True):
+    """dQ, dK, dV = attn_bwd_atomic(...): as attn_bwd, with dQ accumulated by fp32
+    atomic adds in the dK/dV pass (D = 64, bf16 or fp16; dQ not bitwise reproducible)."""
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, S, D]")
+    B, H, S, D = q.shape
+    _check_tensors((("q", q), ("k", k), ("v", v), ("o", o), ("do", do)), q.shape, q.dtype, q.device)
+    _check_tensors((("lse", lse),), (B, H, S), torch.float32, q.device)
+    dt = _dtype_code(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    nws = c_attn_bwd_atomic_workspace_bytes(B, H, S, D, dt)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=q.device)
+    _call(c_attn_bwd_atomic, "attn_bwd_atomic", q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+          do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(),
           B, H, S, D, _scale(scale, D), int(bool(causal)), dt, _stream(q.device))
     return dq, dk, dv
 

@@ -324,6 +324,52 @@ attn_status attn_bwd_dq_delta(const void* q, const void* k, const void* v, const
     return run_dq_delta(a, dtype);
 }
 
+size_t attn_bwd_atomic_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D, attn_dtype dtype) {
+    bool empty = false;
+    if (check_shape(B, H, S, D, dtype, &empty) != ATTN_OK || empty || D != 64 || !is16(dtype)) return 0;
+    const Sizes z = sizes(B, H, S, D, dtype);
+    return round256(z.rows) + (size_t)B * (size_t)H * (size_t)S * (size_t)D * sizeof(float);
+}
+
+attn_status attn_bwd_atomic(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                            int64_t B, int64_t H, int64_t S, int64_t D, float scale, int causal, attn_dtype dtype,
+                            void* stream) {
+    bool empty = false;
+    attn_status st = check_shape(B, H, S, D, dtype, &empty);
+    if (st == ATTN_OK && (D != 64 || !is16(dtype))) st = ATTN_ERR_UNSUPPORTED;
+    if (st == ATTN_OK) st = check_scale_causal(scale, causal);
+    if (st != ATTN_OK || empty) return st;
+    if ((st = check_ptrs({q, k, v, o, dout, lse, dq, dk, dv})) != ATTN_OK) return st;
+    const Sizes z = sizes(B, H, S, D, dtype);
+    const size_t wsz = attn_bwd_atomic_workspace_bytes(B, H, S, D, dtype);
+    if (!workspace || workspace_bytes < wsz) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ATTN_ERR_ALIGNMENT;
+    if ((st = check_alias({{dq, z.tensor}, {dk, z.tensor}, {dv, z.tensor}, {workspace, wsz}},
+                          {{q, z.tensor}, {k, z.tensor}, {v, z.tensor}, {o, z.tensor}, {dout, z.tensor},
+                           {lse, z.rows}})) != ATTN_OK)
+        return st;
+    LaunchArgs a = base_args(B, H, S, D, scale, causal, stream);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o_in = o;
+    a.dout = dout;
+    a.lse_in = lse;
+    a.delta = (float*)workspace;
+    a.delta_in = (const float*)workspace;
+    a.dq_acc = (float*)((char*)workspace + round256(z.rows));
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    if ((st = run_preprocess(a, dtype)) != ATTN_OK) return st;
+    if ((st = from_hip(attn::launch_fill_zero(a.dq_acc, (int64_t)(z.tensor / 2), a.stream))) != ATTN_OK) return st;
+    if ((st = from_hip(dtype == ATTN_BF16 ? attn::launch_bwd_dkdv_dqa_bf16(a) : attn::launch_bwd_dkdv_dqa_f16(a))) !=
+        ATTN_OK)
+        return st;
+    return from_hip(dtype == ATTN_BF16 ? attn::launch_dq_convert_bf16(a) : attn::launch_dq_convert_f16(a));
+}
+
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
                      int64_t S, int64_t D, float scale, int causal, attn_dtype dtype, void* stream) {

@@ -25,6 +25,7 @@
 // transposing LDS read.  The dK/dV pass stages its Q and dO tiles through
 // registers into padded rows; the dQ pass loads its K and V tiles straight from
 // HBM into swizzled rows (attn_direct.h).
+#include <algorithm>
 #include <type_traits>
 
 #include "attn_launch.h"
@@ -57,20 +58,43 @@ struct DkdvCfg {
 // key/value heads (PARTIAL = true) each query head's contribution is stored as
 // fp32 at its own [query head] slot of dKp/dVp, and the sum over the G query
 // heads of a key/value head is formed by bwd_group_sum_kernel.
-template <class E, int D, int BMQ, int NW, bool PARTIAL>
+//
+// DQA (one query head per key/value head): the pass also forms dQ, FlashAttention-2
+// style, with fp32 atomic adds (Forge RESEARCH.md §6 names atomics as the legal,
+// nondeterministic alternative to a separate dQ pass).  Per 32-query block each wave
+// holds dS for its 32 keys; dQ^T = K^T dS^T needs dS with queries on the lanes, so
+// dS goes through a per-wave LDS tile [keys][queries] and both operands come from
+// transposing reads (K^T from a per-wave copy of the wave's K rows).  Each wave
+// stores its fp32 partial for the block in its own LDS slot (the dS tile lives at
+// the start of the slot: it has been read by the time the partial is stored);
+// after a barrier every thread sums the slots of the waves that had work for the
+// block and adds its share to the fp32 accumulator dQacc in HBM (global atomic
+// adds, zero sums skipped); a second barrier frees the slots.  (Summing in one
+// slot with LDS atomics instead measured ~9x slower: eight waves' ds_add_f32 on
+// the same addresses serialise.)
+template <class E, int D, int BMQ, int NW, bool PARTIAL, bool DQA = false>
 __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) void bwd_dkdv_mfma_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ dKp, float* __restrict__ dVp, int S,
-    int nblk, int BH, int H, int GQ, float c, float scale, int causal) {
+    int nblk, int BH, int H, int GQ, float c, float scale, int causal, float* __restrict__ dQacc = nullptr) {
     using Cfg = DkdvCfg<D, BMQ, NW>;
     using V8 = typename E::V8;
     constexpr int NT = Cfg::NT, BNK = Cfg::BNK;
     constexpr int STR = Cfg::STR;
     constexpr int KS = Cfg::KS, DB = Cfg::DB;
+    static_assert(!(DQA && PARTIAL), "atomic dQ is for one query head per key/value head");
+    static_assert(!DQA || (32 * D) % (NW * 64) == 0, "the flush splits a block's 32 x D sums evenly");
     // [Q, dO][2]; both are read transposed, so the last carries the slack
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Cfg::BUF_ELEMS + Cfg::QT::TR_SLACK];
     __shared__ __attribute__((aligned(16))) float sstat[2 * Cfg::BUF_STATS];
+    // DQA: each wave's K rows [32][STR] and dQ slot [32 queries][DQS] (the odd row
+    // stride spreads a column's rows over the banks), its dS tile [32 keys][DSTR]
+    // at the start of the slot
+    constexpr int DSTR = 40, DQS = D + 1;
+    static_assert(32 * DSTR * 2 <= 32 * DQS * 4, "the dS tile fits in the slot");
+    __shared__ __attribute__((aligned(16))) uint16_t kst[DQA ? NW * 32 * STR : 1];
+    __shared__ __attribute__((aligned(16))) float dqs[DQA ? NW * 32 * DQS : 1];
 
     const WorkItem wi = heavy_first(blockIdx.x, BH);
     const int head = wi.head;
@@ -100,6 +124,15 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
         }
         kf[ks] = as_op<E>(a);
         vf[ks] = as_op<E>(b);
+    }
+    uint16_t* kst_w = kst + wave * 32 * STR;
+    float* slot_w = dqs + wave * 32 * DQS;
+    uint16_t* dst_w = reinterpret_cast<uint16_t*>(slot_w);
+    if constexpr (DQA) {
+        // the wave's K rows, for the transposing reads of K^T (zero past S)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            *reinterpret_cast<u32x4*>(kst_w + n * STR + ks * 16 + 8 * h) = __builtin_bit_cast(u32x4, kf[ks]);
     }
 
     f32x16 dkacc[DB], dvacc[DB];
@@ -150,7 +183,10 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
     // MFMAs deliver S - LSE/scale and dP - delta directly (register r of a lane
     // holds query row crow(r, h)); then P = exp2(c * acc) with c = scale*log2(e),
     // and dS = P * acc.
-    auto tile = [&](auto mask_tag, int b, int qt0) {
+    //
+    // DQA: every wave runs the per-block barrier and flush, `active` or not (a
+    // wave is inactive for a tile entirely before its first key).
+    auto tile = [&](auto mask_tag, int b, int qt0, bool active) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const uint16_t* Qs = bufp(b);
         const uint16_t* dOs = Qs + Cfg::QE;
@@ -158,6 +194,7 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
         const float* PIs = SIs + BMQ;
 #pragma unroll
         for (int qb = 0; qb < BMQ / 32; ++qb) {
+          if (!DQA || active) {
             f32x16 sacc, pacc;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
@@ -198,6 +235,52 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
                     dkacc[db] = E::mma(lds_tr_op<E, STR>(Qs, r0, db * 32, lane), sb, dkacc[db]);
                 }
             }
+            if constexpr (DQA) {
+                // dS (rounded as for dK) into the wave's [key][query] tile: lane n
+                // holds key n, queries crow(r, h) = 8g + 4h + 0..3 for r = 4g..4g+3
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    u32x2 u;
+                    u[0] = E::pack2(pacc[4 * g + 0], pacc[4 * g + 1]);
+                    u[1] = E::pack2(pacc[4 * g + 2], pacc[4 * g + 3]);
+                    *reinterpret_cast<u32x2*>(dst_w + n * DSTR + 8 * g + 4 * h) = u;
+                }
+                // dQ^T (d x 32 queries) = K^T dS^T over this wave's 32 keys
+                f32x16 dqp[DB];
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) dqp[db][r] = 0.f;
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    const V8 sb = lds_tr_op<E, DSTR>(dst_w, c2 * 16, 0, lane);
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+                        dqp[db] = E::mma(lds_tr_op<E, STR>(kst_w, c2 * 16, db * 32, lane), sb, dqp[db]);
+                }
+                // the wave's partial: lane n holds query n, d = 32db + crow(r, h)
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) slot_w[n * DQS + db * 32 + crow(r, h)] = dqp[db][r];
+            }
+          }
+          if constexpr (DQA) {
+              __syncthreads();  // every active wave's partial for the block is stored
+              // waves with work for this tile: all, or (causal) those whose first
+              // key is at most the tile's last query
+              const int last = qt0 + BMQ - 1 - n0;
+              const int nact = !causal ? NW : last < 0 ? 0 : min(NW, last / 32 + 1);
+              const size_t qrow0 = (size_t)head * S + qt0 + qb * 32;
+#pragma unroll
+              for (int i = 0; i < 32 * D / NT; ++i) {
+                  const int e = tid + i * NT, row = e / D, col = e % D;
+                  float v = 0.f;
+                  for (int w = 0; w < nact; ++w) v += dqs[w * 32 * DQS + row * DQS + col];
+                  if (qt0 + qb * 32 + row < S && v != 0.f) unsafeAtomicAdd(dQacc + (qrow0 + row) * D + col, v);
+              }
+              __syncthreads();  // slots free for the next block
+          }
         }
     };
 
@@ -205,11 +288,12 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
         const int b = (t - t0) & 1;
         const int qt0 = t * BMQ;
         // wave-uniform: skip query tiles entirely before this wave's first key
-        if (!causal || qt0 + BMQ - 1 >= kw0) {
+        const bool active = !causal || qt0 + BMQ - 1 >= kw0;
+        if (DQA || active) {
             if (causal && qt0 < kw0 + 31)
-                tile(std::true_type{}, b, qt0);
+                tile(std::true_type{}, b, qt0, active);
             else
-                tile(std::false_type{}, b, qt0);
+                tile(std::false_type{}, b, qt0, active);
         }
         if (t + 1 < ntiles) {
             stage(b ^ 1);
@@ -289,6 +373,67 @@ static hipError_t launch_dkdv_type(const LaunchArgs& a) {
 
 hipError_t launch_bwd_dkdv_bf16(const LaunchArgs& a) { return launch_dkdv_type<Bf16>(a); }
 hipError_t launch_bwd_dkdv_f16(const LaunchArgs& a) { return launch_dkdv_type<F16>(a); }
+
+// ---------------------------------------------------- atomic dQ (fused backward)
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(f32x4* __restrict__ p, int64_t n4) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// dQ = scale * dQacc, rounded to the element type; groups of 8 elements
+template <class E>
+__global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict__ acc, uint16_t* __restrict__ dq,
+                                                         int64_t n8, float scale) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(acc + i * 8);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(acc + i * 8 + 4);
+        u32x4 u;
+        u[0] = E::pack2(a[0] * scale, a[1] * scale);
+        u[1] = E::pack2(a[2] * scale, a[3] * scale);
+        u[2] = E::pack2(b[0] * scale, b[1] * scale);
+        u[3] = E::pack2(b[2] * scale, b[3] * scale);
+        *reinterpret_cast<u32x4*>(dq + i * 8) = u;
+    }
+}
+
+static unsigned stream_blocks(int64_t n) { return (unsigned)std::min<int64_t>((n + 255) / 256, 256 * 16); }
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream) {
+    const int64_t n4 = n / 4;  // n is a multiple of 4 (whole rows of D floats)
+    if (n4 == 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(stream_blocks(n4)), dim3(256), 0, stream, (f32x4*)p, n4);
+    return hipGetLastError();
+}
+
+template <class E>
+static hipError_t launch_dkdv_dqa(const LaunchArgs& a) {
+    if (a.D != 64 || a.H != a.Hkv) return hipErrorInvalidValue;
+    using Cfg = DkdvCfg<64, 64, 8>;
+    const int nblk = (int)((a.S + Cfg::BNK - 1) / Cfg::BNK);
+    const int64_t total = (int64_t)nblk * a.BH;
+    if (total > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, 64, 64, 8, false, true>), dim3((unsigned)total), dim3(Cfg::NT), 0,
+                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, a.lse_in, a.delta_in, (uint16_t*)a.dk, (uint16_t*)a.dv, nullptr,
+                       nullptr, (int)a.S, nblk, (int)a.BH, (int)a.H, 1, a.scale * kLog2e, a.scale, a.causal,
+                       a.dq_acc);
+    return hipGetLastError();
+}
+
+template <class E>
+static hipError_t launch_dq_convert(const LaunchArgs& a) {
+    const int64_t n8 = a.BH * a.S * a.D / 8;
+    if (n8 == 0) return hipSuccess;
+    hipLaunchKernelGGL((dq_convert_kernel<E>), dim3(stream_blocks(n8)), dim3(256), 0, a.stream, a.dq_acc,
+                       (uint16_t*)a.dq, n8, a.scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv_dqa_bf16(const LaunchArgs& a) { return launch_dkdv_dqa<Bf16>(a); }
+hipError_t launch_bwd_dkdv_dqa_f16(const LaunchArgs& a) { return launch_dkdv_dqa<F16>(a); }
+hipError_t launch_dq_convert_bf16(const LaunchArgs& a) { return launch_dq_convert<Bf16>(a); }
+hipError_t launch_dq_convert_f16(const LaunchArgs& a) { return launch_dq_convert<F16>(a); }
 
 // ====================================================== grouped key/value heads
 //

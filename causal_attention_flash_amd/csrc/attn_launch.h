@@ -24,6 +24,7 @@ struct LaunchArgs {
     void* dv = nullptr;
     float* dk_part = nullptr;  // grouped key/value heads: per-query-head fp32 dK, dV ([B,H,S,D])
     float* dv_part = nullptr;
+    float* dq_acc = nullptr;  // atomic-dQ backward: fp32 dQ sums ([B,H,S,D], unscaled)
     const int* kv_lens = nullptr;  // decode: rows in use of each sequence's cache ([B]), or null
     int64_t BH = 0;  // batch * query heads
     int64_t H = 0;   // query heads per batch entry
@@ -37,6 +38,13 @@ struct LaunchArgs {
 };
 
 hipError_t launch_fwd_bf16(const LaunchArgs& a);
+// atomic-dQ backward: dK/dV pass that also adds dQ into a.dq_acc (D = 64, H = H_kv),
+// the fill of the accumulator and the final dQ = scale * dq_acc
+hipError_t launch_bwd_dkdv_dqa_bf16(const LaunchArgs& a);
+hipError_t launch_bwd_dkdv_dqa_f16(const LaunchArgs& a);
+hipError_t launch_dq_convert_bf16(const LaunchArgs& a);
+hipError_t launch_dq_convert_f16(const LaunchArgs& a);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 // forward with fp8 (E4M3) Q and K, V and O of the named type
 hipError_t launch_fwd_fp8qk_bf16(const LaunchArgs& a);
 hipError_t launch_fwd_fp8qk_f16(const LaunchArgs& a);

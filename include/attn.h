@@ -166,6 +166,35 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      float scale, int causal, attn_dtype dtype, void* stream);
 
 /*
+ * Bytes of device workspace attn_bwd_atomic needs: the fp32 delta vector (B*H*S*4
+ * bytes, rounded up to 256) and the fp32 dQ accumulator (B*H*S*D*4 bytes).
+ * Returns 0 for an empty, invalid or unsupported problem.
+ */
+size_t attn_bwd_atomic_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D, attn_dtype dtype);
+
+/*
+ * Backward pass with atomic dQ accumulation (opt-in; dQ is NOT bitwise
+ * reproducible: the order of its fp32 additions varies from run to run).
+ * Arguments, outputs and errors as attn_bwd, with a workspace of
+ * attn_bwd_atomic_workspace_bytes() bytes.  Enqueues: delta = rowsum(dO o O)
+ * (fp32), a fill of the dQ accumulator with zeros, one dK/dV pass that also adds
+ * every (query block, key block) contribution to dQ into the accumulator with fp32
+ * atomic adds, and dQ = scale * accumulator rounded to dtype.  dV is
+ * bit-identical to attn_bwd's; dK equals it up to the rounding of delta, which
+ * attn_bwd forms in its dQ pass.  This is the FlashAttention-2 fused backward that
+ * Forge RESEARCH.md §6 describes as the atomic alternative to its separate,
+ * deterministic dQ pass; it saves that pass's recomputation of S and dP.
+ * Supported set: D = 64; dtype ATTN_BF16 or ATTN_F16; one query head per
+ * key/value head; other rules as attn_bwd; anything else -> ATTN_ERR_UNSUPPORTED.
+ */
+attn_status attn_bwd_atomic(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse,
+                            void* dq, void* dk, void* dv,
+                            void* workspace, size_t workspace_bytes,
+                            int64_t B, int64_t H, int64_t S, int64_t D,
+                            float scale, int causal, attn_dtype dtype, void* stream);
+
+/*
  * Backward pass with grouped key/value heads: dQ as attn_bwd; dK and dV of each
  * key/value head are the sums over the G query heads that read it (the chain
  * rule through the shared input).  bf16 or fp16 with G > 1: the dK/dV pass runs per query

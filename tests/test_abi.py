@@ -45,7 +45,8 @@ def test_header_declares_the_boundary():
     assert set(decls) == {"attn_fwd", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_preprocess",
                           "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_delta", "attn_status_string",
                           "attn_fwd_gqa", "attn_bwd_gqa", "attn_bwd_gqa_workspace_bytes",
-                          "attn_decode", "attn_decode_workspace_bytes", "attn_fwd_fp8qk"}
+                          "attn_decode", "attn_decode_workspace_bytes", "attn_fwd_fp8qk",
+                          "attn_bwd_atomic", "attn_bwd_atomic_workspace_bytes"}
     for name, nargs in decls.items():
         assert len(bd.SIGNATURES[name][1]) == nargs, name
 
@@ -303,3 +304,35 @@ def test_fwd_fp8qk_empty_is_ok(lib):
     assert fwd8(B=0, q=0, k=0, v=0, o=0, lse=0) == OK
     assert fwd8(S=0) == OK
     assert fwd8(B=0, D=80) == UNSUP  # the supported set is checked even with nothing to do
+
+
+# ------------------------------------------------------------- atomic-dQ backward
+
+
+def bwda(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], do=P[4], lse=P[5], dq=P[6], dk=P[7], dv=P[8], ws=P[9],
+             ws_bytes=1 << 30, B=2, H=4, S=100, D=64, scale=0.125, causal=1, dtype=BF16)
+    a.update(kw)
+    return bd.c_attn_bwd_atomic(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["ws"],
+                                a["ws_bytes"], a["B"], a["H"], a["S"], a["D"], a["scale"], a["causal"], a["dtype"], 0)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=0), NULL), (dict(dq=0), NULL), (dict(lse=0), NULL),
+    (dict(D=128), UNSUP), (dict(D=80), UNSUP), (dict(dtype=F32), UNSUP), (dict(scale=-1.0), UNSUP),
+    (dict(causal=5), UNSUP), (dict(B=-1), SHAPE),
+    (dict(ws=0), WS), (dict(ws_bytes=16), WS), (dict(ws=P[9] + 8), ALIGN), (dict(dk=P[7] + 4), ALIGN),
+    # dq overlapping q (each [B,H,S,D] bf16 = 51200 bytes), the workspace overlapping lse
+    (dict(dq=P[0] + 51200 - 16), ALIAS), (dict(ws=P[5]), ALIAS), (dict(dv=P[6]), ALIAS),
+])
+def test_bwd_atomic_validation(lib, kw, expect):
+    assert bwda(**kw) == expect
+
+
+def test_bwd_atomic_workspace_and_empty(lib):
+    # delta 2*4*100*4 = 3200 bytes rounded to 3328, then the fp32 dQ sums 2*4*100*64*4 bytes
+    assert bd.c_attn_bwd_atomic_workspace_bytes(2, 4, 100, 64, BF16) == 3328 + 204800
+    assert bd.c_attn_bwd_atomic_workspace_bytes(2, 4, 100, 128, BF16) == 0
+    assert bd.c_attn_bwd_atomic_workspace_bytes(2, 4, 100, 64, F32) == 0
+    assert bwda(B=0, q=0, ws=0, ws_bytes=0) == OK
+    assert bwda(S=0, D=128) == UNSUP
