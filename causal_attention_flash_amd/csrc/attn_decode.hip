@@ -340,12 +340,13 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
 }
 
 // Chunking of the cache: at least 256 rows per chunk, enough chunks that the
-// first pass has about 1024 workgroups, at most 64 chunks.
+// first pass has about 2048 workgroups (measured 3-5% faster than 1024 at both
+// decode workloads; 4096 no better), at most 64 chunks.
 DecodePlan decode_plan(int64_t B, int64_t H, int64_t Hkv, int64_t L, int64_t D) {
     const int64_t G = H / Hkv;
     const int64_t gt = G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
     const int64_t units = B * Hkv * (G / gt);
-    int64_t nsplit = (1024 + units - 1) / units;
+    int64_t nsplit = (2048 + units - 1) / units;
     const int64_t max_split = (L + 255) / 256;
     if (nsplit > max_split) nsplit = max_split;
     if (nsplit > 64) nsplit = 64;  // the merge pass reads one partial per lane
