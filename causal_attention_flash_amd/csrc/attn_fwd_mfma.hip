@@ -61,16 +61,18 @@ struct QkOps<E, D, true> {
     }
 };
 
-// BN keys per tile: 64 at D = 64; 32 for wider heads, where a 64-key tile's
-// registers (the next tile's K operands, the V^T operands, two score sets) pass
-// 256 VGPRs and leave one wave per SIMD (measured: 32-key tiles 10-25% faster at
-// D = 80, 96 and 128 with two waves per SIMD and no AGPR copies).
-template <int D, int QB, int NW_, bool QK8 = false, int BN_ = 64>
+// BN keys per tile: 32.  A 64-key tile's registers (the next tile's K operands,
+// the V^T operands, two score sets) pass 256 VGPRs at D = 80, 96 and 128 and
+// leave one wave per SIMD; 32-key tiles fit two there (measured 10-25% faster)
+// and three at D = 64 (147 VGPRs; 2.5% faster than 64-key tiles at two).
+template <int D, int QB, int NW_, bool QK8 = false, int BN_ = 32>
 struct FwdCfg {
     static constexpr int NW = NW_;
     static constexpr int NT = NW * 64;
     static constexpr int BM = NW * 32 * QB;  // queries per workgroup
     static constexpr int BN = BN_;           // keys per tile
+    // waves per SIMD the register budget is set for
+    static constexpr int WAVES_PER_SIMD = D == 64 && BN == 32 ? 3 : 2;
     using Tile = DTile<BN, D, NW>;           // V tile
     static constexpr int TE = Tile::ELEMS;   // one V tile in LDS (elements)
     using KTile = DTile<BN, QK8 ? D / 2 : D, NW>;  // K tile (fp8 rows: D bytes)
@@ -85,7 +87,7 @@ struct FwdCfg {
 
 // QK8: Q and K hold fp8 (E4M3) bytes and c carries their dequantisation factors.
 template <class E, int D, int QB, int NW, bool QK8, int BN_>
-__global__ __launch_bounds__(NW * 64) void fwd_mfma_kernel(const void* __restrict__ Q,
+__global__ __launch_bounds__(NW * 64, (FwdCfg<D, QB, NW, QK8, BN_>::WAVES_PER_SIMD)) void fwd_mfma_kernel(const void* __restrict__ Q,
                                                        const void* __restrict__ K,
                                                        const uint16_t* __restrict__ V,
                                                        uint16_t* __restrict__ O, float* __restrict__ LSE,
@@ -400,20 +402,18 @@ static hipError_t launch_fwd(const LaunchArgs& a) {
 
 template <class E>
 static hipError_t launch_fwd_type(const LaunchArgs& a) {
-    if (a.D == 64) return launch_fwd<E, 64, 1, 4, false, 64>(a);
+    if (a.D == 64) return launch_fwd<E, 64, 1, 4, false, 32>(a);
     if (a.D == 80) return launch_fwd<E, 80, 1, 4, false, 32>(a);
     if (a.D == 96) return launch_fwd<E, 96, 1, 4, false, 32>(a);
     if (a.D == 128) return launch_fwd<E, 128, 1, 4, false, 32>(a);
     return hipErrorInvalidValue;
 }
 
-#ifndef FP8_BN128
-#define FP8_BN128 32
-#endif
 template <class E>
 static hipError_t launch_fwd_fp8qk_type(const LaunchArgs& a) {
+    // (fp8 rows of 64 bytes: a 32-key K tile is too small to split over 4 waves' loads)
     if (a.D == 64) return launch_fwd<E, 64, 1, 4, true, 64>(a);
-    if (a.D == 128) return launch_fwd<E, 128, 1, 4, true, FP8_BN128>(a);
+    if (a.D == 128) return launch_fwd<E, 128, 1, 4, true, 32>(a);
     return hipErrorInvalidValue;
 }
 

@@ -106,7 +106,10 @@ def test_fp8qk_matches_bf16_forward_on_the_same_values(device):
     o, lse = caf.attn_fwd(qb, kb, gu.to_device(x, "v", "bf16", device), scale=w.scale, causal=True)
     torch.cuda.synchronize()
     assert np.abs(gu.to_host64(o) - o8).max() <= 2 ** -7
-    assert np.abs(gu.to_host64(lse) - l8).max() <= 1e-3
+    # LSE = m + log l with l the sum of the bf16-rounded P (each term off by at most
+    # 2^-9 relative, so log l by at most 2^-9); the two paths can use different key
+    # tiles, hence different reference points for P: they differ by at most 2^-8
+    assert np.abs(gu.to_host64(lse) - l8).max() <= 2 ** -8
 
 
 def test_fp8qk_accumulator_width_cell(device):
