@@ -83,6 +83,9 @@ struct FwdCfg {
     static constexpr int P = NB - 1;
     static constexpr int KS = HeadDim<D>::KSTEPS;
     static constexpr int DB = HeadDim<D>::DB;
+    // the loop masks only a wave's last key tile: a wave's 32 * QB queries must
+    // not reach into an earlier tile (else that tile also crosses the diagonal)
+    static_assert(32 * QB <= BN, "a wave's queries must fit in one key tile");
 };
 
 // QK8: Q and K hold fp8 (E4M3) bytes and c carries their dequantisation factors.
