@@ -35,13 +35,35 @@ PEAK_FP8_TFLOPS = 5033.2   # MI355X dense fp8 MFMA: twice the bf16 rate
 # the bf16 rate: its MFMA-time bound is the harmonic combination of the two.
 PEAK_FP8QK_FWD_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
+WARMUP_SECONDS = 0.3
+
+
+def warm_up(step, args, torch) -> int:
+    """Run the untimed warmup; return the number of steps run.  --warmup W runs
+    exactly W; the default runs steps (in groups of 10) until WARMUP_SECONDS of
+    wall time have passed."""
+    if args.warmup is not None:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        return args.warmup
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < WARMUP_SECONDS:
+        for _ in range(10):
+            step()
+        n += 10
+        torch.cuda.synchronize()
+    return n
 
 
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help=f"untimed warmup steps (default: as many as fill {WARMUP_SECONDS} s, so that the "
+                         "GPU's clocks have settled: after 10 steps the headline workload measured ~15%% below "
+                         "its steady state)")
     ap.add_argument("--workload", default="gpt205m_bf16",
                     choices=sorted(si.WORKLOADS) + sorted(si.GQA_WORKLOADS) + sorted(si.F16_WORKLOADS)
                     + sorted(si.DECODE_WORKLOADS) + sorted(si.FP8_WORKLOADS),
@@ -195,9 +217,7 @@ def decode_bench(args, dev):
         torch.cuda.synchronize()
         print(f"profile run: {args.profile_steps} steps of {w.name}", flush=True)
         return
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    nwarm = warm_up(step, args, torch)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
@@ -224,7 +244,7 @@ def decode_bench(args, dev):
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": nwarm,
         "ms_per_step": round(gpu_ms / args.steps, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -294,9 +314,7 @@ def fp8_bench(args, dev):
         torch.cuda.synchronize()
         print(f"profile run: {args.profile_steps} steps of {w.name}", flush=True)
         return
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    nwarm = warm_up(step, args, torch)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
@@ -326,9 +344,7 @@ def fp8_bench(args, dev):
         if st != 0:
             raise caf.AttnError(st, "fwd_gqa")
 
-    for _ in range(args.warmup):
-        step_bf16()
-    torch.cuda.synchronize()
+    warm_up(step_bf16, args, torch)
     ev0.record()
     for _ in range(args.steps):
         step_bf16()
@@ -343,7 +359,7 @@ def fp8_bench(args, dev):
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": nwarm,
         "ms_per_step": round(gpu_ms / args.steps, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -483,10 +499,7 @@ def main():
         print(f"profile run: copy of {copy_bytes} bytes, then {args.profile_steps} steps of {w.name}", flush=True)
         return
 
-    for _ in range(args.warmup):
-        fwd()
-        bwd()
-    torch.cuda.synchronize()
+    nwarm = warm_up(lambda: (fwd(), bwd()), args, torch)
 
     # ---- timed region: exactly K steps of fwd + bwd
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -539,7 +552,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": nwarm,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
