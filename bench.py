@@ -38,6 +38,28 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
 WARMUP_SECONDS = 0.3
 
 
+def step_statistics(step, k, torch, between=None) -> dict:
+    """k steps, each bracketed by HIP events: median, min and p95 of the step time
+    (ms), and a bootstrap 95% interval of the median (10^4 resamples, fixed seed).
+    `between` runs untimed after each step (a cache-clearing write)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        step()
+        b.record()
+        if between is not None:
+            between()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs])
+    rng = np.random.default_rng(0)
+    boot = np.median(t[rng.integers(0, len(t), size=(10000, len(t)))], axis=1)
+    out = {"n": k, "median": round(float(np.median(t)), 5), "min": round(float(t.min()), 5),
+           "p95": round(float(np.percentile(t, 95)), 5),
+           "ci95_median": [round(float(np.percentile(boot, 2.5)), 5), round(float(np.percentile(boot, 97.5)), 5)]}
+    return out
+
+
 def warm_up(step, args, torch) -> int:
     """Run the untimed warmup; return the number of steps run.  --warmup W runs
     exactly W; the default runs steps (in groups of 10) until WARMUP_SECONDS of
@@ -59,7 +81,7 @@ def warm_up(step, args, torch) -> int:
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=None,
                     help=f"untimed warmup steps (default: as many as fill {WARMUP_SECONDS} s, so that the "
                          "GPU's clocks have settled: after 10 steps the headline workload measured ~15%% below "
@@ -538,6 +560,14 @@ def main():
     per_kernel = {n: statistics.median(d) for n, d in durations.items()}
     per_kernel_mean = {n: sum(d) / len(d) for n, d in durations.items()}
 
+    # ---- per-step distribution (the same K steps, one event pair each); then
+    # cache-cold: 512 MiB written between steps (more than the 256 MB MALL), untimed
+    step_fn = lambda: (fwd(), bwd())  # noqa: E731
+    steps_warm = step_statistics(step_fn, args.steps, torch)
+    scratch = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+    steps_cold = step_statistics(step_fn, args.steps, torch, between=lambda: scratch.fill_(1.0))
+    del scratch
+
     units = kernel_units(w)
     dom = max(names, key=lambda n: per_kernel_mean[n])
     dom_ms = per_kernel_mean[dom]
@@ -566,6 +596,8 @@ def main():
         "wall_s_timed": round(wall, 4),
         "kernel_ms": {n: round(per_kernel_mean[n], 5) for n in names},
         "kernel_ms_median": {n: round(per_kernel[n], 5) for n in names},
+        "step_ms": steps_warm,
+        "step_ms_cache_cold": steps_cold,
         "roofline": {
             "kernel": dom,
             "bound": "mfma",
