@@ -1,0 +1,101 @@
+"""Host logic of bench.py (no GPU): the one-GPU refusal, the warm-up count, the
+per-step statistics, the roofline bookkeeping and the traffic lookup."""
+import os
+import subprocess
+import sys
+import types
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+import seeded_inputs as si  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+class FakeEvent:
+    """Stands in for torch.cuda.Event: elapsed times come from a fixed list."""
+    clock = 0.0
+    times = []
+
+    def __init__(self, enable_timing=True):
+        self.t = None
+
+    def record(self):
+        self.t = FakeEvent.clock
+
+    def elapsed_time(self, other):
+        return other.t - self.t
+
+    def query(self):
+        return True
+
+
+def fake_torch():
+    cuda = types.SimpleNamespace(Event=FakeEvent, synchronize=lambda: None)
+    return types.SimpleNamespace(cuda=cuda)
+
+
+def test_warm_up_runs_exactly_w_steps():
+    calls = []
+    args = types.SimpleNamespace(warmup=7)
+    assert bench.warm_up(lambda: calls.append(1), args, fake_torch()) == 7
+    assert len(calls) == 7
+
+
+def test_warm_up_default_fills_the_time(monkeypatch):
+    monkeypatch.setattr(bench, "WARMUP_SECONDS", 0.02)
+    calls = []
+    n = bench.warm_up(lambda: calls.append(1), types.SimpleNamespace(warmup=None), fake_torch())
+    assert n == len(calls) and n >= 10 and n % 10 == 0
+
+
+def test_step_statistics():
+    durations = iter([1.0, 2.0, 3.0, 4.0, 100.0])
+
+    def step():
+        FakeEvent.clock += next(durations)
+
+    st = bench.step_statistics(step, 5, fake_torch())
+    assert st["n"] == 5 and st["median"] == 3.0 and st["min"] == 1.0
+    assert st["p95"] == pytest.approx(np.percentile([1, 2, 3, 4, 100], 95), abs=1e-5)
+    lo, hi = st["ci95_median"]
+    assert 1.0 <= lo <= 3.0 <= hi <= 100.0
+    # `between` runs after each step, outside its event pair
+    FakeEvent.clock = 0.0
+    durations = iter([1.0] * 4)
+    st = bench.step_statistics(step, 4, fake_torch(), between=lambda: setattr(FakeEvent, "clock", FakeEvent.clock + 50))
+    assert st["median"] == 1.0 and st["min"] == 1.0
+
+
+def test_kernel_units_add_up_to_the_metric():
+    """fwd 2 units + dQ 1 + dK/dV 4 = 7 B H S^2 D (the split backward's recomputed
+    products are not algorithmic)."""
+    w = si.WORKLOADS["gpt205m_bf16"]
+    u = bench.kernel_units(w)
+    assert u["fwd"]["flops"] + u["bwd_dq"]["flops"] + u["bwd_dkdv"]["flops"] == pytest.approx(w.flops)
+    assert u["bwd"]["flops"] == pytest.approx(u["bwd_dq"]["flops"] + u["bwd_dkdv"]["flops"])
+    assert u["fwd"]["flops"] == pytest.approx(2 * w.flops / 7)
+
+
+def test_traffic_lookup_needs_matching_sources():
+    """A recorded traffic figure is used only while its kernel's sources hash to
+    the recorded value."""
+    for kernel in ("fwd", "bwd_dq", "bwd_dkdv"):
+        got = bench.read_traffic(kernel, "gpt205m_bf16")
+        with open(bench.TRAFFIC_FILE) as f:
+            rec = [ln.split() for ln in f if ln.startswith(kernel + " gpt205m_bf16 ")]
+        if rec and rec[0][2] == bench.kernel_sources_hash(kernel):
+            assert got == float(rec[0][3]) + float(rec[0][4])
+        else:
+            assert got is None
+    assert bench.read_traffic("fwd", "no_such_workload") is None
