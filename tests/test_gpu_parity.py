@@ -205,3 +205,28 @@ def test_full_size_invariants(device):
     # LSE_0 = scale * q_0 . k_0 (one visible key)
     lse0 = w.scale * np.einsum("bhd,bhd->bh", x["q"][:, :, 0].astype(np.float64), x["k"][:, :, 0])
     np.testing.assert_allclose(gpu["lse"][:, :, 0], lse0, atol=1e-4)
+
+
+def random_case(i):
+    """Case i of the seeded sweep: head dim, dtype, causality, a ragged S, small
+    B and H, the query/key spread and a scale other than 1/sqrt(D)."""
+    rng = np.random.default_rng(1000 + i)
+    D = int(rng.choice([64, 80, 96, 128]))
+    dtype = str(rng.choice(["bf16", "f16", "f32"]))
+    causal = bool(rng.integers(0, 2))
+    S = int(np.exp(rng.uniform(0.0, np.log(1500.0))))
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    sigma_qk = float(rng.choice([0.5, 1.0, 2.0]))
+    scale = float(rng.uniform(0.5, 1.5)) / np.sqrt(D)
+    return si.Workload(f"rand{i}", B, H, S, D, dtype, sigma_qk, 1.0, 1.0 if dtype == "f32" else 0.1, causal), scale
+
+
+@pytest.mark.parametrize("i", range(48))
+def test_random_shapes(device, i):
+    w, scale = random_case(i)
+    print(f"\n[random {i}] B={w.B} H={w.H} S={w.S} D={w.D} {w.dtype} causal={w.causal} "
+          f"sigma_qk={w.sigma_qk} scale={scale:.4f}", flush=True)
+    x = si.make_inputs(w, seed=5000 + i)
+    gpu = gu.run_gpu(x, w, device, causal=w.causal, scale=scale)
+    ref = oracle_heads(x, w, all_heads(w), causal=w.causal, scale=scale)
+    gu.check(gu.errors(gpu, ref, all_heads(w)), w.dtype, f"random case {i}")
