@@ -119,3 +119,22 @@ def test_grouped_query_outputs_match_repeated_kv_bitwise(device):
     for g, r in ((dk1, dk2), (dv1, dv2)):
         summed = r.float().view(2, 2, 4, 300, 64).sum(dim=2)
         assert (g.float() - summed).abs().max().item() <= 2e-2
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_gqa_random_shapes(device, i):
+    """Seeded sweep: group size G in {2, 3, 4, 8, 16}, key/value heads, head dim,
+    dtype, causality and a ragged S; every group against the oracle."""
+    rng = np.random.default_rng(2000 + i)
+    G = int(rng.choice([2, 3, 4, 8, 16]))
+    Hkv = int(rng.integers(1, 3))
+    D = int(rng.choice([64, 80, 96, 128]))
+    dtype = str(rng.choice(["bf16", "f16", "f32"]))
+    causal = bool(rng.integers(0, 2))
+    S = int(np.exp(rng.uniform(0.0, np.log(700.0))))
+    B = int(rng.integers(1, 3))
+    w = si.Workload(f"gqa_rand{i}", B, G * Hkv, S, D, dtype, 1.0, 1.0, 1.0 if dtype == "f32" else 0.1, causal, Hkv)
+    print(f"\n[gqa random {i}] B={B} H={w.H} Hkv={Hkv} S={S} D={D} {dtype} causal={causal}", flush=True)
+    x = si.make_inputs(w, seed=7000 + i)
+    gpu = run_gqa(x, w, device, causal)
+    check_groups(x, w, gpu, [(b, j) for b in range(B) for j in range(Hkv)], causal, f"gqa random case {i}")
