@@ -78,7 +78,7 @@ struct FwdCfg {
     using KTile = DTile<BN, QK8 ? D / 2 : D, NW>;  // K tile (fp8 rows: D bytes)
     static constexpr int TK = KTile::ELEMS;
     // LDS buffers per operand: a tile is fetched during the iteration before its
-    // use (fetching two ahead measured no faster)
+    // use (fetching two or three ahead measured slower)
     static constexpr int NB = 2;
     static constexpr int P = NB - 1;
     static constexpr int KS = HeadDim<D>::KSTEPS;
