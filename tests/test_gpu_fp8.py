@@ -150,3 +150,31 @@ def test_fp8qk_deterministic_and_float8_dtype(device):
     o, lse = caf.attn_fwd_fp8qk(q8, k8, gu.to_device(x, "v", "bf16", device), x["q_descale"], x["k_descale"])
     torch.cuda.synchronize()
     np.testing.assert_array_equal(gu.to_host64(o), a[0])
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_fp8qk_random_shapes(device, i):
+    """Seeded sweep: group size, head dim, V type, causality, a ragged S, the
+    query/key spread and a scale other than 1/sqrt(D)."""
+    import causal_attention_flash_amd as caf
+    torch = gu.torch_mod()
+    rng = np.random.default_rng(3000 + i)
+    G = int(rng.choice([1, 2, 4, 8]))
+    Hkv = int(rng.integers(1, 3))
+    D = int(rng.choice([64, 128]))
+    v_dtype = str(rng.choice(["bf16", "f16"]))
+    causal = bool(rng.integers(0, 2))
+    S = int(np.exp(rng.uniform(0.0, np.log(1200.0))))
+    sigma_qk = float(rng.choice([0.5, 1.0, 2.0]))
+    w = si.Fp8Workload(f"f8rand{i}", int(rng.integers(1, 3)), G * Hkv, Hkv, S, D, v_dtype, sigma_qk, 1.0, causal)
+    scale = float(rng.uniform(0.5, 1.5)) / np.sqrt(D)
+    print(f"\n[fp8 random {i}] B={w.B} H={w.H} Hkv={Hkv} S={S} D={D} v={v_dtype} causal={causal} "
+          f"sigma_qk={sigma_qk} scale={scale:.4f}", flush=True)
+    x = si.make_fp8_inputs(w, seed=9000 + i)
+    q8 = torch.from_numpy(np.ascontiguousarray(x["q8"])).to(device)
+    k8 = torch.from_numpy(np.ascontiguousarray(x["k8"])).to(device)
+    v = gu.to_device(x, "v", w.v_dtype, device)
+    o, lse = caf.attn_fwd_fp8qk(q8, k8, v, x["q_descale"], x["k_descale"], scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = fp8qk_forward(x["q8"], x["k8"], x["v"], x["q_descale"], x["k_descale"], scale, causal)
+    check(gu.to_host64(o), gu.to_host64(lse), ro, rl, f"fp8 random case {i}")
