@@ -87,3 +87,20 @@ def test_atomic_unsupported(device):
         lse = torch.zeros(1, 2, 8, dtype=torch.float32, device=device)
         with pytest.raises(caf.AttnError):
             caf.attn_bwd_atomic(q, q, q, q, q, lse)
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_atomic_random_shapes(device, i):
+    """Seeded sweep: batch, heads, dtype, causality and a ragged S (D = 64)."""
+    rng = np.random.default_rng(4000 + i)
+    dtype = str(rng.choice(["bf16", "f16"]))
+    causal = bool(rng.integers(0, 2))
+    S = int(np.exp(rng.uniform(0.0, np.log(1500.0))))
+    w = si.Workload(f"atomic_rand{i}", int(rng.integers(1, 3)), int(rng.integers(1, 5)), S, 64, dtype, 1.0, 1.0,
+                    0.1, causal)
+    print(f"\n[atomic random {i}] B={w.B} H={w.H} S={S} {dtype} causal={causal}", flush=True)
+    x = si.make_inputs(w, seed=8000 + i)
+    got, base = run_both(x, w, device, causal)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    gu.check(gu.errors(got, oracle_heads(x, w, heads, causal), heads), dtype, f"atomic random case {i}")
+    check_against_attn_bwd(got, base, dtype)
