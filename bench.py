@@ -8,6 +8,15 @@ forward+backward TFLOP/s under the 7*B*H*S^2*D causal convention, the roofline
 of the dominant kernel (algorithmic FLOPs / its average HIP-event duration over a
 timed pass), and the fp64 CPU oracle timed on a bounded sample of the same
 workload on this host's cores.
+
+Protocol (Iron "Kernel Engineering Guide", §6.1-6.2): a PASS receipt first (the
+session's own outputs at the timed shape against the oracle that the CPU
+baseline runs, on the heads it covers; a mismatch exits with status 3); the
+clock warmed by CLOCK_WARM_SECONDS of untimed steps before the W warm-up steps;
+the shader clock measured over the timed region and reported with the peak at
+that clock; a file lock around the timed sections; both dispatch orders; and a
+second, fresh session (a child process, run after this one's timed sections)
+whose outputs must be bitwise equal to this session's.
 """
 from __future__ import annotations
 
@@ -35,7 +44,114 @@ PEAK_FP8_TFLOPS = 5033.2   # MI355X dense fp8 MFMA: twice the bf16 rate
 # the bf16 rate: its MFMA-time bound is the harmonic combination of the two.
 PEAK_FP8QK_FWD_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
-WARMUP_SECONDS = 0.3
+TIMES_FILE = os.path.join(ROOT, "profiles", "kernel_times.txt")
+# Untimed steps before the warm-up: a cold GPU runs at a lower DVFS clock state
+# (after 10 steps of the headline workload the clock had not settled: ~15% lower
+# throughput than after 0.3 s of steps).
+CLOCK_WARM_SECONDS = 0.3
+DEFAULT_WARMUP = 20
+CU_COUNT = 256
+BF16_FLOP_PER_CLK_CU = 4096  # dense bf16 / fp16 MFMA: 2516.6 TFLOP/s at 2.4 GHz
+LOCK_FILE = os.path.join(os.environ.get("TMPDIR", "/tmp"), "causal_attn_bench.lock")
+OUTPUTS = ("o", "lse", "dq", "dk", "dv")
+# Parity bars of the receipt (the same as the GPU parity tests): bf16 inputs
+# max |gpu - oracle| <= 2e-2; fp16 5e-3 (three more fraction bits than bf16);
+# fp32 max |gpu - oracle| / max |oracle| <= 1e-4 per tensor.
+RECEIPT_TOL = {"bf16": ("abs", 2e-2), "f16": ("abs", 5e-3), "f32": ("rel", 1e-4)}
+
+
+METRIC_TRAIN = "causal attention fwd+bwd TFLOP/s (bf16) on 1 GPU; % of MFMA peak"
+
+
+def host_cores() -> int:
+    """CPUs this process may run on (its affinity mask)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover - non-Linux
+        return os.cpu_count() or 1
+
+
+def blas_threads() -> int:
+    """Threads the host BLAS (numpy's matmul, which the oracle uses) runs with."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        return host_cores()
+
+
+class GpuLock:
+    """An exclusive file lock around the timed sections, so that two invocations
+    on one machine never time against each other."""
+
+    def __enter__(self):
+        import fcntl
+        self.f = open(LOCK_FILE, "w")
+        fcntl.flock(self.f, fcntl.LOCK_EX)
+        return self
+
+    def __exit__(self, *exc):
+        import fcntl
+        fcntl.flock(self.f, fcntl.LOCK_UN)
+        self.f.close()
+        return False
+
+
+def clock_ghz(before, after):
+    """Average shader clock (GHz) over the interval between two clock samples
+    (arrays of [n, 4] uint64 from attn_clock_sample: cycles, 100 MHz ticks, XCC
+    id, 0), from the workgroups that ran on the same XCC in both samples: per XCC
+    the median of the per-workgroup estimates, then the mean over XCCs."""
+    b = np.asarray(before, dtype=np.float64)
+    a = np.asarray(after, dtype=np.float64)
+    same = b[:, 2] == a[:, 2]
+    dt = (a[:, 1] - b[:, 1]) / 100e6
+    ok = same & (dt > 0)
+    if not ok.any():
+        return None
+    est = (a[:, 0] - b[:, 0])[ok] / dt[ok] / 1e9
+    xcc = b[ok, 2]
+    per = {int(x): float(np.median(est[xcc == x])) for x in np.unique(xcc)}
+    return {"mean": round(float(np.mean(list(per.values()))), 4),
+            "per_xcc": {str(k): round(v, 4) for k, v in sorted(per.items())},
+            "interval_s": round(float(np.median(dt[ok])), 6)}
+
+
+def compare_heads(gpu: dict, ref_heads: list, dtype: str, G: int) -> dict:
+    """The receipt: the session's outputs (gpu: name -> callable (b, h) -> float64
+    array) against the oracle's per-head results [((b, h), {o, lse, dq, dk, dv})].
+    O, LSE and dQ compare per query head; dK and dV per key/value head, as the sum
+    of its G query heads' oracle contributions, for the key/value heads whose
+    whole group is in the sample."""
+    kind, tol = RECEIPT_TOL[dtype]
+    err = {n: 0.0 for n in OUTPUTS}
+    big = {n: 0.0 for n in OUTPUTS}
+    groups = {}
+    for (b, h), r in ref_heads:
+        for n in ("o", "lse", "dq"):
+            d = np.abs(gpu[n](b, h) - r[n])
+            err[n] = max(err[n], float(d.max()))
+            big[n] = max(big[n], float(np.abs(r[n]).max()))
+        g = groups.setdefault((b, h // G), {"n": 0, "dk": 0.0, "dv": 0.0})
+        g["n"] += 1
+        g["dk"] = g["dk"] + r["dk"]
+        g["dv"] = g["dv"] + r["dv"]
+    nkv = 0
+    for (b, kh), g in groups.items():
+        if g["n"] != G:
+            continue
+        nkv += 1
+        for n in ("dk", "dv"):
+            err[n] = max(err[n], float(np.abs(gpu[n](b, kh) - g[n]).max()))
+            big[n] = max(big[n], float(np.abs(g[n]).max()))
+    worst = {n: (err[n] / big[n] if big[n] > 0 else err[n]) if kind == "rel" else err[n] for n in OUTPUTS}
+    if nkv == 0:
+        worst.pop("dk")
+        worst.pop("dv")
+    ok = bool(ref_heads) and all(v <= tol for v in worst.values())
+    return {"status": "PASS" if ok else "FAIL", "heads": len(ref_heads), "kv_heads": nkv,
+            "max_err": {n: float(f"{v:.3g}") for n, v in worst.items()},
+            "bar": f"{'max |d| / max |oracle|' if kind == 'rel' else 'max |d|'} <= {tol:g}"}
 
 
 def step_statistics(step, k, torch, between=None) -> dict:
@@ -60,21 +176,25 @@ def step_statistics(step, k, torch, between=None) -> dict:
     return out
 
 
-def warm_up(step, args, torch) -> int:
-    """Run the untimed warmup; return the number of steps run.  --warmup W runs
-    exactly W; the default runs steps (in groups of 10) until WARMUP_SECONDS of
-    wall time have passed."""
-    if args.warmup is not None:
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
-        return args.warmup
+def clock_warm(step, torch, seconds: float = CLOCK_WARM_SECONDS) -> int:
+    """Untimed steps (in groups of 10) until `seconds` of wall time have passed, so
+    that the clock has left its idle state before the warm-up; returns the count."""
     n, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < WARMUP_SECONDS:
+    while time.perf_counter() - t0 < seconds:
         for _ in range(10):
             step()
         n += 10
         torch.cuda.synchronize()
+    return n
+
+
+def warm_up(step, args, torch) -> int:
+    """Run the untimed warm-up (after clock_warm); return the number of steps run:
+    --warmup W runs exactly W, the default DEFAULT_WARMUP."""
+    n = DEFAULT_WARMUP if args.warmup is None else args.warmup
+    for _ in range(n):
+        step()
+    torch.cuda.synchronize()
     return n
 
 
@@ -83,9 +203,8 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=None,
-                    help=f"untimed warmup steps (default: as many as fill {WARMUP_SECONDS} s, so that the "
-                         "GPU's clocks have settled: after 10 steps the headline workload measured ~15%% below "
-                         "its steady state)")
+                    help=f"untimed warm-up steps (default {DEFAULT_WARMUP}); they follow {CLOCK_WARM_SECONDS} s of "
+                         "untimed steps that warm the clock")
     ap.add_argument("--workload", default="gpt205m_bf16",
                     choices=sorted(si.WORKLOADS) + sorted(si.GQA_WORKLOADS) + sorted(si.F16_WORKLOADS)
                     + sorted(si.DECODE_WORKLOADS) + sorted(si.FP8_WORKLOADS),
@@ -97,6 +216,9 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="only run this many fwd+bwd steps and exit (for rocprofv3), no JSON")
+    ap.add_argument("--sessions", type=int, default=2, choices=(1, 2),
+                    help="2: repeat the measurement in a fresh process afterwards (training workloads)")
+    ap.add_argument("--expect-digest", default=None, help=argparse.SUPPRESS)
     return ap.parse_args()
 
 
@@ -139,6 +261,18 @@ def read_traffic(kernel: str, workload: str):
     return fetch_b + write_b
 
 
+def read_kernel_time(kernel: str, workload: str):
+    """Average duration (us) of the kernel under rocprofv3 --kernel-trace --stats, from
+    the committed summary, if it still matches the kernel source."""
+    if not os.path.exists(TIMES_FILE):
+        return None
+    text = open(TIMES_FILE).read()
+    m = re.search(rf"^{re.escape(kernel)}\s+{re.escape(workload)}\s+(\S+)\s+(\S+)\s*$", text, flags=re.M)
+    if not m or kernel_sources_hash(kernel) != m.group(1):
+        return None
+    return float(m.group(2))
+
+
 # The sources each timed kernel is compiled from: its traffic figures stay valid
 # while these are unchanged.
 KERNEL_SOURCES = {
@@ -159,31 +293,32 @@ def kernel_sources_hash(kernel: str) -> str:
 
 
 def cpu_baseline(w, x, target_s: float):
-    """Time the fp64 oracle (fwd + bwd, head by head) on a bounded sample of the workload."""
+    """Time the fp64 oracle (fwd + bwd, head by head) on a bounded sample of the
+    workload; return the baseline record and the oracle's per-head results (the
+    receipt compares the session's outputs against them)."""
     from oracle import attention_head
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover - threadpoolctl is optional
-        cores = os.cpu_count() or 1
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     per_head = w.flops / len(heads)
     G = w.H // w.kv_heads  # query head h reads key/value head h // G
-    done = 0
+    done = []
     t0 = time.perf_counter()
     for b, h in heads:
-        attention_head(x["q"][b, h], x["k"][b, h // G], x["v"][b, h // G], x["do"][b, h], w.scale, w.causal)
-        done += 1
+        r = attention_head(x["q"][b, h], x["k"][b, h // G], x["v"][b, h // G], x["do"][b, h], w.scale, w.causal)
+        done.append(((b, h), r))
         if time.perf_counter() - t0 >= target_s:
             break
     dt = time.perf_counter() - t0
-    return {
-        "value": round(done * per_head / dt / 1e12, 6),
+    rec = {
+        "value": round(len(done) * per_head / dt / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": int(cores),
+        "cores": blas_threads(),
+        "host_cores": host_cores(),
         "kind": "oracle",
-        "sample": f"{done} of {len(heads)} heads (S={w.S}, D={w.D}), fwd+bwd in fp64, {dt:.1f} s",
+        "sample": f"{len(done)} of {len(heads)} heads (S={w.S}, D={w.D}), fwd+bwd in fp64, {dt:.1f} s; "
+                  f"cores = the BLAS threads the oracle's products ran on, host_cores = this process's "
+                  f"CPU affinity",
     }
+    return rec, done
 
 
 def decode_bench(args, dev):
@@ -239,6 +374,7 @@ def decode_bench(args, dev):
         torch.cuda.synchronize()
         print(f"profile run: {args.profile_steps} steps of {w.name}", flush=True)
         return
+    clock_warm(step, torch)
     nwarm = warm_up(step, args, torch)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -284,11 +420,6 @@ def decode_bench(args, dev):
     }
     if not args.no_cpu_baseline:
         from oracle import decode
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-        except Exception:  # pragma: no cover
-            cores = os.cpu_count() or 1
         t0 = time.perf_counter()
         nb = 0
         done_bytes = 0.0
@@ -298,8 +429,8 @@ def decode_bench(args, dev):
             done_bytes += float(lens[nb]) * w.Hkv * w.D * elem * 2 + 2 * w.H * w.D * elem + w.H * 4
             nb += 1
         dtc = time.perf_counter() - t0
-        result["cpu_baseline"] = {"value": round(done_bytes / dtc / 1e9, 4), "unit": "GB/s", "cores": int(cores),
-                                  "kind": "oracle",
+        result["cpu_baseline"] = {"value": round(done_bytes / dtc / 1e9, 4), "unit": "GB/s",
+                                  "cores": blas_threads(), "host_cores": host_cores(), "kind": "oracle",
                                   "sample": f"{nb} of {w.B} sequences, fp64 decode, {dtc:.1f} s"}
     print(json.dumps(result), flush=True)
 
@@ -311,7 +442,6 @@ def fp8_bench(args, dev):
     import torch
 
     import causal_attention_flash_amd as caf
-    from oracle import e4m3_decode
 
     w = si.FP8_WORKLOADS[args.workload]
     x = si.make_fp8_inputs(w, seed=0)
@@ -336,6 +466,7 @@ def fp8_bench(args, dev):
         torch.cuda.synchronize()
         print(f"profile run: {args.profile_steps} steps of {w.name}", flush=True)
         return
+    clock_warm(step, torch)
     nwarm = warm_up(step, args, torch)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -353,11 +484,14 @@ def fp8_bench(args, dev):
         evs[i + 1].record()
     torch.cuda.synchronize()
     mean_ms = sum(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)) / args.steps
-    # the bf16 forward on the decoded values (exact in bf16: power-of-two descales)
-    qb = torch.from_numpy(si.f32_to_bf16_bits((e4m3_decode(x["q8"]) * x["q_descale"]).astype(np.float32))
-                          .view(np.int16)).to(dev).view(torch.bfloat16)
-    kb = torch.from_numpy(si.f32_to_bf16_bits((e4m3_decode(x["k8"]) * x["k_descale"]).astype(np.float32))
-                          .view(np.int16)).to(dev).view(torch.bfloat16)
+    # the bf16 forward on the same values: torch's own E4M3 conversion on the host
+    # (every E4M3 value and its power-of-two descaled form is exact in bf16)
+    def decoded(codes, descale):
+        f = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32) * descale
+        return f.to(torch.bfloat16).to(dev)
+
+    qb = decoded(x["q8"], x["q_descale"])
+    kb = decoded(x["k8"], x["k_descale"])
     vb = v if w.v_dtype == "bf16" else v.to(torch.bfloat16)
 
     def step_bf16():
@@ -398,11 +532,6 @@ def fp8_bench(args, dev):
     }
     if not args.no_cpu_baseline:
         from oracle import fp8qk_forward
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-        except Exception:  # pragma: no cover
-            cores = os.cpu_count() or 1
         G = w.H // w.Hkv
         heads = [(b, h) for b in range(w.B) for h in range(w.H)]
         t0 = time.perf_counter()
@@ -415,7 +544,8 @@ def fp8_bench(args, dev):
                 break
         dtc = time.perf_counter() - t0
         result["cpu_baseline"] = {"value": round(done * w.fwd_flops / len(heads) / dtc / 1e12, 6),
-                                  "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+                                  "unit": "TFLOP/s", "cores": blas_threads(), "host_cores": host_cores(),
+                                  "kind": "oracle",
                                   "sample": f"{done} of {len(heads)} heads (S={w.S}, D={w.D}), fp64 forward, "
                                             f"{dtc:.1f} s"}
     print(json.dumps(result), flush=True)
@@ -521,52 +651,88 @@ def main():
         print(f"profile run: copy of {copy_bytes} bytes, then {args.profile_steps} steps of {w.name}", flush=True)
         return
 
-    nwarm = warm_up(lambda: (fwd(), bwd()), args, torch)
-
-    # ---- timed region: exactly K steps of fwd + bwd
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        fwd()
-        bwd()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
-    ms_per_step = gpu_ms / args.steps
-
-    # ---- per-kernel durations: the same K steps, each kernel attn_bwd launches
-    # (in its order) bracketed by events; the grouped form has no stage entry
-    # points, so there the backward is timed as one (its dQ and dK/dV passes), and
-    # so is the atomic-dQ backward (delta, zero fill, fused pass, dQ conversion)
-    if grouped or atomic:
-        names = ("fwd", "bwd")
-        calls = (fwd, bwd)
-    else:
-        names = ("fwd", "bwd_dq", "bwd_dkdv")
-        calls = (fwd, dq_delta, dkdv)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        evs[i][0].record()
-        for j, fn in enumerate(calls):
-            fn()
-            evs[i][j + 1].record()
-    torch.cuda.synchronize()
-    durations = {n: [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]
-                 for j, n in enumerate(names)}
-    per_kernel = {n: statistics.median(d) for n, d in durations.items()}
-    per_kernel_mean = {n: sum(d) / len(d) for n, d in durations.items()}
-
-    # ---- per-step distribution (the same K steps, one event pair each); then
-    # cache-cold: 512 MiB written between steps (more than the 256 MB MALL), untimed
     step_fn = lambda: (fwd(), bwd())  # noqa: E731
-    steps_warm = step_statistics(step_fn, args.steps, torch)
-    scratch = torch.empty(1 << 27, dtype=torch.float32, device=dev)
-    steps_cold = step_statistics(step_fn, args.steps, torch, between=lambda: scratch.fill_(1.0))
-    del scratch
+    bwd_first = lambda: (bwd(), fwd())  # noqa: E731
+
+    # ---- the session's own outputs at the timed shape (the receipt checks them)
+    step_fn()
+    torch.cuda.synchronize()
+    outs = dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)
+    digest = output_digest(outs, torch, skip=("dq",) if atomic else ())
+    host = {n: t.detach().cpu() for n, t in outs.items()}
+    gpu_head = {n: (lambda t: (lambda b, h: t[b, h].to(torch.float64).numpy()))(t) for n, t in host.items()}
+
+    baseline, receipt = None, None
+    if not args.no_cpu_baseline:
+        baseline, ref_heads = cpu_baseline(w, x, args.cpu_seconds)
+        receipt = compare_heads(gpu_head, ref_heads, w.dtype, w.H // w.kv_heads)
+    elif args.expect_digest:
+        receipt = {"status": "PASS" if digest == args.expect_digest else "FAIL",
+                   "kind": "outputs bitwise equal to the first session's (which passed the oracle check)"}
+    if receipt is not None and receipt["status"] != "PASS":
+        print(json.dumps({"metric": METRIC_TRAIN, "receipt": receipt, "config": {"workload": w.name}}), flush=True)
+        print("bench.py: the receipt failed; no timing is reported", file=sys.stderr)
+        sys.exit(3)
+
+    clk_n = 256
+    clk = [torch.empty((clk_n, 4), dtype=torch.int64, device=dev) for _ in range(2)]
+
+    def clock_sample(i):
+        chk(bd.c_attn_clock_sample(clk[i].data_ptr(), clk_n, stream), "clock_sample")
+
+    with GpuLock():
+        nclock = clock_warm(step_fn, torch)
+        nwarm = warm_up(step_fn, args, torch)
+
+        # ---- timed region: exactly K steps of fwd + bwd, the shader clock sampled
+        # just outside it
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        clock_sample(0)
+        t0 = time.perf_counter()
+        ev0.record()
+        for _ in range(args.steps):
+            fwd()
+            bwd()
+        ev1.record()
+        clock_sample(1)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        gpu_ms = ev0.elapsed_time(ev1)
+        ms_per_step = gpu_ms / args.steps
+        clock = clock_ghz(clk[0].cpu().numpy().view(np.uint64), clk[1].cpu().numpy().view(np.uint64))
+
+        # ---- per-kernel durations: the same K steps, each kernel attn_bwd launches
+        # (in its order) bracketed by events; the grouped form has no stage entry
+        # points, so there the backward is timed as one (its dQ and dK/dV passes), and
+        # so is the atomic-dQ backward (delta, zero fill, fused pass, dQ conversion)
+        if grouped or atomic:
+            names = ("fwd", "bwd")
+            calls = (fwd, bwd)
+        else:
+            names = ("fwd", "bwd_dq", "bwd_dkdv")
+            calls = (fwd, dq_delta, dkdv)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            evs[i][0].record()
+            for j, fn in enumerate(calls):
+                fn()
+                evs[i][j + 1].record()
+        torch.cuda.synchronize()
+        durations = {n: [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]
+                     for j, n in enumerate(names)}
+        per_kernel = {n: statistics.median(d) for n, d in durations.items()}
+        per_kernel_mean = {n: sum(d) / len(d) for n, d in durations.items()}
+
+        # ---- per-step distribution (the same K steps, one event pair each), in
+        # both dispatch orders; then cache-cold: 512 MiB written between steps (more
+        # than the 256 MB MALL), untimed
+        steps_warm = step_statistics(step_fn, args.steps, torch)
+        steps_rev = step_statistics(bwd_first, args.steps, torch)
+        scratch = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+        steps_cold = step_statistics(step_fn, args.steps, torch, between=lambda: scratch.fill_(1.0))
+        del scratch
 
     units = kernel_units(w)
     dom = max(names, key=lambda n: per_kernel_mean[n])
@@ -574,10 +740,11 @@ def main():
     mfma_peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS  # fp16 dense MFMA peak = bf16
     achieved = units[dom]["flops"] / (dom_ms * 1e-3) / 1e12
     traffic = read_traffic(dom, w.name)
+    prof_us = read_kernel_time(dom, w.name)
 
     value = w.flops * args.steps / (gpu_ms * 1e-3) / 1e12
     result = {
-        "metric": "causal attention fwd+bwd TFLOP/s (bf16) on 1 GPU; % of MFMA peak",
+        "metric": METRIC_TRAIN,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -593,10 +760,14 @@ def main():
                    "causal": bool(w.causal), "backward": "attn_bwd_atomic" if atomic else "attn_bwd",
                    "global_batch": w.B, "seq_len": w.S, "parallelism": "none (1 GPU)"},
         "pct_of_mfma_peak": round(100.0 * value / mfma_peak, 3),
+        "receipt": receipt,
+        "clock_warm": {"seconds": CLOCK_WARM_SECONDS, "steps": nclock},
+        "clock_ghz": clock,
         "wall_s_timed": round(wall, 4),
         "kernel_ms": {n: round(per_kernel_mean[n], 5) for n in names},
         "kernel_ms_median": {n: round(per_kernel[n], 5) for n in names},
         "step_ms": steps_warm,
+        "step_ms_bwd_first": steps_rev,
         "step_ms_cache_cold": steps_cold,
         "roofline": {
             "kernel": dom,
@@ -606,11 +777,55 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / mfma_peak, 5),
             "traffic": traffic,
+            "time_base": "mean of the kernel's per-launch HIP-event durations over K steps (second timed pass)",
+            "frac_rocprof": (round(units[dom]["flops"] / (prof_us * 1e-6) / 1e12 / mfma_peak, 5)
+                             if prof_us else None),
         },
+        "output_digest": digest,
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    if clock and w.dtype != "f32":
+        peak_clk = CU_COUNT * BF16_FLOP_PER_CLK_CU * clock["mean"] * 1e9 / 1e12
+        result["roofline"]["peak_at_clock"] = round(peak_clk, 1)
+        result["roofline"]["frac_at_clock"] = round(achieved / peak_clk, 5)
+    if baseline is not None:
+        result["cpu_baseline"] = baseline
+    if args.sessions > 1:
+        result["sessions"] = [session_summary(result)] + second_session(args, digest)
     print(json.dumps(result), flush=True)
+
+
+def output_digest(outs: dict, torch, skip=()) -> str:
+    """sha256 (first 16 hex digits) of the output tensors' bytes, in a fixed order;
+    `skip` leaves out outputs that are not bitwise reproducible (atomic dQ)."""
+    import hashlib
+    h = hashlib.sha256()
+    for n in OUTPUTS:
+        if n in outs and n not in skip:
+            h.update(outs[n].detach().contiguous().view(-1).view(torch.uint8).cpu().numpy().tobytes())
+    return h.hexdigest()[:16]
+
+
+def session_summary(d: dict) -> dict:
+    return {"value": d.get("value"), "ms_per_step": d.get("ms_per_step"),
+            "clock_ghz": (d.get("clock_ghz") or {}).get("mean"), "receipt": (d.get("receipt") or {}).get("status")}
+
+
+def second_session(args, digest: str) -> list:
+    """The same measurement in a fresh process (sequentially, after this one's timed
+    sections), its outputs checked bitwise against this session's."""
+    cmd = [sys.executable, os.path.abspath(__file__), "--gpus", "1", "--steps", str(args.steps),
+           "--workload", args.workload, "--bwd", args.bwd, "--no-cpu-baseline", "--sessions", "1",
+           "--expect-digest", digest]
+    if args.warmup is not None:
+        cmd += ["--warmup", str(args.warmup)]
+    import subprocess
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+    if r.returncode != 0 or not lines:
+        print(r.stderr[-2000:], file=sys.stderr)
+        print("bench.py: the second session failed", file=sys.stderr)
+        sys.exit(3)
+    return [session_summary(json.loads(lines[-1]))]
 
 
 if __name__ == "__main__":

@@ -53,6 +53,7 @@ SIGNATURES = {
     "attn_bwd_dq_delta": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _INT, _INT, _P]),
     "attn_decode_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64, _INT]),
     "attn_decode": (_INT, [_P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64, _I64, _I64, _I64, _F, _INT, _P]),
+    "attn_clock_sample": (_INT, [_P, _I64, _P]),
     "attn_status_string": (ctypes.c_char_p, [_INT]),
 }
 
@@ -134,6 +135,10 @@ def c_attn_bwd_atomic(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, H, S, D,
                       stream=0) -> int:
     return load_library().attn_bwd_atomic(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, H, S, D, scale, causal,
                                           dtype, stream)
+
+
+def c_attn_clock_sample(out, n, stream=0) -> int:
+    return load_library().attn_clock_sample(out, n, stream)
 
 
 def c_attn_bwd_preprocess(o, do, delta, B, H, S, D, dtype, stream=0) -> int:

@@ -5,8 +5,8 @@
 // once per query row (attn_preprocess.hip); a dK/dV pass runs parallel over key
 // tiles and loops over query tiles; a dQ pass runs parallel over query tiles and
 // loops over key tiles.  Both recompute P = exp(S - L) from the saved
-// log-sum-exp, so no rescaling is needed (Forge "Attention kernel design": "the
-// backward pass needs none of this").  Transposed products are obtained by
+// log-sum-exp, so the backward needs no online rescale (Forge paper, "Attention
+// kernel design").  Transposed products are obtained by
 // swapping operand roles rather than moving data (same section): the dK/dV pass
 // forms S = Q K^T and dP = dO V^T with keys on the lanes, and the dQ pass forms
 // S^T = K Q^T and dP^T = V dO^T with queries on the lanes.
@@ -219,6 +219,11 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
             for (int r = 0; r < 16; ++r) {
                 float p = fast_exp2(sacc[r] * c);
                 if constexpr (MASK) p = key > qt0 + qb * 32 + crow(r, h) ? 0.f : p;
+                // DQA: a key slot at or past S (zero K and V rows) has s = 0, so P =
+                // exp(-LSE) can overflow; its dS reaches dQ through K^T dS^T (0 * inf
+                // would be NaN), so it is zeroed.  The split passes leave such values
+                // in columns that are never stored.
+                if constexpr (DQA) p = key < S ? p : 0.f;
                 sacc[r] = p;
                 pacc[r] *= p;
             }

@@ -1,6 +1,7 @@
 // Internal launch interface between the C ABI (attn_api.hip) and the kernel
-// files.  Arguments arrive here already validated: D in {64, 128}, S >= 1,
-// B*H >= 1, pointers non-null, aligned and non-overlapping, scale > 0 finite.
+// files.  Arguments arrive here already validated: D in {64, 80, 96, 128} (64 or
+// 128 for fp8 Q and K), S >= 1, B*H >= 1, B*H*S < 2^31 and S*D < 2^31, pointers
+// non-null, aligned and non-overlapping, scale > 0 and finite.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -19,12 +19,13 @@
  *   dP_ij = dO_i . v_j,   delta_i = dO_i . O_i,   dS_ij = P_ij (dP_ij - delta_i)
  *   dQ_i  = scale * sum_j dS_ij k_j,   dK_j = scale * sum_i dS_ij q_i
  *
- * Sources: attention as S = QK^T, row softmax, O = PV and the causal mask
- * "column > row is masked" follow "Cooperative tensors, reductions, and building
- * a fused attention kernel" (§1, §5.3, §8.7).  The online-softmax forward that
- * saves one log-sum-exp per row, the three-stage atomic-free backward
- * (delta = rowsum(dO o O) preprocess, a dQ pass parallel over queries, a dK/dV
- * pass parallel over keys, both recomputing P from the saved LSE) follow Forge
+ * Sources: attention as S = QK^T, row softmax, O = PV and the causal mask that
+ * hides every key after the query's own position follow "Cooperative tensors,
+ * reductions, and building a fused attention kernel" (§1, §5.3, §8.7).  The
+ * online-softmax forward that saves one log-sum-exp per row, the three-stage
+ * atomic-free backward (delta = rowsum(dO o O) preprocess, a dQ pass parallel
+ * over queries, a dK/dV pass parallel over keys, both recomputing P from the
+ * saved LSE) follow Forge
  * RESEARCH.md §6 "Fused attention design (flash-style)" and the Forge paper,
  * sections "Ecosystem survey" and "Attention kernel design".
  *
@@ -42,8 +43,13 @@
  * accumulation and statistics are the form of the assembled kernel in §9 of
  * "Cooperative tensors, reductions, and building a fused attention kernel", and
  * the Forge paper measures its matmul2d with half operands); causal in {0, 1};
- * finite scale; any S >= 1 (no tile-multiple requirement); B*H*S*D < 2^62 and
- * S*D < 2^31.  B, H or S equal to 0 is an empty problem: ATTN_OK, nothing
+ * scale finite and > 0 (the forward takes each row's maximum over the raw
+ * products, which commutes with the scaling only for a positive factor; a
+ * scale <= 0, NaN or infinite -> ATTN_ERR_UNSUPPORTED); any S >= 1 (no
+ * tile-multiple requirement).  Size limits, checked without overflow:
+ * B*H*S < 2^31 (query rows; H counts query heads) and S*D < 2^31 (one head's
+ * elements), every kernel indexing both in 32 bits; beyond either ->
+ * ATTN_ERR_SHAPE.  B, H or S equal to 0 is an empty problem: ATTN_OK, nothing
  * enqueued, pointers not read.
  *
  * Errors: every argument is validated before anything is enqueued.  On any
@@ -52,8 +58,9 @@
  * hold part of the work).  Outputs must not overlap inputs or each other
  * (ATTN_ERR_ALIAS).  All device pointers must be 16-byte aligned.
  *
- * Determinism: no atomics; results are bitwise identical run to run for the
- * same inputs, sizes and library build.
+ * Determinism: every entry point except attn_bwd_atomic uses no atomics, and its
+ * results are bitwise identical run to run for the same inputs, sizes and
+ * library build.  attn_bwd_atomic's dQ is the one exception (see there).
  */
 #ifndef CAUSAL_ATTN_H
 #define CAUSAL_ATTN_H
@@ -142,7 +149,11 @@ attn_status attn_fwd_fp8qk(const void* q, const void* k, const void* v, void* o,
 
 /*
  * Bytes of device workspace attn_bwd needs: the fp32 delta vector, B*H*S*4 bytes.
- * Returns 0 for an empty or invalid problem.
+ * delta_i = dO_i . O_i is formed once per query row and read by both backward
+ * passes (Forge RESEARCH.md §6, the paragraph on the D term: it is needed by the
+ * dK/dV and the dQ kernel and costs a cubic factor if formed per pair instead of
+ * per row), so it is stored between them.  Returns 0 for an empty or invalid
+ * problem (the same checks as attn_bwd).
  */
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D, attn_dtype dtype);
 
@@ -250,7 +261,6 @@ attn_status attn_bwd_dq_delta(const void* q, const void* k, const void* v, const
                               int64_t B, int64_t H, int64_t S, int64_t D,
                               float scale, int causal, attn_dtype dtype, void* stream);
 
-/* Static, NUL-terminated description of a status code (never NULL). */
 /*
  * Decode attention: one new query row per (batch entry, query head) against a
  * key/value cache.  The query is the newest position, appended after its own key
@@ -281,6 +291,31 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
                         int64_t B, int64_t H, int64_t H_kv, int64_t L, int64_t D,
                         float scale, attn_dtype dtype, void* stream);
 
+/*
+ * Shader-clock sample, for measurement: launches n workgroups (1 <= n <=
+ * ATTN_CLOCK_SAMPLE_MAX) on `stream`; workgroup i writes out[4i .. 4i+3] =
+ * {shader-cycle counter (s_memtime: advances at the current shader clock),
+ * 100 MHz reference counter (s_memrealtime), id of the XCC it ran on, 0}.
+ *   out : device, n*4 uint64, 16-byte aligned, fully overwritten.
+ * Two samples around a timed region give each XCC's average shader clock over it:
+ * (cycles after - before) / ((ticks after - before) / 100 MHz); a throughput is
+ * then read against the peak at that clock.  Source: Iron "Kernel Engineering
+ * Guide", §6.1 (a cold GPU runs at a lower DVFS clock state; warm it before the
+ * first sample).  Errors: n out of range -> ATTN_ERR_SHAPE; out NULL ->
+ * ATTN_ERR_NULL; misaligned -> ATTN_ERR_ALIGNMENT.
+ */
+#define ATTN_CLOCK_SAMPLE_MAX 4096
+attn_status attn_clock_sample(uint64_t* out, int64_t n, void* stream);
+
+/*
+ * Static, NUL-terminated description of a status code (never NULL; an unknown
+ * value gives "unknown attn_status").  The statuses are the up-front argument
+ * checks: argument kinds and counts are verified before any work, as
+ * TorchMetalKernel does at construction ("Cooperative tensors, reductions, and
+ * building a fused attention kernel", §12), and an unsupported combination is
+ * rejected loudly instead of being run wrong (Iron "Kernel Engineering Guide",
+ * §2.5 on dispatch selectors).
+ */
 const char* attn_status_string(attn_status status);
 
 #ifdef __cplusplus

@@ -46,7 +46,7 @@ def test_header_declares_the_boundary():
                           "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_delta", "attn_status_string",
                           "attn_fwd_gqa", "attn_bwd_gqa", "attn_bwd_gqa_workspace_bytes",
                           "attn_decode", "attn_decode_workspace_bytes", "attn_fwd_fp8qk",
-                          "attn_bwd_atomic", "attn_bwd_atomic_workspace_bytes"}
+                          "attn_bwd_atomic", "attn_bwd_atomic_workspace_bytes", "attn_clock_sample"}
     for name, nargs in decls.items():
         assert len(bd.SIGNATURES[name][1]) == nargs, name
 
@@ -97,6 +97,45 @@ def bwd(**kw):
 ])
 def test_fwd_validation(lib, kw, expect):
     assert fwd(**kw) == expect
+
+
+# Each documented limit at its edge.  The size and scale checks run before the
+# pointer checks, so with q = NULL a value the contract accepts returns
+# ATTN_ERR_NULL (it passed) and one it rejects returns its own status; nothing
+# is launched either way.
+@pytest.mark.parametrize("kw,expect", [
+    (dict(B=(1 << 31) - 1, H=1, S=1), NULL),             # B*H*S = 2^31 - 1: accepted
+    (dict(B=1 << 31, H=1, S=1), SHAPE),                  # B*H*S = 2^31
+    (dict(B=1, H=(1 << 31) - 1, S=1), NULL),
+    (dict(B=1 << 16, H=1 << 15, S=1), SHAPE),            # 2^31 through the product B*H
+    (dict(B=1, H=1, S=(1 << 25) - 1, D=64), NULL),       # S*D = 2^31 - 64: accepted
+    (dict(B=1, H=1, S=1 << 25, D=64), SHAPE),            # S*D = 2^31
+    (dict(B=1, H=1, S=(1 << 24) - 1, D=128), NULL),
+    (dict(B=1, H=1, S=1 << 24, D=128), SHAPE),
+    (dict(B=1, H=1, S=(1 << 31) // 80, D=80), NULL),     # largest S with S*80 < 2^31
+    (dict(B=1, H=1, S=(1 << 31) // 80 + 1, D=80), SHAPE),
+    (dict(scale=1.4e-45), NULL),                         # smallest positive float: accepted
+    (dict(scale=3.4028234663852886e38), NULL),           # largest finite float
+    (dict(scale=0.0), UNSUP), (dict(scale=-0.0), UNSUP), (dict(scale=-1.4e-45), UNSUP),
+    (dict(scale=float("inf")), UNSUP), (dict(scale=float("nan")), UNSUP),
+])
+def test_documented_limits_at_their_edges(lib, kw, expect):
+    assert fwd(q=0, **kw) == expect
+    # the backward and the decode call apply the same limits (decode: L for S)
+    assert bwd(q=0, ws_bytes=1 << 62, **kw) == expect
+    dkw = {("L" if key == "S" else key): val for key, val in kw.items()}
+    assert dec(q=0, Hkv=1, **dkw) == expect
+
+
+def test_clock_sample_validation(lib):
+    limit = 4096  # ATTN_CLOCK_SAMPLE_MAX
+    assert f"#define ATTN_CLOCK_SAMPLE_MAX {limit}" in open(HEADER).read()
+    assert bd.c_attn_clock_sample(P[0], 0) == SHAPE
+    assert bd.c_attn_clock_sample(P[0], -1) == SHAPE
+    assert bd.c_attn_clock_sample(P[0], limit + 1) == SHAPE
+    assert bd.c_attn_clock_sample(0, 8) == NULL
+    assert bd.c_attn_clock_sample(0, limit) == NULL
+    assert bd.c_attn_clock_sample(P[0] + 8, 8) == ALIGN
 
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(S=0), dict(B=0, q=0, k=0, v=0, o=0, lse=0)])

@@ -52,11 +52,78 @@ def test_warm_up_runs_exactly_w_steps():
     assert len(calls) == 7
 
 
-def test_warm_up_default_fills_the_time(monkeypatch):
-    monkeypatch.setattr(bench, "WARMUP_SECONDS", 0.02)
+def test_warm_up_default_count():
     calls = []
     n = bench.warm_up(lambda: calls.append(1), types.SimpleNamespace(warmup=None), fake_torch())
+    assert n == len(calls) == bench.DEFAULT_WARMUP
+
+
+def test_clock_warm_fills_the_time():
+    calls = []
+    n = bench.clock_warm(lambda: calls.append(1), fake_torch(), seconds=0.02)
     assert n == len(calls) and n >= 10 and n % 10 == 0
+
+
+def test_clock_from_two_samples():
+    """Per XCC the median of the workgroups' cycles / seconds; workgroups that ran
+    on another XCC in the second sample are left out; the mean over XCCs."""
+    n = 16
+    before = np.zeros((n, 4), dtype=np.uint64)
+    after = np.zeros((n, 4), dtype=np.uint64)
+    for i in range(n):
+        x = i % 8
+        ghz = 2.0 + 0.01 * x
+        before[i] = (1_000_000 + 7 * i, 5_000 + i, x, 0)
+        ticks = 10_000  # 100 us at 100 MHz
+        after[i] = (before[i][0] + int(ghz * 1e9 * 1e-4), before[i][1] + ticks, x, 0)
+    after[3][2] = 5  # moved: not used
+    c = bench.clock_ghz(before, after)
+    assert c["per_xcc"]["0"] == pytest.approx(2.0)
+    assert c["per_xcc"]["7"] == pytest.approx(2.07)
+    assert c["mean"] == pytest.approx(2.035, abs=1e-4)
+    assert c["interval_s"] == pytest.approx(1e-4)
+    assert bench.clock_ghz(before[:0], after[:0]) is None
+
+
+def _fake_results(B, H, G, S, D, rng):
+    refs = []
+    for b in range(B):
+        for h in range(H):
+            refs.append(((b, h), {n: rng.standard_normal((S, D)) if n != "lse" else rng.standard_normal(S)
+                                  for n in bench.OUTPUTS}))
+    return refs
+
+
+def test_receipt_passes_and_fails_at_the_bar():
+    rng = np.random.default_rng(1)
+    B, H, G, S, D = 2, 4, 2, 5, 3
+    refs = _fake_results(B, H, G, S, D, rng)
+    full = {n: np.zeros((B, H if n in ("o", "lse", "dq") else H // G) + ((S, D) if n != "lse" else (S,)))
+            for n in bench.OUTPUTS}
+    for (b, h), r in refs:
+        for n in ("o", "lse", "dq"):
+            full[n][b, h] = r[n]
+        for n in ("dk", "dv"):
+            full[n][b, h // G] += r[n]  # a key/value head's gradient sums its group
+    gpu = {n: (lambda a: (lambda b, h: a[b, h]))(a) for n, a in full.items()}
+    rec = bench.compare_heads(gpu, refs, "bf16", G)
+    assert rec["status"] == "PASS" and rec["heads"] == B * H and rec["kv_heads"] == B * H // G
+    full["dv"][1, 1, 2, 0] += 0.019
+    assert bench.compare_heads(gpu, refs, "bf16", G)["status"] == "PASS"
+    full["dv"][1, 1, 2, 0] += 0.002  # 0.021 > 2e-2
+    rec = bench.compare_heads(gpu, refs, "bf16", G)
+    assert rec["status"] == "FAIL" and rec["max_err"]["dv"] == pytest.approx(0.021, rel=1e-2)
+    assert bench.compare_heads(gpu, refs, "f16", G)["status"] == "FAIL"
+    # a partial group: dK/dV are not compared (their sums need every query head)
+    rec = bench.compare_heads(gpu, refs[:1], "bf16", G)
+    assert rec["kv_heads"] == 0 and "dv" not in rec["max_err"] and rec["status"] == "PASS"
+    # fp32: relative to the tensor's largest magnitude
+    full["dv"][1, 1, 2, 0] -= 0.021
+    full["o"][0, 0, 0, 0] += 1e-5 * np.abs(np.concatenate([r["o"].ravel() for _, r in refs])).max()
+    assert bench.compare_heads(gpu, refs, "f32", G)["status"] == "PASS"
+    full["o"][0, 0, 0, 0] += 2e-4 * np.abs(np.concatenate([r["o"].ravel() for _, r in refs])).max()
+    assert bench.compare_heads(gpu, refs, "f32", G)["status"] == "FAIL"
+    assert bench.compare_heads(gpu, [], "bf16", G)["status"] == "FAIL"  # no sample, no receipt
 
 
 def test_step_statistics():

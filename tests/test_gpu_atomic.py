@@ -89,6 +89,32 @@ def test_atomic_unsupported(device):
             caf.attn_bwd_atomic(q, q, q, q, q, lse)
 
 
+@pytest.mark.parametrize("S", [45, 100])
+def test_atomic_dense_ragged_negative_logits(device, S):
+    """Non-causal, S not a multiple of 32, every scaled score near -20 (so LSE is
+    about -16): the key slots past S in the last key block would give P =
+    exp(-LSE) ~ 1e7 and, in fp16, an infinite dS; those slots must not reach dQ."""
+    w = si.Workload("atomic_neg", 1, 2, S, 64, "f16", 1.0, 1.0, 0.1, False)
+    x = si.make_inputs(w, seed=9100 + S)
+    rng = np.random.default_rng(9200 + S)
+    e1 = np.zeros(64, np.float32)
+    e1[0] = 1.0
+    # q . k * scale ~ 12 * -13.5 / 8 = -20.25, plus a small spread
+    q = 12.0 * e1 + 0.05 * rng.standard_normal((1, 2, S, 64)).astype(np.float32)
+    k = -13.5 * e1 + 0.05 * rng.standard_normal((1, 2, S, 64)).astype(np.float32)
+    for name, val in (("q", q), ("k", k)):
+        bits = si.f32_to_f16_bits(val)
+        x[name + "_bits"] = bits
+        x[name] = si.f16_bits_to_f32(bits)
+    print(f"\n[atomic dense negative logits] S={S} f16", flush=True)
+    got, base = run_both(x, w, device, causal=False)
+    heads = [(0, 0), (0, 1)]
+    ref = oracle_heads(x, w, heads, causal=False)
+    assert ref["lse"].max() < -13.0
+    gu.check(gu.errors(got, ref, heads), "f16", f"dense negative logits S={S}")
+    check_against_attn_bwd(got, base, "f16")
+
+
 @pytest.mark.parametrize("i", range(16))
 def test_atomic_random_shapes(device, i):
     """Seeded sweep: batch, heads, dtype, causality and a ragged S (D = 64)."""

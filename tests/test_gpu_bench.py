@@ -45,6 +45,29 @@ def test_bench_training_step():
         assert st["n"] == 5 and st["min"] <= st["median"] <= st["p95"]
         assert st["ci95_median"][0] <= st["median"] <= st["ci95_median"][1]
     assert set(d["kernel_ms"]) == {"fwd", "bwd_dq", "bwd_dkdv"}
+    st = d["step_ms_bwd_first"]
+    assert st["n"] == 5 and st["min"] <= st["median"] <= st["p95"]
+    assert 0.3 < d["clock_ghz"]["mean"] < 3.0, d["clock_ghz"]
+    assert d["clock_warm"]["steps"] >= 10
+    rf = d["roofline"]
+    assert rf["peak_at_clock"] > 0 and abs(rf["frac_at_clock"] - rf["achieved"] / rf["peak_at_clock"]) < 1e-3
+    # the second, fresh session reproduced this session's outputs bit for bit
+    assert len(d["sessions"]) == 2 and d["sessions"][1]["receipt"] == "PASS", d["sessions"]
+
+
+def test_bench_receipt_against_the_oracle():
+    """With the CPU baseline on, the session's outputs pass the oracle check on the
+    heads the baseline ran (the tiny fp32 workload: every head)."""
+    print("\n[bench] --workload tiny_f32 with the receipt", flush=True)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "5", "--warmup", "2",
+                        "--workload", "tiny_f32", "--cpu-seconds", "2", "--sessions", "1"],
+                       capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads([ln for ln in r.stdout.splitlines() if ln.startswith("{")][0])
+    rc = d["receipt"]
+    assert rc["status"] == "PASS" and rc["heads"] == 4 and rc["kv_heads"] == 4, rc
+    assert max(rc["max_err"].values()) <= 1e-4
+    assert d["cpu_baseline"]["host_cores"] >= 1 and d["cpu_baseline"]["cores"] >= 1
 
 
 def test_bench_decode():
