@@ -27,6 +27,7 @@ STATUS_NAMES = {
     5: "ATTN_ERR_WORKSPACE",
     6: "ATTN_ERR_HIP",
     7: "ATTN_ERR_ALIAS",
+    8: "ATTN_ERR_SCRATCH",
 }
 
 # Every symbol include/attn.h declares, with its ctypes signature.
@@ -44,6 +45,7 @@ SIGNATURES = {
     "attn_bwd": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64, _I64, _I64, _F, _INT, _INT, _P]),
     "attn_bwd_gqa": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64, _I64, _I64, _I64, _F, _INT, _INT,
                             _P]),
+    "attn_bwd_noalloc": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _INT, _INT, _P]),
     "attn_bwd_atomic_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _INT]),
     "attn_bwd_atomic": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64, _I64, _I64, _F, _INT, _INT,
                                _P]),
@@ -125,6 +127,11 @@ def c_attn_bwd_gqa(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, H, H_kv, S,
                    stream=0) -> int:
     return load_library().attn_bwd_gqa(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, H, H_kv, S, D, scale, causal,
                                        dtype, stream)
+
+
+def c_attn_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, B, H, S, D, scale, causal, dtype, stream=0) -> int:
+    return load_library().attn_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, B, H, S, D, scale, causal, dtype,
+                                           stream)
 
 
 def c_attn_bwd_atomic_workspace_bytes(B, H, S, D, dtype) -> int:

@@ -11,10 +11,37 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/attn.h"
 #include "attn_launch.h"
 
+// Scratch of attn_bwd_noalloc: the fp32 delta vector of up to
+// ATTN_NOALLOC_MAX_ROWS query rows.  In host code this name is a stand-in, not a
+// device address: kernels and copies get the per-device address that
+// hipGetSymbolAddress returns (scratch_on_current_device below).
+static __device__ __align__(256) float scratch[ATTN_NOALLOC_MAX_ROWS];
+
 namespace {
+
+// Device address of `scratch` on the current device, looked up once per device
+// (each GPU holds its own copy of the array at its own address); nullptr if the
+// runtime reports an error.
+constexpr int kMaxDevices = 64;
+void* g_scratch[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+void* scratch_on_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch[dev] = p;
+    }
+    return g_scratch[dev];
+}
 
 using attn::LaunchArgs;
 
@@ -156,6 +183,8 @@ const char* attn_status_string(attn_status s) {
         case ATTN_ERR_WORKSPACE: return "workspace is NULL or smaller than attn_bwd_workspace_bytes()";
         case ATTN_ERR_HIP: return "the HIP runtime reported an error at launch";
         case ATTN_ERR_ALIAS: return "an output buffer overlaps an input or another output";
+        case ATTN_ERR_SCRATCH:
+            return "attn_bwd_noalloc: B*H*S exceeds ATTN_NOALLOC_MAX_ROWS, the rows its static scratch holds";
     }
     return "unknown attn_status";
 }
@@ -375,6 +404,39 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      int64_t S, int64_t D, float scale, int causal, attn_dtype dtype, void* stream) {
     return attn_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, S, D, scale, causal,
                         dtype, stream);
+}
+
+attn_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                             const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t S,
+                             int64_t D, float scale, int causal, attn_dtype dtype, void* stream) {
+    bool empty = false;
+    attn_status st = check_shape(B, H, S, D, dtype, &empty);
+    if (st == ATTN_OK) st = check_scale_causal(scale, causal);
+    if (st != ATTN_OK || empty) return st;
+    if (B * H * S > (int64_t)ATTN_NOALLOC_MAX_ROWS) return ATTN_ERR_SCRATCH;
+    if ((st = check_ptrs({q, k, v, o, dout, lse, dq, dk, dv})) != ATTN_OK) return st;
+    const Sizes z = sizes(B, H, S, D, dtype);
+    if ((st = check_alias({{dq, z.tensor}, {dk, z.tensor}, {dv, z.tensor}},
+                          {{q, z.tensor}, {k, z.tensor}, {v, z.tensor}, {o, z.tensor}, {dout, z.tensor},
+                           {lse, z.rows}})) != ATTN_OK)
+        return st;
+    float* delta = static_cast<float*>(scratch_on_current_device());
+    if (!delta) return ATTN_ERR_HIP;
+    LaunchArgs a = base_args(B, H, S, D, scale, causal, stream);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o_in = o;
+    a.dout = dout;
+    a.lse_in = lse;
+    a.delta = delta;
+    a.delta_in = delta;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    // as attn_bwd: the dQ pass forms delta, then the dK/dV pass reads it
+    if ((st = run_dq_delta(a, dtype)) != ATTN_OK) return st;
+    return run_dkdv(a, dtype);
 }
 
 attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,

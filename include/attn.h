@@ -87,7 +87,8 @@ typedef enum attn_status {
     ATTN_ERR_ALIGNMENT = 4,   /* a device pointer not aligned to 16 bytes */
     ATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than attn_bwd_workspace_bytes() */
     ATTN_ERR_HIP = 6,         /* the HIP runtime reported an error when launching */
-    ATTN_ERR_ALIAS = 7        /* an output overlaps an input or another output */
+    ATTN_ERR_ALIAS = 7,       /* an output overlaps an input or another output */
+    ATTN_ERR_SCRATCH = 8      /* attn_bwd_noalloc: more query rows than its static scratch holds */
 } attn_status;
 
 /*
@@ -175,6 +176,28 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      void* workspace, size_t workspace_bytes,
                      int64_t B, int64_t H, int64_t S, int64_t D,
                      float scale, int causal, attn_dtype dtype, void* stream);
+
+/*
+ * attn_bwd without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The delta vector lives in a static device array of the
+ * library (ATTN_NOALLOC_MAX_ROWS fp32 values, 8 MiB, held by every GPU the
+ * library runs on until the process ends); the call allocates nothing.
+ *   Arguments, outputs and errors as attn_bwd, without workspace and
+ *   workspace_bytes; B*H*S > ATTN_NOALLOC_MAX_ROWS -> ATTN_ERR_SCRATCH (nothing
+ *   enqueued).  Same kernels and results (bitwise) as attn_bwd.
+ *   The stream must belong to the current device.  Every call on one GPU uses
+ *   that GPU's single scratch array: calls that overlap on one GPU (other
+ *   streams, other threads) race and must be ordered by the caller.  delta is
+ *   fully written by the dQ pass before the dK/dV pass reads it, so nothing in
+ *   the array needs to start at zero.
+ */
+#define ATTN_NOALLOC_MAX_ROWS (1 << 21)
+attn_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse,
+                             void* dq, void* dk, void* dv,
+                             int64_t B, int64_t H, int64_t S, int64_t D,
+                             float scale, int causal, attn_dtype dtype, void* stream);
 
 /*
  * Bytes of device workspace attn_bwd_atomic needs: the fp32 delta vector (B*H*S*4

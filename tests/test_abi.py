@@ -16,7 +16,7 @@ from causal_attention_flash_amd import _binding as bd
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
 
-OK, NULL, SHAPE, UNSUP, ALIGN, WS, HIP, ALIAS = range(8)
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, HIP, ALIAS, SCRATCH = range(9)
 BF16, F32, F16 = bd.ATTN_BF16, bd.ATTN_F32, bd.ATTN_F16
 
 # distinct, 16-byte aligned, far apart fake device addresses
@@ -46,7 +46,8 @@ def test_header_declares_the_boundary():
                           "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_delta", "attn_status_string",
                           "attn_fwd_gqa", "attn_bwd_gqa", "attn_bwd_gqa_workspace_bytes",
                           "attn_decode", "attn_decode_workspace_bytes", "attn_fwd_fp8qk",
-                          "attn_bwd_atomic", "attn_bwd_atomic_workspace_bytes", "attn_clock_sample"}
+                          "attn_bwd_atomic", "attn_bwd_atomic_workspace_bytes", "attn_clock_sample",
+                          "attn_bwd_noalloc"}
     for name, nargs in decls.items():
         assert len(bd.SIGNATURES[name][1]) == nargs, name
 
@@ -60,7 +61,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(8):
+    for code in range(9):
         s = bd.status_string(code)
         assert isinstance(s, str) and s
     assert bd.status_string(99) == "unknown attn_status"
@@ -125,6 +126,28 @@ def test_documented_limits_at_their_edges(lib, kw, expect):
     assert bwd(q=0, ws_bytes=1 << 62, **kw) == expect
     dkw = {("L" if key == "S" else key): val for key, val in kw.items()}
     assert dec(q=0, Hkv=1, **dkw) == expect
+
+
+def bwd_noalloc(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], do=P[4], lse=P[5], dq=P[6], dk=P[7], dv=P[8],
+             B=2, H=3, S=100, D=64, scale=0.125, causal=1, dtype=BF16)
+    a.update(kw)
+    return bd.c_attn_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                                 a["B"], a["H"], a["S"], a["D"], a["scale"], a["causal"], a["dtype"], 0)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=0), NULL), (dict(dv=0), NULL), (dict(lse=0), NULL),
+    (dict(D=72), UNSUP), (dict(scale=0.0), UNSUP), (dict(causal=3), UNSUP), (dict(S=-1), SHAPE),
+    (dict(dq=P[0] + 8), ALIGN), (dict(dq=P[1]), ALIAS), (dict(dk=P[6]), ALIAS),
+    # the scratch holds 2^21 query rows: at the limit the next check (NULL) is what fails
+    (dict(B=1, H=1, S=1 << 21, q=0), NULL), (dict(B=4, H=1 << 9, S=1 << 10, q=0), NULL),
+    (dict(B=1, H=1, S=(1 << 21) + 1), SCRATCH), (dict(B=3, H=1 << 10, S=1 << 10), SCRATCH),
+    (dict(B=0, q=0, dq=0), OK),
+])
+def test_bwd_noalloc_validation(lib, kw, expect):
+    assert bwd_noalloc(**kw) == expect
+    assert f"#define ATTN_NOALLOC_MAX_ROWS (1 << 21)" in open(HEADER).read()
 
 
 def test_clock_sample_validation(lib):
