@@ -41,9 +41,9 @@ struct DkdvCfg {
     static constexpr int NW = NW_;
     static constexpr int NT = NW * 64;
     static constexpr int BNK = NW * 32;  // keys per workgroup (32 per wave)
-    using QT = RowTile<BMQ, D, NT>;      // Q and dO tiles, row-major
-    static constexpr int STR = QT::STR;
+    using QT = RowTile<BMQ, D, NT>;      // Q and dO tiles, padded rows
     static constexpr int QE = QT::ELEMS;
+    static constexpr int KSTR = D + 8;   // DQA: row stride of each wave's copy of its K rows
     static constexpr int BUF_ELEMS = 2 * QE;   // Q, dO
     static constexpr int BUF_STATS = 2 * BMQ;  // -LSE/scale, -delta (fp32)
     // register budget: 256 VGPRs (two waves per SIMD) up to D = 96
@@ -81,19 +81,19 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
     using Cfg = DkdvCfg<D, BMQ, NW>;
     using V8 = typename E::V8;
     constexpr int NT = Cfg::NT, BNK = Cfg::BNK;
-    constexpr int STR = Cfg::STR;
+    constexpr int KSTR = Cfg::KSTR;
     constexpr int KS = Cfg::KS, DB = Cfg::DB;
     static_assert(!(DQA && PARTIAL), "atomic dQ is for one query head per key/value head");
     static_assert(!DQA || (32 * D) % (NW * 64) == 0, "the flush splits a block's 32 x D sums evenly");
-    // [Q, dO][2]; both are read transposed, so the last carries the slack
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Cfg::BUF_ELEMS + Cfg::QT::TR_SLACK];
+    // [Q, dO][2]
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Cfg::BUF_ELEMS];
     __shared__ __attribute__((aligned(16))) float sstat[2 * Cfg::BUF_STATS];
     // DQA: each wave's K rows [32][STR] and dQ slot [32 queries][DQS] (the odd row
     // stride spreads a column's rows over the banks), its dS tile [32 keys][DSTR]
     // at the start of the slot
     constexpr int DSTR = 40, DQS = D + 1;
     static_assert(32 * DSTR * 2 <= 32 * DQS * 4, "the dS tile fits in the slot");
-    __shared__ __attribute__((aligned(16))) uint16_t kst[DQA ? NW * 32 * STR : 1];
+    __shared__ __attribute__((aligned(16))) uint16_t kst[DQA ? NW * 32 * KSTR + 32 : 1];
     __shared__ __attribute__((aligned(16))) float dqs[DQA ? NW * 32 * DQS : 1];
 
     const WorkItem wi = heavy_first(blockIdx.x, BH);
@@ -125,14 +125,14 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
         kf[ks] = as_op<E>(a);
         vf[ks] = as_op<E>(b);
     }
-    uint16_t* kst_w = kst + wave * 32 * STR;
+    uint16_t* kst_w = kst + wave * 32 * KSTR;
     float* slot_w = dqs + wave * 32 * DQS;
     uint16_t* dst_w = reinterpret_cast<uint16_t*>(slot_w);
     if constexpr (DQA) {
         // the wave's K rows, for the transposing reads of K^T (zero past S)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            *reinterpret_cast<u32x4*>(kst_w + n * STR + ks * 16 + 8 * h) = __builtin_bit_cast(u32x4, kf[ks]);
+            *reinterpret_cast<u32x4*>(kst_w + n * KSTR + ks * 16 + 8 * h) = __builtin_bit_cast(u32x4, kf[ks]);
     }
 
     f32x16 dkacc[DB], dvacc[DB];
@@ -149,6 +149,8 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
     const int ntiles = (S + BMQ - 1) / BMQ;
 
     typename Cfg::QT qt, ot;
+    using QT = typename Cfg::QT;
+    const int rl = QT::row_lane(lane), tl = QT::tr_lane(lane);
     RowStats<BMQ, NT> st;
     auto bufp = [&](int b) { return smem + b * Cfg::BUF_ELEMS; };
     auto stat = [&](int b) { return sstat + b * Cfg::BUF_STATS; };
@@ -210,9 +212,8 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
             // 32 queries x this wave's 32 keys: S - LSE/scale and dP - delta
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const int off = (qb * 32 + n) * STR + ks * 16 + 8 * h;
-                sacc = E::mma(as_op<E>(lds16(Qs + off)), kf[ks], sacc);
-                pacc = E::mma(as_op<E>(lds16(dOs + off)), vf[ks], pacc);
+                sacc = E::mma(QT::template row_op<E>(Qs, qb * 32, ks, rl), kf[ks], sacc);
+                pacc = E::mma(QT::template row_op<E>(dOs, qb * 32, ks, rl), vf[ks], pacc);
             }
             // P and dS
 #pragma unroll
@@ -236,8 +237,8 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     const int r0 = (qb * 2 + c2) * 16;
-                    dvacc[db] = E::mma(lds_tr_op<E, STR>(dOs, r0, db * 32, lane), pb, dvacc[db]);
-                    dkacc[db] = E::mma(lds_tr_op<E, STR>(Qs, r0, db * 32, lane), sb, dkacc[db]);
+                    dvacc[db] = E::mma(QT::template tr_op<E>(dOs, r0, db, tl), pb, dvacc[db]);
+                    dkacc[db] = E::mma(QT::template tr_op<E>(Qs, r0, db, tl), sb, dkacc[db]);
                 }
             }
             if constexpr (DQA) {
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
                     const V8 sb = lds_tr_op<E, DSTR>(dst_w, c2 * 16, 0, lane);
 #pragma unroll
                     for (int db = 0; db < DB; ++db)
-                        dqp[db] = E::mma(lds_tr_op<E, STR>(kst_w, c2 * 16, db * 32, lane), sb, dqp[db]);
+                        dqp[db] = E::mma(lds_tr_op<E, KSTR>(kst_w, c2 * 16, db * 32, lane), sb, dqp[db]);
                 }
                 // the wave's partial: lane n holds query n, d = 32db + crow(r, h)
 #pragma unroll
@@ -500,19 +501,16 @@ struct DqCfg {
     static constexpr int BMQ = NW * 32;  // queries per workgroup (32 per wave)
     // K and V tiles, two buffers each, fetched one iteration ahead.  At D = 64
     // they are staged through registers into padded rows; wider heads load them
-    // straight from HBM into swizzled rows (measured: the direct path is 1-2%
-    // slower at D = 64 and 5-7% faster at D = 128; fetching two tiles ahead was
-    // slower at every size)
+    // straight from HBM into swizzled rows (measured with the earlier layouts:
+    // the direct path 1-2% slower at D = 64 and 5-7% faster at D = 128; fetching
+    // two tiles ahead was slower at every size)
     static constexpr bool DIRECT = D != 64;
-    using KT = RowTile<BNK, D, NT>;  // register-staged: [rows][D + 8]
-    static constexpr int STR = KT::STR;
-    static constexpr int KE = KT::ELEMS;
+    using KT = RowTile<BNK, D, NT>;  // register-staged: padded rows
     using Tile = DTile<BNK, D, NW>;  // direct: swizzled rows
-    static constexpr int TE = Tile::ELEMS;
+    static constexpr int TE = DIRECT ? Tile::ELEMS : KT::ELEMS;  // one tile in LDS
     static constexpr int LOADS = Tile::LOADS;
-    // direct: K[2], V[2]; staged: [K, V][2] (K is read transposed: a V tile
-    // follows each K tile, and the slack keeps the layout rule uniform)
-    static constexpr int SMEM_ELEMS = DIRECT ? 4 * TE : 4 * KE + KT::TR_SLACK;
+    // K[2], V[2]
+    static constexpr int SMEM_ELEMS = 4 * TE;
     // register budget: 168 VGPRs (3 waves per SIMD) fits D = 64 without spills,
     // 256 (two) fits D = 80 and 96
     static constexpr int WAVES_PER_SIMD = D == 64 ? 3 : (D <= 96 ? 2 : 1);
@@ -534,7 +532,7 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
     constexpr int BMQ = Cfg::BMQ;
     constexpr int KS = Cfg::KS, DB = Cfg::DB;
     constexpr bool DIRECT = Cfg::DIRECT;
-    constexpr int STR = Cfg::STR, KE = Cfg::KE, TE = Cfg::TE;
+    constexpr int TE = Cfg::TE;
     __shared__ __attribute__((aligned(16))) uint16_t smem[Cfg::SMEM_ELEMS];
 
     const WorkItem wi = heavy_first(blockIdx.x, BH);
@@ -562,10 +560,18 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
     // load from row S (an empty buffer range) so every path issues the same loads.
     // Staged: after its tile, iteration t stores tile t + 1 from registers and
     // fetches tile t + 2 into them.
-    auto kbuf = [&](int t) { return DIRECT ? smem + (t & 1) * TE : smem + (t & 1) * 2 * KE; };
-    auto vbuf = [&](int t) { return DIRECT ? smem + (2 + (t & 1)) * TE : smem + (t & 1) * 2 * KE + KE; };
+    auto kbuf = [&](int t) { return smem + (t & 1) * TE; };
+    auto vbuf = [&](int t) { return smem + (2 + (t & 1)) * TE; };
     typename Cfg::Tile::Src src;
     DOffsets<typename Cfg::Tile, D> lo;
+    using KT = typename Cfg::KT;
+    int rl = 0, tl = 0;
+    if constexpr (DIRECT) {
+        lo.init(lane);
+    } else {
+        rl = KT::row_lane(lane);
+        tl = KT::tr_lane(lane);
+    }
     auto load_t = [&](int t) {
         const int row = t < ntiles ? t * BNK : S;
         Cfg::Tile::load(Kh, row, S, kbuf(t), src, wave);
@@ -582,7 +588,6 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
     };
     if constexpr (DIRECT) {
         src.init(wave, lane);
-        lo.init(lane);
         load_t(0);
     }
 
@@ -649,9 +654,8 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
                     sacc = E::mma(lo.template row_op<E>(Ks, kb * 32, ks), qf[ks], sacc);
                     pacc = E::mma(lo.template row_op<E>(Vs, kb * 32, ks), of[ks], pacc);
                 } else {
-                    const int off = (kb * 32 + n) * STR + ks * 16 + 8 * h;
-                    sacc = E::mma(as_op<E>(lds16(Ks + off)), qf[ks], sacc);
-                    pacc = E::mma(as_op<E>(lds16(Vs + off)), of[ks], pacc);
+                    sacc = E::mma(KT::template row_op<E>(Ks, kb * 32, ks, rl), qf[ks], sacc);
+                    pacc = E::mma(KT::template row_op<E>(Vs, kb * 32, ks, rl), of[ks], pacc);
                 }
             }
             // direct: K^T operands of this block's dQ product, read transposed from
@@ -682,7 +686,7 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
                     if constexpr (DIRECT)
                         dqacc[db] = E::mma(tr_join<E>(kr[c2][db]), sb, dqacc[db]);
                     else
-                        dqacc[db] = E::mma(lds_tr_op<E, STR>(Ks, (kb * 2 + c2) * 16, db * 32, lane), sb, dqacc[db]);
+                        dqacc[db] = E::mma(KT::template tr_op<E>(Ks, (kb * 2 + c2) * 16, db, tl), sb, dqacc[db]);
                 }
             }
         }

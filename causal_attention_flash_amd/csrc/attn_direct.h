@@ -5,37 +5,20 @@
 // every wave's loads for it have drained (s_waitcnt vmcnt) and a barrier has
 // passed; the kernels count their own loads for that.
 //
-// LDS layout: row r of a tile holds RP 16-byte slots (RP = D/8 rounded up to a
-// power of two); logical 16-byte chunk c of the row sits in slot c ^ swz(r).  A
-// wave's load fills 64 consecutive slots, and each lane fetches the logical chunk
-// that belongs in its slot, so the swizzle costs nothing at load time.  Slots past
-// the row's D/8 chunks are loaded from an offset beyond the buffer range and read
-// as zero.  Rows at or beyond S also read as zero: the buffer range of a tile ends
-// at row S.
-//
-// swz(r) = 2*(r % 4) + (r / 4) % 2 makes both operand reads conflict-free (rows
-// of 128 or 256 bytes start on the same bank; a 16-byte slot covers 4 of the 32
-// four-byte banks a 16-byte read of 8 lanes spans):
-// * 16-byte row reads (8 consecutive rows, one logical chunk): swz takes 8
-//   distinct values over 8 consecutive rows, so the 8 slots are distinct;
-// * transposing reads (groups of 4 consecutive rows r..r+3, r % 4 == 0, each
-//   reading a pair of adjacent chunks 2p, 2p+1): swz / 2 = r % 4 differs across
-//   the 4 rows and swz keeps pairs together, so the 4 pairs occupy distinct slot
-//   pairs.
-// Rows of 64 bytes (4 slots; fp8 rows of 64 elements, read only as 16-byte row
-// operands) use swz4(r) = (r / 2) % 4: even and odd rows start 64 bytes apart,
-// and over 8 consecutive rows the 4 even (and the 4 odd) ones take 4 distinct
-// slots.
+// LDS layout: the swizzled row layout of attn_tiles.h (row r holds RP 16-byte
+// slots, logical chunk c in slot c ^ slot_swizzle<RP>(r)).  A wave's load fills 64
+// consecutive slots, and each lane fetches the logical chunk that belongs in its
+// slot, so the swizzle costs nothing at load time.  Slots past the row's D/8
+// chunks are loaded from an offset beyond the buffer range and read as zero.
+// Rows at or beyond S also read as zero: the buffer range of a tile ends at row
+// S.  Rows of 64 bytes (RP = 4) hold fp8 rows of 64 elements, read only as
+// 16-byte row operands.
 #pragma once
 
 #include "attn_tiles.h"
 
 namespace attn {
 
-constexpr int pow2_up(int x) { return x <= 1 ? 1 : 2 * pow2_up((x + 1) / 2); }
-
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-__device__ __forceinline__ int swz4(int r) { return (r >> 1) & 3; }
 
 // Byte address within LDS of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -86,8 +69,7 @@ struct DTile {
     static constexpr int ELEMS = ROWS * RS;        // LDS footprint (elements)
     static constexpr int LOADS = ROWS * RP / (64 * NW);  // load instructions per wave per tile
     static_assert(ROWS * RP % (64 * NW) == 0, "tile must split evenly over the waves");
-    static_assert(RP == 4 || RP == 8 || RP == 16, "swizzles cover rows of 4, 8 or 16 slots");
-    __device__ static __forceinline__ int sw(int r) { return RP == 4 ? swz4(r) : swz(r); }
+    __host__ __device__ static __forceinline__ constexpr int sw(int r) { return slot_swizzle<RP>(r); }
 
     // Byte offsets (within the tile's global rows) each lane fetches, one per
     // load instruction; slots with no logical chunk get an offset past any range.
@@ -121,14 +103,14 @@ struct DTile {
     }
 
     // element offset of logical (row, col), col % 4 == 0
-    __device__ static __forceinline__ int at(int r, int col) {
+    __host__ __device__ static __forceinline__ int at(int r, int col) {
         return r * RS + ((((col >> 3) ^ sw(r)) << 3) | (col & 7));
     }
 };
 
-// Per-lane LDS offsets for the two operand reads of a DTile, computed once (the
-// swizzle depends on the row modulo 8 only, and every row step the kernels add
-// is a multiple of 8).
+// Per-lane LDS offsets for the two operand reads of a swizzled tile (DTile or
+// RowTile), computed once (the swizzle depends on the row modulo 16 only, and
+// every row step the kernels add is a multiple of 16).
 //   row[ks]   : 16-byte row operand, row n, columns 16ks + 8h .. +7
 //   tr[db][e] : transposing read (the lds_tr_operand lane map) for columns
 //               32db.., rows +0 (e = 0) and +8 (e = 1) of a 16-row step
@@ -156,7 +138,15 @@ struct DOffsets {
         return as_op<E>(lds16(T + r0 * TILE::RS + row[ks]));
     }
     // Transposing read of the operand contracting over rows r0 .. r0+15 (r0 a
-    // multiple of 16), columns 32db + n, issued as inline assembly into two raw
+    // multiple of 16), columns 32db + n (the lds_tr_operand lane map), through the
+    // compiler's builtin: it waits for the read where the operand is used.
+    template <class E>
+    __device__ __forceinline__ typename E::V8 tr_op(const uint16_t* T, int r0, int db) const {
+        const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(T + r0 * TILE::RS + tr[db][0]));
+        const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(T + r0 * TILE::RS + tr[db][1]));
+        return __builtin_bit_cast(typename E::V8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    // The same read issued as inline assembly into two raw
     // halves.  The compiler does not see an LDS read there, so it adds no wait for
     // the loads in flight (which it would otherwise do before every transposing
     // read, unable to tell it from a load's LDS write).  The halves hold data only
