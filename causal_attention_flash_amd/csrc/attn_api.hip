@@ -45,6 +45,8 @@ void* scratch_on_current_device() {
 
 using attn::LaunchArgs;
 
+int g_cus[kMaxDevices] = {};
+
 struct Span {
     const void* p;
     size_t bytes;
@@ -167,6 +169,17 @@ attn_status run_dq_delta(const LaunchArgs& a, attn_dtype dt) {
 }
 
 }  // namespace
+
+int attn::cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    if (g_cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        g_cus[dev] = n;
+    }
+    return g_cus[dev];
+}
 
 extern "C" {
 

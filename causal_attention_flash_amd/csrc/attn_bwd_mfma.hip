@@ -36,7 +36,11 @@ namespace attn {
 
 // ============================================================== dK / dV pass
 
-template <int D, int BMQ, int NW_>
+// MODE: 0 = dK and dV (one pass), 1 = dV only, 2 = dK only.  The one-accumulator
+// passes are the pages' remedy for the register pressure of this pass (Forge
+// paper, "Finding 3: register pressure dominates attention backward": separate
+// dK and dV kernels, each holding one accumulator and recomputing what it needs).
+template <int D, int BMQ, int NW_, int MODE = 0>
 struct DkdvCfg {
     static constexpr int NW = NW_;
     static constexpr int NT = NW * 64;
@@ -46,8 +50,9 @@ struct DkdvCfg {
     static constexpr int KSTR = D + 8;   // DQA: row stride of each wave's copy of its K rows
     static constexpr int BUF_ELEMS = 2 * QE;   // Q, dO
     static constexpr int BUF_STATS = 2 * BMQ;  // -LSE/scale, -delta (fp32)
-    // register budget: 256 VGPRs (two waves per SIMD) up to D = 96
-    static constexpr int WAVES_PER_SIMD = D <= 96 ? 2 : 1;
+    // register budget: 256 VGPRs (two waves per SIMD) up to D = 96, and for the
+    // one-accumulator passes at D = 128
+    static constexpr int WAVES_PER_SIMD = (D <= 96 || MODE != 0) ? 2 : 1;
     static constexpr int KS = HeadDim<D>::KSTEPS;
     static constexpr int DB = HeadDim<D>::DB;
 };
@@ -72,15 +77,17 @@ struct DkdvCfg {
 // adds, zero sums skipped); a second barrier frees the slots.  (Summing in one
 // slot with LDS atomics instead measured ~9x slower: eight waves' ds_add_f32 on
 // the same addresses serialise.)
-template <class E, int D, int BMQ, int NW, bool PARTIAL, bool DQA = false>
-__global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) void bwd_dkdv_mfma_kernel(
+template <class E, int D, int BMQ, int NW, bool PARTIAL, bool DQA = false, int MODE = 0>
+__global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW, MODE>::WAVES_PER_SIMD)) void bwd_dkdv_mfma_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ dKp, float* __restrict__ dVp, int S,
     int nblk, int BH, int H, int GQ, float c, float scale, int causal, float* __restrict__ dQacc = nullptr) {
-    using Cfg = DkdvCfg<D, BMQ, NW>;
+    using Cfg = DkdvCfg<D, BMQ, NW, MODE>;
     using V8 = typename E::V8;
     constexpr int NT = Cfg::NT, BNK = Cfg::BNK;
+    constexpr bool WANT_DK = MODE != 1, WANT_DV = MODE != 2;
+    static_assert(MODE == 0 || !DQA, "atomic dQ runs in the one-pass form");
     constexpr int KSTR = Cfg::KSTR;
     constexpr int KS = Cfg::KS, DB = Cfg::DB;
     static_assert(!(DQA && PARTIAL), "atomic dQ is for one query head per key/value head");
@@ -120,7 +127,7 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
         u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
         if (key < S) {
             a = ldg16(K + kvbase + (size_t)key * D + ks * 16 + 8 * h);
-            b = ldg16(V + kvbase + (size_t)key * D + ks * 16 + 8 * h);
+            if (WANT_DK) b = ldg16(V + kvbase + (size_t)key * D + ks * 16 + 8 * h);
         }
         kf[ks] = as_op<E>(a);
         vf[ks] = as_op<E>(b);
@@ -202,7 +209,8 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
             for (int g = 0; g < 4; ++g) {
                 const int rl = qb * 32 + 8 * g + 4 * h;
                 const f32x4 si = *reinterpret_cast<const f32x4*>(SIs + rl);
-                const f32x4 pi = *reinterpret_cast<const f32x4*>(PIs + rl);
+                f32x4 pi = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (WANT_DK) pi = *reinterpret_cast<const f32x4*>(PIs + rl);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     sacc[4 * g + i] = si[i];
@@ -213,7 +221,7 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 sacc = E::mma(QT::template row_op<E>(Qs, qb * 32, ks, rl), kf[ks], sacc);
-                pacc = E::mma(QT::template row_op<E>(dOs, qb * 32, ks, rl), vf[ks], pacc);
+                if constexpr (WANT_DK) pacc = E::mma(QT::template row_op<E>(dOs, qb * 32, ks, rl), vf[ks], pacc);
             }
             // P and dS
 #pragma unroll
@@ -226,19 +234,20 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
                 // in columns that are never stored.
                 if constexpr (DQA) p = key < S ? p : 0.f;
                 sacc[r] = p;
-                pacc[r] *= p;
+                if constexpr (WANT_DK) pacc[r] *= p;
             }
             // dV^T += dO^T P ; dK^T += Q^T dS  (contraction over these 32 queries;
             // dO^T and Q^T read transposed from the row-major tiles)
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
-                const V8 pb = pack_op<E>(sacc, c2);
-                const V8 sb = pack_op<E>(pacc, c2);
+                V8 pb{}, sb{};
+                if constexpr (WANT_DV) pb = pack_op<E>(sacc, c2);
+                if constexpr (WANT_DK) sb = pack_op<E>(pacc, c2);
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     const int r0 = (qb * 2 + c2) * 16;
-                    dvacc[db] = E::mma(QT::template tr_op<E>(dOs, r0, db, tl), pb, dvacc[db]);
-                    dkacc[db] = E::mma(QT::template tr_op<E>(Qs, r0, db, tl), sb, dkacc[db]);
+                    if constexpr (WANT_DV) dvacc[db] = E::mma(QT::template tr_op<E>(dOs, r0, db, tl), pb, dvacc[db]);
+                    if constexpr (WANT_DK) dkacc[db] = E::mma(QT::template tr_op<E>(Qs, r0, db, tl), sb, dkacc[db]);
                 }
             }
             if constexpr (DQA) {
@@ -323,8 +332,8 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
                     fk[i] = dkacc[db][4 * g + i] * scale;
                     fv[i] = dvacc[db][4 * g + i];
                 }
-                *reinterpret_cast<f32x4*>(dKr + d) = fk;
-                *reinterpret_cast<f32x4*>(dVr + d) = fv;
+                if (WANT_DK) *reinterpret_cast<f32x4*>(dKr + d) = fk;
+                if (WANT_DV) *reinterpret_cast<f32x4*>(dVr + d) = fv;
             }
     }
     if (!PARTIAL && key < S) {
@@ -341,31 +350,44 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW>::WAVES_PER_SIMD)) voi
                 uk[1] = E::pack2(dkacc[db][4 * g + 2] * scale, dkacc[db][4 * g + 3] * scale);
                 uv[0] = E::pack2(dvacc[db][4 * g + 0], dvacc[db][4 * g + 1]);
                 uv[1] = E::pack2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]);
-                *reinterpret_cast<u32x2*>(dKr + d) = uk;
-                *reinterpret_cast<u32x2*>(dVr + d) = uv;
+                if (WANT_DK) *reinterpret_cast<u32x2*>(dKr + d) = uk;
+                if (WANT_DV) *reinterpret_cast<u32x2*>(dVr + d) = uv;
             }
     }
+
 }
 
-template <class E, int D, int BMQ, int NW>
+template <class E, int D, int BMQ, int NW, int MODE = 0>
 static hipError_t launch_dkdv(const LaunchArgs& a) {
-    using Cfg = DkdvCfg<D, BMQ, NW>;
+    using Cfg = DkdvCfg<D, BMQ, NW, MODE>;
     const int nblk = (int)((a.S + Cfg::BNK - 1) / Cfg::BNK);
     const int64_t total = (int64_t)nblk * a.BH;
     if (total > INT32_MAX) return hipErrorInvalidValue;
     const int GQ = (int)(a.H / a.Hkv);
     if (GQ == 1)
-        hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D, BMQ, NW, false>), dim3((unsigned)total), dim3(Cfg::NT), 0,
+        hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D, BMQ, NW, false, false, MODE>), dim3((unsigned)total), dim3(Cfg::NT), 0,
                            a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                            (const uint16_t*)a.dout, a.lse_in, a.delta_in, (uint16_t*)a.dk, (uint16_t*)a.dv,
                            nullptr, nullptr, (int)a.S, nblk, (int)a.BH, (int)a.H, 1, a.scale * kLog2e, a.scale,
                            a.causal);
     else
-        hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D, BMQ, NW, true>), dim3((unsigned)total), dim3(Cfg::NT), 0,
+        hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<E, D, BMQ, NW, true, false, MODE>), dim3((unsigned)total), dim3(Cfg::NT), 0,
                            a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                            (const uint16_t*)a.dout, a.lse_in, a.delta_in, nullptr, nullptr, a.dk_part, a.dv_part,
                            (int)a.S, nblk, (int)a.BH, (int)a.H, GQ, a.scale * kLog2e, a.scale, a.causal);
     return hipGetLastError();
+}
+
+// dK and dV in two one-accumulator passes (MODE 1 then 2) on the stream.  At
+// D = 128 the one-pass form holds both 32 x 128 accumulators (329 registers with
+// the AGPRs: one wave per SIMD); each one-accumulator pass fits 256 and runs two,
+// with 64-query tiles and eight waves.  Measured 2.6-3.5% faster for the pair of
+// passes on 8191-token and 2048-token heads; at D = 96 the extra pass over Q and
+// dO costs more than the occupancy gains (33% slower).
+template <class E, int D, int BMQ, int NW>
+static hipError_t launch_dkdv_split(const LaunchArgs& a) {
+    const hipError_t e = launch_dkdv<E, D, BMQ, NW, 1>(a);
+    return e != hipSuccess ? e : launch_dkdv<E, D, BMQ, NW, 2>(a);
 }
 
 template <class E>
@@ -373,7 +395,7 @@ static hipError_t launch_dkdv_type(const LaunchArgs& a) {
     if (a.D == 64) return launch_dkdv<E, 64, 64, 8>(a);
     if (a.D == 80) return launch_dkdv<E, 80, 64, 8>(a);
     if (a.D == 96) return launch_dkdv<E, 96, 64, 8>(a);
-    if (a.D == 128) return launch_dkdv<E, 128, 32, 4>(a);
+    if (a.D == 128) return launch_dkdv_split<E, 128, 64, 8>(a);
     return hipErrorInvalidValue;
 }
 
@@ -729,6 +751,7 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
                 *reinterpret_cast<u32x2*>(dQr + db * 32 + 8 * g + 4 * h) = u;
             }
     }
+
 }
 
 template <class E, int D, int BNK, int NW, bool DELTA_FROM_O>

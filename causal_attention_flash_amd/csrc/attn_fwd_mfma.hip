@@ -83,6 +83,11 @@ struct FwdCfg {
     static constexpr int P = NB - 1;
     static constexpr int KS = HeadDim<D>::KSTEPS;
     static constexpr int DB = HeadDim<D>::DB;
+    // Paired query blocks (see the kernel): at D = 128 two workgroups fill a CU,
+    // and half as many workgroups, each with the same work, fill it evenly
+    // (measured 5% faster on 8191-token heads).  Where three workgroups fill a
+    // CU (D = 64) pairs leave a third of it idle: 5% slower there.
+    static constexpr bool PAIRABLE = D == 128 && !QK8;
     // the loop masks only a wave's last key tile: a wave's 32 * QB queries must
     // not reach into an earlier tile (else that tile also crosses the diagonal)
     static_assert(32 * QB <= BN, "a wave's queries must fit in one key tile");
@@ -95,7 +100,7 @@ __global__ __launch_bounds__(NW * 64, (FwdCfg<D, QB, NW, QK8, BN_>::WAVES_PER_SI
                                                        const uint16_t* __restrict__ V,
                                                        uint16_t* __restrict__ O, float* __restrict__ LSE,
                                                        int S, int nblk, int BH, int H, int GQ, float c,
-                                                       int causal) {
+                                                       int causal, int paired) {
     using Cfg = FwdCfg<D, QB, NW, QK8, BN_>;
     using V8 = typename E::V8;
     using QK = QkOps<E, D, QK8>;
@@ -108,298 +113,312 @@ __global__ __launch_bounds__(NW * 64, (FwdCfg<D, QB, NW, QK8, BN_>::WAVES_PER_SI
     // K[NB], V[NB]
     __shared__ __attribute__((aligned(16))) uint16_t smem[NB * (TK + TE)];
 
+    // Work: one query block per workgroup, heaviest first (heavy_first), or, with
+    // `paired` (Cfg::PAIRABLE configurations only), a pair of query blocks j and
+    // nblk-1-j per workgroup, one after the other: in a causal head every pair
+    // holds the same number of key tiles, so the workgroups finish together
+    // instead of the heaviest blocks running on alone at the end of the grid.
     const WorkItem wi = heavy_first(blockIdx.x, BH);
-    const int head = wi.head;
-    const int qblk = nblk - 1 - wi.rank;  // most work first
-    const int q0 = qblk * BM;
-    const size_t base = (size_t)head * S * D;
-    const size_t kvbase = (size_t)kv_head_of(head, H, GQ) * S * D;
-    // Q and K rows as 16-bit slots (QK::KD per row; fp8 rows of D bytes are D / 2)
-    const uint16_t* Qh = (const uint16_t*)Q + (QK8 ? base / 2 : base);
-    const uint16_t* Kh = (const uint16_t*)K + (QK8 ? kvbase / 2 : kvbase);
-    const uint16_t* Vh = V + kvbase;
+    const int head = wi.head, rank = wi.rank;
+    const int nparts = Cfg::PAIRABLE && paired && nblk - 1 - rank != rank ? 2 : 1;
+    for (int part = 0; part < nparts; ++part) {
+        if (part > 0) __syncthreads();  // every wave is done with the LDS of the first block
+        const int qblk = part == 0 ? nblk - 1 - rank : rank;  // most work first
+        const int q0 = qblk * BM;
+        const size_t base = (size_t)head * S * D;
+        const size_t kvbase = (size_t)kv_head_of(head, H, GQ) * S * D;
+        // Q and K rows as 16-bit slots (QK::KD per row; fp8 rows of D bytes are D / 2)
+        const uint16_t* Qh = (const uint16_t*)Q + (QK8 ? base / 2 : base);
+        const uint16_t* Kh = (const uint16_t*)K + (QK8 ? kvbase / 2 : kvbase);
+        const uint16_t* Vh = V + kvbase;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int h = lane >> 5, n = lane & 31;
-    const int qw0 = q0 + wave * 32 * QB;
+        const int tid = threadIdx.x;
+        const int lane = tid & 63, wave = tid >> 6;
+        const int h = lane >> 5, n = lane & 31;
+        const int qw0 = q0 + wave * 32 * QB;
 
-    const int kend = causal ? min(S, q0 + BM) : S;
-    const int ntiles = (kend + BN - 1) / BN;  // tiles the workgroup stages
-    // tiles this wave multiplies: the causal ones up to its last query
-    const int nw = causal ? min(ntiles, (qw0 + 32 * QB - 1) / BN + 1) : ntiles;
+        const int kend = causal ? min(S, q0 + BM) : S;
+        const int ntiles = (kend + BN - 1) / BN;  // tiles the workgroup stages
+        // tiles this wave multiplies: the causal ones up to its last query
+        const int nw = causal ? min(ntiles, (qw0 + 32 * QB - 1) / BN + 1) : ntiles;
 
-    auto kbuf = [&](int t) { return smem + (t % NB) * TK; };
-    auto vbuf = [&](int t) { return smem + NB * TK + (t % NB) * TE; };
-    typename Cfg::Tile::Src src;
-    src.init(wave, lane);
-    typename Cfg::KTile::Src ksrc;
-    ksrc.init(wave, lane);
-    DOffsets<typename Cfg::Tile, D> lo;
-    lo.init(lane);
-    // K row operand offsets: 16-bit, the DOffsets row reads; fp8, two 16-byte
-    // chunks per step (indices 64s + 32h .. +31: slots 32s + 16h and +8)
-    int k8[QK8 ? QS : 1][2];
-    if constexpr (QK8) {
-#pragma unroll
-        for (int st = 0; st < QS; ++st) {
-            k8[st][0] = Cfg::KTile::at(n, st * 32 + 16 * h);
-            k8[st][1] = Cfg::KTile::at(n, st * 32 + 16 * h + 8);
-        }
-    }
-
-    // Q as the B operand of S^T = K Q^T: lane holds query qw0+32qb+n; 16-bit:
-    // d = 16ks+8h..+7; fp8: d = 64s+32h..+31.
-    QOp qf[QB][QS];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int q = qw0 + qb * 32 + n;
-#pragma unroll
-        for (int st = 0; st < QS; ++st) {
-            const uint16_t* row = Qh + (size_t)q * QK::KD;
-            if constexpr (QK8) {
-                u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-                if (q < S) {
-                    a = ldg16(row + st * 32 + 16 * h);
-                    b = ldg16(row + st * 32 + 16 * h + 8);
-                }
-                qf[qb][st] = Fp8E4M3::join(a, b);
-            } else {
-                u32x4 u = {0u, 0u, 0u, 0u};
-                if (q < S) u = ldg16(row + st * 16 + 8 * h);
-                qf[qb][st] = as_op<E>(u);
-            }
-        }
-    }
-
-    f32x16 oacc[QB][DB];
-    float m[QB], l[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        m[qb] = -FLT_MAX;
-        l[qb] = 0.f;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
-    }
-
-    // K rows of tile t as A operands of S^T = K Q^T: kf[kb][st] holds key
-    // t*BN + 32kb + n, at the contraction indices of the Q operand.
-    auto load_k = [&](QOp (&kf)[KB][QS], int t) {
-        const uint16_t* Ks = kbuf(t);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
+        auto kbuf = [&](int t) { return smem + (t % NB) * TK; };
+        auto vbuf = [&](int t) { return smem + NB * TK + (t % NB) * TE; };
+        typename Cfg::Tile::Src src;
+        src.init(wave, lane);
+        typename Cfg::KTile::Src ksrc;
+        ksrc.init(wave, lane);
+        DOffsets<typename Cfg::Tile, D> lo;
+        lo.init(lane);
+        // K row operand offsets: 16-bit, the DOffsets row reads; fp8, two 16-byte
+        // chunks per step (indices 64s + 32h .. +31: slots 32s + 16h and +8)
+        int k8[QK8 ? QS : 1][2];
+        if constexpr (QK8) {
+    #pragma unroll
             for (int st = 0; st < QS; ++st) {
-                if constexpr (QK8) {
-                    const uint16_t* r = Ks + kb * 32 * Cfg::KTile::RS;
-                    kf[kb][st] = Fp8E4M3::join(lds16(r + k8[st][0]), lds16(r + k8[st][1]));
-                } else {
-                    kf[kb][st] = lo.template row_op<E>(Ks, kb * 32, st);
-                }
+                k8[st][0] = Cfg::KTile::at(n, st * 32 + 16 * h);
+                k8[st][1] = Cfg::KTile::at(n, st * 32 + 16 * h + 8);
             }
-    };
-    // S^T tile from K operands already in registers; the first contraction step
-    // starts from a zero accumulator.
-    auto mma_scores = [&](f32x16 (&sacc)[QB][KB], const QOp (&kf)[KB][QS]) {
-#pragma unroll
-        for (int st = 0; st < QS; ++st)
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-                    sacc[qb][kb] = QK::mma(kf[kb][st], qf[qb][st], st == 0 ? f32x16{} : sacc[qb][kb]);
-    };
-
-    // One key tile t: softmax of its scores `cur` and O += V_t P_t.  With NEXT,
-    // the scores of tile t+1 are computed into `nxt` in the same straight-line
-    // block as this tile's exp work, so the MFMAs run under the VALU work.
-    // MASK instantiates the per-element causal / sequence-end mask; only a
-    // wave's last tile can need it (its earlier tiles lie entirely below the
-    // diagonal and before S), and the last tile has no successor.
-    auto step = [&](auto mask_tag, auto next_tag, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB], int t) {
-        constexpr bool MASK = decltype(mask_tag)::value;
-        constexpr bool NEXT = decltype(next_tag)::value;
-        QOp kf[KB][QS];
-        if constexpr (NEXT) load_k(kf, t + 1);
-        // V^T operands, read transposed from the V tile (asynchronous: used after lds_wait)
-        i16x4 vr[BN / 16][DB][2];
-        {
-            const uint16_t* Vs = vbuf(t);
-#pragma unroll
-            for (int ks = 0; ks < BN / 16; ++ks)
-#pragma unroll
-                for (int db = 0; db < DB; ++db) lo.tr_async(Vs, ks * 16, db, vr[ks][db]);
         }
 
-        // ---- mask, row max (raw scores; c > 0 so max commutes with scaling)
-        const int k0 = t * BN;
-        float mx[QB];
-        bool grow = false;
-#pragma unroll
+        // Q as the B operand of S^T = K Q^T: lane holds query qw0+32qb+n; 16-bit:
+        // d = 16ks+8h..+7; fp8: d = 64s+32h..+31.
+        QOp qf[QB][QS];
+    #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const int q = qw0 + qb * 32 + n;
-            float v = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    if constexpr (MASK) {
-                        const int key = k0 + kb * 32 + crow(r, h);
-                        const bool kill = (causal && key > q) || key >= S;
-                        cur[qb][kb][r] = kill ? -INFINITY : cur[qb][kb][r];
+    #pragma unroll
+            for (int st = 0; st < QS; ++st) {
+                const uint16_t* row = Qh + (size_t)q * QK::KD;
+                if constexpr (QK8) {
+                    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+                    if (q < S) {
+                        a = ldg16(row + st * 32 + 16 * h);
+                        b = ldg16(row + st * 32 + 16 * h + 8);
                     }
-                    v = fmaxf(v, cur[qb][kb][r]);
+                    qf[qb][st] = Fp8E4M3::join(a, b);
+                } else {
+                    u32x4 u = {0u, 0u, 0u, 0u};
+                    if (q < S) u = ldg16(row + st * 16 + 8 * h);
+                    qf[qb][st] = as_op<E>(u);
                 }
-            v = half_max(v) * c;
-            mx[qb] = v;
-            grow |= v > m[qb] + kRescaleSlack;
-        }
-        // The reference point of the exponent moves only when some row max in
-        // the wave grew past the slack (wave-uniform decision); P values are
-        // otherwise bounded by 2^kRescaleSlack, which fp32 accumulation and
-        // bf16 P absorb.
-        const bool resc = __builtin_amdgcn_ballot_w64(grow) != 0;
-        float mn[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) mn[qb] = resc ? fmaxf(m[qb], mx[qb]) : m[qb];
-
-        if constexpr (NEXT) mma_scores(nxt, kf);
-
-        // ---- P = exp2(s*c - m) rounded to bf16; the row sum adds the same
-        // rounded values the PV product multiplies, so numerator and
-        // denominator of O = (P V) / l carry the same rounding (a row whose
-        // weight sits on one key reproduces that key's V row).
-        V8 pf[QB][BN / 16];
-        float ls[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            ls[qb] = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) cur[qb][kb][r] = fast_exp2(fmaf(cur[qb][kb][r], c, -mn[qb]));
-                pf[qb][2 * kb] = pack_op<E>(cur[qb][kb], 0);
-                pf[qb][2 * kb + 1] = pack_op<E>(cur[qb][kb], 1);
-                ls[qb] = sum8<E>(pf[qb][2 * kb], ls[qb]);
-                ls[qb] = sum8<E>(pf[qb][2 * kb + 1], ls[qb]);
             }
         }
-        if (resc) {
-            // rare (the reference point moves only past the slack): keep it a
-            // branch; the empty volatile asm stops the compiler from executing
-            // the rescale unconditionally
-            asm volatile("");
-#pragma unroll
+
+        f32x16 oacc[QB][DB];
+        float m[QB], l[QB];
+    #pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            m[qb] = -FLT_MAX;
+            l[qb] = 0.f;
+    #pragma unroll
+            for (int db = 0; db < DB; ++db)
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
+        }
+
+        // K rows of tile t as A operands of S^T = K Q^T: kf[kb][st] holds key
+        // t*BN + 32kb + n, at the contraction indices of the Q operand.
+        auto load_k = [&](QOp (&kf)[KB][QS], int t) {
+            const uint16_t* Ks = kbuf(t);
+    #pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+    #pragma unroll
+                for (int st = 0; st < QS; ++st) {
+                    if constexpr (QK8) {
+                        const uint16_t* r = Ks + kb * 32 * Cfg::KTile::RS;
+                        kf[kb][st] = Fp8E4M3::join(lds16(r + k8[st][0]), lds16(r + k8[st][1]));
+                    } else {
+                        kf[kb][st] = lo.template row_op<E>(Ks, kb * 32, st);
+                    }
+                }
+        };
+        // S^T tile from K operands already in registers; the first contraction step
+        // starts from a zero accumulator.
+        auto mma_scores = [&](f32x16 (&sacc)[QB][KB], const QOp (&kf)[KB][QS]) {
+    #pragma unroll
+            for (int st = 0; st < QS; ++st)
+    #pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+    #pragma unroll
+                    for (int qb = 0; qb < QB; ++qb)
+                        sacc[qb][kb] = QK::mma(kf[kb][st], qf[qb][st], st == 0 ? f32x16{} : sacc[qb][kb]);
+        };
+
+        // One key tile t: softmax of its scores `cur` and O += V_t P_t.  With NEXT,
+        // the scores of tile t+1 are computed into `nxt` in the same straight-line
+        // block as this tile's exp work, so the MFMAs run under the VALU work.
+        // MASK instantiates the per-element causal / sequence-end mask; only a
+        // wave's last tile can need it (its earlier tiles lie entirely below the
+        // diagonal and before S), and the last tile has no successor.
+        auto step = [&](auto mask_tag, auto next_tag, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB], int t) {
+            constexpr bool MASK = decltype(mask_tag)::value;
+            constexpr bool NEXT = decltype(next_tag)::value;
+            QOp kf[KB][QS];
+            if constexpr (NEXT) load_k(kf, t + 1);
+            // V^T operands, read transposed from the V tile (asynchronous: used after lds_wait)
+            i16x4 vr[BN / 16][DB][2];
+            {
+                const uint16_t* Vs = vbuf(t);
+    #pragma unroll
+                for (int ks = 0; ks < BN / 16; ++ks)
+    #pragma unroll
+                    for (int db = 0; db < DB; ++db) lo.tr_async(Vs, ks * 16, db, vr[ks][db]);
+            }
+
+            // ---- mask, row max (raw scores; c > 0 so max commutes with scaling)
+            const int k0 = t * BN;
+            float mx[QB];
+            bool grow = false;
+    #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                const float f = fast_exp2(m[qb] - mn[qb]);
-                l[qb] *= f;
-#pragma unroll
+                const int q = qw0 + qb * 32 + n;
+                float v = -INFINITY;
+    #pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        if constexpr (MASK) {
+                            const int key = k0 + kb * 32 + crow(r, h);
+                            const bool kill = (causal && key > q) || key >= S;
+                            cur[qb][kb][r] = kill ? -INFINITY : cur[qb][kb][r];
+                        }
+                        v = fmaxf(v, cur[qb][kb][r]);
+                    }
+                v = half_max(v) * c;
+                mx[qb] = v;
+                grow |= v > m[qb] + kRescaleSlack;
+            }
+            // The reference point of the exponent moves only when some row max in
+            // the wave grew past the slack (wave-uniform decision); P values are
+            // otherwise bounded by 2^kRescaleSlack, which fp32 accumulation and
+            // bf16 P absorb.
+            const bool resc = __builtin_amdgcn_ballot_w64(grow) != 0;
+            float mn[QB];
+    #pragma unroll
+            for (int qb = 0; qb < QB; ++qb) mn[qb] = resc ? fmaxf(m[qb], mx[qb]) : m[qb];
+
+            if constexpr (NEXT) mma_scores(nxt, kf);
+
+            // ---- P = exp2(s*c - m) rounded to bf16; the row sum adds the same
+            // rounded values the PV product multiplies, so numerator and
+            // denominator of O = (P V) / l carry the same rounding (a row whose
+            // weight sits on one key reproduces that key's V row).
+            V8 pf[QB][BN / 16];
+            float ls[QB];
+    #pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                ls[qb] = 0.f;
+    #pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) cur[qb][kb][r] = fast_exp2(fmaf(cur[qb][kb][r], c, -mn[qb]));
+                    pf[qb][2 * kb] = pack_op<E>(cur[qb][kb], 0);
+                    pf[qb][2 * kb + 1] = pack_op<E>(cur[qb][kb], 1);
+                    ls[qb] = sum8<E>(pf[qb][2 * kb], ls[qb]);
+                    ls[qb] = sum8<E>(pf[qb][2 * kb + 1], ls[qb]);
+                }
+            }
+            if (resc) {
+                // rare (the reference point moves only past the slack): keep it a
+                // branch; the empty volatile asm stops the compiler from executing
+                // the rescale unconditionally
+                asm volatile("");
+    #pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    const float f = fast_exp2(m[qb] - mn[qb]);
+                    l[qb] *= f;
+    #pragma unroll
+                    for (int db = 0; db < DB; ++db)
+    #pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= f;
+                }
+            }
+    #pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                m[qb] = mn[qb];
+                l[qb] += ls[qb];
+            }
+            lds_wait(reinterpret_cast<i16x4 (&)[(BN / 16) * DB * 2]>(vr));
+            V8 vf[BN / 16][DB];
+    #pragma unroll
+            for (int ks = 0; ks < BN / 16; ++ks)
+    #pragma unroll
+                for (int db = 0; db < DB; ++db) vf[ks][db] = tr_join<E>(vr[ks][db]);
+            // ---- O^T += V^T P^T
+    #pragma unroll
+            for (int ks = 0; ks < BN / 16; ++ks)
+    #pragma unroll
                 for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= f;
+    #pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = E::mma(vf[ks][db], pf[qb][ks], oacc[qb][db]);
+        };
+
+        // ---- prologue: loads of K_0, then (K_{i+1}, V_i) for i < P, straight into
+        // LDS.  Iteration t reads K_{t+1} and V_t and issues K_{t+1+P} and V_{t+P}
+        // into the buffers of K_t and V_{t-1} (read in the previous iteration, so
+        // free once the iteration's barrier has passed).  Each wave then finds the
+        // tiles it needs complete once at most 2 (P - 1) tiles of its own loads are
+        // outstanding: that count is the same in every iteration.  A tile index at
+        // or past ntiles loads from row S: an empty buffer range, so the tile reads
+        // as zeros and the count of loads stays the same on every path.
+        auto row_of = [&](int t) { return t < ntiles ? t * BN : S; };
+        auto load_kt = [&](int t) { Cfg::KTile::load(Kh, row_of(t), S, kbuf(t), ksrc, wave); };
+        auto load_vt = [&](int t) { Cfg::Tile::load(Vh, row_of(t), S, vbuf(t), src, wave); };
+        load_kt(0);
+    #pragma unroll
+        for (int i = 0; i < P; ++i) {
+            load_kt(i + 1);
+            load_vt(i);
+        }
+        wait_vmcnt<P * LOADS2>();  // K_0 landed
+        bare_barrier();
+
+        f32x16 sa[QB][KB], sb[QB][KB];
+        if (nw > 0) {
+            QOp kf[KB][QS];
+            load_k(kf, 0);
+            mma_scores(sa, kf);
+        }
+
+        // Iteration t: wait for K_{t+1} and V_t (own loads, then everyone's), issue
+        // the loads of K_{t+1+P} and V_{t+P}, compute.
+        auto iteration = [&](int t, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB]) {
+            wait_vmcnt<(P - 1) * LOADS2>();
+            bare_barrier();
+            load_kt(t + 1 + P);
+            load_vt(t + P);
+            if (t + 1 < nw)
+                step(std::false_type{}, std::true_type{}, cur, nxt, t);
+            else if (t + 1 == nw)
+                step(std::true_type{}, std::false_type{}, cur, nxt, t);
+        };
+        for (int t = 0; t < ntiles; t += 2) {
+            iteration(t, sa, sb);
+            if (t + 1 < ntiles) iteration(t + 1, sb, sa);
+        }
+        // no load may still be writing this workgroup's LDS when it exits
+        wait_vmcnt<0>();
+
+        // ---- epilogue: O = O / l (l == 0 -> 0), LSE = (m + log2 l) * ln 2
+        uint16_t* Oh = O + base;
+        float* Lh = LSE + (size_t)head * S;
+    #pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int q = qw0 + qb * 32 + n;
+            const float lt = half_sum(l[qb]);
+            const float inv = lt > 0.f ? 1.f / lt : 0.f;
+            if (q < S) {
+    #pragma unroll
+                for (int db = 0; db < DB; ++db)
+    #pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        if (!HeadDim<D>::live(db, g)) continue;
+                        u32x2 u;
+                        u[0] = E::pack2(oacc[qb][db][4 * g + 0] * inv, oacc[qb][db][4 * g + 1] * inv);
+                        u[1] = E::pack2(oacc[qb][db][4 * g + 2] * inv, oacc[qb][db][4 * g + 3] * inv);
+                        *reinterpret_cast<u32x2*>(Oh + (size_t)q * D + db * 32 + 8 * g + 4 * h) = u;
+                    }
+                if (h == 0) Lh[q] = lt > 0.f ? (m[qb] + __log2f(lt)) * kLn2 : -INFINITY;
             }
         }
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            m[qb] = mn[qb];
-            l[qb] += ls[qb];
-        }
-        lds_wait(reinterpret_cast<i16x4 (&)[(BN / 16) * DB * 2]>(vr));
-        V8 vf[BN / 16][DB];
-#pragma unroll
-        for (int ks = 0; ks < BN / 16; ++ks)
-#pragma unroll
-            for (int db = 0; db < DB; ++db) vf[ks][db] = tr_join<E>(vr[ks][db]);
-        // ---- O^T += V^T P^T
-#pragma unroll
-        for (int ks = 0; ks < BN / 16; ++ks)
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = E::mma(vf[ks][db], pf[qb][ks], oacc[qb][db]);
-    };
-
-    // ---- prologue: loads of K_0, then (K_{i+1}, V_i) for i < P, straight into
-    // LDS.  Iteration t reads K_{t+1} and V_t and issues K_{t+1+P} and V_{t+P}
-    // into the buffers of K_t and V_{t-1} (read in the previous iteration, so
-    // free once the iteration's barrier has passed).  Each wave then finds the
-    // tiles it needs complete once at most 2 (P - 1) tiles of its own loads are
-    // outstanding: that count is the same in every iteration.  A tile index at
-    // or past ntiles loads from row S: an empty buffer range, so the tile reads
-    // as zeros and the count of loads stays the same on every path.
-    auto row_of = [&](int t) { return t < ntiles ? t * BN : S; };
-    auto load_kt = [&](int t) { Cfg::KTile::load(Kh, row_of(t), S, kbuf(t), ksrc, wave); };
-    auto load_vt = [&](int t) { Cfg::Tile::load(Vh, row_of(t), S, vbuf(t), src, wave); };
-    load_kt(0);
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-        load_kt(i + 1);
-        load_vt(i);
-    }
-    wait_vmcnt<P * LOADS2>();  // K_0 landed
-    bare_barrier();
-
-    f32x16 sa[QB][KB], sb[QB][KB];
-    if (nw > 0) {
-        QOp kf[KB][QS];
-        load_k(kf, 0);
-        mma_scores(sa, kf);
     }
 
-    // Iteration t: wait for K_{t+1} and V_t (own loads, then everyone's), issue
-    // the loads of K_{t+1+P} and V_{t+P}, compute.
-    auto iteration = [&](int t, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB]) {
-        wait_vmcnt<(P - 1) * LOADS2>();
-        bare_barrier();
-        load_kt(t + 1 + P);
-        load_vt(t + P);
-        if (t + 1 < nw)
-            step(std::false_type{}, std::true_type{}, cur, nxt, t);
-        else if (t + 1 == nw)
-            step(std::true_type{}, std::false_type{}, cur, nxt, t);
-    };
-    for (int t = 0; t < ntiles; t += 2) {
-        iteration(t, sa, sb);
-        if (t + 1 < ntiles) iteration(t + 1, sb, sa);
-    }
-    // no load may still be writing this workgroup's LDS when it exits
-    wait_vmcnt<0>();
-
-    // ---- epilogue: O = O / l (l == 0 -> 0), LSE = (m + log2 l) * ln 2
-    uint16_t* Oh = O + base;
-    float* Lh = LSE + (size_t)head * S;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int q = qw0 + qb * 32 + n;
-        const float lt = half_sum(l[qb]);
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        if (q < S) {
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    if (!HeadDim<D>::live(db, g)) continue;
-                    u32x2 u;
-                    u[0] = E::pack2(oacc[qb][db][4 * g + 0] * inv, oacc[qb][db][4 * g + 1] * inv);
-                    u[1] = E::pack2(oacc[qb][db][4 * g + 2] * inv, oacc[qb][db][4 * g + 3] * inv);
-                    *reinterpret_cast<u32x2*>(Oh + (size_t)q * D + db * 32 + 8 * g + 4 * h) = u;
-                }
-            if (h == 0) Lh[q] = lt > 0.f ? (m[qb] + __log2f(lt)) * kLn2 : -INFINITY;
-        }
-    }
 }
 
 template <class E, int D, int QB, int NW, bool QK8, int BN>
 static hipError_t launch_fwd(const LaunchArgs& a) {
     using Cfg = FwdCfg<D, QB, NW, QK8, BN>;
     const int nblk = (int)((a.S + Cfg::BM - 1) / Cfg::BM);
-    const int64_t total = (int64_t)nblk * a.BH;
+    // pairs when one query block per workgroup would not fit in one round of the
+    // device's workgroup slots (CUs x workgroups per CU)
+    const int64_t slots = (int64_t)cu_count() * Cfg::WAVES_PER_SIMD * 4 / Cfg::NW;
+    const int paired = Cfg::PAIRABLE && a.causal && (int64_t)nblk * a.BH > slots ? 1 : 0;
+    const int64_t total = (int64_t)(paired ? (nblk + 1) / 2 : nblk) * a.BH;
     if (total > INT32_MAX) return hipErrorInvalidValue;
     hipLaunchKernelGGL((fwd_mfma_kernel<E, D, QB, NW, QK8, BN>), dim3((unsigned)total), dim3(Cfg::NT), 0, a.stream,
                        a.q, a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, (int)a.S, nblk, (int)a.BH,
-                       (int)a.H, (int)(a.H / a.Hkv), a.scale * a.qk_descale * kLog2e, a.causal);
+                       (int)a.H, (int)(a.H / a.Hkv), a.scale * a.qk_descale * kLog2e, a.causal, paired);
     return hipGetLastError();
 }
 

@@ -38,6 +38,10 @@ struct LaunchArgs {
     hipStream_t stream = nullptr;
 };
 
+// Compute units of the current device (looked up once per device; 256 on MI355X
+// if the query fails).
+int cu_count();
+
 hipError_t launch_fwd_bf16(const LaunchArgs& a);
 // atomic-dQ backward: dK/dV pass that also adds dQ into a.dq_acc (D = 64, H = H_kv),
 // the fill of the accumulator and the final dQ = scale * dq_acc
