@@ -21,12 +21,16 @@
 //   O^T += V^T P^T; V stays row-major in LDS and its transposed operand comes
 //   from ds_read_b64_tr_b16, in the key order of the C registers.  The rescale
 //   O *= factor is a per-lane multiply (no diag-matrix product).
-// * The O rescale is skipped unless some row max in the wave grew by more than
-//   kRescaleSlack (log2 units): P values are then bounded by 2^kRescaleSlack,
-//   which fp32 accumulation and bf16 P absorb; the result is the same function,
-//   only the reference point of the exponent differs.
+// * The row max is not formed per tile.  P = exp2(s*c - m) is computed against
+//   the row's reference point m, and m moves (to the row max, with O and l
+//   rescaled and P formed again) only when some lane's sum of its P values
+//   exceeds kPBound, i.e. when some P could: always on a row's first tile (m
+//   starts at -FLT_MAX), after that only when scores grow past m by log2 of the
+//   bound (64 for bf16 P, 15 for fp16).  fp32 accumulation and the P types
+//   absorb values up to the bound; the result is the same function, only the
+//   reference point of the exponent differs.
 // * Software pipeline: K runs one tile ahead of V in LDS, so iteration t issues
-//   the MFMAs of S^T for tile t+1 next to the exp/max/sum VALU work of tile t
+//   the MFMAs of S^T for tile t+1 next to the exp/sum VALU work of tile t
 //   (the MFMA unit works asynchronously from the VALU), then O += V_t P_t.
 //   Q stays in registers for the whole loop; K/V tiles go from HBM straight to
 //   LDS (buffer loads with the lds flag, swizzled rows) one tile ahead of their
@@ -39,7 +43,11 @@
 namespace attn {
 
 
-constexpr float kRescaleSlack = 8.0f;
+// Largest P value the loop lets through without moving the reference point:
+// bf16 P (and fp32 O and l accumulation) holds 2^64 with room to spare for any
+// sum over a row; fp16 P tops out at 65504.
+template <class E>
+constexpr float kPBound = std::is_same<E, F16>::value ? 0x1p15f : 0x1p64f;
 
 // The S^T = K Q^T product: 16-bit Q and K of the element type E, or fp8 (E4M3)
 // Q and K.  Op is the MFMA operand, STEPS the MFMAs per 32x32 score block, KD the
@@ -246,77 +254,82 @@ __global__ __launch_bounds__(NW * 64, (FwdCfg<D, QB, NW, QK8, BN_>::WAVES_PER_SI
                     for (int db = 0; db < DB; ++db) lo.tr_async(Vs, ks * 16, db, vr[ks][db]);
             }
 
-            // ---- mask, row max (raw scores; c > 0 so max commutes with scaling)
+            // ---- mask (raw scores; only a wave's last tile)
             const int k0 = t * BN;
-            float mx[QB];
-            bool grow = false;
+            if constexpr (MASK) {
     #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const int q = qw0 + qb * 32 + n;
-                float v = -INFINITY;
+                for (int qb = 0; qb < QB; ++qb) {
+                    const int q = qw0 + qb * 32 + n;
     #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
+                    for (int kb = 0; kb < KB; ++kb)
     #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        if constexpr (MASK) {
+                        for (int r = 0; r < 16; ++r) {
                             const int key = k0 + kb * 32 + crow(r, h);
                             const bool kill = (causal && key > q) || key >= S;
                             cur[qb][kb][r] = kill ? -INFINITY : cur[qb][kb][r];
                         }
-                        v = fmaxf(v, cur[qb][kb][r]);
-                    }
-                v = half_max(v) * c;
-                mx[qb] = v;
-                grow |= v > m[qb] + kRescaleSlack;
+                }
             }
-            // The reference point of the exponent moves only when some row max in
-            // the wave grew past the slack (wave-uniform decision); P values are
-            // otherwise bounded by 2^kRescaleSlack, which fp32 accumulation and
-            // bf16 P absorb.
-            const bool resc = __builtin_amdgcn_ballot_w64(grow) != 0;
-            float mn[QB];
-    #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) mn[qb] = resc ? fmaxf(m[qb], mx[qb]) : m[qb];
 
             if constexpr (NEXT) mma_scores(nxt, kf);
 
-            // ---- P = exp2(s*c - m) rounded to bf16; the row sum adds the same
-            // rounded values the PV product multiplies, so numerator and
-            // denominator of O = (P V) / l carry the same rounding (a row whose
-            // weight sits on one key reproduces that key's V row).
+            // ---- P = exp2(s*c - m) rounded to bf16 against the reference point
+            // m; the row sum adds the same rounded values the PV product
+            // multiplies, so numerator and denominator of O = (P V) / l carry the
+            // same rounding (a row whose weight sits on one key reproduces that
+            // key's V row).  The raw scores stay in `cur` for the rare path.
             V8 pf[QB][BN / 16];
             float ls[QB];
+            auto probs = [&]() {
     #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                ls[qb] = 0.f;
+                for (int qb = 0; qb < QB; ++qb) {
+                    ls[qb] = 0.f;
     #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
+                    for (int kb = 0; kb < KB; ++kb) {
+                        f32x16 e;
     #pragma unroll
-                    for (int r = 0; r < 16; ++r) cur[qb][kb][r] = fast_exp2(fmaf(cur[qb][kb][r], c, -mn[qb]));
-                    pf[qb][2 * kb] = pack_op<E>(cur[qb][kb], 0);
-                    pf[qb][2 * kb + 1] = pack_op<E>(cur[qb][kb], 1);
-                    ls[qb] = sum8<E>(pf[qb][2 * kb], ls[qb]);
-                    ls[qb] = sum8<E>(pf[qb][2 * kb + 1], ls[qb]);
+                        for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(cur[qb][kb][r], c, -m[qb]));
+                        pf[qb][2 * kb] = pack_op<E>(e, 0);
+                        pf[qb][2 * kb + 1] = pack_op<E>(e, 1);
+                        ls[qb] = sum8<E>(pf[qb][2 * kb], ls[qb]);
+                        ls[qb] = sum8<E>(pf[qb][2 * kb + 1], ls[qb]);
+                    }
                 }
-            }
-            if (resc) {
-                // rare (the reference point moves only past the slack): keep it a
-                // branch; the empty volatile asm stops the compiler from executing
-                // the rescale unconditionally
+            };
+            probs();
+            // The reference point stays put while every P is at most kPBound:
+            // no lane's sum of its P values (all >= 0) above the bound means no
+            // single P above it, so the tile needs no row max.  Otherwise
+            // (wave-uniform; a row's first tile, where m starts at -FLT_MAX and
+            // every P is infinite, and after that only when a row's scores grow
+            // past its reference point by log2 of the bound) m moves to the row
+            // max, O and l are rescaled and P is formed again.
+            bool big = false;
+    #pragma unroll
+            for (int qb = 0; qb < QB; ++qb) big |= !(ls[qb] <= kPBound<E>);
+            if (__builtin_amdgcn_ballot_w64(big) != 0) {
                 asm volatile("");
     #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
-                    const float f = fast_exp2(m[qb] - mn[qb]);
+                    float v = -INFINITY;
+    #pragma unroll
+                    for (int kb = 0; kb < KB; ++kb)
+    #pragma unroll
+                        for (int r = 0; r < 16; ++r) v = fmaxf(v, cur[qb][kb][r]);
+                    // c > 0, so the max commutes with the scaling
+                    const float mn = fmaxf(m[qb], half_max(v) * c);
+                    const float f = fast_exp2(m[qb] - mn);
+                    m[qb] = mn;
                     l[qb] *= f;
     #pragma unroll
                     for (int db = 0; db < DB; ++db)
     #pragma unroll
                         for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= f;
                 }
+                probs();
             }
     #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                m[qb] = mn[qb];
                 l[qb] += ls[qb];
             }
             lds_wait(reinterpret_cast<i16x4 (&)[(BN / 16) * DB * 2]>(vr));
