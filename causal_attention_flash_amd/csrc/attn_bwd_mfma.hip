@@ -521,16 +521,13 @@ struct DqCfg {
     static constexpr int NW = NW_;
     static constexpr int NT = NW * 64;
     static constexpr int BMQ = NW * 32;  // queries per workgroup (32 per wave)
-    // K and V tiles, two buffers each, fetched one iteration ahead.  At D = 64
-    // they are staged through registers into padded rows; wider heads load them
-    // straight from HBM into swizzled rows (measured with the earlier layouts:
-    // the direct path 1-2% slower at D = 64 and 5-7% faster at D = 128; fetching
-    // two tiles ahead was slower at every size)
-    static constexpr bool DIRECT = D != 64;
-    using KT = RowTile<BNK, D, NT>;  // register-staged: padded rows
-    using Tile = DTile<BNK, D, NW>;  // direct: swizzled rows
-    static constexpr int TE = DIRECT ? Tile::ELEMS : KT::ELEMS;  // one tile in LDS
-    static constexpr int LOADS = Tile::LOADS;
+    // K and V tiles, two buffers each, loaded straight from HBM into swizzled
+    // rows one iteration ahead.  (Staging them through registers into padded
+    // rows measured 3-4.5% slower at D = 64 with the conflict-free layouts of
+    // both, and 5-7% slower at D = 128 earlier; fetching two tiles ahead was
+    // slower at every size.)
+    using Tile = DTile<BNK, D, NW>;
+    static constexpr int TE = Tile::ELEMS;  // one tile in LDS
     // K[2], V[2]
     static constexpr int SMEM_ELEMS = 4 * TE;
     // register budget: 168 VGPRs (3 waves per SIMD) fits D = 64 without spills,
@@ -553,7 +550,6 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
     using V8 = typename E::V8;
     constexpr int BMQ = Cfg::BMQ;
     constexpr int KS = Cfg::KS, DB = Cfg::DB;
-    constexpr bool DIRECT = Cfg::DIRECT;
     constexpr int TE = Cfg::TE;
     __shared__ __attribute__((aligned(16))) uint16_t smem[Cfg::SMEM_ELEMS];
 
@@ -575,43 +571,23 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
     const int kend = causal ? min(S, q0 + BMQ) : S;
     const int ntiles = (kend + BNK - 1) / BNK;
 
-    // Tile t uses buffer t % 2.
-    // Direct: iteration t issues tile t + 1 into the buffers of tile t - 1 (read in
-    // the previous iteration, free once the iteration's barrier has passed), and
-    // waits for all of its own loads before that barrier.  Tiles at or past ntiles
-    // load from row S (an empty buffer range) so every path issues the same loads.
-    // Staged: after its tile, iteration t stores tile t + 1 from registers and
-    // fetches tile t + 2 into them.
+    // Tile t uses buffer t % 2.  Iteration t issues tile t + 1 into the buffers of
+    // tile t - 1 (read in the previous iteration, free once the iteration's
+    // barrier has passed), and waits for all of its own loads before that
+    // barrier.  Tiles at or past ntiles load from row S (an empty buffer range) so
+    // every path issues the same loads.
     auto kbuf = [&](int t) { return smem + (t & 1) * TE; };
     auto vbuf = [&](int t) { return smem + (2 + (t & 1)) * TE; };
     typename Cfg::Tile::Src src;
     DOffsets<typename Cfg::Tile, D> lo;
-    using KT = typename Cfg::KT;
-    int rl = 0, tl = 0;
-    if constexpr (DIRECT) {
-        lo.init(lane);
-    } else {
-        rl = KT::row_lane(lane);
-        tl = KT::tr_lane(lane);
-    }
+    lo.init(lane);
     auto load_t = [&](int t) {
         const int row = t < ntiles ? t * BNK : S;
         Cfg::Tile::load(Kh, row, S, kbuf(t), src, wave);
         Cfg::Tile::load(Vh, row, S, vbuf(t), src, wave);
     };
-    typename Cfg::KT kt, vt;
-    auto stage = [&](int t) {
-        kt.store(kbuf(t), tid);
-        vt.store(vbuf(t), tid);
-    };
-    auto fetch = [&](int t) {
-        kt.load(Kh, t * BNK, S, tid);
-        vt.load(Vh, t * BNK, S, tid);
-    };
-    if constexpr (DIRECT) {
-        src.init(wave, lane);
-        load_t(0);
-    }
+    src.init(wave, lane);
+    load_t(0);
 
     V8 qf[KS], of[KS];
 #pragma unroll
@@ -648,13 +624,6 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
 #pragma unroll
         for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
 
-    if constexpr (!DIRECT) {
-        fetch(0);
-        stage(0);
-        if (ntiles > 1) fetch(1);
-        __syncthreads();
-    }
-
     // One key tile against this wave's 32 queries; MASK instantiates the causal
     // and sequence-end mask for tiles that cross the diagonal or the end.
     auto tile = [&](auto mask_tag, int t, int k0) {
@@ -672,23 +641,16 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
             }
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                if constexpr (DIRECT) {
-                    sacc = E::mma(lo.template row_op<E>(Ks, kb * 32, ks), qf[ks], sacc);
-                    pacc = E::mma(lo.template row_op<E>(Vs, kb * 32, ks), of[ks], pacc);
-                } else {
-                    sacc = E::mma(KT::template row_op<E>(Ks, kb * 32, ks, rl), qf[ks], sacc);
-                    pacc = E::mma(KT::template row_op<E>(Vs, kb * 32, ks, rl), of[ks], pacc);
-                }
+                sacc = E::mma(lo.template row_op<E>(Ks, kb * 32, ks), qf[ks], sacc);
+                pacc = E::mma(lo.template row_op<E>(Vs, kb * 32, ks), of[ks], pacc);
             }
-            // direct: K^T operands of this block's dQ product, read transposed from
-            // the K tile (asynchronous: used after lds_wait)
+            // K^T operands of this block's dQ product, read transposed from the K
+            // tile (asynchronous: used after lds_wait)
             i16x4 kr[2][DB][2];
-            if constexpr (DIRECT) {
 #pragma unroll
-                for (int c2 = 0; c2 < 2; ++c2)
+            for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-                    for (int db = 0; db < DB; ++db) lo.tr_async(Ks, (kb * 2 + c2) * 16, db, kr[c2][db]);
-            }
+                for (int db = 0; db < DB; ++db) lo.tr_async(Ks, (kb * 2 + c2) * 16, db, kr[c2][db]);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float p = fast_exp2(fmaf(sacc[r], c, -l2));
@@ -699,27 +661,20 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
                 pacc[r] = p * (pacc[r] - dl);
             }
             // dQ^T += K^T dS^T (contraction over these 32 keys)
-            if constexpr (DIRECT) lds_wait(reinterpret_cast<i16x4 (&)[2 * DB * 2]>(kr));
+            lds_wait(reinterpret_cast<i16x4 (&)[2 * DB * 2]>(kr));
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
                 const V8 sb = pack_op<E>(pacc, c2);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    if constexpr (DIRECT)
-                        dqacc[db] = E::mma(tr_join<E>(kr[c2][db]), sb, dqacc[db]);
-                    else
-                        dqacc[db] = E::mma(KT::template tr_op<E>(Ks, (kb * 2 + c2) * 16, db, tl), sb, dqacc[db]);
-                }
+                for (int db = 0; db < DB; ++db) dqacc[db] = E::mma(tr_join<E>(kr[c2][db]), sb, dqacc[db]);
             }
         }
     };
 
     for (int t = 0; t < ntiles; ++t) {
-        if constexpr (DIRECT) {
-            wait_vmcnt<0>();  // own loads of tile t
-            bare_barrier();   // everyone's; tile t - 1 no longer read
-            load_t(t + 1);
-        }
+        wait_vmcnt<0>();  // own loads of tile t
+        bare_barrier();   // everyone's; tile t - 1 no longer read
+        load_t(t + 1);
         const int k0 = t * BNK;
         // wave-uniform: skip key tiles entirely after this wave's last query
         if (!causal || k0 <= qw0 + 31) {
@@ -728,15 +683,8 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
             else
                 tile(std::false_type{}, t, k0);
         }
-        if constexpr (!DIRECT) {
-            if (t + 1 < ntiles) {
-                stage(t + 1);
-                if (t + 2 < ntiles) fetch(t + 2);
-            }
-            __syncthreads();
-        }
     }
-    if constexpr (DIRECT) wait_vmcnt<0>();  // no load into LDS outlives the workgroup
+    wait_vmcnt<0>();  // no load into LDS outlives the workgroup
 
     if (q < S) {
         uint16_t* dQr = dQ + base + (size_t)q * D;
