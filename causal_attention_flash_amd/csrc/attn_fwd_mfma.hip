@@ -91,11 +91,11 @@ struct FwdCfg {
     static constexpr int P = NB - 1;
     static constexpr int KS = HeadDim<D>::KSTEPS;
     static constexpr int DB = HeadDim<D>::DB;
-    // Paired query blocks (see the kernel): at D = 128 two workgroups fill a CU,
-    // and half as many workgroups, each with the same work, fill it evenly
-    // (measured 5% faster on 8191-token heads).  Where three workgroups fill a
-    // CU (D = 64) pairs leave a third of it idle: 5% slower there.
-    static constexpr bool PAIRABLE = D == 128 && !QK8;
+    // Paired query blocks (see the kernel): from D = 80 up two workgroups fill a
+    // CU, and half as many workgroups, each with the same work, fill it evenly
+    // (measured 2-5% faster where the pairs still cover every slot).  Where three
+    // workgroups fill a CU (D = 64) pairs leave a third of it idle: 5% slower there.
+    static constexpr bool PAIRABLE = D >= 80 && !QK8;
     // the loop masks only a wave's last key tile: a wave's 32 * QB queries must
     // not reach into an earlier tile (else that tile also crosses the diagonal)
     static_assert(32 * QB <= BN, "a wave's queries must fit in one key tile");
@@ -424,9 +424,13 @@ static hipError_t launch_fwd(const LaunchArgs& a) {
     using Cfg = FwdCfg<D, QB, NW, QK8, BN>;
     const int nblk = (int)((a.S + Cfg::BM - 1) / Cfg::BM);
     // pairs when one query block per workgroup would not fit in one round of the
-    // device's workgroup slots (CUs x workgroups per CU)
+    // device's workgroup slots (CUs x workgroups per CU) and the pairs still cover
+    // every slot (fewer workgroups than slots leave CUs idle)
     const int64_t slots = (int64_t)cu_count() * Cfg::WAVES_PER_SIMD * 4 / Cfg::NW;
-    const int paired = Cfg::PAIRABLE && a.causal && (int64_t)nblk * a.BH > slots ? 1 : 0;
+    const int paired = Cfg::PAIRABLE && a.causal && (int64_t)nblk * a.BH > slots &&
+                               (int64_t)((nblk + 1) / 2) * a.BH >= slots
+                           ? 1
+                           : 0;
     const int64_t total = (int64_t)(paired ? (nblk + 1) / 2 : nblk) * a.BH;
     if (total > INT32_MAX) return hipErrorInvalidValue;
     hipLaunchKernelGGL((fwd_mfma_kernel<E, D, QB, NW, QK8, BN>), dim3((unsigned)total), dim3(Cfg::NT), 0, a.stream,

@@ -98,16 +98,19 @@ def test_ragged_tails_long_d128_large_logits(device, S):
     gu.check(gu.errors(gpu, ref, all_heads(w)), "bf16", f"long draw S={S}")
 
 
-def test_paired_query_blocks_odd_count(device):
-    """D = 128 forward with more query blocks than workgroup slots runs pairs of
-    blocks (j, nblk-1-j) per workgroup; 15 blocks per head leave the middle block
-    on its own and the last one ragged (1900 = 14 * 128 + 108)."""
-    w = si.WORKLOADS["long8191_bf16"].with_shape(B=1, H=40, S=1900)
-    assert 15 * w.B * w.H > 512  # more blocks than two workgroups on each of 256 CUs
-    x = si.make_inputs(w, seed=19)
+@pytest.mark.parametrize("D", [80, 96, 128])
+def test_paired_query_blocks_odd_count(device, D):
+    """The forward at D >= 80 with more query blocks than workgroup slots (two per CU
+    on 256 CUs: 512), when the pairs still cover every slot, runs pairs of blocks
+    (j, nblk-1-j) per workgroup; 15 blocks per head leave the middle block on its own
+    and the last one ragged (1900 = 14 * 128 + 108)."""
+    w = si.WORKLOADS["long8191_bf16"].with_shape(B=1, H=64, S=1900, D=D)
+    nblk = 15
+    assert nblk * w.B * w.H > 512 and (nblk + 1) // 2 * w.B * w.H >= 512
+    x = si.make_inputs(w, seed=19 + D)
     gpu = gu.run_gpu(x, w, device)
     ref = oracle_heads(x, w, all_heads(w))
-    gu.check(gu.errors(gpu, ref, all_heads(w)), "bf16", "paired blocks S=1900 H=40")
+    gu.check(gu.errors(gpu, ref, all_heads(w)), "bf16", f"paired blocks S=1900 H=64 D={D}")
 
 
 def test_accumulator_width_cell(device):
