@@ -117,6 +117,39 @@ def clock_ghz(before, after):
             "interval_s": round(float(np.median(dt[ok])), 6)}
 
 
+class ClockWindow:
+    """Shader-clock samples (attn_clock_sample) on the launch stream just outside a
+    timed region; .ghz() gives clock_ghz() over the interval."""
+
+    def __init__(self, torch, dev, stream, bd, n=256):
+        self.bd, self.stream, self.n = bd, stream, n
+        self.buf = [torch.empty((n, 4), dtype=torch.int64, device=dev) for _ in range(2)]
+
+    def sample(self, i):
+        st = self.bd.c_attn_clock_sample(self.buf[i].data_ptr(), self.n, self.stream)
+        if st != 0:
+            raise RuntimeError(f"attn_clock_sample: {self.bd.status_string(st)}")
+
+    def ghz(self):
+        return clock_ghz(self.buf[0].cpu().numpy().view(np.uint64), self.buf[1].cpu().numpy().view(np.uint64))
+
+
+def receipt_of(errs: dict, bigs: dict, dtype: str, what: str) -> dict:
+    """PASS / FAIL receipt from max |GPU - oracle| (errs) and max |oracle| (bigs)."""
+    kind, tol = RECEIPT_TOL[dtype]
+    worst = {n: (errs[n] / bigs[n] if bigs[n] > 0 else errs[n]) if kind == "rel" else errs[n] for n in errs}
+    ok = all(np.isfinite(v) and v <= tol for v in worst.values())
+    return {"status": "PASS" if ok else "FAIL", "checked": what,
+            "max_err": {n: float(f"{v:.3g}") for n, v in worst.items()},
+            "bar": f"max |d| <= {tol}" if kind == "abs" else f"max |d| / max |oracle| <= {tol}"}
+
+
+def fail_receipt(metric: str, receipt: dict, workload: str):
+    print(json.dumps({"metric": metric, "receipt": receipt, "config": {"workload": workload}}), flush=True)
+    print("bench.py: the receipt failed; no timing is reported", file=sys.stderr)
+    sys.exit(3)
+
+
 def compare_heads(gpu: dict, ref_heads: list, dtype: str, G: int) -> dict:
     """The receipt: the session's outputs (gpu: name -> callable (b, h) -> float64
     array) against the oracle's per-head results [((b, h), {o, lse, dq, dk, dv})].
@@ -374,15 +407,57 @@ def decode_bench(args, dev):
         torch.cuda.synchronize()
         print(f"profile run: {args.profile_steps} steps of {w.name}", flush=True)
         return
+    # the session's own first step, then the oracle on the sequences the CPU
+    # baseline covers and the receipt, before any timing
+    step()
+    torch.cuda.synchronize()
+    o_host = o.to(torch.float64).cpu().numpy()
+    lse_host = lse.to(torch.float64).cpu().numpy()
+    cpu_rec, receipt = None, None
+    if not args.no_cpu_baseline:
+        from oracle import decode
+        t0 = time.perf_counter()
+        nb = 0
+        done_bytes = 0.0
+        errs = {"o": 0.0, "lse": 0.0}
+        bigs = {"o": 0.0, "lse": 0.0}
+        lse_pattern = True
+        while nb < w.B and time.perf_counter() - t0 < args.cpu_seconds:
+            b = slice(nb, nb + 1)
+            ro, rl = decode(x["q"][b], x["k"][b], x["v"][b], w.scale, lens[b])
+            errs["o"] = max(errs["o"], float(np.abs(o_host[b] - ro).max()))
+            bigs["o"] = max(bigs["o"], float(np.abs(ro).max()))
+            fin = np.isfinite(rl)
+            lse_pattern &= bool((np.isfinite(lse_host[b]) == fin).all())
+            if fin.any():
+                errs["lse"] = max(errs["lse"], float(np.abs(lse_host[b][fin] - rl[fin]).max()))
+                bigs["lse"] = max(bigs["lse"], float(np.abs(rl[fin]).max()))
+            done_bytes += float(lens[nb]) * w.Hkv * w.D * elem * 2 + 2 * w.H * w.D * elem + w.H * 4
+            nb += 1
+        dtc = time.perf_counter() - t0
+        cpu_rec = {"value": round(done_bytes / dtc / 1e9, 4), "unit": "GB/s",
+                   "cores": blas_threads(), "host_cores": host_cores(), "kind": "oracle",
+                   "sample": f"{nb} of {w.B} sequences, fp64 decode, {dtc:.1f} s"}
+        receipt = receipt_of(errs, bigs, w.dtype, f"O and LSE of {nb} of {w.B} sequences, all heads")
+        if not lse_pattern:
+            receipt["status"] = "FAIL"
+            receipt["lse_pattern"] = "empty sequences (LSE = -inf) differ from the oracle's"
+        if receipt["status"] != "PASS":
+            fail_receipt("decode attention step, algorithmic HBM GB/s on 1 GPU", receipt, w.name)
+    clk = ClockWindow(torch, dev, stream, bd)
     clock_warm(step, torch)
     nwarm = warm_up(step, args, torch)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    clk.sample(0)
     t0 = time.perf_counter()
     ev0.record()
     for _ in range(args.steps):
         step()
     ev1.record()
+    clk.sample(1)
     torch.cuda.synchronize()
+    clock = clk.ghz()
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1)
     # per-call durations (events around each call on the launch stream)
@@ -416,22 +491,14 @@ def decode_bench(args, dev):
         "kernel_ms": {"decode": round(mean_ms, 5)},
         "roofline": {"kernel": "decode (split + merge passes)", "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 5),
-                     "traffic": None},
+                     "traffic": None,
+                     "time_base": "mean of the per-call HIP-event durations over K steps (second timed pass)"},
+        "clock_ghz": clock,
     }
-    if not args.no_cpu_baseline:
-        from oracle import decode
-        t0 = time.perf_counter()
-        nb = 0
-        done_bytes = 0.0
-        while nb < w.B and time.perf_counter() - t0 < args.cpu_seconds:
-            b = slice(nb, nb + 1)
-            decode(x["q"][b], x["k"][b], x["v"][b], w.scale, lens[b])
-            done_bytes += float(lens[nb]) * w.Hkv * w.D * elem * 2 + 2 * w.H * w.D * elem + w.H * 4
-            nb += 1
-        dtc = time.perf_counter() - t0
-        result["cpu_baseline"] = {"value": round(done_bytes / dtc / 1e9, 4), "unit": "GB/s",
-                                  "cores": blas_threads(), "host_cores": host_cores(), "kind": "oracle",
-                                  "sample": f"{nb} of {w.B} sequences, fp64 decode, {dtc:.1f} s"}
+    if receipt is not None:
+        result["receipt"] = receipt
+    if cpu_rec is not None:
+        result["cpu_baseline"] = cpu_rec
     print(json.dumps(result), flush=True)
 
 
@@ -466,17 +533,58 @@ def fp8_bench(args, dev):
         torch.cuda.synchronize()
         print(f"profile run: {args.profile_steps} steps of {w.name}", flush=True)
         return
+    # the session's own first step, then the oracle on the heads the CPU baseline
+    # covers and the receipt, before any timing
+    step()
+    torch.cuda.synchronize()
+    o_host = o.to(torch.float64).cpu().numpy()
+    lse_host = lse.to(torch.float64).cpu().numpy()
+    metric = "causal attention forward TFLOP/s, fp8 (E4M3) Q and K, on 1 GPU"
+    cpu_rec, receipt = None, None
+    if not args.no_cpu_baseline:
+        from oracle import fp8qk_forward
+        G = w.H // w.Hkv
+        heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+        t0 = time.perf_counter()
+        done = 0
+        errs = {"o": 0.0, "lse": 0.0}
+        bigs = {"o": 0.0, "lse": 0.0}
+        for b, h in heads:
+            ro, rl = fp8qk_forward(x["q8"][b:b + 1, h:h + 1], x["k8"][b:b + 1, h // G:h // G + 1],
+                                   x["v"][b:b + 1, h // G:h // G + 1], x["q_descale"], x["k_descale"], w.scale,
+                                   w.causal)
+            errs["o"] = max(errs["o"], float(np.abs(o_host[b, h] - ro[0, 0]).max()))
+            bigs["o"] = max(bigs["o"], float(np.abs(ro).max()))
+            errs["lse"] = max(errs["lse"], float(np.abs(lse_host[b, h] - rl[0, 0]).max()))
+            bigs["lse"] = max(bigs["lse"], float(np.abs(rl).max()))
+            done += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        dtc = time.perf_counter() - t0
+        cpu_rec = {"value": round(done * w.fwd_flops / len(heads) / dtc / 1e12, 6),
+                   "unit": "TFLOP/s", "cores": blas_threads(), "host_cores": host_cores(), "kind": "oracle",
+                   "sample": f"{done} of {len(heads)} heads (S={w.S}, D={w.D}), fp64 forward, {dtc:.1f} s"}
+        # the fp8 parity bar: O and LSE within the bf16 bar (the oracle sees the
+        # same E4M3 values, so the bar covers the kernel's own rounding)
+        receipt = receipt_of(errs, bigs, "bf16", f"O and LSE of {done} of {len(heads)} heads")
+        if receipt["status"] != "PASS":
+            fail_receipt(metric, receipt, w.name)
+    clk = ClockWindow(torch, dev, stream, bd)
     clock_warm(step, torch)
     nwarm = warm_up(step, args, torch)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    clk.sample(0)
     t0 = time.perf_counter()
     ev0.record()
     for _ in range(args.steps):
         step()
     ev1.record()
+    clk.sample(1)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1)
+    clock = clk.ghz()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     evs[0].record()
     for i in range(args.steps):
@@ -510,7 +618,7 @@ def fp8_bench(args, dev):
     value = w.fwd_flops * args.steps / (gpu_ms * 1e-3) / 1e12
     achieved = w.fwd_flops / (mean_ms * 1e-3) / 1e12
     result = {
-        "metric": "causal attention forward TFLOP/s, fp8 (E4M3) Q and K, on 1 GPU",
+        "metric": metric,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -528,26 +636,14 @@ def fp8_bench(args, dev):
         "kernel_ms": {"fwd_fp8qk": round(mean_ms, 5), "fwd_bf16_same_values": round(bf16_ms, 5)},
         "roofline": {"kernel": "fwd_fp8qk", "bound": "mfma", "achieved": round(achieved, 3),
                      "peak": round(PEAK_FP8QK_FWD_TFLOPS, 1), "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_FP8QK_FWD_TFLOPS, 5), "traffic": None},
+                     "frac": round(achieved / PEAK_FP8QK_FWD_TFLOPS, 5), "traffic": None,
+                     "time_base": "mean of the per-launch HIP-event durations over K steps (second timed pass)"},
+        "clock_ghz": clock,
     }
-    if not args.no_cpu_baseline:
-        from oracle import fp8qk_forward
-        G = w.H // w.Hkv
-        heads = [(b, h) for b in range(w.B) for h in range(w.H)]
-        t0 = time.perf_counter()
-        done = 0
-        for b, h in heads:
-            fp8qk_forward(x["q8"][b:b + 1, h:h + 1], x["k8"][b:b + 1, h // G:h // G + 1],
-                          x["v"][b:b + 1, h // G:h // G + 1], x["q_descale"], x["k_descale"], w.scale, w.causal)
-            done += 1
-            if time.perf_counter() - t0 >= args.cpu_seconds:
-                break
-        dtc = time.perf_counter() - t0
-        result["cpu_baseline"] = {"value": round(done * w.fwd_flops / len(heads) / dtc / 1e12, 6),
-                                  "unit": "TFLOP/s", "cores": blas_threads(), "host_cores": host_cores(),
-                                  "kind": "oracle",
-                                  "sample": f"{done} of {len(heads)} heads (S={w.S}, D={w.D}), fp64 forward, "
-                                            f"{dtc:.1f} s"}
+    if receipt is not None:
+        result["receipt"] = receipt
+    if cpu_rec is not None:
+        result["cpu_baseline"] = cpu_rec
     print(json.dumps(result), flush=True)
 
 

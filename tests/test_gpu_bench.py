@@ -79,3 +79,21 @@ def test_bench_decode():
 def test_bench_fp8qk():
     d = run_bench("--workload", "gpt205m_fp8qk")
     check_common(d, "gpt205m_fp8qk")
+
+
+@pytest.mark.parametrize("workload", ["decode_gpt205m_bf16", "gpt205m_fp8qk"])
+def test_bench_receipt_and_clock_other_modes(workload):
+    """The decode and fp8-QK modes check their first step against the oracle heads
+    the CPU baseline computes (a PASS receipt before any timing) and report the
+    shader clock over the timed region."""
+    print(f"\n[bench] --workload {workload} with the receipt", flush=True)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "5", "--warmup", "2",
+                        "--workload", workload, "--cpu-seconds", "2"],
+                       capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads([ln for ln in r.stdout.splitlines() if ln.startswith("{")][-1])
+    check_common(d, workload)
+    rc = d["receipt"]
+    assert rc["status"] == "PASS" and set(rc["max_err"]) == {"o", "lse"}, rc
+    assert 0.3 < d["clock_ghz"]["mean"] < 3.0, d["clock_ghz"]
+    assert d["cpu_baseline"]["kind"] == "oracle" and d["cpu_baseline"]["host_cores"] >= 1
