@@ -166,3 +166,17 @@ def test_traffic_lookup_needs_matching_sources():
         else:
             assert got is None
     assert bench.read_traffic("fwd", "no_such_workload") is None
+
+
+def test_receipt_of_output_pairs():
+    """The decode / fp8 receipt: absolute bar for 16-bit types, relative for fp32, and
+    a non-finite error fails."""
+    ok = bench.receipt_of({"o": 0.019, "lse": 0.001}, {"o": 3.0, "lse": 10.0}, "bf16", "x")
+    assert ok["status"] == "PASS" and ok["max_err"] == {"o": 0.019, "lse": 0.001}
+    assert bench.receipt_of({"o": 0.021, "lse": 0.0}, {"o": 3.0, "lse": 1.0}, "bf16", "x")["status"] == "FAIL"
+    assert bench.receipt_of({"o": 0.004, "lse": 0.0}, {"o": 3.0, "lse": 1.0}, "f16", "x")["status"] == "PASS"
+    assert bench.receipt_of({"o": 0.006, "lse": 0.0}, {"o": 3.0, "lse": 1.0}, "f16", "x")["status"] == "FAIL"
+    # fp32: relative to max |oracle|
+    assert bench.receipt_of({"o": 2e-4, "lse": 0.0}, {"o": 10.0, "lse": 1.0}, "f32", "x")["status"] == "PASS"
+    assert bench.receipt_of({"o": 2e-3, "lse": 0.0}, {"o": 10.0, "lse": 1.0}, "f32", "x")["status"] == "FAIL"
+    assert bench.receipt_of({"o": float("nan"), "lse": 0.0}, {"o": 1.0, "lse": 1.0}, "bf16", "x")["status"] == "FAIL"
