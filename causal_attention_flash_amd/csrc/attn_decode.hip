@@ -12,7 +12,10 @@
 // * a key row is read by a group of lanes with 16-byte loads (D*elem/16 of them,
 //   rounded up to a power of two), consecutive lane groups on consecutive rows,
 //   so a wave's loads cover whole rows and whole cache lines; loads are issued one
-//   batch of rows ahead of the arithmetic;
+//   batch of two rows per lane group ahead of the arithmetic, as nontemporal loads
+//   (each cache row is read once per call; measured 4-7% faster than plain loads
+//   with batches of four rows, which also cost enough registers to leave part of
+//   the grid waiting for a slot);
 // * each lane keeps, per query head, the running max m, the running sum l and its
 //   slice of the unnormalised output o (fp32, exponent in log2 units with
 //   scale*log2(e) folded into q); the lane groups of a workgroup are merged by
@@ -138,7 +141,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const void* __restric
     using Cfg = DecodeCfg<T, D>;
     constexpr int E = Cfg::E, CPR = Cfg::CPR, DG = Cfg::DG, R = Cfg::R, NT = Cfg::NT;
     constexpr int EB = 16 / E;  // bytes per element
-    constexpr int U = GT >= 8 ? 2 : 4;  // rows per lane group per batch of loads
+    constexpr int U = 2;  // rows per lane group per batch of loads
     __shared__ float sm[NT / 64][GT][2];
     __shared__ float so[NT / 64][GT][D];
 
@@ -181,8 +184,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const void* __restric
             const int key = r + u * R;
             kk[u] = vv[u] = u32x4{0u, 0u, 0u, 0u};
             if (act && key < k_end) {
-                kk[u] = ldg16(Kb + (size_t)key * D * EB);
-                vv[u] = ldg16(Vb + (size_t)key * D * EB);
+                kk[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kb + (size_t)key * D * EB));
+                vv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Vb + (size_t)key * D * EB));
             }
         }
     };
