@@ -90,23 +90,6 @@ __device__ __forceinline__ void merge(Run<E>& a, float m2, float l2, const float
     for (int e = 0; e < E; ++e) a.o[e] = a.o[e] * f1 + o2[e] * f2;
 }
 
-// Sum over aligned groups of DG lanes (DG a power of two <= 32), the result in
-// every lane of the group: DPP adds within rows of 16 lanes (pairs, quads, the
-// two halves of a row, the two halves of 16), then one cross-row exchange.
-template <int CTRL>
-__device__ __forceinline__ float plus_dpp(float x) {
-    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
-template <int DG>
-__device__ __forceinline__ float group_sum(float x) {
-    if constexpr (DG >= 2) x = plus_dpp<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
-    if constexpr (DG >= 4) x = plus_dpp<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
-    if constexpr (DG >= 8) x = plus_dpp<0x141>(x);  // row_half_mirror: the other quad of 8
-    if constexpr (DG >= 16) x = plus_dpp<0x140>(x); // row_mirror: the other 8 of 16
-    if constexpr (DG >= 32) x += __shfl_xor(x, 16);
-    return x;
-}
-
 // q . k over one lane's 16-byte slices (q pre-widened for fp32, packed for 16-bit)
 template <class T>
 struct SliceDot {
@@ -201,7 +184,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const void* __restric
             const bool valid = r + u * R < k_end;
 #pragma unroll
             for (int g = 0; g < GT; ++g) {
-                const float s = group_sum<DG>(SliceDot<T>::dot(qs[g], kc[u])) * c;
+                const float s = lane_group_sum<DG>(SliceDot<T>::dot(qs[g], kc[u])) * c;
                 sc[u][g] = valid ? s : -INFINITY;
             }
         }

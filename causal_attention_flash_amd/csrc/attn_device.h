@@ -246,6 +246,26 @@ __device__ __forceinline__ float half_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Sum over aligned groups of G lanes (G a power of two, at most 32), the result in
+// every lane of the group: DPP adds within rows of 16 lanes (pairs, quads, the two
+// halves of a row of 8, the two halves of 16), then one cross-row exchange.  Each
+// step adds a lane's value and its partner's in either order, so every lane of a
+// group ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float plus_dpp(float x) {
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+template <int G>
+__device__ __forceinline__ float lane_group_sum(float x) {
+    static_assert(G >= 1 && G <= 32 && (G & (G - 1)) == 0, "group of 1, 2, 4, 8, 16 or 32 lanes");
+    if constexpr (G >= 2) x = plus_dpp<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+    if constexpr (G >= 4) x = plus_dpp<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (G >= 8) x = plus_dpp<0x141>(x);  // row_half_mirror: the other quad of 8
+    if constexpr (G >= 16) x = plus_dpp<0x140>(x); // row_mirror: the other 8 of 16
+    if constexpr (G >= 32) x += __shfl_xor(x, 16);
+    return x;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // s_waitcnt vmcnt(0): every vector memory load issued so far has returned.

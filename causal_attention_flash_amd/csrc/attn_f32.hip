@@ -4,10 +4,11 @@
 // saved LSE; atomic-free backward recomputing P from the LSE; delta from the
 // preprocess), laid out for exact fp32 products instead of matrix cores: G lanes
 // share one row (a query, or a key for the dK/dV pass), each lane holding E = D/G
-// consecutive columns (G = 2 at D = 64, else 4), and dot products are finished
-// with cross-lane xors inside the G-lane group.  The streamed rows are staged in LDS, where all groups read
-// the same row (a broadcast).  This path serves fp32 callers and small problems;
-// the bf16 kernels carry the throughput.
+// consecutive columns (G = 2 at D = 64, else 4, for grids that fill the device;
+// 8 for smaller ones, see kNarrowG), and dot products are finished with DPP adds
+// inside the G-lane group (lane_group_sum).  The streamed rows are staged in LDS,
+// where all groups read the same row (a broadcast).  This path serves fp32 callers
+// and small problems; the bf16 kernels carry the throughput.
 #include "attn_launch.h"
 #include "attn_device.h"
 
@@ -16,20 +17,22 @@ namespace attn {
 constexpr int kF32Tile = 32;  // streamed rows per LDS tile
 
 // Row split: G lanes per row, E columns per lane, R rows per 256-thread block.
-template <int D>
+template <int D, int G_>
 struct F32Split {
-    static constexpr int G = D <= 64 ? 2 : 4;
+    static constexpr int G = G_;
     static constexpr int E = D / G;
     static constexpr int R = 256 / G;
     static_assert(D % G == 0 && E % 4 == 0, "head dimension");
 };
+// The wide split (fewest lane exchanges and repeated exps per score) serves grids
+// whose row blocks cover the device at least twice; smaller grids take eight lanes
+// per row (four at D = 80): a quarter of the rows per block, so four times the
+// blocks, and a quarter of each lane's chain of dependent FMAs per score.
+template <int D>
+constexpr int kWideG = D <= 64 ? 2 : 4;
+template <int D>
+constexpr int kNarrowG = D == 80 ? 4 : 8;
 
-template <int G>
-__device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-    for (int s = 1; s < G; s <<= 1) x += __shfl_xor(x, s);
-    return x;
-}
 
 // Cooperative load of `rows` rows of D floats starting at row0 into LDS
 // (zero beyond S).
@@ -46,13 +49,13 @@ __device__ __forceinline__ void stage_rows_f32(float* dst, const float* __restri
     }
 }
 
-template <int D>
+template <int D, int GS>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                       const float* __restrict__ V, float* __restrict__ O,
                                                       float* __restrict__ LSE, int S, int nblk, int BH, int H, int GQ,
                                                       float c,
                                                       int causal) {
-    constexpr int G = F32Split<D>::G, R = F32Split<D>::R, E = F32Split<D>::E;
+    constexpr int G = F32Split<D, GS>::G, R = F32Split<D, GS>::R, E = F32Split<D, GS>::E;
     __shared__ __attribute__((aligned(16))) float Ks[kF32Tile * D];
     __shared__ __attribute__((aligned(16))) float Vs[kF32Tile * D];
     const WorkItem wi = heavy_first(blockIdx.x, BH);
@@ -85,7 +88,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
             float d = 0.f;
 #pragma unroll
             for (int e = 0; e < E; ++e) d = fmaf(qv[e], Ks[j * D + part * E + e], d);
-            d = group_sum<G>(d);
+            d = lane_group_sum<G>(d);
             const int key = k0 + j;
             const bool vis = key < S && (!causal || key <= q);
             sv[j] = vis ? d : -INFINITY;
@@ -117,7 +120,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
 
 // DELTA_FROM_O: delta = rowsum(dO o O) is formed here from the O rows and
 // written to DeltaOut; otherwise it is read from Delta.
-template <int D, bool DELTA_FROM_O>
+template <int D, int GS, bool DELTA_FROM_O>
 __global__ __launch_bounds__(256) void dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                      const float* __restrict__ V, const float* __restrict__ O,
                                                      const float* __restrict__ dO, const float* __restrict__ LSE,
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(const float* __restrict__ Q
                                                      float* __restrict__ dQ, int S, int nblk, int BH, int H, int GQ,
                                                      float c,
                                                      float scale, int causal) {
-    constexpr int G = F32Split<D>::G, R = F32Split<D>::R, E = F32Split<D>::E;
+    constexpr int G = F32Split<D, GS>::G, R = F32Split<D, GS>::R, E = F32Split<D, GS>::E;
     __shared__ __attribute__((aligned(16))) float Ks[kF32Tile * D];
     __shared__ __attribute__((aligned(16))) float Vs[kF32Tile * D];
     const WorkItem wi = heavy_first(blockIdx.x, BH);
@@ -153,7 +156,7 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(const float* __restrict__ Q
 #pragma unroll
         for (int e = 0; e < E; ++e)
             dsum = fmaf(dov[e], q < S ? O[base + (size_t)q * D + part * E + e] : 0.f, dsum);
-        dl = group_sum<G>(dsum);
+        dl = lane_group_sum<G>(dsum);
         if (part == 0 && q < S) DeltaOut[(size_t)head * S + q] = dl;
     } else {
         dl = q < S ? Delta[(size_t)head * S + q] : 0.f;
@@ -172,8 +175,8 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(const float* __restrict__ Q
                 s = fmaf(qv[e], Ks[j * D + part * E + e], s);
                 dp = fmaf(dov[e], Vs[j * D + part * E + e], dp);
             }
-            s = group_sum<G>(s);
-            dp = group_sum<G>(dp);
+            s = lane_group_sum<G>(s);
+            dp = lane_group_sum<G>(dp);
             const int key = k0 + j;
             const bool vis = key < S && (!causal || key <= q);
             const float p = vis ? exp2f(fmaf(s, c, -l2)) : 0.f;
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(const float* __restrict__ Q
     }
 }
 
-template <int D>
+template <int D, int GS>
 __global__ __launch_bounds__(256) void dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                        const float* __restrict__ V, const float* __restrict__ dO,
                                                        const float* __restrict__ LSE,
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(const float* __restrict__
                                                        float* __restrict__ dV, int S, int nblk, int BH, int H, int GQ,
                                                        float c,
                                                        float scale, int causal) {
-    constexpr int G = F32Split<D>::G, R = F32Split<D>::R, E = F32Split<D>::E;
+    constexpr int G = F32Split<D, GS>::G, R = F32Split<D, GS>::R, E = F32Split<D, GS>::E;
     __shared__ __attribute__((aligned(16))) float Qs[kF32Tile * D];
     __shared__ __attribute__((aligned(16))) float Os[kF32Tile * D];
     __shared__ float L2s[kF32Tile], DLs[kF32Tile];
@@ -244,8 +247,8 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(const float* __restrict__
                 s = fmaf(kv[e], Qs[j * D + part * E + e], s);
                 dp = fmaf(vv[e], Os[j * D + part * E + e], dp);
             }
-            s = group_sum<G>(s);
-            dp = group_sum<G>(dp);
+            s = lane_group_sum<G>(s);
+            dp = lane_group_sum<G>(dp);
             const int qq = qt0 + j;
             const bool vis = qq < S && (!causal || key <= qq);
             const float p = vis ? exp2f(fmaf(s, c, -L2s[j])) : 0.f;
@@ -267,32 +270,45 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(const float* __restrict__
     }
 }
 
-template <int D>
-static int f32_blocks(const LaunchArgs& a, int* nblk) {
-    constexpr int R = F32Split<D>::R;
+template <int D, int GS>
+static int f32_blocks(const LaunchArgs& a, int64_t units, int* nblk) {
+    constexpr int R = F32Split<D, GS>::R;
     *nblk = (int)((a.S + R - 1) / R);
-    const int64_t total = (int64_t)(*nblk) * a.BH;
+    const int64_t total = (int64_t)(*nblk) * units;
     return total > INT32_MAX ? -1 : (int)total;
 }
 
+// True where the wide split's grid over `units` heads would cover the device fewer
+// than two times.
 template <int D>
-static hipError_t fwd_f32(const LaunchArgs& a) {
+static bool f32_narrow(const LaunchArgs& a, int64_t units) {
+    constexpr int R = F32Split<D, kWideG<D>>::R;
+    return units * ((a.S + R - 1) / R) < 2 * (int64_t)cu_count();
+}
+
+template <int D, int GS>
+static hipError_t fwd_f32_g(const LaunchArgs& a) {
     int nblk;
-    const int total = f32_blocks<D>(a, &nblk);
+    const int total = f32_blocks<D, GS>(a, a.BH, &nblk);
     if (total < 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3(total), dim3(256), 0, a.stream, (const float*)a.q,
+    hipLaunchKernelGGL((fwd_f32_kernel<D, GS>), dim3(total), dim3(256), 0, a.stream, (const float*)a.q,
                        (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, (int)a.S, nblk, (int)a.BH, (int)a.H,
                        (int)(a.H / a.Hkv),
                        a.scale * kLog2e, a.causal);
     return hipGetLastError();
 }
 
-template <int D, bool DELTA_FROM_O>
-static hipError_t dq_f32(const LaunchArgs& a) {
+template <int D>
+static hipError_t fwd_f32(const LaunchArgs& a) {
+    return f32_narrow<D>(a, a.BH) ? fwd_f32_g<D, kNarrowG<D>>(a) : fwd_f32_g<D, kWideG<D>>(a);
+}
+
+template <int D, int GS, bool DELTA_FROM_O>
+static hipError_t dq_f32_g(const LaunchArgs& a) {
     int nblk;
-    const int total = f32_blocks<D>(a, &nblk);
+    const int total = f32_blocks<D, GS>(a, a.BH, &nblk);
     if (total < 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((dq_f32_kernel<D, DELTA_FROM_O>), dim3(total), dim3(256), 0, a.stream, (const float*)a.q,
+    hipLaunchKernelGGL((dq_f32_kernel<D, GS, DELTA_FROM_O>), dim3(total), dim3(256), 0, a.stream, (const float*)a.q,
                        (const float*)a.k, (const float*)a.v, (const float*)a.o_in, (const float*)a.dout, a.lse_in,
                        a.delta_in, a.delta, (float*)a.dq, (int)a.S, nblk, (int)a.BH, (int)a.H, (int)(a.H / a.Hkv),
                        a.scale * kLog2e, a.scale,
@@ -300,18 +316,29 @@ static hipError_t dq_f32(const LaunchArgs& a) {
     return hipGetLastError();
 }
 
-template <int D>
-static hipError_t dkdv_f32(const LaunchArgs& a) {
+template <int D, bool DELTA_FROM_O>
+static hipError_t dq_f32(const LaunchArgs& a) {
+    return f32_narrow<D>(a, a.BH) ? dq_f32_g<D, kNarrowG<D>, DELTA_FROM_O>(a)
+                                  : dq_f32_g<D, kWideG<D>, DELTA_FROM_O>(a);
+}
+
+template <int D, int GS>
+static hipError_t dkdv_f32_g(const LaunchArgs& a, int64_t bhkv) {
     int nblk;
     // one block per key block of each key/value head
-    const int64_t bhkv = a.BH / a.H * a.Hkv;
-    if (f32_blocks<D>(a, &nblk) < 0) return hipErrorInvalidValue;
-    const int total = nblk * (int)bhkv;
-    hipLaunchKernelGGL((dkdv_f32_kernel<D>), dim3(total), dim3(256), 0, a.stream, (const float*)a.q,
+    const int total = f32_blocks<D, GS>(a, bhkv, &nblk);
+    if (total < 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((dkdv_f32_kernel<D, GS>), dim3(total), dim3(256), 0, a.stream, (const float*)a.q,
                        (const float*)a.k, (const float*)a.v, (const float*)a.dout, a.lse_in, a.delta_in,
                        (float*)a.dk, (float*)a.dv, (int)a.S, nblk, (int)bhkv, (int)a.H, (int)(a.H / a.Hkv),
                        a.scale * kLog2e, a.scale, a.causal);
     return hipGetLastError();
+}
+
+template <int D>
+static hipError_t dkdv_f32(const LaunchArgs& a) {
+    const int64_t bhkv = a.BH / a.H * a.Hkv;
+    return f32_narrow<D>(a, bhkv) ? dkdv_f32_g<D, kNarrowG<D>>(a, bhkv) : dkdv_f32_g<D, kWideG<D>>(a, bhkv);
 }
 
 hipError_t launch_fwd_f32(const LaunchArgs& a) {

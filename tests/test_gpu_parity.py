@@ -113,6 +113,24 @@ def test_paired_query_blocks_odd_count(device, D):
     gu.check(gu.errors(gpu, ref, all_heads(w)), "bf16", f"paired blocks S=1900 H=64 D={D}")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("B,H,S,D", [(4, 16, 1024, 64), (2, 16, 2048, 128)])
+def test_f32_wide_split(device, B, H, S, D, causal):
+    """fp32 grids that cover the device twice (256 CUs) with the wide lane split (two
+    lanes per row at D = 64, 128 rows per block; four at D = 128, 64 rows): every other
+    fp32 case here is small enough to take eight lanes per row.  Sampled heads against
+    the oracle."""
+    rows = 128 if D == 64 else 64
+    assert B * H * (S // rows) >= 2 * 256
+    w = si.Workload("f32wide", B, H, S, D, "f32", 1.0, 1.0, 1.0, causal)
+    print(f"\n[f32 wide] B={B} H={H} S={S} D={D} causal={causal}", flush=True)
+    x = si.make_inputs(w, seed=S + D + int(causal))
+    heads = [(0, 0), (B - 1, H - 1), (B // 2, 5)]
+    gpu = gu.run_gpu(x, w, device, causal=causal)
+    ref = oracle_heads(x, w, heads, causal=causal)
+    gu.check(gu.errors(gpu, ref, heads), "f32", f"f32 wide B={B} H={H} S={S} D={D} causal={causal}")
+
+
 def test_accumulator_width_cell(device):
     """Rigel §6: 448 + 127 * 0.0625 = 455.9375 needs a wide (fp32) accumulator for QK^T."""
     import causal_attention_flash_amd as caf
