@@ -34,20 +34,32 @@ template <int D>
 constexpr int kNarrowG = D == 80 ? 4 : 8;
 
 
-// Cooperative load of `rows` rows of D floats starting at row0 into LDS
-// (zero beyond S).
+// One tile of kF32Tile rows of D floats (rows row0 .. row0 + kF32Tile - 1, zero at
+// and beyond S), held in registers between its loads and its store to LDS, so that
+// the next tile's loads are in flight during the current tile's arithmetic.
 template <int D>
-__device__ __forceinline__ void stage_rows_f32(float* dst, const float* __restrict__ src, int row0, int S, int tid) {
-    constexpr int CH = kF32Tile * D / 4;  // 16-byte chunks
+struct F32Rows {
+    static constexpr int CH = kF32Tile * D / 4;  // 16-byte chunks
+    static constexpr int PT = (CH + 255) / 256;  // per thread
+    f32x4 r[PT];
+    __device__ __forceinline__ void load(const float* __restrict__ src, int row0, int S, int tid) {
 #pragma unroll
-    for (int c = tid; c < CH; c += 256) {
-        const int row = c / (D / 4);
-        const int col = (c % (D / 4)) * 4;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (row0 + row < S) v = *reinterpret_cast<const f32x4*>(src + (size_t)(row0 + row) * D + col);
-        *reinterpret_cast<f32x4*>(dst + row * D + col) = v;
+        for (int i = 0; i < PT; ++i) {
+            const int c = tid + i * 256;
+            const int row = c / (D / 4), col = (c % (D / 4)) * 4;
+            r[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if ((CH % 256 == 0 || c < CH) && row0 + row < S)
+                r[i] = *reinterpret_cast<const f32x4*>(src + (size_t)(row0 + row) * D + col);
+        }
     }
-}
+    __device__ __forceinline__ void store(float* dst, int tid) const {
+#pragma unroll
+        for (int i = 0; i < PT; ++i) {
+            const int c = tid + i * 256;
+            if (CH % 256 == 0 || c < CH) *reinterpret_cast<f32x4*>(dst + c * 4) = r[i];
+        }
+    }
+};
 
 template <int D, int GS>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
@@ -76,11 +88,18 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
     }
     float m = -FLT_MAX, l = 0.f;
     const int kend = causal ? min(S, q0 + R) : S;
+    F32Rows<D> kt, vt;
+    kt.load(K + kvbase, 0, S, tid);
+    vt.load(V + kvbase, 0, S, tid);
     for (int k0 = 0; k0 < kend; k0 += kF32Tile) {
+        __syncthreads();  // the previous tile is no longer read
+        kt.store(Ks, tid);
+        vt.store(Vs, tid);
         __syncthreads();
-        stage_rows_f32<D>(Ks, K + kvbase, k0, S, tid);
-        stage_rows_f32<D>(Vs, V + kvbase, k0, S, tid);
-        __syncthreads();
+        if (k0 + kF32Tile < kend) {
+            kt.load(K + kvbase, k0 + kF32Tile, S, tid);
+            vt.load(V + kvbase, k0 + kF32Tile, S, tid);
+        }
         float sv[kF32Tile];
         float mx = -INFINITY;
 #pragma unroll
@@ -162,11 +181,18 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(const float* __restrict__ Q
         dl = q < S ? Delta[(size_t)head * S + q] : 0.f;
     }
     const int kend = causal ? min(S, q0 + R) : S;
+    F32Rows<D> kt, vt;
+    kt.load(K + kvbase, 0, S, tid);
+    vt.load(V + kvbase, 0, S, tid);
     for (int k0 = 0; k0 < kend; k0 += kF32Tile) {
+        __syncthreads();  // the previous tile is no longer read
+        kt.store(Ks, tid);
+        vt.store(Vs, tid);
         __syncthreads();
-        stage_rows_f32<D>(Ks, K + kvbase, k0, S, tid);
-        stage_rows_f32<D>(Vs, V + kvbase, k0, S, tid);
-        __syncthreads();
+        if (k0 + kF32Tile < kend) {
+            kt.load(K + kvbase, k0 + kF32Tile, S, tid);
+            vt.load(V + kvbase, k0 + kF32Tile, S, tid);
+        }
 #pragma unroll 4
         for (int j = 0; j < kF32Tile; ++j) {
             float s = 0.f, dp = 0.f;
@@ -226,19 +252,35 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(const float* __restrict__
     // all add into dk and dv
     const int Hkv = H / GQ;
     const int qh0 = (head / Hkv) * H + (head % Hkv) * GQ;
-    for (int g = 0; g < GQ; ++g)
-    for (int qt0 = qstart; qt0 < S; qt0 += kF32Tile) {
-        const int qh = qh0 + g;
+    // query tiles of the GQ query heads in turn, the next one fetched into
+    // registers during the current one's arithmetic
+    const int nq = (S - qstart + kF32Tile - 1) / kF32Tile;
+    const int ntot = GQ * nq;
+    F32Rows<D> qtl, otl;
+    float l2n = INFINITY, dln = 0.f;
+    auto fetch = [&](int i) {
+        const int qh = qh0 + i / nq, qt = qstart + (i % nq) * kF32Tile;
         const size_t qbase = (size_t)qh * S * D;
-        __syncthreads();
-        stage_rows_f32<D>(Qs, Q + qbase, qt0, S, tid);
-        stage_rows_f32<D>(Os, dO + qbase, qt0, S, tid);
+        qtl.load(Q + qbase, qt, S, tid);
+        otl.load(dO + qbase, qt, S, tid);
         if (tid < kF32Tile) {
-            const int qq = qt0 + tid;
-            L2s[tid] = qq < S ? LSE[(size_t)qh * S + qq] * kLog2e : INFINITY;
-            DLs[tid] = qq < S ? Delta[(size_t)qh * S + qq] : 0.f;
+            const int qq = qt + tid;
+            l2n = qq < S ? LSE[(size_t)qh * S + qq] * kLog2e : INFINITY;
+            dln = qq < S ? Delta[(size_t)qh * S + qq] : 0.f;
+        }
+    };
+    if (ntot > 0) fetch(0);
+    for (int i = 0; i < ntot; ++i) {
+        const int qt0 = qstart + (i % nq) * kF32Tile;
+        __syncthreads();  // the previous tile is no longer read
+        qtl.store(Qs, tid);
+        otl.store(Os, tid);
+        if (tid < kF32Tile) {
+            L2s[tid] = l2n;
+            DLs[tid] = dln;
         }
         __syncthreads();
+        if (i + 1 < ntot) fetch(i + 1);
 #pragma unroll 4
         for (int j = 0; j < kF32Tile; ++j) {
             float s = 0.f, dp = 0.f;
