@@ -252,8 +252,10 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(const float* __restrict__
     // all add into dk and dv
     const int Hkv = H / GQ;
     const int qh0 = (head / Hkv) * H + (head % Hkv) * GQ;
-    // query tiles of the GQ query heads in turn, the next one fetched into
-    // registers during the current one's arithmetic
+    // query tiles of the GQ query heads in turn; with the narrow split (E <= 16)
+    // the next one is fetched into registers during the current one's arithmetic
+    // (the wide split's four E-long row arrays leave no registers for it)
+    constexpr bool PF = E <= 16;
     const int nq = (S - qstart + kF32Tile - 1) / kF32Tile;
     const int ntot = GQ * nq;
     F32Rows<D> qtl, otl;
@@ -269,9 +271,10 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(const float* __restrict__
             dln = qq < S ? Delta[(size_t)qh * S + qq] : 0.f;
         }
     };
-    if (ntot > 0) fetch(0);
+    if (PF && ntot > 0) fetch(0);
     for (int i = 0; i < ntot; ++i) {
         const int qt0 = qstart + (i % nq) * kF32Tile;
+        if (!PF) fetch(i);
         __syncthreads();  // the previous tile is no longer read
         qtl.store(Qs, tid);
         otl.store(Os, tid);
@@ -280,8 +283,8 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(const float* __restrict__
             DLs[tid] = dln;
         }
         __syncthreads();
-        if (i + 1 < ntot) fetch(i + 1);
-#pragma unroll 4
+        if (PF && i + 1 < ntot) fetch(i + 1);
+#pragma unroll(E > 8 ? 1 : 4)  // wider rows keep 2 * E LDS values live per unrolled query
         for (int j = 0; j < kF32Tile; ++j) {
             float s = 0.f, dp = 0.f;
 #pragma unroll
