@@ -143,6 +143,9 @@ struct Bf16 {
     static __device__ __forceinline__ f32x16 mma(const V8& a, const V8& b, const f32x16& c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
+    static __device__ __forceinline__ f32x4 mma16(const V8& a, const V8& b, const f32x4& c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
     static __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
     // acc + a.lo*b.lo + a.hi*b.hi in fp32, on packed pairs
     static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
@@ -157,6 +160,9 @@ struct F16 {
     using V2 = f16x2;
     static __device__ __forceinline__ f32x16 mma(const V8& a, const V8& b, const f32x16& c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 mma16(const V8& a, const V8& b, const f32x4& c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
     }
     static __device__ __forceinline__ uint32_t pack2(float a, float b) {
         const f16x2 r = {(_Float16)a, (_Float16)b};
@@ -208,6 +214,19 @@ __device__ __forceinline__ typename E::V8 pack_op(const f32x16& acc, int c) {
     u[3] = E::pack2(acc[8 * c + 6], acc[8 * c + 7]);
     return __builtin_bit_cast(typename E::V8, u);
 }
+// Per-lane sums of B operands of the 32x32x16 product, taken on the 16x16x32
+// product.  As a 16x16x32 B operand, lane l is column l % 16 and contraction group
+// g = l / 16 (A and B pair their values group by group, element by element, so how
+// the hardware numbers a group's eight contraction indices does not matter here).
+// This A operand is 1 in row 4g over group g and 0 elsewhere, so output register 0
+// of lane l (row 4g, column l % 16) is the fp32 sum of lane l's own eight values.
+template <class E>
+__device__ __forceinline__ typename E::V8 lane_sum_selector(int lane) {
+    const int i = lane & 15, g = lane >> 4;
+    const uint32_t w = i == 4 * g ? E::pack2(1.0f, 1.0f) : 0u;
+    return __builtin_bit_cast(typename E::V8, u32x4{w, w, w, w});
+}
+
 // acc + the sum of the eight values of x (fp32 accumulation)
 template <class E>
 __device__ __forceinline__ float sum8(const typename E::V8& x, float acc) {

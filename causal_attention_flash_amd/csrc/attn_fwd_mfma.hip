@@ -15,8 +15,9 @@
 // * NW waves per workgroup, split-Q: each wave owns QB blocks of 32 query rows
 //   and never shares row statistics with another wave.
 // * The score tile is computed transposed, S^T = K Q^T, so each lane owns one
-//   query (C column) and the row max / row sum are in-lane reductions plus one
-//   exchange between the two lane halves (v_permlane32_swap).
+//   query (C column) and the row max / row sum are per-lane reductions (the sum
+//   on the matrix cores, see FwdCfg::MFMA_ROW_SUM) plus one exchange between the
+//   two lane halves (v_permlane32_swap).
 // * P^T, packed to bf16 straight from the C registers, is the B operand of
 //   O^T += V^T P^T; V stays row-major in LDS and its transposed operand comes
 //   from ds_read_b64_tr_b16, in the key order of the C registers.  The rescale
@@ -96,6 +97,11 @@ struct FwdCfg {
     // (measured 2-5% faster where the pairs still cover every slot).  Where three
     // workgroups fill a CU (D = 64) pairs leave a third of it idle: 5% slower there.
     static constexpr bool PAIRABLE = D >= 80 && !QK8;
+    // Per-lane row sums of each tile's P on the matrix cores (two 16x16x32 products
+    // against a selector, lane_sum_selector) instead of eight v_dot2, which hold the
+    // MFMA pipe while they run: bitwise the same sums, 0.5-2% faster at D = 64; at
+    // D = 128 (16-bit Q and K) the selector's registers would spill.
+    static constexpr bool MFMA_ROW_SUM = D <= 96 || QK8;
     // the loop masks only a wave's last key tile: a wave's 32 * QB queries must
     // not reach into an earlier tile (else that tile also crosses the diagonal)
     static_assert(32 * QB <= BN, "a wave's queries must fit in one key tile");
@@ -158,6 +164,7 @@ __global__ __launch_bounds__(NW * 64, (FwdCfg<D, QB, NW, QK8, BN_>::WAVES_PER_SI
         ksrc.init(wave, lane);
         DOffsets<typename Cfg::Tile, D> lo;
         lo.init(lane);
+        const V8 rsel = lane_sum_selector<E>(lane);  // used where Cfg::MFMA_ROW_SUM
         // K row operand offsets: 16-bit, the DOffsets row reads; fp8, two 16-byte
         // chunks per step (indices 64s + 32h .. +31: slots 32s + 16h and +8)
         int k8[QK8 ? QS : 1][2];
@@ -284,6 +291,7 @@ __global__ __launch_bounds__(NW * 64, (FwdCfg<D, QB, NW, QK8, BN_>::WAVES_PER_SI
     #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
                     ls[qb] = 0.f;
+                    f32x4 rs = {0.f, 0.f, 0.f, 0.f};
     #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) {
                         f32x16 e;
@@ -291,9 +299,15 @@ __global__ __launch_bounds__(NW * 64, (FwdCfg<D, QB, NW, QK8, BN_>::WAVES_PER_SI
                         for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(cur[qb][kb][r], c, -m[qb]));
                         pf[qb][2 * kb] = pack_op<E>(e, 0);
                         pf[qb][2 * kb + 1] = pack_op<E>(e, 1);
-                        ls[qb] = sum8<E>(pf[qb][2 * kb], ls[qb]);
-                        ls[qb] = sum8<E>(pf[qb][2 * kb + 1], ls[qb]);
+                        if constexpr (Cfg::MFMA_ROW_SUM) {
+                            rs = E::mma16(rsel, pf[qb][2 * kb], rs);
+                            rs = E::mma16(rsel, pf[qb][2 * kb + 1], rs);
+                        } else {
+                            ls[qb] = sum8<E>(pf[qb][2 * kb], ls[qb]);
+                            ls[qb] = sum8<E>(pf[qb][2 * kb + 1], ls[qb]);
+                        }
                     }
+                    if constexpr (Cfg::MFMA_ROW_SUM) ls[qb] = rs[0];
                 }
             };
             probs();
