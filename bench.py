@@ -807,7 +807,8 @@ def main():
         # (in its order) bracketed by events; the grouped form has no stage entry
         # points, so there the backward is timed as one (its dQ and dK/dV passes), and
         # so is the atomic-dQ backward (delta, zero fill, fused pass, dQ conversion)
-        if grouped or atomic:
+        # and the fp32 backward (one launch for grids too small to fill the device)
+        if grouped or atomic or w.dtype == "f32":
             names = ("fwd", "bwd")
             calls = (fwd, bwd)
         else:

@@ -167,6 +167,13 @@ attn_status run_dq_delta(const LaunchArgs& a, attn_dtype dt) {
                     : dt == ATTN_F16 ? attn::launch_bwd_dq_delta_f16(a)
                                      : attn::launch_bwd_dq_delta_f32(a));
 }
+// The dQ pass, which forms delta, then the dK/dV pass that reads it; fp32 runs the
+// two in one launch where its grids are too small to fill the device.
+attn_status run_bwd_passes(const LaunchArgs& a, attn_dtype dt) {
+    if (dt == ATTN_F32) return from_hip(attn::launch_bwd_f32(a));
+    const attn_status st = run_dq_delta(a, dt);
+    return st != ATTN_OK ? st : run_dkdv(a, dt);
+}
 
 }  // namespace
 
@@ -448,8 +455,7 @@ attn_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const 
     a.dk = dk;
     a.dv = dv;
     // as attn_bwd: the dQ pass forms delta, then the dK/dV pass reads it
-    if ((st = run_dq_delta(a, dtype)) != ATTN_OK) return st;
-    return run_dkdv(a, dtype);
+    return run_bwd_passes(a, dtype);
 }
 
 attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -497,8 +503,7 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void
     }
     // dQ first: it forms delta, which the dK/dV pass reads; with grouped heads in
     // bf16/fp16 the dK/dV pass leaves per-query-head partials that the group sum adds
-    if ((st = run_dq_delta(a, dtype)) != ATTN_OK) return st;
-    if ((st = run_dkdv(a, dtype)) != ATTN_OK) return st;
+    if ((st = run_bwd_passes(a, dtype)) != ATTN_OK) return st;
     return partials ? run_group_sum(a, dtype) : ATTN_OK;
 }
 

@@ -137,20 +137,25 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
     }
 }
 
-// DELTA_FROM_O: delta = rowsum(dO o O) is formed here from the O rows and
-// written to DeltaOut; otherwise it is read from Delta.
+// LDS of one dQ block (K and V tiles) or one dK/dV block (Q and dO tiles, then the
+// rows' -LSE*log2(e) and delta), in floats.
+template <int D>
+constexpr int kF32Smem = 2 * kF32Tile * D + 2 * kF32Tile;
+
+// dQ of query block `bid` (heaviest first over the BH heads).  DELTA_FROM_O:
+// delta = rowsum(dO o O) is formed here from the O rows and written to DeltaOut;
+// otherwise it is read from Delta.
 template <int D, int GS, bool DELTA_FROM_O>
-__global__ __launch_bounds__(256) void dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
-                                                     const float* __restrict__ V, const float* __restrict__ O,
-                                                     const float* __restrict__ dO, const float* __restrict__ LSE,
-                                                     const float* __restrict__ Delta, float* __restrict__ DeltaOut,
-                                                     float* __restrict__ dQ, int S, int nblk, int BH, int H, int GQ,
-                                                     float c,
-                                                     float scale, int causal) {
+__device__ __forceinline__ void dq_f32_block(float* smem, int bid, const float* __restrict__ Q,
+                                             const float* __restrict__ K, const float* __restrict__ V,
+                                             const float* __restrict__ O, const float* __restrict__ dO,
+                                             const float* __restrict__ LSE, const float* __restrict__ Delta,
+                                             float* __restrict__ DeltaOut, float* __restrict__ dQ, int S, int nblk,
+                                             int BH, int H, int GQ, float c, float scale, int causal) {
     constexpr int G = F32Split<D, GS>::G, R = F32Split<D, GS>::R, E = F32Split<D, GS>::E;
-    __shared__ __attribute__((aligned(16))) float Ks[kF32Tile * D];
-    __shared__ __attribute__((aligned(16))) float Vs[kF32Tile * D];
-    const WorkItem wi = heavy_first(blockIdx.x, BH);
+    float* Ks = smem;
+    float* Vs = smem + kF32Tile * D;
+    const WorkItem wi = heavy_first(bid, BH);
     const int head = wi.head;
     const int blk = nblk - 1 - wi.rank;
     const int q0 = blk * R;
@@ -217,19 +222,36 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(const float* __restrict__ Q
     }
 }
 
-template <int D, int GS>
-__global__ __launch_bounds__(256) void dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
-                                                       const float* __restrict__ V, const float* __restrict__ dO,
-                                                       const float* __restrict__ LSE,
-                                                       const float* __restrict__ Delta, float* __restrict__ dK,
-                                                       float* __restrict__ dV, int S, int nblk, int BH, int H, int GQ,
-                                                       float c,
-                                                       float scale, int causal) {
+template <int D, int GS, bool DELTA_FROM_O>
+__global__ __launch_bounds__(256) void dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                                     const float* __restrict__ V, const float* __restrict__ O,
+                                                     const float* __restrict__ dO, const float* __restrict__ LSE,
+                                                     const float* __restrict__ Delta, float* __restrict__ DeltaOut,
+                                                     float* __restrict__ dQ, int S, int nblk, int BH, int H, int GQ,
+                                                     float c, float scale, int causal) {
+    __shared__ __attribute__((aligned(16))) float smem[kF32Smem<D>];
+    dq_f32_block<D, GS, DELTA_FROM_O>(smem, blockIdx.x, Q, K, V, O, dO, LSE, Delta, DeltaOut, dQ, S, nblk, BH, H,
+                                      GQ, c, scale, causal);
+}
+
+// dK and dV of key block `bid` (heaviest first over the BH key/value heads).
+// DELTA_FROM_O: each query tile's delta = rowsum(dO o O) is formed here from the
+// dO and O rows (eight lanes per row, D/8 columns each: the partition and order of
+// the dQ block's eight-lane split, so the same bits there); otherwise it is read
+// from Delta.
+template <int D, int GS, bool DELTA_FROM_O>
+__device__ __forceinline__ void dkdv_f32_block(float* smem, int bid, const float* __restrict__ Q,
+                                               const float* __restrict__ K, const float* __restrict__ V,
+                                               const float* __restrict__ O, const float* __restrict__ dO,
+                                               const float* __restrict__ LSE, const float* __restrict__ Delta,
+                                               float* __restrict__ dK, float* __restrict__ dV, int S, int nblk, int BH,
+                                               int H, int GQ, float c, float scale, int causal) {
     constexpr int G = F32Split<D, GS>::G, R = F32Split<D, GS>::R, E = F32Split<D, GS>::E;
-    __shared__ __attribute__((aligned(16))) float Qs[kF32Tile * D];
-    __shared__ __attribute__((aligned(16))) float Os[kF32Tile * D];
-    __shared__ float L2s[kF32Tile], DLs[kF32Tile];
-    const WorkItem wi = heavy_first(blockIdx.x, BH);
+    float* Qs = smem;
+    float* Os = smem + kF32Tile * D;
+    float* L2s = smem + 2 * kF32Tile * D;
+    float* DLs = L2s + kF32Tile;
+    const WorkItem wi = heavy_first(bid, BH);
     const int head = wi.head;
     const int blk = wi.rank;
     const int n0 = blk * R;
@@ -260,6 +282,10 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(const float* __restrict__
     const int ntot = GQ * nq;
     F32Rows<D> qtl, otl;
     float l2n = INFINITY, dln = 0.f;
+    // DELTA_FROM_O: lane group tid / 8 holds D/8 columns of dO and O of row tid / 8
+    constexpr int EP = D / 8;
+    static_assert(kF32Tile * 8 == 256 && D % 8 == 0, "eight lanes per query row of a tile");
+    float dd[DELTA_FROM_O ? EP : 1], oo[DELTA_FROM_O ? EP : 1];
     auto fetch = [&](int i) {
         const int qh = qh0 + i / nq, qt = qstart + (i % nq) * kF32Tile;
         const size_t qbase = (size_t)qh * S * D;
@@ -268,7 +294,16 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(const float* __restrict__
         if (tid < kF32Tile) {
             const int qq = qt + tid;
             l2n = qq < S ? LSE[(size_t)qh * S + qq] * kLog2e : INFINITY;
-            dln = qq < S ? Delta[(size_t)qh * S + qq] : 0.f;
+            if constexpr (!DELTA_FROM_O) dln = qq < S ? Delta[(size_t)qh * S + qq] : 0.f;
+        }
+        if constexpr (DELTA_FROM_O) {
+            const int qq = qt + (tid >> 3);
+            const size_t off = qbase + (size_t)qq * D + (tid & 7) * EP;
+#pragma unroll
+            for (int e = 0; e < EP; ++e) {
+                dd[e] = qq < S ? dO[off + e] : 0.f;
+                oo[e] = qq < S ? O[off + e] : 0.f;
+            }
         }
     };
     if (PF && ntot > 0) fetch(0);
@@ -280,7 +315,14 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(const float* __restrict__
         otl.store(Os, tid);
         if (tid < kF32Tile) {
             L2s[tid] = l2n;
-            DLs[tid] = dln;
+            if constexpr (!DELTA_FROM_O) DLs[tid] = dln;
+        }
+        if constexpr (DELTA_FROM_O) {
+            float dsum = 0.f;
+#pragma unroll
+            for (int e = 0; e < EP; ++e) dsum = fmaf(dd[e], oo[e], dsum);
+            dsum = lane_group_sum<8>(dsum);
+            if ((tid & 7) == 0) DLs[tid >> 3] = dsum;
         }
         __syncthreads();
         if (PF && i + 1 < ntot) fetch(i + 1);
@@ -313,6 +355,37 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(const float* __restrict__
             dV[off] = dv[e];
         }
     }
+}
+
+template <int D, int GS>
+__global__ __launch_bounds__(256) void dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                                       const float* __restrict__ V, const float* __restrict__ dO,
+                                                       const float* __restrict__ LSE,
+                                                       const float* __restrict__ Delta, float* __restrict__ dK,
+                                                       float* __restrict__ dV, int S, int nblk, int BH, int H, int GQ,
+                                                       float c, float scale, int causal) {
+    __shared__ __attribute__((aligned(16))) float smem[kF32Smem<D>];
+    dkdv_f32_block<D, GS, false>(smem, blockIdx.x, Q, K, V, nullptr, dO, LSE, Delta, dK, dV, S, nblk, BH, H, GQ, c,
+                                 scale, causal);
+}
+
+// The whole backward of a grid too small to fill the device, in one launch: blocks
+// below ndq are dQ blocks (which also store delta), the rest dK/dV blocks, which form
+// delta themselves, so the two kinds run side by side instead of one pass after the
+// other.
+template <int D, int GS>
+__global__ __launch_bounds__(256) void bwd_f32_fused_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    const float* __restrict__ O, const float* __restrict__ dO, const float* __restrict__ LSE,
+    float* __restrict__ DeltaOut, float* __restrict__ dQ, float* __restrict__ dK, float* __restrict__ dV, int S,
+    int nblk, int ndq, int BH, int BHkv, int H, int GQ, float c, float scale, int causal) {
+    __shared__ __attribute__((aligned(16))) float smem[kF32Smem<D>];
+    if ((int)blockIdx.x < ndq)
+        dq_f32_block<D, GS, true>(smem, blockIdx.x, Q, K, V, O, dO, LSE, nullptr, DeltaOut, dQ, S, nblk, BH, H, GQ,
+                                  c, scale, causal);
+    else
+        dkdv_f32_block<D, GS, true>(smem, (int)blockIdx.x - ndq, Q, K, V, O, dO, LSE, nullptr, dK, dV, S, nblk,
+                                    BHkv, H, GQ, c, scale, causal);
 }
 
 template <int D, int GS>
@@ -386,6 +459,27 @@ static hipError_t dkdv_f32(const LaunchArgs& a) {
     return f32_narrow<D>(a, bhkv) ? dkdv_f32_g<D, kNarrowG<D>>(a, bhkv) : dkdv_f32_g<D, kWideG<D>>(a, bhkv);
 }
 
+// attn_bwd's passes: one fused launch when both take the narrow split, else the dQ
+// pass (forming delta) and then the dK/dV pass.
+template <int D>
+static hipError_t bwd_f32(const LaunchArgs& a) {
+    const int64_t bhkv = a.BH / a.H * a.Hkv;
+    if (!f32_narrow<D>(a, a.BH) || !f32_narrow<D>(a, bhkv)) {
+        const hipError_t e = dq_f32<D, true>(a);
+        return e != hipSuccess ? e : dkdv_f32<D>(a);
+    }
+    constexpr int GS = kNarrowG<D>;
+    int nblk;
+    const int ndq = f32_blocks<D, GS>(a, a.BH, &nblk);
+    const int nkv = f32_blocks<D, GS>(a, bhkv, &nblk);
+    if (ndq < 0 || nkv < 0 || (int64_t)ndq + nkv > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_f32_fused_kernel<D, GS>), dim3(ndq + nkv), dim3(256), 0, a.stream, (const float*)a.q,
+                       (const float*)a.k, (const float*)a.v, (const float*)a.o_in, (const float*)a.dout, a.lse_in,
+                       a.delta, (float*)a.dq, (float*)a.dk, (float*)a.dv, (int)a.S, nblk, ndq, (int)a.BH, (int)bhkv,
+                       (int)a.H, (int)(a.H / a.Hkv), a.scale * kLog2e, a.scale, a.causal);
+    return hipGetLastError();
+}
+
 hipError_t launch_fwd_f32(const LaunchArgs& a) {
     if (a.D == 64) return fwd_f32<64>(a);
     if (a.D == 80) return fwd_f32<80>(a);
@@ -408,6 +502,14 @@ hipError_t launch_bwd_dq_delta_f32(const LaunchArgs& a) {
     if (a.D == 128) return dq_f32<128, true>(a);
     return hipErrorInvalidValue;
 }
+hipError_t launch_bwd_f32(const LaunchArgs& a) {
+    if (a.D == 64) return bwd_f32<64>(a);
+    if (a.D == 80) return bwd_f32<80>(a);
+    if (a.D == 96) return bwd_f32<96>(a);
+    if (a.D == 128) return bwd_f32<128>(a);
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_bwd_dkdv_f32(const LaunchArgs& a) {
     if (a.D == 64) return dkdv_f32<64>(a);
     if (a.D == 80) return dkdv_f32<80>(a);
