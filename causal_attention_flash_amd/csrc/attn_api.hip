@@ -167,12 +167,12 @@ attn_status run_dq_delta(const LaunchArgs& a, attn_dtype dt) {
                     : dt == ATTN_F16 ? attn::launch_bwd_dq_delta_f16(a)
                                      : attn::launch_bwd_dq_delta_f32(a));
 }
-// The dQ pass, which forms delta, then the dK/dV pass that reads it; fp32 runs the
-// two in one launch where its grids are too small to fill the device.
+// The dQ pass, which forms delta, then the dK/dV pass that reads it, or both in one
+// launch where the grids are too small to fill the device.
 attn_status run_bwd_passes(const LaunchArgs& a, attn_dtype dt) {
-    if (dt == ATTN_F32) return from_hip(attn::launch_bwd_f32(a));
-    const attn_status st = run_dq_delta(a, dt);
-    return st != ATTN_OK ? st : run_dkdv(a, dt);
+    return from_hip(dt == ATTN_BF16  ? attn::launch_bwd_bf16(a)
+                    : dt == ATTN_F16 ? attn::launch_bwd_f16(a)
+                                     : attn::launch_bwd_f32(a));
 }
 
 }  // namespace

@@ -77,12 +77,29 @@ struct DkdvCfg {
 // adds, zero sums skipped); a second barrier frees the slots.  (Summing in one
 // slot with LDS atomics instead measured ~9x slower: eight waves' ds_add_f32 on
 // the same addresses serialise.)
-template <class E, int D, int BMQ, int NW, bool PARTIAL, bool DQA = false, int MODE = 0>
-__global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW, MODE>::WAVES_PER_SIMD)) void bwd_dkdv_mfma_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ dKp, float* __restrict__ dVp, int S,
-    int nblk, int BH, int H, int GQ, float c, float scale, int causal, float* __restrict__ dQacc = nullptr) {
+// The LDS of one dK/dV workgroup: the double-buffered Q and dO tiles, their row
+// statistics and (DQA) the per-wave K rows and dQ slots.
+template <int D, int BMQ, int NW, int MODE, bool DQA>
+struct DkdvSmem {
+    using Cfg = DkdvCfg<D, BMQ, NW, MODE>;
+    static constexpr int KSTR = Cfg::KSTR, DQS = D + 1;
+    __attribute__((aligned(16))) uint16_t smem[2 * Cfg::BUF_ELEMS];
+    __attribute__((aligned(16))) float sstat[2 * Cfg::BUF_STATS];
+    __attribute__((aligned(16))) uint16_t kst[DQA ? NW * 32 * KSTR + 32 : 1];
+    __attribute__((aligned(16))) float dqs[DQA ? NW * 32 * DQS : 1];
+};
+
+// One dK/dV workgroup: key block `bid` in heavy-first order over the BH heads.
+// DFLY (one query head per key/value head): each query tile's delta = rowsum(dO o O)
+// is formed here from the tile's dO rows and the matching O rows, instead of being
+// read from Delta.
+template <class E, int D, int BMQ, int NW, bool PARTIAL, bool DQA, int MODE, bool DFLY>
+__device__ __forceinline__ void dkdv_block(
+    DkdvSmem<D, BMQ, NW, MODE, DQA>& lds, int bid, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ Delta, uint16_t* __restrict__ dK,
+    uint16_t* __restrict__ dV, float* __restrict__ dKp, float* __restrict__ dVp, int S, int nblk, int BH, int H,
+    int GQ, float c, float scale, int causal, float* __restrict__ dQacc) {
     using Cfg = DkdvCfg<D, BMQ, NW, MODE>;
     using V8 = typename E::V8;
     constexpr int NT = Cfg::NT, BNK = Cfg::BNK;
@@ -92,18 +109,18 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW, MODE>::WAVES_PER_SIMD
     constexpr int KS = Cfg::KS, DB = Cfg::DB;
     static_assert(!(DQA && PARTIAL), "atomic dQ is for one query head per key/value head");
     static_assert(!DQA || (32 * D) % (NW * 64) == 0, "the flush splits a block's 32 x D sums evenly");
-    // [Q, dO][2]
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Cfg::BUF_ELEMS];
-    __shared__ __attribute__((aligned(16))) float sstat[2 * Cfg::BUF_STATS];
-    // DQA: each wave's K rows [32][STR] and dQ slot [32 queries][DQS] (the odd row
-    // stride spreads a column's rows over the banks), its dS tile [32 keys][DSTR]
-    // at the start of the slot
+    // LDS: [Q, dO][2] tiles and their statistics; DQA: each wave's K rows [32][STR]
+    // and dQ slot [32 queries][DQS] (the odd row stride spreads a column's rows over
+    // the banks), its dS tile [32 keys][DSTR] at the start of the slot
     constexpr int DSTR = 40, DQS = D + 1;
     static_assert(32 * DSTR * 2 <= 32 * DQS * 4, "the dS tile fits in the slot");
-    __shared__ __attribute__((aligned(16))) uint16_t kst[DQA ? NW * 32 * KSTR + 32 : 1];
-    __shared__ __attribute__((aligned(16))) float dqs[DQA ? NW * 32 * DQS : 1];
+    static_assert(!DFLY || (!PARTIAL && !DQA), "delta formed in place: one query head per key/value head");
+    uint16_t* smem = lds.smem;
+    float* sstat = lds.sstat;
+    uint16_t* kst = lds.kst;
+    float* dqs = lds.dqs;
 
-    const WorkItem wi = heavy_first(blockIdx.x, BH);
+    const WorkItem wi = heavy_first(bid, BH);
     const int head = wi.head;
     const int kblk = wi.rank;  // low key blocks see the most queries: first
     const int n0 = kblk * BNK;
@@ -112,7 +129,8 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW, MODE>::WAVES_PER_SIMD
     const uint16_t* Qh = Q + base;
     const uint16_t* dOh = dO + base;
     const float* Lh = LSE + (size_t)head * S;
-    const float* Dh = Delta + (size_t)head * S;
+    const float* Dh = DFLY ? nullptr : Delta + (size_t)head * S;
+    const uint16_t* Oh = DFLY ? O + base : nullptr;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -158,7 +176,13 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW, MODE>::WAVES_PER_SIMD
     typename Cfg::QT qt, ot;
     using QT = typename Cfg::QT;
     const int rl = QT::row_lane(lane), tl = QT::tr_lane(lane);
-    RowStats<BMQ, NT> st;
+    RowStats<BMQ, NT, !DFLY> st;
+    // DFLY: the tile's O rows, chunk for chunk beside its dO rows; a row's chunks are
+    // held by QT::CPR consecutive lanes
+    typename Cfg::QT otv;
+    static_assert(!DFLY || (QT::CPR <= 16 && (QT::CPR & (QT::CPR - 1)) == 0 && QT::CHUNKS % NT == 0 &&
+                            NT % QT::CPR == 0 && QT::CPR == 2 * KS),
+                  "a row's chunks fill an aligned group within a 16-lane DPP row, two per contraction step");
     auto bufp = [&](int b) { return smem + b * Cfg::BUF_ELEMS; };
     auto stat = [&](int b) { return sstat + b * Cfg::BUF_STATS; };
     auto stage = [&](int b) {
@@ -166,11 +190,34 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW, MODE>::WAVES_PER_SIMD
         qt.store(s, tid);
         ot.store(s + Cfg::QE, tid);
         st.store(stat(b), stat(b) + BMQ, rscale, tid);
+        if constexpr (DFLY) {
+            // delta of each row, stored negated, in the dQ pass's order (so the same
+            // bits as attn_bwd_dq_delta): two chains of dot8 over the row's chunks of
+            // one parity (chunks h, h+2, h+4, ... for h = 0, 1; the running sum moves
+            // two lanes per step), then the sum of the two chains
+#pragma unroll
+            for (int i = 0; i < QT::PT; ++i) {
+                const int ch = tid + i * NT, j = ch % QT::CPR;
+                float p = 0.f;
+#pragma unroll
+                for (int step = 0; step < QT::CPR / 2; ++step) {
+                    const float prev = step == 0 ? 0.f
+                                                 : __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                       0, __builtin_bit_cast(int, p), 0x112, 0xF, 0xF, false));
+                    const float mine = dot8<E>(as_op<E>(ot.r[i]), as_op<E>(otv.r[i]), prev);  // row_shr:2
+                    p = (j >> 1) == step ? mine : p;
+                }
+                const float other = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                        0, __builtin_bit_cast(int, p), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+                if (j == QT::CPR - 2) stat(b)[BMQ + ch / QT::CPR] = -(p + other);
+            }
+        }
     };
     auto fetch = [&](int t) {
         qt.load(Qh, t * BMQ, S, tid);
         ot.load(dOh, t * BMQ, S, tid);
         st.load(Lh, Dh, t * BMQ, S, tid);
+        if constexpr (DFLY) otv.load(Oh, t * BMQ, S, tid);
     };
 
     if (t0 < ntiles) {
@@ -357,6 +404,17 @@ __global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW, MODE>::WAVES_PER_SIMD
 
 }
 
+template <class E, int D, int BMQ, int NW, bool PARTIAL, bool DQA = false, int MODE = 0>
+__global__ __launch_bounds__(NW * 64, (DkdvCfg<D, BMQ, NW, MODE>::WAVES_PER_SIMD)) void bwd_dkdv_mfma_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ dKp, float* __restrict__ dVp, int S,
+    int nblk, int BH, int H, int GQ, float c, float scale, int causal, float* __restrict__ dQacc = nullptr) {
+    __shared__ DkdvSmem<D, BMQ, NW, MODE, DQA> lds;
+    dkdv_block<E, D, BMQ, NW, PARTIAL, DQA, MODE, false>(lds, blockIdx.x, Q, K, V, nullptr, dO, LSE, Delta, dK, dV,
+                                                         dKp, dVp, S, nblk, BH, H, GQ, c, scale, causal, dQacc);
+}
+
 template <class E, int D, int BMQ, int NW, int MODE = 0>
 static hipError_t launch_dkdv(const LaunchArgs& a) {
     using Cfg = DkdvCfg<D, BMQ, NW, MODE>;
@@ -540,20 +598,21 @@ struct DqCfg {
 // DELTA_FROM_O: delta = rowsum(dO o O) is formed here, from the O rows of this
 // wave's queries (fp32 sums of bf16 products), and written to DeltaOut for the
 // dK/dV pass; otherwise delta is read from Delta.
+// One dQ workgroup: query block `bid` in heavy-first order over the BH heads, its
+// K/V tiles in `smem` (Cfg::SMEM_ELEMS elements).
 template <class E, int D, int BNK, int NW, bool DELTA_FROM_O>
-__global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void bwd_dq_mfma_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
-    const float* __restrict__ Delta, float* __restrict__ DeltaOut, uint16_t* __restrict__ dQ, int S, int nblk,
-    int BH, int H, int GQ, float c, float scale, int causal) {
+__device__ __forceinline__ void dq_block(
+    uint16_t* smem, int bid, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ Delta, float* __restrict__ DeltaOut,
+    uint16_t* __restrict__ dQ, int S, int nblk, int BH, int H, int GQ, float c, float scale, int causal) {
     using Cfg = DqCfg<D, BNK, NW>;
     using V8 = typename E::V8;
     constexpr int BMQ = Cfg::BMQ;
     constexpr int KS = Cfg::KS, DB = Cfg::DB;
     constexpr int TE = Cfg::TE;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[Cfg::SMEM_ELEMS];
 
-    const WorkItem wi = heavy_first(blockIdx.x, BH);
+    const WorkItem wi = heavy_first(bid, BH);
     const int head = wi.head;
     const int qblk = nblk - 1 - wi.rank;  // high query blocks see the most keys: first
     const int q0 = qblk * BMQ;
@@ -703,6 +762,17 @@ __global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void 
 }
 
 template <class E, int D, int BNK, int NW, bool DELTA_FROM_O>
+__global__ __launch_bounds__(NW * 64, (DqCfg<D, BNK, NW>::WAVES_PER_SIMD)) void bwd_dq_mfma_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
+    const float* __restrict__ Delta, float* __restrict__ DeltaOut, uint16_t* __restrict__ dQ, int S, int nblk,
+    int BH, int H, int GQ, float c, float scale, int causal) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[DqCfg<D, BNK, NW>::SMEM_ELEMS];
+    dq_block<E, D, BNK, NW, DELTA_FROM_O>(smem, blockIdx.x, Q, K, V, O, dO, LSE, Delta, DeltaOut, dQ, S, nblk, BH, H,
+                                          GQ, c, scale, causal);
+}
+
+template <class E, int D, int BNK, int NW, bool DELTA_FROM_O>
 static hipError_t launch_dq(const LaunchArgs& a) {
     using Cfg = DqCfg<D, BNK, NW>;
     const int nblk = (int)((a.S + Cfg::BMQ - 1) / Cfg::BMQ);
@@ -724,6 +794,53 @@ static hipError_t launch_dq_type(const LaunchArgs& a) {
     if (a.D == 128) return launch_dq<E, 128, 32, 4, DELTA_FROM_O>(a);
     return hipErrorInvalidValue;
 }
+
+// The whole backward of a small grid in one launch (D = 64, one query head per
+// key/value head): blocks below ndq are dQ blocks (128 queries, storing delta), the
+// rest four-wave dK/dV blocks of 128 keys that form each query tile's delta
+// themselves (dkdv_block's DFLY), so the two kinds run side by side instead of one
+// pass after the other on a device that each would leave mostly idle.
+template <class E>
+__global__ __launch_bounds__(256, 2) void bwd_small_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
+    float* __restrict__ DeltaOut, uint16_t* __restrict__ dQ, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+    int S, int nblk_q, int nblk_k, int ndq, int BH, int H, float c, float scale, int causal) {
+    using DQ = DqCfg<64, 64, 4>;
+    __shared__ union {
+        __attribute__((aligned(16))) uint16_t dq[DQ::SMEM_ELEMS];
+        DkdvSmem<64, 64, 4, 0, false> kv;
+    } lds;
+    if ((int)blockIdx.x < ndq)
+        dq_block<E, 64, 64, 4, true>(lds.dq, blockIdx.x, Q, K, V, O, dO, LSE, nullptr, DeltaOut, dQ, S, nblk_q, BH, H,
+                                     1, c, scale, causal);
+    else
+        dkdv_block<E, 64, 64, 4, false, false, 0, true>(lds.kv, (int)blockIdx.x - ndq, Q, K, V, O, dO, LSE, nullptr,
+                                                        dK, dV, nullptr, nullptr, S, nblk_k, BH, H, 1, c, scale,
+                                                        causal, nullptr);
+}
+
+// attn_bwd's passes for 16-bit inputs: the one-launch form where it applies (D = 64,
+// one query head per key/value head, and the two kinds of blocks, two per CU, all
+// resident at once), else the dQ pass (forming delta) and then the dK/dV pass.
+template <class E>
+static hipError_t launch_bwd_type(const LaunchArgs& a) {
+    const int64_t nq = (a.S + 127) / 128;  // 128-query dQ blocks and 128-key dK/dV blocks
+    if (a.D == 64 && a.H == a.Hkv && 2 * nq * a.BH <= 2 * (int64_t)cu_count()) {
+        const int ndq = (int)(nq * a.BH);
+        hipLaunchKernelGGL((bwd_small_kernel<E>), dim3(2 * ndq), dim3(256), 0, a.stream, (const uint16_t*)a.q,
+                           (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.o_in,
+                           (const uint16_t*)a.dout, a.lse_in, a.delta, (uint16_t*)a.dq, (uint16_t*)a.dk,
+                           (uint16_t*)a.dv, (int)a.S, (int)nq, (int)nq, ndq, (int)a.BH, (int)a.H, a.scale * kLog2e,
+                           a.scale, a.causal);
+        return hipGetLastError();
+    }
+    const hipError_t e = launch_dq_type<E, true>(a);
+    return e != hipSuccess ? e : launch_dkdv_type<E>(a);
+}
+
+hipError_t launch_bwd_bf16(const LaunchArgs& a) { return launch_bwd_type<Bf16>(a); }
+hipError_t launch_bwd_f16(const LaunchArgs& a) { return launch_bwd_type<F16>(a); }
 
 hipError_t launch_bwd_dq_bf16(const LaunchArgs& a) { return launch_dq_type<Bf16, false>(a); }
 hipError_t launch_bwd_dq_delta_bf16(const LaunchArgs& a) { return launch_dq_type<Bf16, true>(a); }

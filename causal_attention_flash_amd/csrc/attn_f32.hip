@@ -236,9 +236,9 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(const float* __restrict__ Q
 
 // dK and dV of key block `bid` (heaviest first over the BH key/value heads).
 // DELTA_FROM_O: each query tile's delta = rowsum(dO o O) is formed here from the
-// dO and O rows (eight lanes per row, D/8 columns each: the partition and order of
-// the dQ block's eight-lane split, so the same bits there); otherwise it is read
-// from Delta.
+// dO and O rows, in the order of dq_f32_block with the same split (G lanes of an
+// eight-lane group per row, E columns each, then the G-lane sum), so the same bits
+// as the dQ pass; otherwise it is read from Delta.
 template <int D, int GS, bool DELTA_FROM_O>
 __device__ __forceinline__ void dkdv_f32_block(float* smem, int bid, const float* __restrict__ Q,
                                                const float* __restrict__ K, const float* __restrict__ V,
@@ -282,10 +282,10 @@ __device__ __forceinline__ void dkdv_f32_block(float* smem, int bid, const float
     const int ntot = GQ * nq;
     F32Rows<D> qtl, otl;
     float l2n = INFINITY, dln = 0.f;
-    // DELTA_FROM_O: lane group tid / 8 holds D/8 columns of dO and O of row tid / 8
-    constexpr int EP = D / 8;
-    static_assert(kF32Tile * 8 == 256 && D % 8 == 0, "eight lanes per query row of a tile");
-    float dd[DELTA_FROM_O ? EP : 1], oo[DELTA_FROM_O ? EP : 1];
+    // DELTA_FROM_O: lanes 0 .. G-1 of group tid / 8 hold E columns of dO and O of
+    // row tid / 8 (the dQ split's partition)
+    static_assert(kF32Tile * 8 == 256 && G <= 8, "eight lanes per query row of a tile");
+    float dd[DELTA_FROM_O ? E : 1], oo[DELTA_FROM_O ? E : 1];
     auto fetch = [&](int i) {
         const int qh = qh0 + i / nq, qt = qstart + (i % nq) * kF32Tile;
         const size_t qbase = (size_t)qh * S * D;
@@ -297,12 +297,13 @@ __device__ __forceinline__ void dkdv_f32_block(float* smem, int bid, const float
             if constexpr (!DELTA_FROM_O) dln = qq < S ? Delta[(size_t)qh * S + qq] : 0.f;
         }
         if constexpr (DELTA_FROM_O) {
-            const int qq = qt + (tid >> 3);
-            const size_t off = qbase + (size_t)qq * D + (tid & 7) * EP;
+            const int qq = qt + (tid >> 3), p8 = tid & 7;
+            const bool on = qq < S && p8 < G;
+            const size_t off = qbase + (size_t)qq * D + (on ? p8 : 0) * E;
 #pragma unroll
-            for (int e = 0; e < EP; ++e) {
-                dd[e] = qq < S ? dO[off + e] : 0.f;
-                oo[e] = qq < S ? O[off + e] : 0.f;
+            for (int e = 0; e < E; ++e) {
+                dd[e] = on ? dO[off + e] : 0.f;
+                oo[e] = on ? O[off + e] : 0.f;
             }
         }
     };
@@ -320,8 +321,8 @@ __device__ __forceinline__ void dkdv_f32_block(float* smem, int bid, const float
         if constexpr (DELTA_FROM_O) {
             float dsum = 0.f;
 #pragma unroll
-            for (int e = 0; e < EP; ++e) dsum = fmaf(dd[e], oo[e], dsum);
-            dsum = lane_group_sum<8>(dsum);
+            for (int e = 0; e < E; ++e) dsum = fmaf(dd[e], oo[e], dsum);
+            dsum = lane_group_sum<G>(dsum);
             if ((tid & 7) == 0) DLs[tid >> 3] = dsum;
         }
         __syncthreads();

@@ -69,8 +69,11 @@ hipError_t launch_group_sum_f16(const LaunchArgs& a);
 
 hipError_t launch_fwd_f32(const LaunchArgs& a);
 hipError_t launch_bwd_dkdv_f32(const LaunchArgs& a);
-// attn_bwd's fp32 passes: fused into one launch for grids too small to fill the device
+// attn_bwd's passes (one query head per key/value head, or the fp32 grouped form):
+// fused into one launch for grids too small to fill the device
 hipError_t launch_bwd_f32(const LaunchArgs& a);
+hipError_t launch_bwd_bf16(const LaunchArgs& a);
+hipError_t launch_bwd_f16(const LaunchArgs& a);
 hipError_t launch_bwd_dq_f32(const LaunchArgs& a);
 hipError_t launch_bwd_dq_delta_f32(const LaunchArgs& a);
 

@@ -132,8 +132,9 @@ struct RowTile {
 // accumulators start from: -LSE/scale (S - LSE/scale is the exponent of P
 // before the factor scale*log2(e)) and -delta.  Rows past S get -inf, so P is
 // exactly 0 there.  load() only issues the loads; the transform happens in
-// store(), so no wait for the loads is placed at the point of issue.
-template <int ROWS, int NT = 256>
+// store(), so no wait for the loads is placed at the point of issue.  Without
+// DELTA only -LSE/scale is loaded and stored (the caller forms delta).
+template <int ROWS, int NT = 256, bool DELTA = true>
 struct RowStats {
     float l, d;
     bool ok;
@@ -141,15 +142,17 @@ struct RowStats {
                                          int row0, int S, int tid) {
         const int rows = max(0, min(S - row0, ROWS));
         const __amdgpu_buffer_rsrc_t rl = buffer_rsrc(lse + row0, rows * 4);
-        const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(delta + row0, rows * 4);
         l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, tid * 4, 0, 0));
-        d = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, tid * 4, 0, 0));
+        if constexpr (DELTA) {
+            const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(delta + row0, rows * 4);
+            d = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, tid * 4, 0, 0));
+        }
         ok = tid < rows;
     }
     __device__ __forceinline__ void store(float* sa, float* sb, float rscale, int tid) const {
         if (tid < ROWS) {
             sa[tid] = ok ? -l * rscale : -INFINITY;
-            sb[tid] = -d;
+            if constexpr (DELTA) sb[tid] = -d;
         }
     }
 };
