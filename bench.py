@@ -808,9 +808,10 @@ def main():
         # points, so there the backward is timed as one (its dQ and dK/dV passes), and
         # so is the atomic-dQ backward (delta, zero fill, fused pass, dQ conversion),
         # the fp32 backward and the 16-bit D = 64 backward of grids whose 128-row dQ
-        # and dK/dV blocks all fit at two per CU: attn_bwd runs those as one launch
+        # and dK/dV blocks fit in three rounds at two per CU: attn_bwd runs those as
+        # one launch
         cus = torch.cuda.get_device_properties(dev).multi_processor_count
-        one_launch = w.dtype == "f32" or (D == 64 and 2 * -(-S // 128) * B * H <= 2 * cus)
+        one_launch = w.dtype == "f32" or (D == 64 and 2 * -(-S // 128) * B * H <= 6 * cus)
         if grouped or atomic or one_launch:
             names = ("fwd", "bwd")
             calls = (fwd, bwd)

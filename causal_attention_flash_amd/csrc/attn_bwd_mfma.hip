@@ -799,7 +799,8 @@ static hipError_t launch_dq_type(const LaunchArgs& a) {
 // key/value head): blocks below ndq are dQ blocks (128 queries, storing delta), the
 // rest four-wave dK/dV blocks of 128 keys that form each query tile's delta
 // themselves (dkdv_block's DFLY), so the two kinds run side by side instead of one
-// pass after the other on a device that each would leave mostly idle.
+// pass after the other, each of which would leave much of the device idle or end in
+// a tail.
 template <class E>
 __global__ __launch_bounds__(256, 2) void bwd_small_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -821,12 +822,14 @@ __global__ __launch_bounds__(256, 2) void bwd_small_kernel(
 }
 
 // attn_bwd's passes for 16-bit inputs: the one-launch form where it applies (D = 64,
-// one query head per key/value head, and the two kinds of blocks, two per CU, all
-// resident at once), else the dQ pass (forming delta) and then the dK/dV pass.
+// one query head per key/value head, and the two kinds of blocks, two per CU, within
+// three rounds of the device), else the dQ pass (forming delta) and then the dK/dV
+// pass.  Measured: B=8 H=6 S=256 (one round) 0.0303 -> 0.0186 ms per step, B=8 H=12
+// S=1024 (three rounds) 2% faster, B=4 H=16 S=2048 (four rounds) 3.4% slower.
 template <class E>
 static hipError_t launch_bwd_type(const LaunchArgs& a) {
     const int64_t nq = (a.S + 127) / 128;  // 128-query dQ blocks and 128-key dK/dV blocks
-    if (a.D == 64 && a.H == a.Hkv && 2 * nq * a.BH <= 2 * (int64_t)cu_count()) {
+    if (a.D == 64 && a.H == a.Hkv && 2 * nq * a.BH <= 6 * (int64_t)cu_count()) {
         const int ndq = (int)(nq * a.BH);
         hipLaunchKernelGGL((bwd_small_kernel<E>), dim3(2 * ndq), dim3(256), 0, a.stream, (const uint16_t*)a.q,
                            (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.o_in,

@@ -167,9 +167,9 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D, attn
  *                      caller; clobbered; must not overlap any other argument.
  * Enqueues, in order: the dQ pass, which also forms delta = rowsum(dO o O) (fp32)
  * in the workspace, then the dK/dV pass, which reads it; for grids too small to
- * fill the device (fp32 grids whose blocks cover it less than twice, 16-bit D = 64
- * grids with one query head per key/value head whose dQ and dK/dV blocks all fit
- * at once) one launch runs the dQ blocks and dK/dV blocks side by side, the latter
+ * fill the device well (fp32 grids whose blocks cover it less than twice, 16-bit
+ * D = 64 grids with one query head per key/value head whose dQ and dK/dV blocks fit
+ * in three rounds) one launch runs the dQ blocks and dK/dV blocks side by side, the latter
  * forming delta themselves in the dQ pass's order: the same bits either way.
  * Source: Forge RESEARCH.md §6 (the "D term" paragraph and the two-kernel,
  * atomic-free backward that recomputes P = exp(S - L) per tile).

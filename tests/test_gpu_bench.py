@@ -44,7 +44,8 @@ def test_bench_training_step():
         st = d[k]
         assert st["n"] == 5 and st["min"] <= st["median"] <= st["p95"]
         assert st["ci95_median"][0] <= st["median"] <= st["ci95_median"][1]
-    assert set(d["kernel_ms"]) == {"fwd", "bwd_dq", "bwd_dkdv"}
+    # this grid's backward runs as one launch (dQ and dK/dV blocks side by side)
+    assert set(d["kernel_ms"]) == {"fwd", "bwd"}
     st = d["step_ms_bwd_first"]
     assert st["n"] == 5 and st["min"] <= st["median"] <= st["p95"]
     assert 0.3 < d["clock_ghz"]["mean"] < 3.0, d["clock_ghz"]
@@ -53,6 +54,15 @@ def test_bench_training_step():
     assert rf["peak_at_clock"] > 0 and abs(rf["frac_at_clock"] - rf["achieved"] / rf["peak_at_clock"]) < 1e-3
     # the second, fresh session reproduced this session's outputs bit for bit
     assert len(d["sessions"]) == 2 and d["sessions"][1]["receipt"] == "PASS", d["sessions"]
+
+
+def test_bench_headline_passes_timed_apart():
+    """At the headline workload attn_bwd runs the dQ and dK/dV passes one after the
+    other, and the bench times each (the roofline's dominant kernel is one of them)."""
+    d = run_bench("--workload", "gpt205m_bf16", "--sessions", "1")
+    check_common(d, "gpt205m_bf16")
+    assert set(d["kernel_ms"]) == {"fwd", "bwd_dq", "bwd_dkdv"}
+    assert d["roofline"]["kernel"] in d["kernel_ms"]
 
 
 def test_bench_receipt_against_the_oracle():
