@@ -201,10 +201,11 @@ __device__ __forceinline__ void dkdv_block(
                 float p = 0.f;
 #pragma unroll
                 for (int step = 0; step < QT::CPR / 2; ++step) {
+                    // the chain so far, from lane j - 2 (DPP row_shr:2)
                     const float prev = step == 0 ? 0.f
                                                  : __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
                                                        0, __builtin_bit_cast(int, p), 0x112, 0xF, 0xF, false));
-                    const float mine = dot8<E>(as_op<E>(ot.r[i]), as_op<E>(otv.r[i]), prev);  // row_shr:2
+                    const float mine = dot8<E>(as_op<E>(ot.r[i]), as_op<E>(otv.r[i]), prev);
                     p = (j >> 1) == step ? mine : p;
                 }
                 const float other = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
@@ -595,11 +596,11 @@ struct DqCfg {
     static constexpr int DB = HeadDim<D>::DB;
 };
 
-// DELTA_FROM_O: delta = rowsum(dO o O) is formed here, from the O rows of this
-// wave's queries (fp32 sums of bf16 products), and written to DeltaOut for the
-// dK/dV pass; otherwise delta is read from Delta.
 // One dQ workgroup: query block `bid` in heavy-first order over the BH heads, its
-// K/V tiles in `smem` (Cfg::SMEM_ELEMS elements).
+// K/V tiles in `smem` (Cfg::SMEM_ELEMS elements).  DELTA_FROM_O: delta =
+// rowsum(dO o O) is formed here, from the O rows of this wave's queries (fp32 sums
+// of bf16 products), and written to DeltaOut for the dK/dV pass; otherwise delta is
+// read from Delta.
 template <class E, int D, int BNK, int NW, bool DELTA_FROM_O>
 __device__ __forceinline__ void dq_block(
     uint16_t* smem, int bid, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
