@@ -331,6 +331,20 @@ struct WorkItem {
 };
 __device__ __forceinline__ WorkItem heavy_first(int bid, int BH) { return {bid % BH, bid / BH}; }
 
+// Issue priority of a causal workgroup by its share of the work: the heaviest
+// quarter of the ranks (rank 0 heaviest, of nblk) 3, the next 2, then 1, the
+// lightest quarter 0.  The heavy blocks are the grid's critical path; the waves of
+// lighter ones sharing their SIMDs take the issue slots they leave.
+__device__ __forceinline__ void weight_priority(int rank, int nblk) {
+    const int p = 3 - (4 * rank) / nblk;
+    if (p >= 3)
+        __builtin_amdgcn_s_setprio(3);
+    else if (p == 2)
+        __builtin_amdgcn_s_setprio(2);
+    else if (p == 1)
+        __builtin_amdgcn_s_setprio(1);
+}
+
 // Grouped key/value heads: with H query heads per batch entry sharing H / GQ
 // key/value heads, query head qh (index over batch x H) reads key/value head
 // (qh / H) * (H / GQ) + (qh % H) / GQ (index over batch x H / GQ).  GQ = 1 is

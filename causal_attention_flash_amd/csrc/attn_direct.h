@@ -161,4 +161,48 @@ struct DOffsets {
     }
 };
 
+// Stores a wave's 32 x D output tile held in C registers (lane (n, h): row n,
+// columns 32db + 8g + 4h + 0..3 in registers 4g .. 4g+3 of acc[db]), times the
+// lane's s and rounded to E, to rows row0 .. row0+31 of the [S][D] matrix g (rows
+// at or beyond S are skipped).  The tile goes through the wave's LDS scratch w
+// (SCR elements, written and read by this wave only) in passes of up to 32 rows in
+// DTile's swizzled layout, so that each global store instruction writes 64
+// consecutive 16-byte chunks (whole rows) instead of 16 bytes of each of 32 rows.
+// Returns with the wave's LDS reads of w complete.
+template <class E, int D, int SCR>
+__device__ __forceinline__ void store_tile_rows(uint16_t* w, const f32x16 (&acc)[HeadDim<D>::DB], float s,
+                                                uint16_t* __restrict__ g, int row0, int S, int lane) {
+    constexpr int CPR = D / 8;
+    constexpr int PR = 32 * DTile<32, D, 1>::RS <= SCR ? 32 : 16;  // rows per pass
+    using T = DTile<PR, D, 1>;
+    static_assert(T::ELEMS <= SCR, "the scratch holds a pass");
+    constexpr int CH = PR * CPR;  // 16-byte chunks per pass
+    const int n = lane & 31, h = lane >> 5;
+    const int rows = max(0, min(S - row0, 32));
+#pragma unroll
+    for (int p = 0; p < 32 / PR; ++p) {
+        if (n >= p * PR && n < (p + 1) * PR) {
+#pragma unroll
+            for (int db = 0; db < HeadDim<D>::DB; ++db)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (!HeadDim<D>::live(db, q)) continue;
+                    u32x2 u;
+                    u[0] = E::pack2(acc[db][4 * q + 0] * s, acc[db][4 * q + 1] * s);
+                    u[1] = E::pack2(acc[db][4 * q + 2] * s, acc[db][4 * q + 3] * s);
+                    *reinterpret_cast<u32x2*>(w + T::at(n - p * PR, db * 32 + 8 * q + 4 * h)) = u;
+                }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        uint16_t* gr = g + (size_t)(row0 + p * PR) * D;
+#pragma unroll
+        for (int i = 0; i < (CH + 63) / 64; ++i) {
+            const int e = i * 64 + lane, row = e / CPR, c = e % CPR;
+            if ((CH % 64 == 0 || e < CH) && p * PR + row < rows)
+                *reinterpret_cast<u32x4*>(gr + (size_t)e * 8) = lds16(w + T::at(row, 8 * c));
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the scratch may be written again
+    }
+}
+
 }  // namespace attn
