@@ -365,7 +365,13 @@ __device__ __forceinline__ void dkdv_block(
         __syncthreads();
     }
 
-    if (PARTIAL && key < S) {
+    if constexpr (PARTIAL && D == 64) {
+        // as below, for the fp32 partials of grouped key/value heads
+        constexpr int SCR = 2 * Cfg::BUF_ELEMS / NW / 8 * 8;
+        uint16_t* w = smem + wave * SCR;
+        if (WANT_DK) store_tile_rows_f32<D, SCR>(w, dkacc, scale, dKp + base, kw0, S, lane);
+        if (WANT_DV) store_tile_rows_f32<D, SCR>(w, dvacc, 1.f, dVp + base, kw0, S, lane);
+    } else if (PARTIAL && key < S) {
         float* dKr = dKp + base + (size_t)key * D;
         float* dVr = dVp + base + (size_t)key * D;
 #pragma unroll

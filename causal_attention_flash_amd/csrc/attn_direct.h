@@ -205,4 +205,42 @@ __device__ __forceinline__ void store_tile_rows(uint16_t* w, const f32x16 (&acc)
     }
 }
 
+// The same for fp32 outputs (g is an [S][D] fp32 matrix): each lane's four values of a
+// group are one 16-byte chunk of its row, laid out as a row of 2D 16-bit elements.
+template <int D, int SCR>
+__device__ __forceinline__ void store_tile_rows_f32(uint16_t* w, const f32x16 (&acc)[HeadDim<D>::DB], float s,
+                                                    float* __restrict__ g, int row0, int S, int lane) {
+    constexpr int CPR = D / 4;
+    constexpr int PR = 32 * DTile<32, 2 * D, 1>::RS <= SCR ? 32 : 16;  // rows per pass
+    using T = DTile<PR, 2 * D, 1>;
+    static_assert(T::ELEMS <= SCR, "the scratch holds a pass");
+    constexpr int CH = PR * CPR;
+    const int n = lane & 31, h = lane >> 5;
+    const int rows = max(0, min(S - row0, 32));
+#pragma unroll
+    for (int p = 0; p < 32 / PR; ++p) {
+        if (n >= p * PR && n < (p + 1) * PR) {
+#pragma unroll
+            for (int db = 0; db < HeadDim<D>::DB; ++db)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (!HeadDim<D>::live(db, q)) continue;
+                    f32x4 v;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = acc[db][4 * q + i] * s;
+                    *reinterpret_cast<f32x4*>(w + T::at(n - p * PR, 2 * (db * 32 + 8 * q + 4 * h))) = v;
+                }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        float* gr = g + (size_t)(row0 + p * PR) * D;
+#pragma unroll
+        for (int i = 0; i < (CH + 63) / 64; ++i) {
+            const int e = i * 64 + lane, row = e / CPR, c = e % CPR;
+            if ((CH % 64 == 0 || e < CH) && p * PR + row < rows)
+                *reinterpret_cast<u32x4*>(gr + (size_t)e * 4) = lds16(w + T::at(row, 8 * c));
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the scratch may be written again
+    }
+}
+
 }  // namespace attn
