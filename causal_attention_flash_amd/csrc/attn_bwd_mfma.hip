@@ -366,7 +366,8 @@ __device__ __forceinline__ void dkdv_block(
     }
 
     if constexpr (PARTIAL && D == 64) {
-        // as below, for the fp32 partials of grouped key/value heads
+        // as below, for the fp32 partials of grouped key/value heads (rows of D = 64
+        // fp32 values fit the swizzled layout; the other head dims store directly)
         constexpr int SCR = 2 * Cfg::BUF_ELEMS / NW / 8 * 8;
         uint16_t* w = smem + wave * SCR;
         if (WANT_DK) store_tile_rows_f32<D, SCR>(w, dkacc, scale, dKp + base, kw0, S, lane);
@@ -390,13 +391,12 @@ __device__ __forceinline__ void dkdv_block(
                 if (WANT_DV) *reinterpret_cast<f32x4*>(dVr + d) = fv;
             }
     }
-    if constexpr (!PARTIAL && D == 64) {
+    if constexpr (!PARTIAL) {
         // The loop's last barrier has passed, so the tile buffers are free: each wave
         // stores dK and dV through its own share of them, whole rows per store
-        // instruction.  (With one workgroup per CU nothing hides this pass's stores;
-        // 16 bytes of 32 rows per instruction measured 5% slower at D = 64.  At D = 128
-        // the same measured no gain, and D = 80, 96 have no registers to spare: they
-        // keep the direct stores.)
+        // instruction.  (With one workgroup per CU nothing hides this pass's stores:
+        // 16 bytes of 32 rows per instruction measured 5% slower at B=4 H=16 S=2048
+        // D=64, 1-4% at D = 80, 96, 128; the less so the longer a workgroup runs.)
         constexpr int SCR = 2 * Cfg::BUF_ELEMS / NW / 8 * 8;
         uint16_t* w = smem + wave * SCR;
         if (WANT_DK) store_tile_rows<E, D, SCR>(w, dkacc, scale, dK + kvbase, kw0, S, lane);
