@@ -13,7 +13,11 @@
 //
 // gfx950 mapping:
 // * NW waves per workgroup, split-Q: each wave owns QB blocks of 32 query rows
-//   and never shares row statistics with another wave.
+//   and never shares row statistics with another wave.  Small grids at D = 64
+//   instead split each query block's keys between two waves (FwdCfg::SPLIT): each
+//   takes one 32-key half of every staged 64-key tile, with its own reference
+//   point, and the two partial (m, l, O) are merged through LDS after the loop,
+//   as the online softmax merges any two key ranges.
 // * The score tile is computed transposed, S^T = K Q^T, so each lane owns one
 //   query (C column) and the row max / row sum are per-lane reductions (the sum
 //   on the matrix cores, see FwdCfg::MFMA_ROW_SUM) plus one exchange between the
@@ -74,12 +78,18 @@ struct QkOps<E, D, true> {
 // the V^T operands, two score sets) pass 256 VGPRs at D = 80, 96 and 128 and
 // leave one wave per SIMD; 32-key tiles fit two there (measured 10-25% faster)
 // and three at D = 64 (147 VGPRs; 2.5% faster than 64-key tiles at two).
-template <int D, int QB, int NW_, bool QK8 = false, int BN_ = 32>
+template <int D, int QB, int NW_, bool QK8 = false, int BN_ = 32, bool SPLIT_ = false>
 struct FwdCfg {
     static constexpr int NW = NW_;
     static constexpr int NT = NW * 64;
-    static constexpr int BM = NW * 32 * QB;  // queries per workgroup
-    static constexpr int BN = BN_;           // keys per tile
+    // SPLIT: the waves form two key groups: wave w takes the query block w % (NW/2)
+    // and, of each staged key tile, the 32-key half w / (NW/2), so a query block's
+    // keys are shared by two waves whose partial (m, l, O) are merged at the end
+    static constexpr bool SPLIT = SPLIT_;
+    static constexpr int QW = SPLIT ? NW / 2 : NW;  // query blocks per workgroup
+    static constexpr int BM = QW * 32 * QB;  // queries per workgroup
+    static constexpr int BN = BN_;           // keys per staged tile
+    static constexpr int KBW = SPLIT ? 1 : BN / 32;  // 32-key blocks a wave multiplies per tile
     // waves per SIMD the register budget is set for
     static constexpr int WAVES_PER_SIMD = D == 64 && BN == 32 ? 3 : 2;
     using Tile = DTile<BN, D, NW>;           // V tile
@@ -96,7 +106,7 @@ struct FwdCfg {
     // CU, and half as many workgroups, each with the same work, fill it evenly
     // (measured 2-5% faster where the pairs still cover every slot).  Where three
     // workgroups fill a CU (D = 64) pairs leave a third of it idle: 5% slower there.
-    static constexpr bool PAIRABLE = D >= 80 && !QK8;
+    static constexpr bool PAIRABLE = D >= 80 && !QK8 && !SPLIT_;
     // Per-lane row sums of each tile's P on the matrix cores (two 16x16x32 products
     // against a selector, lane_sum_selector) instead of eight v_dot2, which hold the
     // MFMA pipe while they run: bitwise the same sums, 0.5-2% faster at D = 64; at
@@ -105,24 +115,25 @@ struct FwdCfg {
     // the loop masks only a wave's last key tile: a wave's 32 * QB queries must
     // not reach into an earlier tile (else that tile also crosses the diagonal)
     static_assert(32 * QB <= BN, "a wave's queries must fit in one key tile");
+    static_assert(!SPLIT || (BN == 64 && QB == 1 && NW % 2 == 0 && !QK8), "split tiles: two 32-key halves");
 };
 
 // QK8: Q and K hold fp8 (E4M3) bytes and c carries their dequantisation factors.
-template <class E, int D, int QB, int NW, bool QK8, int BN_>
-__global__ __launch_bounds__(NW * 64, (FwdCfg<D, QB, NW, QK8, BN_>::WAVES_PER_SIMD)) void fwd_mfma_kernel(const void* __restrict__ Q,
+template <class E, int D, int QB, int NW, bool QK8, int BN_, bool SPLIT>
+__global__ __launch_bounds__(NW * 64, (FwdCfg<D, QB, NW, QK8, BN_, SPLIT>::WAVES_PER_SIMD)) void fwd_mfma_kernel(const void* __restrict__ Q,
                                                        const void* __restrict__ K,
                                                        const uint16_t* __restrict__ V,
                                                        uint16_t* __restrict__ O, float* __restrict__ LSE,
                                                        int S, int nblk, int BH, int H, int GQ, float c,
                                                        int causal, int paired) {
-    using Cfg = FwdCfg<D, QB, NW, QK8, BN_>;
+    using Cfg = FwdCfg<D, QB, NW, QK8, BN_, SPLIT>;
     using V8 = typename E::V8;
     using QK = QkOps<E, D, QK8>;
     using QOp = typename QK::Op;
     constexpr int BM = Cfg::BM, BN = Cfg::BN, TE = Cfg::TE, TK = Cfg::TK, NB = Cfg::NB, P = Cfg::P;
     // loads per wave of one K tile plus one V tile
     constexpr int LOADS2 = Cfg::KTile::LOADS + Cfg::Tile::LOADS;
-    constexpr int KB = BN / 32;  // 32-key blocks per tile
+    constexpr int KB = Cfg::KBW;  // 32-key blocks this wave multiplies per tile
     constexpr int QS = QK::STEPS, DB = Cfg::DB;
     // K[NB], V[NB]
     __shared__ __attribute__((aligned(16))) uint16_t smem[NB * (TK + TE)];
@@ -153,12 +164,17 @@ __global__ __launch_bounds__(NW * 64, (FwdCfg<D, QB, NW, QK8, BN_>::WAVES_PER_SI
         const int tid = threadIdx.x;
         const int lane = tid & 63, wave = tid >> 6;
         const int h = lane >> 5, n = lane & 31;
-        const int qw0 = q0 + wave * 32 * QB;
+        const int qg = Cfg::SPLIT ? wave % Cfg::QW : wave;  // query block of the workgroup
+        const int koff = Cfg::SPLIT ? 32 * (wave / Cfg::QW) : 0;  // this wave's rows of a tile
+        const int qw0 = q0 + qg * 32 * QB;
 
         const int kend = causal ? min(S, q0 + BM) : S;
         const int ntiles = (kend + BN - 1) / BN;  // tiles the workgroup stages
-        // tiles this wave multiplies: the causal ones up to its last query
-        const int nw = causal ? min(ntiles, (qw0 + 32 * QB - 1) / BN + 1) : ntiles;
+        // tiles this wave multiplies: the causal ones up to its last query; split:
+        // those whose half of the tile starts before the wave's key limit
+        const int klim = causal ? min(S, qw0 + 32 * QB) : S;
+        const int nw = Cfg::SPLIT ? max(0, (klim - koff + BN - 1) / BN)
+                                  : causal ? min(ntiles, (qw0 + 32 * QB - 1) / BN + 1) : ntiles;
 
         auto kbuf = [&](int t) { return smem + (t % NB) * TK; };
         auto vbuf = [&](int t) { return smem + NB * TK + (t % NB) * TE; };
@@ -228,7 +244,7 @@ __global__ __launch_bounds__(NW * 64, (FwdCfg<D, QB, NW, QK8, BN_>::WAVES_PER_SI
                         const uint16_t* r = Ks + kb * 32 * Cfg::KTile::RS;
                         kf[kb][st] = Fp8E4M3::join(lds16(r + k8[st][0]), lds16(r + k8[st][1]));
                     } else {
-                        kf[kb][st] = lo.template row_op<E>(Ks, kb * 32, st);
+                        kf[kb][st] = lo.template row_op<E>(Ks, koff + kb * 32, st);
                     }
                 }
         };
@@ -256,17 +272,17 @@ __global__ __launch_bounds__(NW * 64, (FwdCfg<D, QB, NW, QK8, BN_>::WAVES_PER_SI
             QOp kf[KB][QS];
             if constexpr (NEXT) load_k(kf, t + 1);
             // V^T operands, read transposed from the V tile (asynchronous: used after lds_wait)
-            i16x4 vr[BN / 16][DB][2];
+            i16x4 vr[KB * 2][DB][2];
             {
                 const uint16_t* Vs = vbuf(t);
     #pragma unroll
-                for (int ks = 0; ks < BN / 16; ++ks)
+                for (int ks = 0; ks < KB * 2; ++ks)
     #pragma unroll
-                    for (int db = 0; db < DB; ++db) lo.tr_async(Vs, ks * 16, db, vr[ks][db]);
+                    for (int db = 0; db < DB; ++db) lo.tr_async(Vs, koff + ks * 16, db, vr[ks][db]);
             }
 
             // ---- mask (raw scores; only a wave's last tile)
-            const int k0 = t * BN;
+            const int k0 = t * BN + koff;
             if constexpr (MASK) {
     #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
@@ -289,7 +305,7 @@ __global__ __launch_bounds__(NW * 64, (FwdCfg<D, QB, NW, QK8, BN_>::WAVES_PER_SI
             // multiplies, so numerator and denominator of O = (P V) / l carry the
             // same rounding (a row whose weight sits on one key reproduces that
             // key's V row).  The raw scores stay in `cur` for the rare path.
-            V8 pf[QB][BN / 16];
+            V8 pf[QB][KB * 2];
             float ls[QB];
             auto probs = [&]() {
     #pragma unroll
@@ -350,15 +366,15 @@ __global__ __launch_bounds__(NW * 64, (FwdCfg<D, QB, NW, QK8, BN_>::WAVES_PER_SI
             for (int qb = 0; qb < QB; ++qb) {
                 l[qb] += ls[qb];
             }
-            lds_wait(reinterpret_cast<i16x4 (&)[(BN / 16) * DB * 2]>(vr));
-            V8 vf[BN / 16][DB];
+            lds_wait(reinterpret_cast<i16x4 (&)[(KB * 2) * DB * 2]>(vr));
+            V8 vf[KB * 2][DB];
     #pragma unroll
-            for (int ks = 0; ks < BN / 16; ++ks)
+            for (int ks = 0; ks < KB * 2; ++ks)
     #pragma unroll
                 for (int db = 0; db < DB; ++db) vf[ks][db] = tr_join<E>(vr[ks][db]);
             // ---- O^T += V^T P^T
     #pragma unroll
-            for (int ks = 0; ks < BN / 16; ++ks)
+            for (int ks = 0; ks < KB * 2; ++ks)
     #pragma unroll
                 for (int db = 0; db < DB; ++db)
     #pragma unroll
@@ -411,6 +427,37 @@ __global__ __launch_bounds__(NW * 64, (FwdCfg<D, QB, NW, QK8, BN_>::WAVES_PER_SI
         // no load may still be writing this workgroup's LDS when it exits
         wait_vmcnt<0>();
 
+        if constexpr (Cfg::SPLIT) {
+            // Merge the two key groups of each query block through LDS (the tile
+            // buffers are free once every wave has passed this barrier): the second
+            // group's waves store m, their lane's share of l and O; the first group's
+            // waves rescale both to the larger reference point and add.  A group with
+            // no tiles holds m = -FLT_MAX, l = 0, O = 0 and adds nothing.
+            constexpr int ITEMS = 2 + DB * 16;
+            static_assert(Cfg::QW * ITEMS * 64 * 4 <= (int)sizeof(smem), "the merge fits in the tile buffers");
+            float* mb = reinterpret_cast<float*>(smem) + qg * ITEMS * 64 + lane;
+            __syncthreads();
+            if (koff != 0) {
+                mb[0] = m[0];
+                mb[64] = l[0];
+    #pragma unroll
+                for (int db = 0; db < DB; ++db)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) mb[(2 + db * 16 + r) * 64] = oacc[0][db][r];
+            }
+            __syncthreads();
+            if (koff != 0) continue;
+            const float m1 = mb[0], l1 = mb[64];
+            const float mn = fmaxf(m[0], m1);
+            const float f0 = fast_exp2(m[0] - mn), f1 = fast_exp2(m1 - mn);
+            m[0] = mn;
+            l[0] = l[0] * f0 + l1 * f1;
+    #pragma unroll
+            for (int db = 0; db < DB; ++db)
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[0][db][r] = oacc[0][db][r] * f0 + mb[(2 + db * 16 + r) * 64] * f1;
+        }
+
         // ---- epilogue: O = O / l (l == 0 -> 0), LSE = (m + log2 l) * ln 2
         uint16_t* Oh = O + base;
         float* Lh = LSE + (size_t)head * S;
@@ -437,9 +484,9 @@ __global__ __launch_bounds__(NW * 64, (FwdCfg<D, QB, NW, QK8, BN_>::WAVES_PER_SI
 
 }
 
-template <class E, int D, int QB, int NW, bool QK8, int BN>
+template <class E, int D, int QB, int NW, bool QK8, int BN, bool SPLIT = false>
 static hipError_t launch_fwd(const LaunchArgs& a) {
-    using Cfg = FwdCfg<D, QB, NW, QK8, BN>;
+    using Cfg = FwdCfg<D, QB, NW, QK8, BN, SPLIT>;
     const int nblk = (int)((a.S + Cfg::BM - 1) / Cfg::BM);
     // pairs when one query block per workgroup would not fit in one round of the
     // device's workgroup slots (CUs x workgroups per CU) and the pairs still cover
@@ -451,7 +498,7 @@ static hipError_t launch_fwd(const LaunchArgs& a) {
                            : 0;
     const int64_t total = (int64_t)(paired ? (nblk + 1) / 2 : nblk) * a.BH;
     if (total > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((fwd_mfma_kernel<E, D, QB, NW, QK8, BN>), dim3((unsigned)total), dim3(Cfg::NT), 0, a.stream,
+    hipLaunchKernelGGL((fwd_mfma_kernel<E, D, QB, NW, QK8, BN, SPLIT>), dim3((unsigned)total), dim3(Cfg::NT), 0, a.stream,
                        a.q, a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, (int)a.S, nblk, (int)a.BH,
                        (int)a.H, (int)(a.H / a.Hkv), a.scale * a.qk_descale * kLog2e, a.causal, paired);
     return hipGetLastError();
@@ -459,7 +506,20 @@ static hipError_t launch_fwd(const LaunchArgs& a) {
 
 template <class E>
 static hipError_t launch_fwd_type(const LaunchArgs& a) {
-    if (a.D == 64) return launch_fwd<E, 64, 1, 4, false, 32>(a);
+    if (a.D == 64) {
+        // Split key groups (64-query workgroups, each staged key tile shared by two
+        // waves instead of four) where the unsplit grid fills at most two thirds of
+        // one round of the device's workgroup slots: such a grid is bound by its
+        // longest waves, whose tile chains the split halves.  Forward, measured:
+        // B=8 H=6 S=256 7.7 -> 6.2 us, B=4 H=12 S=1024 18.7 -> 13.9, B=1 H=16 S=2048
+        // 31.9 -> 20.1, B=2 H=16 S=2048 32.9 -> 27.5; fuller grids lose more to the
+        // halved tile sharing than they gain (B=6 H=12 S=1024 +3.5%, B=8 H=12 S=1024
+        // +6%, B=4 H=16 S=2048 +6%, B=8 H=16 S=2048 +19%).
+        using Cfg = FwdCfg<64, 1, 4, false, 32>;
+        const int64_t slots = (int64_t)cu_count() * Cfg::WAVES_PER_SIMD * 4 / Cfg::NW;
+        if (3 * ((a.S + Cfg::BM - 1) / Cfg::BM) * a.BH <= 2 * slots) return launch_fwd<E, 64, 1, 4, false, 64, true>(a);
+        return launch_fwd<E, 64, 1, 4, false, 32>(a);
+    }
     if (a.D == 80) return launch_fwd<E, 80, 1, 4, false, 32>(a);
     if (a.D == 96) return launch_fwd<E, 96, 1, 4, false, 32>(a);
     if (a.D == 128) return launch_fwd<E, 128, 1, 4, false, 32>(a);

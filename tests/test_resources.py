@@ -27,12 +27,13 @@ ALLOWED_SPILLS = {
 
 # waves per SIMD the hot kernels must keep
 OCCUPANCY = {
-    "fwd_mfma_kernel<Bf16, 64, 1, 4, false, 32>": 3,
-    "fwd_mfma_kernel<Bf16, 80, 1, 4, false, 32>": 2,
-    "fwd_mfma_kernel<Bf16, 96, 1, 4, false, 32>": 2,
-    "fwd_mfma_kernel<Bf16, 128, 1, 4, false, 32>": 2,
-    "fwd_mfma_kernel<Bf16, 64, 1, 4, true, 64>": 2,
-    "fwd_mfma_kernel<Bf16, 128, 1, 4, true, 32>": 2,
+    "fwd_mfma_kernel<Bf16, 64, 1, 4, false, 32, false>": 3,
+    "fwd_mfma_kernel<Bf16, 64, 1, 4, false, 64, true>": 3,
+    "fwd_mfma_kernel<Bf16, 80, 1, 4, false, 32, false>": 2,
+    "fwd_mfma_kernel<Bf16, 96, 1, 4, false, 32, false>": 2,
+    "fwd_mfma_kernel<Bf16, 128, 1, 4, false, 32, false>": 2,
+    "fwd_mfma_kernel<Bf16, 64, 1, 4, true, 64, false>": 2,
+    "fwd_mfma_kernel<Bf16, 128, 1, 4, true, 32, false>": 2,
     "bwd_dq_mfma_kernel<Bf16, 64, 64, 4, true>": 3,
     "bwd_dq_mfma_kernel<Bf16, 128, 32, 4, true>": 2,
     "bwd_dkdv_mfma_kernel<Bf16, 64, 64, 8, false, false, 0>": 2,
