@@ -74,6 +74,26 @@ def test_edge_shapes(device, S, D, dtype, causal):
     gu.check(gu.errors(gpu, ref, all_heads(w)), dtype, f"S={S} D={D} {dtype} causal={causal}")
 
 
+@pytest.mark.parametrize("B,H,S,dtype,causal", [
+    (2, 16, 2048, "bf16", True),   # 512 unsplit blocks: 2/3 of 768 slots -> split
+    (4, 12, 1024, "f16", True),    # 384 -> split
+    (4, 12, 1000, "bf16", False),  # 384, dense, ragged 64-key tail -> split
+    (6, 12, 1024, "bf16", True),   # 576 -> the unsplit kernel
+])
+def test_split_key_forward_threshold(device, B, H, S, dtype, causal):
+    """The D = 64 forward splits each query block's keys between two waves (merged
+    through LDS) where the 128-query grid fills at most 2/3 of the device's 768
+    workgroup slots (256 CUs x 3): shapes on both sides of that line, sampled heads
+    against the oracle (every element of each sampled head)."""
+    w = si.Workload("split", B, H, S, 64, dtype, 1.0, 1.0, 0.1, causal)
+    print(f"\n[split threshold] B={B} H={H} S={S} {dtype} causal={causal}", flush=True)
+    x = si.make_inputs(w, seed=B * 1000 + S)
+    gpu = gu.run_gpu(x, w, device, causal=causal)
+    heads = [(0, 0), (B // 2, H // 2), (B - 1, H - 1)]
+    ref = oracle_heads(x, w, heads, causal=causal)
+    gu.check(gu.errors(gpu, ref, heads), dtype, f"split threshold B={B} H={H} S={S}")
+
+
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("D", [80, 96])
