@@ -13,8 +13,8 @@
 //
 // gfx950 mapping:
 // * NW waves per workgroup, split-Q: each wave owns QB blocks of 32 query rows
-//   and never shares row statistics with another wave.  Small grids at D = 64
-//   instead split each query block's keys between two waves (FwdCfg::SPLIT): each
+//   and never shares row statistics with another wave.  Small grids instead
+//   split each query block's keys between two waves (FwdCfg::SPLIT): each
 //   takes one 32-key half of every staged 64-key tile, with its own reference
 //   point, and the two partial (m, l, O) are merged through LDS after the loop,
 //   as the online softmax merges any two key ranges.
@@ -504,25 +504,34 @@ static hipError_t launch_fwd(const LaunchArgs& a) {
     return hipGetLastError();
 }
 
+// The forward for one head dim: split key groups (64-query workgroups, each staged
+// key tile shared by two waves instead of four) where the unsplit grid is small
+// against one round of the device's workgroup slots, since such a grid is bound by
+// its longest waves, whose tile chains the split halves; else one query block (or,
+// from D = 80 up, a pair of blocks) per workgroup.  The line, measured (forward):
+// at D = 64 (three workgroups per CU) two thirds of a round: B=2 H=16 S=2048 (2/3)
+// 32.9 -> 27.5 us, B=4 H=12 S=1024 18.7 -> 13.9, B=8 H=6 S=256 7.7 -> 6.2, but
+// B=6 H=12 S=1024 (3/4) +3.5%, B=8 H=12 S=1024 (one round) +6%, B=4 H=16 S=2048 +6%,
+// B=8 H=16 S=2048 +19%; from D = 80 up (two per CU) one round: D = 128 B=1 H=8
+// S=4096 (1/2) 77.9 -> 55.9 us, B=1 H=4 S=8191 148.9 -> 105.1, B=1 H=24 S=2048 (3/4)
+// 46.1 -> 39.8, B=1 H=16 S=4096 (one round) 91.5 -> 86.2, D = 80 B=1 H=24 S=2048
+// 36.1 -> 29.7, but B=2 H=32 S=2048 (two rounds, paired) +17%.
+template <class E, int D>
+static hipError_t launch_fwd_dim(const LaunchArgs& a) {
+    using Cfg = FwdCfg<D, 1, 4, false, 32>;
+    const int64_t slots = (int64_t)cu_count() * Cfg::WAVES_PER_SIMD * 4 / Cfg::NW;
+    const int64_t blocks = (a.S + Cfg::BM - 1) / Cfg::BM * a.BH;
+    const bool split = D == 64 ? 3 * blocks <= 2 * slots : blocks <= slots;
+    if (split) return launch_fwd<E, D, 1, 4, false, 64, true>(a);
+    return launch_fwd<E, D, 1, 4, false, 32>(a);
+}
+
 template <class E>
 static hipError_t launch_fwd_type(const LaunchArgs& a) {
-    if (a.D == 64) {
-        // Split key groups (64-query workgroups, each staged key tile shared by two
-        // waves instead of four) where the unsplit grid fills at most two thirds of
-        // one round of the device's workgroup slots: such a grid is bound by its
-        // longest waves, whose tile chains the split halves.  Forward, measured:
-        // B=8 H=6 S=256 7.7 -> 6.2 us, B=4 H=12 S=1024 18.7 -> 13.9, B=1 H=16 S=2048
-        // 31.9 -> 20.1, B=2 H=16 S=2048 32.9 -> 27.5; fuller grids lose more to the
-        // halved tile sharing than they gain (B=6 H=12 S=1024 +3.5%, B=8 H=12 S=1024
-        // +6%, B=4 H=16 S=2048 +6%, B=8 H=16 S=2048 +19%).
-        using Cfg = FwdCfg<64, 1, 4, false, 32>;
-        const int64_t slots = (int64_t)cu_count() * Cfg::WAVES_PER_SIMD * 4 / Cfg::NW;
-        if (3 * ((a.S + Cfg::BM - 1) / Cfg::BM) * a.BH <= 2 * slots) return launch_fwd<E, 64, 1, 4, false, 64, true>(a);
-        return launch_fwd<E, 64, 1, 4, false, 32>(a);
-    }
-    if (a.D == 80) return launch_fwd<E, 80, 1, 4, false, 32>(a);
-    if (a.D == 96) return launch_fwd<E, 96, 1, 4, false, 32>(a);
-    if (a.D == 128) return launch_fwd<E, 128, 1, 4, false, 32>(a);
+    if (a.D == 64) return launch_fwd_dim<E, 64>(a);
+    if (a.D == 80) return launch_fwd_dim<E, 80>(a);
+    if (a.D == 96) return launch_fwd_dim<E, 96>(a);
+    if (a.D == 128) return launch_fwd_dim<E, 128>(a);
     return hipErrorInvalidValue;
 }
 

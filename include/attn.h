@@ -101,11 +101,12 @@ typedef enum attn_status {
  *   causal  : 1 = query i sees keys j <= i; 0 = every key.
  * Source: Forge RESEARCH.md §6 (online-softmax recurrence, divide by the row sum
  * once after the loop, L = m + log l saved per row).
- * Summation order: at D = 64, grids of few query blocks (B*H*ceil(S/128) up to 2/3
- * of the device's workgroup slots) split each block's keys between two waves and
- * merge the two partial softmax states; a head's O and LSE can therefore differ in
- * the last bits between calls whose B*H or S put them on different sides of that
- * line (both within the accuracy the tests hold them to).
+ * Summation order: grids of few query blocks (B*H*ceil(S/128) up to 2/3 of the
+ * device's workgroup slots at D = 64, up to all of them from D = 80 up) split each
+ * block's keys between two waves and merge the two partial softmax states; a head's
+ * O and LSE can therefore differ in the last bits between calls whose B*H or S put
+ * them on different sides of that line (both within the accuracy the tests hold
+ * them to).
  */
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                      int64_t B, int64_t H, int64_t S, int64_t D,

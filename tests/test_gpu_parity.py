@@ -74,24 +74,30 @@ def test_edge_shapes(device, S, D, dtype, causal):
     gu.check(gu.errors(gpu, ref, all_heads(w)), dtype, f"S={S} D={D} {dtype} causal={causal}")
 
 
-@pytest.mark.parametrize("B,H,S,dtype,causal", [
-    (2, 16, 2048, "bf16", True),   # 512 unsplit blocks: 2/3 of 768 slots -> split
-    (4, 12, 1024, "f16", True),    # 384 -> split
-    (4, 12, 1000, "bf16", False),  # 384, dense, ragged 64-key tail -> split
-    (6, 12, 1024, "bf16", True),   # 576 -> the unsplit kernel
+@pytest.mark.parametrize("B,H,S,D,dtype,causal", [
+    (2, 16, 2048, 64, "bf16", True),   # 512 unsplit blocks: 2/3 of 768 slots -> split
+    (4, 12, 1024, 64, "f16", True),    # 384 -> split
+    (4, 12, 1000, 64, "bf16", False),  # 384, dense, ragged 64-key tail -> split
+    (6, 12, 1024, 64, "bf16", True),   # 576 -> the unsplit kernel
+    (1, 16, 4096, 128, "bf16", True),  # 512 of 512 slots (two per CU) -> split
+    (1, 24, 2000, 128, "f16", True),   # 384, ragged -> split
+    (1, 40, 2048, 128, "bf16", True),  # 640 -> the unsplit kernel
+    (2, 12, 1024, 96, "bf16", False),  # 192, dense -> split
+    (1, 24, 2048, 80, "bf16", True),   # 384 -> split
 ])
-def test_split_key_forward_threshold(device, B, H, S, dtype, causal):
-    """The D = 64 forward splits each query block's keys between two waves (merged
-    through LDS) where the 128-query grid fills at most 2/3 of the device's 768
-    workgroup slots (256 CUs x 3): shapes on both sides of that line, sampled heads
-    against the oracle (every element of each sampled head)."""
-    w = si.Workload("split", B, H, S, 64, dtype, 1.0, 1.0, 0.1, causal)
-    print(f"\n[split threshold] B={B} H={H} S={S} {dtype} causal={causal}", flush=True)
-    x = si.make_inputs(w, seed=B * 1000 + S)
+def test_split_key_forward_threshold(device, B, H, S, D, dtype, causal):
+    """The forward splits each query block's keys between two waves (merged through
+    LDS) where the 128-query grid fills at most 2/3 of the device's 768 workgroup
+    slots at D = 64 (256 CUs x 3), at most all 512 from D = 80 up (256 CUs x 2):
+    shapes on both sides of that line, sampled heads against the oracle (every
+    element of each sampled head)."""
+    w = si.Workload("split", B, H, S, D, dtype, 1.0, 1.0, 0.1, causal)
+    print(f"\n[split threshold] B={B} H={H} S={S} D={D} {dtype} causal={causal}", flush=True)
+    x = si.make_inputs(w, seed=B * 1000 + S + D)
     gpu = gu.run_gpu(x, w, device, causal=causal)
     heads = [(0, 0), (B // 2, H // 2), (B - 1, H - 1)]
     ref = oracle_heads(x, w, heads, causal=causal)
-    gu.check(gu.errors(gpu, ref, heads), dtype, f"split threshold B={B} H={H} S={S}")
+    gu.check(gu.errors(gpu, ref, heads), dtype, f"split threshold B={B} H={H} S={S} D={D}")
 
 
 @pytest.mark.parametrize("causal", [True, False])
