@@ -26,6 +26,7 @@
 // registers into padded rows; the dQ pass loads its K and V tiles straight from
 // HBM into swizzled rows (attn_direct.h).
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "attn_launch.h"
@@ -813,6 +814,105 @@ static hipError_t launch_dq_type(const LaunchArgs& a) {
     return hipErrorInvalidValue;
 }
 
+// delta = rowsum(dO o O) for every query row, in exactly the dQ pass's order (lane n
+// of a wave holds row n; lane half h sums chunks d = 16ks + 8h .. +7 in ks order with
+// dot8, then the two halves are added), so that passes reading it produce the same
+// bits as the dQ pass that forms delta itself.  128 rows per 256-thread block.
+template <class E, int D>
+__global__ __launch_bounds__(256) void delta_dq_order_kernel(const uint16_t* __restrict__ O,
+                                                             const uint16_t* __restrict__ dO,
+                                                             float* __restrict__ delta, int64_t rows) {
+    constexpr int KS = HeadDim<D>::KSTEPS;
+    const int lane = threadIdx.x & 63, h = lane >> 5;
+    const int64_t row = (int64_t)blockIdx.x * 128 + (threadIdx.x >> 6) * 32 + (lane & 31);
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+        if (row < rows) {
+            a = ldg16(dO + row * D + ks * 16 + 8 * h);
+            b = ldg16(O + row * D + ks * 16 + 8 * h);
+        }
+        part = dot8<E>(as_op<E>(a), as_op<E>(b), part);
+    }
+    const float dl = half_sum(part);
+    if (h == 0 && row < rows) delta[row] = dl;
+}
+
+// Side streams of the concurrent small-grid backward (below), per device: created on
+// first use with the default priority, never destroyed; one mutex orders the
+// fork-join sequences of calls from several host threads.
+namespace {
+constexpr int kMaxDevices = 64;
+struct SideStreams {
+    hipStream_t st[2] = {nullptr, nullptr};
+    hipEvent_t fork = nullptr;
+    hipEvent_t join[2] = {nullptr, nullptr};
+};
+std::mutex g_side_mu;
+SideStreams g_side[kMaxDevices];
+
+hipError_t side_streams(SideStreams*& out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    SideStreams& sd = g_side[dev];
+    if (sd.fork == nullptr) {
+        for (int i = 0; i < 2; ++i) {
+            if ((e = hipStreamCreateWithFlags(&sd.st[i], hipStreamNonBlocking)) != hipSuccess) return e;
+            if ((e = hipEventCreateWithFlags(&sd.join[i], hipEventDisableTiming)) != hipSuccess) return e;
+        }
+        if ((e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    }
+    out = &sd;
+    return hipSuccess;
+}
+}  // namespace
+
+// The backward of a grid whose dQ pass and dK/dV pass(es) each fit in one round of the
+// device (each alone would leave much of it idle): delta in the dQ pass's order on
+// the caller's stream, then the dQ pass there and the dK/dV pass (at D = 128 its dV
+// and dK passes, each on a side stream of its own) beside it, joined back into the
+// caller's stream.  Same kernels and inputs as the serial passes: the same bits.
+template <class E>
+static hipError_t launch_bwd_concurrent(const LaunchArgs& a) {
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStreams* sd = nullptr;
+    hipError_t e = side_streams(sd);
+    if (e != hipSuccess) return e;
+    const int64_t rows = a.BH * a.S;
+    const unsigned grid = (unsigned)((rows + 127) / 128);
+    const uint16_t* O = (const uint16_t*)a.o_in;
+    const uint16_t* dO = (const uint16_t*)a.dout;
+    if (a.D == 64) hipLaunchKernelGGL((delta_dq_order_kernel<E, 64>), dim3(grid), dim3(256), 0, a.stream, O, dO, a.delta, rows);
+    else if (a.D == 80) hipLaunchKernelGGL((delta_dq_order_kernel<E, 80>), dim3(grid), dim3(256), 0, a.stream, O, dO, a.delta, rows);
+    else if (a.D == 96) hipLaunchKernelGGL((delta_dq_order_kernel<E, 96>), dim3(grid), dim3(256), 0, a.stream, O, dO, a.delta, rows);
+    else hipLaunchKernelGGL((delta_dq_order_kernel<E, 128>), dim3(grid), dim3(256), 0, a.stream, O, dO, a.delta, rows);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    LaunchArgs b = a;
+    b.delta_in = a.delta;
+    const int nside = a.D == 128 ? 2 : 1;
+    if ((e = hipEventRecord(sd->fork, a.stream)) != hipSuccess) return e;
+    for (int i = 0; i < nside; ++i)
+        if ((e = hipStreamWaitEvent(sd->st[i], sd->fork, 0)) != hipSuccess) return e;
+    if ((e = launch_dq_type<E, false>(b)) != hipSuccess) return e;
+    LaunchArgs c = b;
+    c.stream = sd->st[0];
+    if (a.D == 128) {
+        if ((e = launch_dkdv<E, 128, 64, 8, 1>(c)) != hipSuccess) return e;
+        c.stream = sd->st[1];
+        if ((e = launch_dkdv<E, 128, 64, 8, 2>(c)) != hipSuccess) return e;
+    } else if ((e = launch_dkdv_type<E>(c)) != hipSuccess) {
+        return e;
+    }
+    for (int i = 0; i < nside; ++i) {
+        if ((e = hipEventRecord(sd->join[i], sd->st[i])) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(a.stream, sd->join[i], 0)) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 // The whole backward of a small grid in one launch (D = 64, one query head per
 // key/value head): blocks below ndq are dQ blocks (128 queries, storing delta), the
 // rest four-wave dK/dV blocks of 128 keys that form each query tile's delta
@@ -855,6 +955,26 @@ static hipError_t launch_bwd_type(const LaunchArgs& a) {
                            (uint16_t*)a.dv, (int)a.S, (int)nq, (int)nq, ndq, (int)a.BH, (int)a.H, a.scale * kLog2e,
                            a.scale, a.causal);
         return hipGetLastError();
+    }
+    if (a.H == a.Hkv) {
+        // dQ and dK/dV passes side by side where each fits in one round by itself
+        // (the D = 64 grids up to three rounds run as one launch above) and, below
+        // D = 128, the sequences are long enough for the overlap to outweigh the
+        // delta pass and the stream joins; not while the caller's stream is being
+        // captured into a graph.  Backward, measured: D = 128 B=1 H=4 S=8191 724.5 ->
+        // 371.6 us, B=1 H=8 S=4096 373.9 -> 209.2, B=1 H=16 S=2048 198.5 -> 123.1,
+        // B=1 H=16 S=1024 107.5 -> 73.1; D = 96 B=1 H=12 S=2048 124.1 -> 105.4, D = 80
+        // B=1 H=16 S=2048 115.2 -> 102.2; but D = 80 B=4 H=8 S=1024 +3.8%, D = 96 B=2
+        // H=12 S=1024 +1.3%.
+        const int dq_waves = a.D == 64 ? 3 : 2;  // occupancy of the 4-wave dQ blocks
+        const int64_t dq_blocks = (a.S + 127) / 128 * a.BH, dkdv_blocks = (a.S + 255) / 256 * a.BH;
+        if (dq_blocks <= (int64_t)cu_count() * dq_waves && dkdv_blocks <= cu_count() &&
+            (a.D == 128 || a.S >= 2048)) {
+            hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+            const hipError_t ce = hipStreamIsCapturing(a.stream, &cap);
+            if (ce != hipSuccess) return ce;
+            if (cap == hipStreamCaptureStatusNone) return launch_bwd_concurrent<E>(a);
+        }
     }
     const hipError_t e = launch_dq_type<E, true>(a);
     return e != hipSuccess ? e : launch_dkdv_type<E>(a);

@@ -177,6 +177,16 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D, attn
  * D = 64 grids with one query head per key/value head whose dQ and dK/dV blocks fit
  * in three rounds) one launch runs the dQ blocks and dK/dV blocks side by side, the latter
  * forming delta themselves in the dQ pass's order: the same bits either way.
+ * 16-bit grids with one query head per key/value head whose dQ pass and dK/dV
+ * pass(es) each fit in one round of the device (D = 128, or D = 80, 96 with S >= 2048)
+ * form delta first, in the dQ pass's order, then run the dQ pass on `stream` and the
+ * dK/dV pass (at D = 128 its dV and dK passes) on internal streams beside it, joined
+ * back into `stream` with events before the call returns: work enqueued on `stream`
+ * afterwards sees the whole backward, and the results are the same bits.  The
+ * internal streams (default priority) and events are created on the first such call
+ * on a device and kept until the process ends; a mutex orders such calls from several
+ * host threads.  While `stream` is being captured into a graph the passes are
+ * enqueued on `stream` alone.
  * Source: Forge RESEARCH.md §6 (the "D term" paragraph and the two-kernel,
  * atomic-free backward that recomputes P = exp(S - L) per tile).
  */

@@ -313,6 +313,38 @@ def test_stages_equal_attn_bwd_and_deterministic(device):
         assert (a.float() - b.float()).abs().max().item() <= 2e-3
 
 
+@pytest.mark.parametrize("B,H,S,D,dtype", [
+    (1, 2, 8191, 128, "bf16"),
+    (1, 4, 3000, 128, "f16"),
+    (1, 16, 2048, 80, "bf16"),
+    (2, 6, 2500, 96, "bf16"),
+])
+def test_concurrent_backward_equals_stages(device, B, H, S, D, dtype):
+    """Grids whose dQ pass and dK/dV pass(es) each fit in one round of the device run
+    them side by side on two or three streams, after a delta pass in the dQ pass's
+    order: attn_bwd must equal attn_bwd_dq_delta + attn_bwd_dkdv bit for bit (and run
+    to run), and sampled heads match the oracle."""
+    import causal_attention_flash_amd as caf
+    torch = gu.torch_mod()
+    w = si.Workload("conc", B, H, S, D, dtype, 1.0, 1.0, 0.1, True)
+    print(f"\n[concurrent bwd] B={B} H={H} S={S} D={D} {dtype}", flush=True)
+    x = si.make_inputs(w, seed=S + D)
+    q, k, v, do = (gu.to_device(x, n, dtype, device) for n in ("q", "k", "v", "do"))
+    o, lse = caf.attn_fwd(q, k, v)
+    dq, dk, dv = caf.attn_bwd(q, k, v, o, do, lse)
+    dq2, delta2 = caf.attn_bwd_dq_delta(q, k, v, o, do, lse)
+    dk2, dv2 = caf.attn_bwd_dkdv(q, k, v, do, lse, delta2)
+    dq3, dk3, dv3 = caf.attn_bwd(q, k, v, o, do, lse)
+    torch.cuda.synchronize()
+    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2), (dq, dq3), (dk, dk3), (dv, dv3)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    heads = [(0, 0), (B - 1, H - 1)]
+    ref = oracle_heads(x, w, heads)
+    got = {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+    got = {n: t.to(torch.float64).cpu().numpy() for n, t in got.items()}
+    gu.check(gu.errors(got, ref, heads), dtype, f"concurrent bwd B={B} H={H} S={S} D={D}")
+
+
 def test_empty_problem(device):
     import causal_attention_flash_amd as caf
     torch = gu.torch_mod()
