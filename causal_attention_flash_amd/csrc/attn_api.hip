@@ -454,7 +454,9 @@ attn_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const 
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
-    // as attn_bwd: the dQ pass forms delta, then the dK/dV pass reads it
+    // as attn_bwd: the dQ pass forms delta, then the dK/dV pass reads it (always on
+    // `stream`: no internal streams, which would be created on first use)
+    a.side_streams = 0;
     return run_bwd_passes(a, dtype);
 }
 

@@ -956,7 +956,7 @@ static hipError_t launch_bwd_type(const LaunchArgs& a) {
                            a.scale, a.causal);
         return hipGetLastError();
     }
-    if (a.H == a.Hkv) {
+    if (a.H == a.Hkv && a.side_streams) {
         // dQ and dK/dV passes side by side where each fits in one round by itself
         // (the D = 64 grids up to three rounds run as one launch above) and, below
         // D = 128, the sequences are long enough for the overlap to outweigh the

@@ -36,6 +36,9 @@ struct LaunchArgs {
     float qk_descale = 1.f;  // fp8 Q/K: product of their dequantisation factors
     int causal = 1;
     hipStream_t stream = nullptr;
+    // attn_bwd of small grids may run its passes on internal streams created on first
+    // use; attn_bwd_noalloc clears this so that it creates nothing
+    int side_streams = 1;
 };
 
 // Compute units of the current device (looked up once per device; 256 on MI355X

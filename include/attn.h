@@ -205,7 +205,8 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
  * library runs on until the process ends); the call allocates nothing.
  *   Arguments, outputs and errors as attn_bwd, without workspace and
  *   workspace_bytes; B*H*S > ATTN_NOALLOC_MAX_ROWS -> ATTN_ERR_SCRATCH (nothing
- *   enqueued).  Same kernels and results (bitwise) as attn_bwd.
+ *   enqueued).  Same kernels and results (bitwise) as attn_bwd, every pass on
+ *   `stream` (never attn_bwd's internal streams, which would be created on first use).
  *   The stream must belong to the current device.  Every call on one GPU uses
  *   that GPU's single scratch array: calls that overlap on one GPU (other
  *   streams, other threads) race and must be ordered by the caller.  delta is
