@@ -875,6 +875,8 @@ hipError_t side_streams(SideStreams*& out) {
 // the caller's stream, then the dQ pass there and the dK/dV pass (at D = 128 its dV
 // and dK passes, each on a side stream of its own) beside it, joined back into the
 // caller's stream.  Same kernels and inputs as the serial passes: the same bits.
+// With grouped key/value heads the dK/dV passes leave per-query-head partials, which
+// the group sum enqueued after the join adds.
 template <class E>
 static hipError_t launch_bwd_concurrent(const LaunchArgs& a) {
     std::lock_guard<std::mutex> lock(g_side_mu);
@@ -956,7 +958,7 @@ static hipError_t launch_bwd_type(const LaunchArgs& a) {
                            a.scale, a.causal);
         return hipGetLastError();
     }
-    if (a.H == a.Hkv && a.side_streams) {
+    if (a.side_streams) {
         // dQ and dK/dV passes side by side where each fits in one round by itself
         // (the D = 64 grids up to three rounds run as one launch above) and, below
         // D = 128, the sequences are long enough for the overlap to outweigh the

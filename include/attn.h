@@ -177,8 +177,8 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D, attn
  * D = 64 grids with one query head per key/value head whose dQ and dK/dV blocks fit
  * in three rounds) one launch runs the dQ blocks and dK/dV blocks side by side, the latter
  * forming delta themselves in the dQ pass's order: the same bits either way.
- * 16-bit grids with one query head per key/value head whose dQ pass and dK/dV
- * pass(es) each fit in one round of the device (D = 128, or D = 80, 96 with S >= 2048)
+ * 16-bit grids (without the one-launch form) whose dQ pass and dK/dV pass(es) each
+ * fit in one round of the device (D = 128, or D < 128 with S >= 2048)
  * form delta first, in the dQ pass's order, then run the dQ pass on `stream` and the
  * dK/dV pass (at D = 128 its dV and dK passes) on internal streams beside it, joined
  * back into `stream` with events before the call returns: work enqueued on `stream`
@@ -256,6 +256,8 @@ attn_status attn_bwd_atomic(const void* q, const void* k, const void* v, const v
  * head and leaves fp32 partials in the workspace, and a group-sum pass adds them
  * (no atomics; deterministic).  q, o, dout, dq: [B,H,S,D]; k, v, dk, dv:
  * [B,H_kv,S,D]; lse: [B,H,S]; workspace: attn_bwd_gqa_workspace_bytes() bytes.
+ * Small grids run the dQ and dK/dV passes on internal streams as attn_bwd does
+ * (the group sum follows the join on `stream`).
  * attn_bwd is this call with H_kv = H.  Source: Forge RESEARCH.md §6 ("GQA").
  */
 /*
